@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs for Dual-QK decode attention over an INT2 KV cache.
+
+This module draws random numbers and lays them out; it holds none of the
+method's arithmetic (no transform application, quantization, selection or
+attention).  Both the CPU oracle (``oracle/``) and the HIP path
+(``page_set_amd``) consume exactly these buffers.
+
+The workload shapes follow the throughput settings of "Dual-QK: Sharp Queries
+and Flat Keys for Prunable 2-bit KV Caches" (§4.1 and §4.4: single-GPU decode
+up to 128K context, GQA, head_dim 128).  The pages measure on real models and
+benchmark suites that are not available here; seeded Gaussians stand in:
+
+* q, k, v ~ N(0, 1), rounded to bf16 (round to nearest even).
+* k gets 4 outlier channels per KV head (drawn from 1..127 without
+  replacement) scaled by 10, and channel 0 offset by +3, before rounding.
+* One transform pair per KV head (§3.1: "each layer and KV head uses a fixed
+  transform pair"): T_K = bf16(R diag(u)) with R Haar-orthogonal (QR of a
+  Gaussian, sign-fixed) and u ~ U[0.5, 2]; T_Q = (T_K as stored)^{-T}, computed
+  in fp64 and rounded to fp32, so that (q T_Q)(k T_K)^T = q k^T (§3.1, Eq. 1).
+* 128-token pages.  Identity page table unless ``shuffle_pages``.
+
+bf16 values are carried as ``numpy.uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import List, Optional
+
+import numpy as np
+
+HEAD_DIM = 128
+PAGE = 128
+
+# stream identifiers for numpy SeedSequence spawning
+_ID_Q, _ID_K, _ID_V, _ID_T, _ID_OUTLIER, _ID_LEN, _ID_PERM = 1, 2, 3, 4, 5, 6, 7
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even) and return the bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> 16) & 1
+    return ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def n_keep_for_sparsity(sparsity: float, d: int = HEAD_DIM) -> int:
+    """Channels kept at a given query-channel sparsity: never prune more than stated."""
+    return d - int(math.floor(sparsity * d + 1e-9))
+
+
+@dataclasses.dataclass
+class Shape:
+    batch: int
+    hq: int
+    hkv: int
+    seq_lens: List[int]
+    n_keep: int
+    name: str = "custom"
+    shuffle_pages: bool = False
+    outliers: int = 4
+    outlier_scale: float = 10.0
+    ch0_offset: float = 3.0
+
+    @property
+    def group(self) -> int:
+        return self.hq // self.hkv
+
+    @property
+    def max_pages(self) -> int:
+        return max((L + PAGE - 1) // PAGE for L in self.seq_lens)
+
+    @property
+    def pages_per_seq(self) -> List[int]:
+        return [(L + PAGE - 1) // PAGE for L in self.seq_lens]
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.seq_lens))
+
+
+def log_uniform_lengths(n: int, lo: int, hi: int, seed: int) -> List[int]:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _ID_LEN])))
+    u = rng.uniform(math.log(lo), math.log(hi), size=n)
+    return [int(min(hi, max(lo, math.floor(math.exp(x))))) for x in u]
+
+
+def config_shape(cfg: int, seed: int = 0, sparsity: float = 0.4) -> Shape:
+    """The five workloads of the decode-attention study (sizes only)."""
+    nk = n_keep_for_sparsity(sparsity)
+    if cfg == 0:
+        return Shape(1, 8, 8, [4096], nk, name="tiny-mha-4k")
+    if cfg == 1:
+        return Shape(1, 32, 8, [32768], nk, name="gqa32x8-32k-b1")
+    if cfg == 2:
+        return Shape(16, 32, 8, [32768] * 16, nk, name="gqa32x8-32k-b16")
+    if cfg == 3:
+        return Shape(4, 32, 8, [131072] * 4, nk, name="gqa32x8-128k-b4")
+    if cfg == 4:
+        lens = log_uniform_lengths(32, 1024, 131072, seed)
+        return Shape(32, 32, 8, lens, nk, name="gqa32x8-ragged-b32", shuffle_pages=True)
+    raise ValueError(f"unknown config {cfg}")
+
+
+def _rng(seed: int, *ids: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *ids])))
+
+
+def make_transforms(hkv: int, seed: int):
+    """T_K (bf16 bits, [hkv][128][128]) and T_Q (fp32, [hkv][128][128]).
+
+    T[i][j]: i = input channel, j = output channel (row-vector convention)."""
+    rng = _rng(seed, _ID_T)
+    tk = np.empty((hkv, HEAD_DIM, HEAD_DIM), dtype=np.uint16)
+    tq = np.empty((hkv, HEAD_DIM, HEAD_DIM), dtype=np.float32)
+    for g in range(hkv):
+        a = rng.standard_normal((HEAD_DIM, HEAD_DIM))
+        qm, rm = np.linalg.qr(a)
+        qm = qm * np.sign(np.diag(rm))[None, :]
+        u = rng.uniform(0.5, 2.0, size=HEAD_DIM)
+        tk[g] = f32_to_bf16_bits((qm * u[None, :]).astype(np.float32))
+        tk64 = bf16_bits_to_f32(tk[g]).astype(np.float64)
+        tq[g] = np.linalg.inv(tk64).T.astype(np.float32)
+    return tk, tq
+
+
+def outlier_channels(hkv: int, n: int, seed: int) -> np.ndarray:
+    rng = _rng(seed, _ID_OUTLIER)
+    out = np.zeros((hkv, n), dtype=np.int64)
+    for g in range(hkv):
+        out[g] = rng.choice(np.arange(1, HEAD_DIM), size=n, replace=False)
+    return out
+
+
+def make_q(shape: Shape, seed: int) -> np.ndarray:
+    rng = _rng(seed, _ID_Q)
+    x = rng.standard_normal((shape.batch, shape.hq, HEAD_DIM), dtype=np.float32)
+    return f32_to_bf16_bits(x)
+
+
+def make_kv_seq(shape: Shape, seed: int, b: int, outl: Optional[np.ndarray] = None):
+    """bf16 K and V of sequence b: each [L_b][hkv][128]."""
+    L = shape.seq_lens[b]
+    rk = _rng(seed, _ID_K, b)
+    rv = _rng(seed, _ID_V, b)
+    k = rk.standard_normal((L, shape.hkv, HEAD_DIM), dtype=np.float32)
+    v = rv.standard_normal((L, shape.hkv, HEAD_DIM), dtype=np.float32)
+    if outl is None:
+        outl = outlier_channels(shape.hkv, shape.outliers, seed)
+    for g in range(shape.hkv):
+        if shape.outliers:
+            k[:, g, outl[g]] *= np.float32(shape.outlier_scale)
+    k[:, :, 0] += np.float32(shape.ch0_offset)
+    return f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def make_page_table(shape: Shape, seed: int):
+    """int32 [batch][max_pages] page table (unused slots = -1) and pool size."""
+    pps = shape.pages_per_seq
+    total = int(sum(pps))
+    phys = np.arange(total, dtype=np.int32)
+    if shape.shuffle_pages:
+        phys = _rng(seed, _ID_PERM).permutation(total).astype(np.int32)
+    pt = np.full((shape.batch, shape.max_pages), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(pps):
+        pt[b, :n] = phys[off:off + n]
+        off += n
+    return pt, total
+
+
+@dataclasses.dataclass
+class Problem:
+    shape: Shape
+    seed: int
+    q: np.ndarray            # bf16 bits [B][Hq][128]
+    t_k: np.ndarray          # bf16 bits [Hkv][128][128]
+    t_q: np.ndarray          # fp32 [Hkv][128][128]
+    page_table: np.ndarray   # int32 [B][max_pages]
+    num_pages: int
+    seq_lens: np.ndarray     # int32 [B]
+    cu_tokens: np.ndarray    # int32 [B+1]
+    outliers: np.ndarray     # int64 [Hkv][n]
+    k: Optional[np.ndarray] = None  # bf16 bits [total_tokens][Hkv][128]
+    v: Optional[np.ndarray] = None
+
+    @property
+    def sm_scale(self) -> float:
+        return 1.0 / math.sqrt(HEAD_DIM)
+
+    def kv_seq(self, b: int):
+        if self.k is not None:
+            s, e = int(self.cu_tokens[b]), int(self.cu_tokens[b + 1])
+            return self.k[s:e], self.v[s:e]
+        return make_kv_seq(self.shape, self.seed, b, self.outliers)
+
+
+def make_problem(shape: Shape, seed: int = 0, materialize_kv: bool = True) -> Problem:
+    tk, tq = make_transforms(shape.hkv, seed)
+    outl = outlier_channels(shape.hkv, shape.outliers, seed) if shape.outliers else np.zeros((shape.hkv, 0), np.int64)
+    pt, total_pages = make_page_table(shape, seed)
+    lens = np.asarray(shape.seq_lens, dtype=np.int32)
+    cu = np.zeros(shape.batch + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    prob = Problem(shape, seed, make_q(shape, seed), tk, tq, pt, total_pages, lens, cu, outl)
+    if materialize_kv:
+        ks, vs = [], []
+        for b in range(shape.batch):
+            kb, vb = make_kv_seq(shape, seed, b, outl)
+            ks.append(kb)
+            vs.append(vb)
+        prob.k = np.concatenate(ks, axis=0)
+        prob.v = np.concatenate(vs, axis=0)
+    return prob

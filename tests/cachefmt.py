@@ -1,0 +1,65 @@
+"""Independent numpy reader of the paged INT2 cache format (test helper).
+
+Layout per physical page p and KV head g:
+  k_codes u8 [P][Hkv][128 ch][32]   token t at byte t>>2, bits 2*(t&3)
+  k_meta f16 [P][Hkv][128 ch][2]    (scale, zero)
+  k_ch0 bf16 [P][Hkv][128 tok]
+  v_codes u8 [P][Hkv][128 tok][32]  channel c at byte c>>2, bits 2*(c&3)
+  v_meta f16 [P][Hkv][2][4][128]    [0]=scale, [1]=zero per (group, token)
+Dequantized value = code * scale + zero; code*scale is exact in fp32 (binary16
+scale times an integer below 4), so fp32 multiply-then-add equals fmaf.
+"""
+import numpy as np
+
+
+def f16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def bf16(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def unpack_rows(rows: np.ndarray) -> np.ndarray:
+    """[..., 32] bytes -> [..., 128] 2-bit fields, little-endian within bytes."""
+    r = rows.astype(np.uint8)
+    fields = np.stack([(r >> (2 * i)) & 3 for i in range(4)], axis=-1)  # [...,32,4]
+    return fields.reshape(*rows.shape[:-1], 128)
+
+
+def k_codes(cache, p, g):
+    """codes [128 ch][128 tok]"""
+    return unpack_rows(cache.k_codes[p, g])
+
+
+def v_codes(cache, p, g):
+    """codes [128 tok][128 ch]"""
+    return unpack_rows(cache.v_codes[p, g])
+
+
+def decode_k(cache, p, g):
+    """Dequantized k' of a page: [128 tok][128 ch] fp32 (channel 0 from bf16)."""
+    c = k_codes(cache, p, g).astype(np.float32)            # [ch][tok]
+    s = f16(cache.k_meta[p, g, :, 0])[:, None]
+    z = f16(cache.k_meta[p, g, :, 1])[:, None]
+    k = (c * s + z).T.copy()
+    k[:, 0] = bf16(cache.k_ch0[p, g])
+    return k
+
+
+def decode_v(cache, p, g):
+    c = v_codes(cache, p, g).astype(np.float32)            # [tok][ch]
+    s = f16(cache.v_meta[p, g, 0])                           # [4][tok]
+    z = f16(cache.v_meta[p, g, 1])
+    grp = np.arange(128) // 32
+    return c * s[grp].T + z[grp].T
+
+
+def gather_seq(cache, page_table, b, L, g):
+    """Dequantized (k', v) of sequence b, KV head g: [L][128] each."""
+    ks, vs = [], []
+    for pi in range((L + 127) // 128):
+        p = int(page_table[b, pi])
+        ks.append(decode_k(cache, p, g))
+        vs.append(decode_v(cache, p, g))
+    return np.concatenate(ks)[:L], np.concatenate(vs)[:L]
