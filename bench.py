@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+Workload (default): batch 4, GQA 32 query / 8 KV heads, head_dim 128, 131072
+tokens of context per sequence, INT2 keys/values with channel 0 in bf16, 40%
+query-channel sparsity (77 of 128 channels kept).  One step = one decode step
+of one attention layer: dqk_select_channels (q' = q T_Q, pooled-energy top-k)
+followed by dqk_decode_attn (split-K decode + log-sum-exp merge) over the
+whole batch.  Inputs are seeded synthetic data (see synth/), already resident
+in HBM; the INT2 cache is built once on the GPU by dqk_quantize_append.  Each
+step reads a different one of several identical cache copies so that no step
+finds its cache in the 256 MB Infinity Cache.
+
+Prints one JSON line (metric, value = decode-attention tokens/s, roofline of
+the decode kernel, CPU-oracle baseline on a bounded sample).
+"""
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "decode-attn tokens/s @128K, INT2 KV, 40% q-prune; achieved HBM GB/s %"
+PEAK_HBM_GBS = 8000.0
+DECODE_SOURCES = ["page_set_amd/csrc/dqk_decode_mfma.hip", "page_set_amd/csrc/dqk_decode.hip",
+                  "page_set_amd/csrc/dqk_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_hash):
+    """HBM traffic per decode launch from committed rocprofv3 PMC runs, if the
+    decode kernel has not changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_hash") != kernel_hash:
+        return None
+    return rec
+
+
+def build_cache(prob, shape, d, pa, torch):
+    """Pack the whole batch into the INT2 cache on the GPU, sequence by sequence."""
+    cache = pa.Cache(prob.num_pages, shape.hkv)
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        futs = [ex.submit(synth.make_kv_seq, shape, prob.seed, b, prob.outliers) for b in range(shape.batch)]
+        for b, f in enumerate(futs):
+            kb, vb = f.result()
+            L = kb.shape[0]
+            k_d = torch.from_numpy(kb.view(np.int16)).to("cuda")
+            v_d = torch.from_numpy(vb.view(np.int16)).to("cuda")
+            cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+            pa.dqk_quantize_append(cache, k_d, v_d, d["t_k"], cu, d["page_table"][b:b + 1].contiguous())
+            torch.cuda.synchronize()
+            del k_d, v_d
+    return cache
+
+
+def cpu_baseline(shape, seed, n_keep, reps):
+    """The CPU oracle (single thread, as written) on one (sequence, KV head)
+    unit of the same workload: select + decode repeated `reps` times, scaled to
+    the batch's units per step."""
+    import oracle
+    prob = synth.make_problem(shape, seed, materialize_kv=False)
+    L = shape.seq_lens[0]
+    g = 0
+    grp = shape.hq // shape.hkv
+    kb, vb = synth.make_kv_seq(shape, seed, 0, prob.outliers)
+    kk = np.ascontiguousarray(kb[:, g:g + 1])
+    vv = np.ascontiguousarray(vb[:, g:g + 1])
+    npg = (L + 127) // 128
+    pt = np.arange(npg, dtype=np.int32)[None]
+    cache, _ = oracle.quantize_append(kk, vv, prob.t_k[g:g + 1], np.array([0, L], np.int32), pt, npg)
+    q = np.ascontiguousarray(prob.q[0:1, g * grp:(g + 1) * grp])
+    lens = np.array([L], np.int32)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        qp, sel = oracle.select_channels(q, prob.t_q[g:g + 1], 1, n_keep)
+        oracle.decode_attn(cache, qp, sel, pt, lens, prob.sm_scale)
+    dt = (time.perf_counter() - t0) / reps
+    units = shape.batch * shape.hkv
+    t_step = dt * units
+    return {"value": shape.batch / t_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"1 of {units} (sequence, KV head) units ({grp} query heads x {L} tokens), select + decode, "
+                      f"{reps} repetitions, {dt:.3f} s each; step time = {units} x unit time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--sparsity", type=float, default=0.4)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps (MALL eviction)")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy kernel (PMC calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import page_set_amd as pa
+    from page_set_amd import traffic
+
+    shape = synth.config_shape(args.config, args.seed, args.sparsity)
+    n_keep = shape.n_keep
+    log(f"[bench] workload {shape.name}: B={shape.batch} Hq/Hkv={shape.hq}/{shape.hkv} ctx={max(shape.seq_lens)} "
+        f"n_keep={n_keep}")
+    prob = synth.make_problem(shape, args.seed, materialize_kv=False)
+    d = {"q": torch.from_numpy(prob.q.view(np.int16)).to("cuda"),
+         "t_q": torch.from_numpy(prob.t_q).to("cuda"),
+         "t_k": torch.from_numpy(prob.t_k.view(np.int16)).to("cuda"),
+         "page_table": torch.from_numpy(prob.page_table).to("cuda"),
+         "seq_lens": torch.from_numpy(prob.seq_lens).to("cuda")}
+    t0 = time.time()
+    cache = build_cache(prob, shape, d, pa, torch)
+    log(f"[bench] cache built on GPU in {time.time() - t0:.1f}s ({cache.nbytes() / 1e6:.1f} MB)")
+    caches = [cache]
+    for _ in range(args.copies - 1):
+        c2 = pa.Cache(cache.num_pages, cache.num_kv_heads)
+        for a, b in zip(cache.arrays(), c2.arrays()):
+            b.copy_(a)
+        caches.append(c2)
+    torch.cuda.synchronize()
+
+    B, hq, hkv = shape.batch, shape.hq, shape.hkv
+    max_pages = int(prob.page_table.shape[1])
+    q_prime = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, hkv, n_keep), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws_bytes = pa.dqk_decode_workspace_size(B, hq, hkv, max_pages, args.num_splits)
+    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        pa.dqk_select_channels(d["q"], d["t_q"], hkv, n_keep, q_prime=q_prime, sel_idx=sel, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pa.dqk_decode_attn(caches[i % len(caches)], q_prime, sel, d["page_table"], d["seq_lens"], prob.sm_scale,
+                           num_splits=args.num_splits, workspace=ws, out=out, want_lse=False, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms_avg = float(np.mean(dec_ms))
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step; decode call {dec_ms_avg * 1e3:.1f} us "
+        f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})")
+
+    sel_h = sel.cpu().numpy()
+    cache_bytes = traffic.decode_cache_bytes(prob.seq_lens, sel_h)
+    fixed = traffic.decode_fixed_bytes(B, hq, hkv, n_keep, max_pages)
+    alg_bytes = cache_bytes + fixed["decode"]
+    achieved = alg_bytes / (dec_ms_avg * 1e-3) / 1e9
+    khash = source_hash()
+    tr = committed_traffic(khash)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": (tr["hbm_bytes_per_launch"] if tr else None),
+            "kernel": "dqk_decode_attn (split decode + merge)", "algorithmic_bytes_per_launch": int(alg_bytes),
+            "bytes_per_token_head": round(cache_bytes / (B * hkv * max(shape.seq_lens)), 3),
+            "avg_launch_us": round(dec_ms_avg * 1e3, 2), "kernel_source_hash": khash}
+
+    if args.calib_copy:
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        del x, y
+
+    rec = {"metric": METRIC, "value": round(B / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int2-kv/fp32-accumulate",
+           "data": "synthetic (seeded Gaussian q/k/v, 4 outlier key channels x10, channel-0 offset +3)",
+           "config": {"workload": shape.name, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
+                      "context": max(shape.seq_lens), "n_keep": n_keep, "sparsity": args.sparsity,
+                      "cache_copies": len(caches), "num_splits": args.num_splits or "auto"},
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline(shape, args.seed, n_keep, args.cpu_reps)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,6 +1,6 @@
-"""Storage and read-volume accounting for 2-bit KV cache formats.
+"""Storage and read-volume accounting for 2-bit KV cache formats (host-side arithmetic only).
 
-TEST AND MEASUREMENT INFRASTRUCTURE: used by the tests (to pin the accounting
+Used by the tests (to pin the accounting
 against the figures the paper prints) and by the benchmark (to turn a
 measured time into algorithmic bytes per second).
 

@@ -120,7 +120,8 @@ def test_decode_parity(name, shape):
     rel = gu.row_rel_err(out, ref)
     _say(f"  max row rel err {rel.max():.3e}")
     assert (rel <= gu.TOL).all(), rel.max()
-    np.testing.assert_allclose(lse, ref_lse, rtol=1e-5, atol=1e-5)
+    # logits carry q' * scale as an fp16 hi/lo pair (~2^-22 relative)
+    np.testing.assert_allclose(lse, ref_lse, rtol=2e-5, atol=2e-5)
 
 
 def test_decode_config1_full():
@@ -131,16 +132,20 @@ def test_decode_config1_full():
     assert (rel <= gu.TOL).all()
 
 
-def test_decode_split_invariance_and_permutation():
-    _say("decode splits/permutation")
-    shape = synth.Shape(2, 32, 8, [4000, 2500], 77)
+@pytest.mark.parametrize("hq,hkv,tol", [(32, 8, 5e-4), (16, 8, 1e-5)], ids=["mfma-g4", "generic-g2"])
+def test_decode_split_invariance_and_permutation(hq, hkv, tol):
+    """Split count changes only rounding: the group-4 MFMA path rounds the
+    probabilities to fp16 relative to each split's running maximum, the
+    generic path keeps fp32 throughout."""
+    _say("decode splits/permutation", hq, hkv)
+    shape = synth.Shape(2, hq, hkv, [4000, 2500], 77)
     outs = []
     for ns in (1, 2, 7, 0):
         prob, cache, qp, sel, ref, ref_lse, out, lse = _decode_case(shape, 9, num_splits=ns)
         outs.append(out)
         assert (gu.row_rel_err(out, ref) <= gu.TOL).all()
     for o in outs[1:]:
-        assert (gu.row_rel_err(o, outs[0]) <= 1e-5).all()
+        assert (gu.row_rel_err(o, outs[0]) <= tol).all()
 
     def permute(cache, prob):
         perm = np.random.default_rng(4).permutation(prob.num_pages)
