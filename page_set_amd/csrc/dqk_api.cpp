@@ -59,7 +59,7 @@ int dqk_select_channels(const void *q_bf16, const float *t_q, int32_t batch, int
                         int32_t n_keep, float *q_prime, int32_t *sel_idx, hipStream_t stream) {
     if (!q_bf16 || !t_q || !q_prime || !sel_idx) return DQK_ERR_NULL;
     if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM) return DQK_ERR_SHAPE;
-    if (hq / hkv > 128 || batch > 65535) return DQK_ERR_UNSUPPORTED;
+    if (hq / hkv > 64 || batch > 65535) return DQK_ERR_UNSUPPORTED;
     if (!aligned16(q_bf16) || !aligned16(t_q) || !aligned16(q_prime) || !aligned16(sel_idx)) return DQK_ERR_ALIGN;
     return hip_status(dqk::launch_select(static_cast<const uint16_t *>(q_bf16), t_q, batch, hq, hkv, n_keep, q_prime,
                                          sel_idx, stream));

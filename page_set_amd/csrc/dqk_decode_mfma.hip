@@ -27,6 +27,8 @@
 //    points accumulate as sum_t P z_{t,q} with v_dot2_f32_f16.
 #include "dqk_internal.h"
 
+#include <utility>
+
 namespace dqk {
 
 namespace {
@@ -88,268 +90,408 @@ __device__ __forceinline__ int sel4n(const int (&a)[4], int i) {
     return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
 }
 
+// ---------------------------------------------------------------- staging through LDS
+// Direct global -> LDS loads (16 or 4 bytes per lane, written at M0 + lane * size).
+// They are issued from asm so that the compiler's conservative wait-for-all
+// before every LDS read does not apply; completion is awaited explicitly with
+// s_waitcnt vmcnt(N), N = DMA instructions this wave issued afterwards (any
+// other vector memory op only makes that wait stricter).
+__device__ __forceinline__ void dma16_s(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %0" ::"s"(sbase), "v"(voff), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_v(const void *addr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_v(const void *addr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(lds) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_dma() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that waits only for this wave's LDS operations.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+
+template <int KSM>
+struct Lay {
+    static constexpr int NCH = 8 * KSM;            // compacted channel slots
+    static constexpr int KHR = 2 * NCH;            // 16-byte key half rows per page
+    static constexpr int KPS = 32 * NCH + 32;      // key page stride: row groups of the 4 pages start 8 banks apart
+    static constexpr int KINS = (KHR + 63) / 64;   // DMA instructions per key page
+    static constexpr int KMI = (4 * NCH + 63) / 64;  // 4-byte DMA instructions for key metadata
+    static constexpr int VBS = 32 * ROW_BYTES + 32;  // value block (32 tokens) stride, 8 banks apart
+    static constexpr int VPS = 4 * VBS;
+    static constexpr int OFF_K = 0;
+    static constexpr int KAREA = 4 * KPS > 4 * GRP * PG * 2 ? 4 * KPS : 4 * GRP * PG * 2;  // key rows, later P
+    static constexpr int OFF_KM = OFF_K + KAREA;       // u32 (scale | zero << 16) [4][NCH]
+    static constexpr int OFF_K0 = OFF_KM + 16 * NCH;   // bf16 [4][128]
+    static constexpr int OFF_VC = OFF_K0 + 4 * 256;    // value codes [4][4 blocks][32 rows][32 B]
+    static constexpr int OFF_VM = OFF_VC + 4 * VPS;    // fp16 [4][2][4][128]
+    static constexpr int QB = OFF_VM + 4 * 2048;       // one 4-page block
+    static constexpr int NDMA = 4 * KINS + KMI + 1 + 16 + 8;
+    static constexpr int NW = (NDMA + WAVES - 1) / WAVES;  // DMA instructions per wave per block
+    static_assert(OFF_K0 % 16 == 0 && OFF_VC % 16 == 0 && OFF_VM % 16 == 0 && QB % 16 == 0, "alignment");
+};
+
+struct Quad {
+    int64_t pg[4];  // physical page * hkv + g
+    int nv[4];      // valid tokens (0 for slots past the range)
+};
+
+// Pages of logical pages lp0 .. lp0+3; slots past P1 reuse page lp0 (always valid).
+__device__ __forceinline__ Quad quad_pages(const int32_t *__restrict__ ptab, int lp0, int P1, int L, int hkv, int g) {
+    Quad q;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int lp = lp0 + p;
+        const bool ok = lp < P1;
+        q.pg[p] = (int64_t)ptab[ok ? lp : lp0] * hkv + g;
+        q.nv[p] = ok ? min(PG, L - lp * PG) : 0;
+    }
+    return q;
+}
+
+__device__ __forceinline__ int64_t sel4l(const int64_t (&a)[4], int i) {
+    const int64_t lo = (i & 1) ? a[1] : a[0];
+    const int64_t hi = (i & 1) ? a[3] : a[2];
+    return (i & 2) ? hi : lo;
+}
+
+// 16-byte chunks (row r of 4, chunk c of 16: tokens 8c .. 8c+7) of a 1 KB
+// [4][128] fp16 table are stored at slot 16 (c & 3) + 4 (c >> 2) + r, so that
+// the 16 chunks (r, 4G + k) read together for a k-step fall in distinct banks.
+// LDS slot l of a DMA receives the chunk read from this byte offset:
+__device__ __forceinline__ uint32_t vm_chunk(int l) {
+    const int r = l & 3, c = 4 * ((l >> 2) & 3) + (l >> 4);
+    return (uint32_t)(r * 256 + c * 16);
+}
+__device__ __forceinline__ constexpr int chunk_slot(int r, int c) { return 16 * (c & 3) + 4 * (c >> 2) + r; }
+
+// One DMA instruction of a block fill; D_ is its compile-time index.
+template <int KSM, int D_>
+__device__ __forceinline__ void block_dma(const dqk_cache &c, const Quad &Q, uint32_t qb, int lane,
+                                          const uint32_t (&kro)[Lay<KSM>::KINS],
+                                          const uint32_t (&kmo)[Lay<KSM>::KMI], const int (&kmp)[Lay<KSM>::KMI]) {
+    using Ly = Lay<KSM>;
+    constexpr int NK = 4 * Ly::KINS, NKM = NK + Ly::KMI, NK0 = NKM + 1, NVC = NK0 + 16;
+    constexpr int d = D_ < Ly::NDMA ? D_ : NKM;  // spare slots repeat the channel-0 load (same bytes)
+    if constexpr (d < NK) {  // selected key rows of page p, 64 half rows per instruction
+        constexpr int p = d / Ly::KINS, j = d % Ly::KINS;
+        if (64 * j + lane < Ly::KHR)
+            dma16_s(c.k_codes + Q.pg[p] * (D * ROW_BYTES), kro[j], qb + Ly::OFF_K + p * Ly::KPS + 64 * j * 16);
+    } else if constexpr (d < NKM) {  // (scale, zero) of the selected channels of the 4 pages
+        constexpr int t = d - NK;
+        if (64 * t + lane < 4 * Ly::NCH)
+            dma4_v(reinterpret_cast<const uint8_t *>(c.k_meta) + sel4l(Q.pg, kmp[t]) * (D * 4) + kmo[t],
+                   qb + Ly::OFF_KM + 64 * t * 4);
+    } else if constexpr (d < NK0) {  // channel 0 of the 4 pages
+        dma16_v(reinterpret_cast<const uint8_t *>(c.k_ch0) + sel4l(Q.pg, lane >> 4) * (PG * 2) + (lane & 15) * 16,
+                qb + Ly::OFF_K0);
+    } else if constexpr (d < NVC) {  // value codes: page p, 32-token block bb
+        constexpr int p = (d - NK0) >> 2, bb = (d - NK0) & 3;
+        dma16_s(c.v_codes + Q.pg[p] * (PG * ROW_BYTES) + bb * 1024, (uint32_t)lane * 16u,
+                qb + Ly::OFF_VC + p * Ly::VPS + bb * Ly::VBS);
+    } else {  // value metadata: page p, half hf (scales / zeros), chunks permuted (see vm_chunk)
+        constexpr int p = (d - NVC) >> 1, hf = (d - NVC) & 1;
+        dma16_s(reinterpret_cast<const uint8_t *>(c.v_meta) + Q.pg[p] * (2 * VGROUPS * PG * 2) + hf * 1024,
+                vm_chunk(lane), qb + Ly::OFF_VM + p * 2048 + hf * 1024);
+    }
+}
+
+template <int KSM, int... Ds>
+__device__ __forceinline__ void issue_all(const dqk_cache &c, const Quad &Q, uint32_t qb, int w, int lane,
+                                          const uint32_t (&kro)[Lay<KSM>::KINS],
+                                          const uint32_t (&kmo)[Lay<KSM>::KMI], const int (&kmp)[Lay<KSM>::KMI],
+                                          std::integer_sequence<int, Ds...>) {
+    ((w == (Ds & (WAVES - 1)) ? block_dma<KSM, Ds>(c, Q, qb, lane, kro, kmo, kmp) : (void)0), ...);
+}
+
+// Issue this wave's share (NW instructions) of the DMAs that fill one block buffer.
+template <int KSM>
+__device__ __forceinline__ void issue_block(const dqk_cache &c, const Quad &Q, uint32_t qb, int w, int lane,
+                                            const uint32_t (&kro)[Lay<KSM>::KINS],
+                                            const uint32_t (&kmo)[Lay<KSM>::KMI], const int (&kmp)[Lay<KSM>::KMI]) {
+    issue_all<KSM>(c, Q, qb, w, lane, kro, kmo, kmp, std::make_integer_sequence<int, WAVES * Lay<KSM>::NW>{});
+}
+
+__device__ __forceinline__ uint32_t lds_u16(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t *>((uintptr_t)a);
+}
+__device__ __forceinline__ uint32_t lds_u32(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>((uintptr_t)a);
+}
+__device__ __forceinline__ u32x4 lds_u128(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)a);
+}
+__device__ __forceinline__ void lds_st32(uint32_t a, uint32_t v) {
+    *reinterpret_cast<__attribute__((address_space(3))) uint32_t *>((uintptr_t)a) = v;
+}
+__device__ __forceinline__ void lds_stf(uint32_t a, float v) {
+    *reinterpret_cast<__attribute__((address_space(3))) float *>((uintptr_t)a) = v;
+}
+__device__ __forceinline__ float lds_f(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) float *>((uintptr_t)a);
+}
+
+// Score tiles 2W, 2W+1 of one k-step (hi and lo halves of q~).
+template <int W>
+__device__ __forceinline__ void qk_step(f32x4 (&S)[2], const u32x4 &X, const half8 &Bh, const half8 &Bl) {
+    Packed P;
+    if (W == 0) P.L = X << 4;
+    if (W == 2 || W == 3) P.R = X >> 6;
+    P.X = X;
+    const half8 a0 = as_half8(tile_codes<2 * W>(P));
+    const half8 a1 = as_half8(tile_codes<2 * W + 1>(P));
+    S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bh, S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bh, S[1], 0, 0, 0);
+    S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bl, S[0], 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bl, S[1], 0, 0, 0);
+}
+
+template <int KSM>
 __global__ __launch_bounds__(256) void decode_g4_kernel(dqk_cache c, const float *__restrict__ q_prime,
-                                                           const int32_t *__restrict__ sel_idx, int n_keep, int hq,
-                                                           const int32_t *__restrict__ page_table, int max_pages,
-                                                           const int32_t *__restrict__ seq_lens, float sm_scale,
-                                                           int nsplit, float *__restrict__ partials) {
-    __shared__ __attribute__((aligned(16))) float qsel[GRP][D];               // C * q'_{h, jrow[jj]}
-    __shared__ __attribute__((aligned(16))) _Float16 qt[2][WAVES][4][GRP][D];  // q~ hi/lo per wave [p][h][jj]
-    __shared__ __attribute__((aligned(16))) _Float16 zero16[16];
-    __shared__ float comb[WAVES][GRP][D + 2];
+                                                        const int32_t *__restrict__ sel_idx, int n_keep, int hq,
+                                                        const int32_t *__restrict__ page_table, int max_pages,
+                                                        const int32_t *__restrict__ seq_lens, float sm_scale,
+                                                        int nsplit, float *__restrict__ partials) {
+    using Ly = Lay<KSM>;
+    constexpr int NCH = Ly::NCH;
+    // two block buffers; the scores' probabilities reuse the key rows of the
+    // current buffer once every wave is past its score MFMAs
+    __shared__ __attribute__((aligned(16))) uint8_t blk[2][Ly::QB];
+    __shared__ __attribute__((aligned(16))) _Float16 qt[2][4][GRP][NCH];  // q~ hi/lo [p][h][jj]
+    __shared__ __attribute__((aligned(16))) float colmax[WAVES][16];
+    __shared__ __attribute__((aligned(16))) float bias_lds[4][GRP];
+    __shared__ __attribute__((aligned(16))) _Float16 zero16[8];
+    static_assert(4 * GRP * PG * 2 <= Ly::KAREA, "probabilities fit in the key-row area");
 
     const int split = blockIdx.x, bg = blockIdx.y;
     const int hkv = c.num_kv_heads;
     const int b = bg / hkv, g = bg - b * hkv;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform by construction
     const int G = lane >> 4, n = lane & 15;
     const int L = seq_lens[b];
     const int npages = (L + PG - 1) / PG;
     const int per = (((npages + nsplit - 1) / nsplit) + 15) & ~15;
     const int P0 = min(npages, split * per), P1 = min(npages, P0 + per);
+    const int nq = (P1 - P0 + 3) >> 2;
 
     const float C = sm_scale * LOG2E;
     const int32_t *sel = sel_idx + ((size_t)b * hkv + g) * n_keep;
     const int has0 = sel[0] == 0;  // the list is ascending
-    const int R = n_keep - has0;   // selected INT2 channels
+    const int R = n_keep - has0;   // selected INT2 channels (R <= NCH)
     const int KS = (R + 7) >> 3;
     const float *qp = q_prime + ((size_t)b * hq + (size_t)g * GRP) * D;
+    auto chan = [&](int jj) { return jj < R ? sel[jj + has0] : 0; };
 
-    for (int i = tid; i < GRP * D; i += 256) {
-        const int h = i >> 7, jj = i & (D - 1);
-        qsel[h][jj] = jj < R ? qp[h * D + sel[jj + has0]] * C : 0.0f;
+    // per-lane DMA source offsets (fixed for the whole split)
+    uint32_t kro[Ly::KINS];
+#pragma unroll
+    for (int j = 0; j < Ly::KINS; ++j) {
+        const int hr = 64 * j + lane;
+        kro[j] = hr < Ly::KHR ? (uint32_t)chan(hr >> 1) * ROW_BYTES + (hr & 1) * 16 : 0u;
     }
-    if (tid < 16) zero16[tid] = (_Float16)0.0f;
-    __syncthreads();
-
-    // score-layout lane: column n = (page slot pc, head hc)
-    const int pc = n >> 2, hc = n & 3;
+    uint32_t kmo[Ly::KMI];
+    int kmp[Ly::KMI];
+#pragma unroll
+    for (int t = 0; t < Ly::KMI; ++t) {
+        const int idx = min(64 * t + lane, 4 * NCH - 1);
+        kmp[t] = idx / NCH;
+        kmo[t] = (uint32_t)chan(idx - kmp[t] * NCH) * 4u;
+    }
+    // staging lane: channels 2*lane, 2*lane+1 of page slot w; C * q' of them for the 4 heads
+    float qs[GRP][2];
+#pragma unroll
+    for (int h = 0; h < GRP; ++h)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int jj = 2 * lane + e;
+            qs[h][e] = jj < R ? qp[h * D + chan(jj)] * C : 0.0f;
+        }
+    const int pc = n >> 2, hc = n & 3;  // score lane: column (page slot, head)
+    const int qv = n >> 2, hv = n & 3;  // value lane: row (group, head)
     const float q0c = has0 ? qp[hc * D] * C : 0.0f;
-    // value-operand lane: row n = (group qv, head hv)
-    const int qv = n >> 2, hv = n & 3;
-    // staging lane: page slot G, channels 8n .. 8n+7 of the compacted list
-    int chan[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int jj = 8 * n + e;
-        chan[e] = jj < R ? sel[jj + has0] : 0;
-    }
+    if (tid < 8) zero16[tid] = (_Float16)0.0f;
 
-    float m_run[GRP];
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) m_run[h] = -__builtin_huge_valf();
+    const uint32_t blk0 = lds_addr(&blk[0][0]);
+    const int32_t *ptab = page_table + (size_t)b * max_pages;
+    if (nq > 0) issue_block<KSM>(c, quad_pages(ptab, P0, P1, L, hkv, g), blk0, w, lane, kro, kmo, kmp);
+    if (nq > 1) issue_block<KSM>(c, quad_pages(ptab, P0 + 4, P1, L, hkv, g), blk0 + Ly::QB, w, lane, kro, kmo, kmp);
+
+    float m_lane = -__builtin_huge_valf();  // running max (log2 domain) of head n & 3
     float l_lane = 0.0f, z_lane = 0.0f;
     f32x4 O[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) O[t] = {0.f, 0.f, 0.f, 0.f};
 
-    const int nq = (P1 - P0 + 3) >> 2;
-    const int32_t *ptab = page_table + (size_t)b * max_pages;
-    for (int u = w; u < nq; u += WAVES) {
-        const int lp0 = P0 + 4 * u;
-        int64_t pgi[4];  // (physical page * hkv + g), always a valid page
-        int nv[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const int lp = lp0 + p;
-            const bool ok = lp < P1;
-            pgi[p] = (int64_t)ptab[ok ? lp : lp0] * hkv + g;
-            nv[p] = ok ? min(PG, L - lp * PG) : 0;
-        }
+    for (int u = 0; u < nq; ++u) {
+        const uint32_t qb = blk0 + (uint32_t)(u & 1) * Ly::QB;
+        if (u + 1 < nq)
+            wait_dma<Ly::NW>();
+        else
+            wait_dma<0>();
+        lds_barrier();
 
-        // ---- stage q~ (fp16) for page slot G and channels 8n..8n+7; bias partials
-        float bpart[GRP] = {0.f, 0.f, 0.f, 0.f};
-        if (n < KS) {
-            const uint16_t *km = c.k_meta + sel4i(pgi, G) * (D * 2);
-            const bool pv = sel4n(nv, G) > 0;
-            float s[8], z[8];
+        // ---- stage q~ (fp16 hi/lo) for page slot w, channels 2 lane, 2 lane + 1; bias partials
+        {
+            float bp[GRP] = {0.f, 0.f, 0.f, 0.f};
+            if (2 * lane < NCH) {
+                const bool pv = P0 + 4 * u + w < P1;
+                const uint32_t sz0 = lds_u32(qb + Ly::OFF_KM + (w * NCH + 2 * lane) * 4);
+                const uint32_t sz1 = lds_u32(qb + Ly::OFF_KM + (w * NCH + 2 * lane + 1) * 4);
+                const float s0 = pv ? h2f((uint16_t)sz0) : 0.f, z0 = pv ? h2f((uint16_t)(sz0 >> 16)) : 0.f;
+                const float s1 = pv ? h2f((uint16_t)sz1) : 0.f, z1 = pv ? h2f((uint16_t)(sz1 >> 16)) : 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sz = pv ? *reinterpret_cast<const uint32_t *>(km + chan[e] * 2) : 0u;
-                const bool live = 8 * n + e < R;
-                s[e] = live ? h2f((uint16_t)(sz & 0xFFFFu)) : 0.0f;
-                z[e] = live ? h2f((uint16_t)(sz >> 16)) : 0.0f;
+                for (int h = 0; h < GRP; ++h) {
+                    const float t0 = qs[h][0] * s0, t1 = qs[h][1] * s1;
+                    half2v hi, lo;
+                    hi[0] = (_Float16)t0;
+                    hi[1] = (_Float16)t1;
+                    lo[0] = (_Float16)(t0 - (float)hi[0]);
+                    lo[1] = (_Float16)(t1 - (float)hi[1]);
+                    *reinterpret_cast<half2v *>(&qt[0][w][h][2 * lane]) = hi;
+                    *reinterpret_cast<half2v *>(&qt[1][w][h][2 * lane]) = lo;
+                    bp[h] = __builtin_fmaf(qs[h][1], z1, qs[h][0] * z0);
+                }
             }
 #pragma unroll
             for (int h = 0; h < GRP; ++h) {
-                const float4 qa = *reinterpret_cast<const float4 *>(&qsel[h][8 * n]);
-                const float4 qb = *reinterpret_cast<const float4 *>(&qsel[h][8 * n + 4]);
-                const float qv8[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-                half8 thi, tlo;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float t = qv8[e] * s[e];
-                    thi[e] = (_Float16)t;
-                    tlo[e] = (_Float16)(t - (float)thi[e]);
-                    bpart[h] = __builtin_fmaf(qv8[e], z[e], bpart[h]);
-                }
-                *reinterpret_cast<half8 *>(&qt[0][w][G][h][8 * n]) = thi;
-                *reinterpret_cast<half8 *>(&qt[1][w][G][h][8 * n]) = tlo;
+                for (int o = 32; o >= 1; o >>= 1) bp[h] += __shfl_xor(bp[h], o);
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int h = 0; h < GRP; ++h) bias_lds[w][h] = bp[h];
             }
         }
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-            bpart[h] += __shfl_xor(bpart[h], 1);
-            bpart[h] += __shfl_xor(bpart[h], 2);
-            bpart[h] += __shfl_xor(bpart[h], 4);
-            bpart[h] += __shfl_xor(bpart[h], 8);
-        }
-        // lane (row p, n') offers the bias of head n' & 3; column (pc, hc) reads lane 16 pc + hc
-        const float bias = __shfl(sel4(bpart, n & 3), 16 * pc + hc);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        lds_barrier();
 
-        // ---- scores
-        f32x4 S[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) S[t] = {0.f, 0.f, 0.f, 0.f};
-        const uint8_t *krow = c.k_codes + sel4i(pgi, G) * (D * ROW_BYTES) + 2 * n;
-        const _Float16 *bhi = pc == G ? &qt[0][w][pc][hc][0] : &zero16[0];
-        const _Float16 *blo = pc == G ? &qt[1][w][pc][hc][0] : &zero16[0];
-        const int bstep = pc == G ? 8 : 0;
-        for (int kk = 0; kk < KS; ++kk) {
-            const half8 Bq = *reinterpret_cast<const half8 *>(bhi + bstep * kk);
-            const half8 Bl = *reinterpret_cast<const half8 *>(blo + bstep * kk);
-            u32x4 X;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int j0 = 8 * kk + 2 * e2;
-                const int ca = j0 < R ? sel[j0 + has0] : 0;
-                const int cb = j0 + 1 < R ? sel[j0 + 1 + has0] : 0;
-                X[e2] = ld_u16(krow + ca * ROW_BYTES) | (ld_u16(krow + cb * ROW_BYTES) << 16);
-            }
-            const Packed XP = pack_shifts(X);
-            S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<0>(XP)), Bq, S[0], 0, 0, 0);
-            S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<0>(XP)), Bl, S[0], 0, 0, 0);
-            S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<1>(XP)), Bq, S[1], 0, 0, 0);
-            S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<1>(XP)), Bl, S[1], 0, 0, 0);
-            S[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<2>(XP)), Bq, S[2], 0, 0, 0);
-            S[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<2>(XP)), Bl, S[2], 0, 0, 0);
-            S[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<3>(XP)), Bq, S[3], 0, 0, 0);
-            S[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<3>(XP)), Bl, S[3], 0, 0, 0);
-            S[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<4>(XP)), Bq, S[4], 0, 0, 0);
-            S[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<4>(XP)), Bl, S[4], 0, 0, 0);
-            S[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<5>(XP)), Bq, S[5], 0, 0, 0);
-            S[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<5>(XP)), Bl, S[5], 0, 0, 0);
-            S[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<6>(XP)), Bq, S[6], 0, 0, 0);
-            S[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<6>(XP)), Bl, S[6], 0, 0, 0);
-            S[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<7>(XP)), Bq, S[7], 0, 0, 0);
-            S[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<7>(XP)), Bl, S[7], 0, 0, 0);
-        }
-
-        // ---- logits (log2 domain) for tokens 32G + 8r + m of page slot pc, head hc
-        const int nvl = sel4n(nv, pc);
-        float x[8][4];
+        // ---- scores: tiles 2w, 2w+1 of all 4 pages (block-diagonal over the page slots)
+        f32x4 S[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         {
-            uint32_t k0w[16];
-            if (has0) {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(c.k_ch0 + sel4i(pgi, pc) * PG + 32 * G);
+            const _Float16 *bhi = pc == G ? &qt[0][pc][hc][0] : &zero16[0];
+            const _Float16 *blo = pc == G ? &qt[1][pc][hc][0] : &zero16[0];
+            const int bstep = pc == G ? 8 : 0;
+            const uint32_t krow = qb + Ly::OFF_K + G * Ly::KPS + 2 * n;
 #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4) {
-                    const u32x4 t4 = src[v4];
-                    k0w[4 * v4 + 0] = t4[0];
-                    k0w[4 * v4 + 1] = t4[1];
-                    k0w[4 * v4 + 2] = t4[2];
-                    k0w[4 * v4 + 3] = t4[3];
+            for (int kk = 0; kk < KSM; ++kk) {
+                if (kk < KS) {
+                    const half8 Bh = *reinterpret_cast<const half8 *>(bhi + bstep * kk);
+                    const half8 Bl = *reinterpret_cast<const half8 *>(blo + bstep * kk);
+                    u32x4 X;
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2)
+                        X[e2] = lds_u16(krow + (8 * kk + 2 * e2) * ROW_BYTES) |
+                                (lds_u16(krow + (8 * kk + 2 * e2 + 1) * ROW_BYTES) << 16);
+                    switch (w) {
+                        case 0: qk_step<0>(S, X, Bh, Bl); break;
+                        case 1: qk_step<1>(S, X, Bh, Bl); break;
+                        case 2: qk_step<2>(S, X, Bh, Bl); break;
+                        default: qk_step<3>(S, X, Bh, Bl); break;
+                    }
                 }
             }
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tl = 8 * r + m;  // token within the lane's 32
-                    float v = __builtin_fmaf(S[m][r], tile_comp(m), bias);
-                    if (has0) {
-                        const uint32_t wd = k0w[tl >> 1];
-                        const float k0 = __uint_as_float((tl & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
-                        v = __builtin_fmaf(q0c, k0, v);
-                    }
-                    x[m][r] = 32 * G + tl < nvl ? v : -__builtin_huge_valf();
-                }
         }
-        float xm = x[0][0];
+        // ---- logits (log2 domain): tokens 32G + 8r + 2w + t of page slot pc, head hc
+        const int lpc = P0 + 4 * u + pc;
+        const int nvl = lpc < P1 ? min(PG, L - lpc * PG) : 0;
+        const float bias = bias_lds[pc][hc];
+        float x[2][4];
+        {
+            const float cmp0 = w == 0 ? tile_comp(0) : w == 1 ? tile_comp(2) : w == 2 ? tile_comp(4) : tile_comp(6);
+            const float cmp1 = w == 0 ? tile_comp(1) : w == 1 ? tile_comp(3) : w == 2 ? tile_comp(5) : tile_comp(7);
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) xm = fmaxf(xm, x[m][r]);
+            for (int r = 0; r < 4; ++r) {
+                const int tok = 32 * G + 8 * r + 2 * w;
+                const uint32_t k0p = has0 ? lds_u32(qb + Ly::OFF_K0 + (pc * PG + tok) * 2) : 0u;
+                float v0 = __builtin_fmaf(S[0][r], cmp0, bias);
+                float v1 = __builtin_fmaf(S[1][r], cmp1, bias);
+                v0 = __builtin_fmaf(q0c, __uint_as_float(k0p << 16), v0);
+                v1 = __builtin_fmaf(q0c, __uint_as_float(k0p & 0xFFFF0000u), v1);
+                x[0][r] = tok < nvl ? v0 : -__builtin_huge_valf();
+                x[1][r] = tok + 1 < nvl ? v1 : -__builtin_huge_valf();
+            }
+        }
+        float xm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
         xm = fmaxf(xm, __shfl_xor(xm, 16));
         xm = fmaxf(xm, __shfl_xor(xm, 32));
-        xm = fmaxf(xm, __shfl_xor(xm, 4));
-        xm = fmaxf(xm, __shfl_xor(xm, 8));
-        float alpha[GRP];
-        bool changed = false;
+        if (lane < 16) colmax[w][lane] = xm;
+        lds_barrier();
+
+        // ---- running max per head over the block (identical in every wave); each
+        //      lane tracks the head n & 3 its score column and value row belong to
+        float cm = lane < 16 ? fmaxf(fmaxf(colmax[0][n], colmax[1][n]), fmaxf(colmax[2][n], colmax[3][n]))
+                             : -__builtin_huge_valf();
+        cm = fmaxf(cm, __shfl_xor(cm, 4));
+        cm = fmaxf(cm, __shfl_xor(cm, 8));  // lane h (< 4) holds the block max of head h
+        const float m_new = fmaxf(m_lane, __shfl(cm, hc));
+        const float alpha_lane = __builtin_amdgcn_exp2f(m_lane - m_new);
+        if (__builtin_amdgcn_ballot_w64(m_new != m_lane)) {
+            float alpha[GRP];
 #pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-            const float mq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xm), h));  // lane h: column (0, h)
-            const float mn = fmaxf(m_run[h], mq);
-            alpha[h] = __builtin_amdgcn_exp2f(m_run[h] - mn);
-            changed |= mn != m_run[h];
-            m_run[h] = mn;
-        }
-        if (changed) {
+            for (int h = 0; h < GRP; ++h)
+                alpha[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha_lane), h));
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) O[t][r] *= alpha[r];
-            z_lane *= sel4(alpha, hv);
-            l_lane *= sel4(alpha, hc);
+            z_lane *= alpha_lane;
+            l_lane *= alpha_lane;
         }
-        const float mh = sel4(m_run, hc);
-        // probabilities, packed as fp16 pairs per value k-step: Pk[kv][e2] = (P[2e2][kv], P[2e2+1][kv])
-        uint32_t Pk[4][4];
+        m_lane = m_new;
+        // probabilities to LDS (key-row area of this buffer): P[p][h][token] fp16
         {
+            const float mh = m_lane;
+            const uint32_t pbase = qb + Ly::OFF_K + pc * 1024;  // [p] 1 KB, chunks as in vm_chunk
             float ls = 0.0f;
 #pragma unroll
-            for (int kv = 0; kv < 4; ++kv)
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const float pa = __builtin_amdgcn_exp2f(x[2 * e2][kv] - mh);
-                    const float pb = __builtin_amdgcn_exp2f(x[2 * e2 + 1][kv] - mh);
-                    ls += pa + pb;
-                    half2v hp;
-                    hp[0] = (_Float16)pa;
-                    hp[1] = (_Float16)pb;
-                    Pk[kv][e2] = as_u32(hp);
-                }
+            for (int r = 0; r < 4; ++r) {
+                const float pa = __builtin_amdgcn_exp2f(x[0][r] - mh);
+                const float pb = __builtin_amdgcn_exp2f(x[1][r] - mh);
+                ls += pa + pb;
+                half2v hp;
+                hp[0] = (_Float16)pa;
+                hp[1] = (_Float16)pb;
+                lds_st32(pbase + chunk_slot(hc, 4 * G + r) * 16 + 4 * w, as_u32(hp));
+            }
             l_lane += ls;
         }
+        lds_barrier();
 
-        // ---- values, page by page
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            if (nv[p] == 0) continue;
-            const uint8_t *vrow = c.v_codes + pgi[p] * (PG * ROW_BYTES) + 2 * n;
-            const uint16_t *vm = c.v_meta + pgi[p] * (2 * VGROUPS * PG);
-            const bool partial = nv[p] < PG;
+        // ---- values of page slot w
+        const int lpw = P0 + 4 * u + w;
+        const int nvp = lpw < P1 ? min(PG, L - lpw * PG) : 0;
+        if (nvp > 0) {
+            const bool partial = nvp < PG;
+            const uint32_t pb = qb + Ly::OFF_K + w * 1024 + chunk_slot(hv, 4 * G) * 16;   // + 256 per k-step
+            const uint32_t sb = qb + Ly::OFF_VM + w * 2048 + chunk_slot(qv, 4 * G) * 16;
+            const uint32_t vb = qb + Ly::OFF_VC + w * Ly::VPS + G * Ly::VBS + 2 * n;
+            const half2v c15 = {(_Float16)1.5f, (_Float16)1.5f};
+            const half2v m15 = {(_Float16)-1.5f, (_Float16)-1.5f};
 #pragma unroll
             for (int kv = 0; kv < 4; ++kv) {
-                const int tok0 = 32 * G + 8 * kv;
-                // P of (page p, head hv) for tokens tok0 .. tok0+7, from lane 16G + 4p + hv
-                uint32_t Pp[4];
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    uint32_t v = Pk[kv][e2];
-                    Pp[e2] = p == 0   ? swz<0x13 | (0 << 5)>(v)
-                             : p == 1 ? swz<0x13 | (4 << 5)>(v)
-                             : p == 2 ? swz<0x13 | (8 << 5)>(v)
-                                      : swz<0x13 | (12 << 5)>(v);
-                }
-                u32x4 sp = *reinterpret_cast<const u32x4 *>(vm + (0 * VGROUPS + qv) * PG + tok0);
-                u32x4 zp = *reinterpret_cast<const u32x4 *>(vm + (1 * VGROUPS + qv) * PG + tok0);
+                u32x4 Pp = lds_u128(pb + 256 * kv);
+                u32x4 sp = lds_u128(sb + 256 * kv);
+                u32x4 zp = lds_u128(sb + 1024 + 256 * kv);
                 if (partial) {
+                    const int tok0 = 32 * G + 8 * kv;
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
-                        const uint32_t keep = (tok0 + 2 * e2 < nv[p] ? 0x0000FFFFu : 0u) |
-                                              (tok0 + 2 * e2 + 1 < nv[p] ? 0xFFFF0000u : 0u);
+                        const uint32_t keep = (tok0 + 2 * e2 < nvp ? 0x0000FFFFu : 0u) |
+                                              (tok0 + 2 * e2 + 1 < nvp ? 0xFFFF0000u : 0u);
                         sp[e2] &= keep;
                         zp[e2] &= keep;
                         Pp[e2] &= keep;
                     }
                 }
                 u32x4 A;
-                const half2v c15 = {(_Float16)1.5f, (_Float16)1.5f};
-                const half2v m15 = {(_Float16)-1.5f, (_Float16)-1.5f};
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const half2v a2 = as_half2(Pp[e2]) * as_half2(sp[e2]);
@@ -359,12 +501,12 @@ __global__ __launch_bounds__(256) void decode_g4_kernel(dqk_cache c, const float
                     z_lane = __builtin_amdgcn_fdot2(as_half2(Pp[e2]), zc, z_lane, false);
                     z_lane = __builtin_amdgcn_fdot2(a2, m15, z_lane, false);
                 }
-                const half8 Ah = as_half8(A);
                 u32x4 X;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2)
-                    X[e2] = ld_u16(vrow + (tok0 + 2 * e2) * ROW_BYTES) |
-                            (ld_u16(vrow + (tok0 + 2 * e2 + 1) * ROW_BYTES) << 16);
+                    X[e2] = lds_u16(vb + (8 * kv + 2 * e2) * ROW_BYTES) |
+                            (lds_u16(vb + (8 * kv + 2 * e2 + 1) * ROW_BYTES) << 16);
+                const half8 Ah = as_half8(A);
                 const Packed XP = pack_shifts(X);
                 O[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<0>(XP)), O[0], 0, 0, 0);
                 O[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<1>(XP)), O[1], 0, 0, 0);
@@ -376,56 +518,49 @@ __global__ __launch_bounds__(256) void decode_g4_kernel(dqk_cache c, const float
                 O[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<7>(XP)), O[7], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        lds_barrier();  // every wave is done with this buffer
+        if (u + 2 < nq)
+            issue_block<KSM>(c, quad_pages(ptab, P0 + 4 * (u + 2), P1, L, hkv, g), qb, w, lane, kro, kmo, kmp);
     }
 
-    // ---- per-wave totals
+    // ---- totals: each wave holds page slot w's value sums; all share m_run
+    wait_dma<0>();
     l_lane += __shfl_xor(l_lane, 4);
     l_lane += __shfl_xor(l_lane, 8);
     l_lane += __shfl_xor(l_lane, 16);
-    l_lane += __shfl_xor(l_lane, 32);   // lanes with hc = h hold l of head h
+    l_lane += __shfl_xor(l_lane, 32);  // lanes with hc = h: this wave's share of l of head h
     z_lane += __shfl_xor(z_lane, 16);
-    z_lane += __shfl_xor(z_lane, 32);   // lane (., 4q + h) holds Z_{q,h}
+    z_lane += __shfl_xor(z_lane, 32);  // lane (., 4q + h): zero-point term of (q, h)
     float zq[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) zq[r] = __shfl(z_lane, 16 * G + 4 * G + r);  // Z_{q = G, h = r}
+    for (int r = 0; r < 4; ++r) zq[r] = __shfl(z_lane, 16 * G + 4 * G + r);  // (q = G, h = r)
+    float m_fin[GRP];
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) m_fin[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_lane), h));
+    float *comb = reinterpret_cast<float *>(&blk[0][0]);  // [WAVES][GRP][D + 1]
+    lds_barrier();
     if ((n >> 2) == G) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) comb[w][r][8 * n + t] = __builtin_fmaf(O[t][r], tile_comp(t), zq[r]);
+            for (int r = 0; r < 4; ++r)
+                comb[(w * GRP + r) * (D + 1) + 8 * n + t] = __builtin_fmaf(O[t][r], tile_comp(t), zq[r]);
     }
-    if (lane < GRP) {
-        comb[w][lane][D] = sel4(m_run, lane);
-        comb[w][lane][D + 1] = l_lane;
-    }
-    __syncthreads();
-
-    // ---- combine the 4 waves and write the split partial (m in natural-log units)
+    if (lane < GRP) comb[(w * GRP + lane) * (D + 1) + D] = l_lane;
+    lds_barrier();
     for (int i = tid; i < GRP * D; i += 256) {
         const int h = i >> 7, ch = i & (D - 1);
-        float M = -__builtin_huge_valf();
-#pragma unroll
-        for (int ww = 0; ww < WAVES; ++ww) M = fmaxf(M, comb[ww][h][D]);
         float acc = 0.0f, lsum = 0.0f;
-        if (M > -__builtin_huge_valf()) {
 #pragma unroll
-            for (int ww = 0; ww < WAVES; ++ww) {
-                const float mw = comb[ww][h][D];
-                if (mw > -__builtin_huge_valf()) {
-                    const float f = __builtin_amdgcn_exp2f(mw - M);
-                    acc = __builtin_fmaf(comb[ww][h][ch], f, acc);
-                    lsum = __builtin_fmaf(comb[ww][h][D + 1], f, lsum);
-                }
-            }
+        for (int ww = 0; ww < WAVES; ++ww) {
+            acc += comb[(ww * GRP + h) * (D + 1) + ch];
+            lsum += comb[(ww * GRP + h) * (D + 1) + D];
         }
         float *dst = partials + (((size_t)b * hq + (size_t)g * GRP + h) * nsplit + split) * PART_FLOATS;
-        dst[ch] = acc;
+        dst[ch] = nq > 0 ? acc : 0.0f;
         if (ch == 0) {
-            dst[D] = M * LN2;
-            dst[D + 1] = lsum;
+            dst[D] = nq > 0 ? m_fin[h] * LN2 : -__builtin_huge_valf();
+            dst[D + 1] = nq > 0 ? lsum : 0.0f;
         }
     }
 }
@@ -443,11 +578,23 @@ int decode_splits_mfma(int batch, int hkv, int max_pages) {
     return s < 1 ? 1 : s;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
+template <int KSM>
+static hipError_t launch_ksm(const DecodeArgs &a, hipStream_t s) {
     dim3 grid(a.num_splits, a.batch * a.hkv);
-    hipLaunchKernelGGL(decode_g4_kernel, grid, dim3(256), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep, a.hq,
+    hipLaunchKernelGGL(decode_g4_kernel<KSM>, grid, dim3(256), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep, a.hq,
                        a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials);
     return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
+    // key k-steps of 8 channels needed for n_keep selected channels
+    const int ks = (a.n_keep + 7) / 8;
+    if (ks <= 2) return launch_ksm<2>(a, s);
+    if (ks <= 4) return launch_ksm<4>(a, s);
+    if (ks <= 7) return launch_ksm<7>(a, s);
+    if (ks <= 10) return launch_ksm<10>(a, s);
+    if (ks <= 13) return launch_ksm<13>(a, s);
+    return launch_ksm<16>(a, s);
 }
 
 }  // namespace dqk

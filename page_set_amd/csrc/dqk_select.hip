@@ -17,52 +17,92 @@ namespace {
 
 constexpr int HCHUNK = 8;  // query heads per register chunk
 
-__global__ __launch_bounds__(128) void select_kernel(const uint16_t *__restrict__ q, const float *__restrict__ t_q,
-                                                     int hq, int hkv, int n_keep, float *__restrict__ q_prime,
-                                                     int32_t *__restrict__ sel_idx) {
-    extern __shared__ float q_lds[];  // [grp][128] bf16 -> fp32 (exact)
-    __shared__ float s_lds[D];
-    __shared__ int keep_lds[D];
-    const int g = blockIdx.x, b = blockIdx.y, j = threadIdx.x;
+constexpr int THREADS = 256;
+constexpr int HALVES = THREADS / D;  // query-head interleave across the two lane halves
+
+__global__ __launch_bounds__(THREADS) void select_kernel(const uint16_t *__restrict__ q, const float *__restrict__ t_q,
+                                                         int hq, int hkv, int n_keep, float *__restrict__ q_prime,
+                                                         int32_t *__restrict__ sel_idx) {
+    __shared__ __attribute__((aligned(16))) float t_lds[D * D];  // T_Q of this KV head (64 KB)
+    extern __shared__ __attribute__((aligned(16))) float q_lds[];  // [grp][128] q (bf16 -> fp32), then [grp][128] q'
+    __shared__ __attribute__((aligned(16))) float s_lds[D];
+    __shared__ unsigned long long mask0;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int grp = hq / hkv;
+    // all loads of the 64 KB transform are issued before any is stored
+    {
+        const float4 *tsrc = reinterpret_cast<const float4 *>(t_q + (size_t)g * D * D);
+        float4 *tdst = reinterpret_cast<float4 *>(t_lds);
+        constexpr int PER = D * D / 4 / THREADS;  // 16 float4 per lane
+        float4 stage[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) stage[k] = tsrc[tid + k * THREADS];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) tdst[tid + k * THREADS] = stage[k];
+    }
     const uint16_t *qg = q + ((size_t)b * hq + (size_t)g * grp) * D;
-    for (int i = j; i < grp * D; i += D) q_lds[i] = bf2f(qg[i]);
+    for (int i = tid; i < grp * D; i += THREADS) q_lds[i] = bf2f(qg[i]);
     __syncthreads();
 
-    const float *T = t_q + (size_t)g * D * D + j;
+    // q'_{h,j}: lane (half, j) runs the chains of heads half, half + 2, ... (ascending i each)
+    float *qpl = q_lds + grp * D;  // q' [grp][128]
+    const int j = tid & (D - 1), half = tid >> 7;
     float *qp = q_prime + ((size_t)b * hq + (size_t)g * grp) * D + j;
-    float S = 0.0f;
-    for (int h0 = 0; h0 < grp; h0 += HCHUNK) {
-        const int nh = grp - h0 < HCHUNK ? grp - h0 : HCHUNK;
+    for (int h0 = half; h0 < grp; h0 += HALVES * HCHUNK) {
         float acc[HCHUNK];
 #pragma unroll
         for (int k = 0; k < HCHUNK; ++k) acc[k] = 0.0f;
+#pragma unroll 8
         for (int i = 0; i < D; ++i) {
-            const float t = T[(size_t)i * D];
+            const float t = t_lds[i * D + j];
 #pragma unroll
-            for (int k = 0; k < HCHUNK; ++k)
-                if (k < nh) acc[k] = __builtin_fmaf(q_lds[(h0 + k) * D + i], t, acc[k]);
+            for (int k = 0; k < HCHUNK; ++k) {
+                const int h = h0 + HALVES * k;
+                if (h < grp) acc[k] = __builtin_fmaf(q_lds[h * D + i], t, acc[k]);
+            }
         }
 #pragma unroll
-        for (int k = 0; k < HCHUNK; ++k)
-            if (k < nh) {
-                qp[(size_t)(h0 + k) * D] = acc[k];
-                S = __builtin_fmaf(acc[k], acc[k], S);
+        for (int k = 0; k < HCHUNK; ++k) {
+            const int h = h0 + HALVES * k;
+            if (h < grp) {
+                qp[(size_t)h * D] = acc[k];
+                qpl[h * D + j] = acc[k];
             }
+        }
     }
-    s_lds[j] = S;
     __syncthreads();
-    int rank = 0;
-    for (int jj = 0; jj < D; ++jj) {
-        const float o = s_lds[jj];
-        rank += (o > S) | ((o == S) & (jj < j));
+    // pooled energy S_j: fma chain over ascending head
+    if (tid < D) {
+        float S = 0.0f;
+        for (int h = 0; h < grp; ++h) {
+            const float v = qpl[h * D + j];
+            S = __builtin_fmaf(v, v, S);
+        }
+        s_lds[j] = S;
     }
-    const int keep = rank < n_keep;
-    keep_lds[j] = keep;
+    __syncthreads();
+    bool keep = false;
+    if (tid < D) {
+        const float S = s_lds[j];
+        int rank = 0;
+#pragma unroll 4
+        for (int jj = 0; jj < D; jj += 4) {
+            const float4 o = *reinterpret_cast<const float4 *>(&s_lds[jj]);
+            rank += (o.x > S) | ((o.x == S) & (jj < j));
+            rank += (o.y > S) | ((o.y == S) & (jj + 1 < j));
+            rank += (o.z > S) | ((o.z == S) & (jj + 2 < j));
+            rank += (o.w > S) | ((o.w == S) & (jj + 3 < j));
+        }
+        keep = rank < n_keep;
+    }
+    // ascending output position = kept channels below j (lanes 0..63 are channels 0..63)
+    const unsigned long long m = __ballot(keep);
+    if (tid == 0) mask0 = m;
     __syncthreads();
     if (keep) {
-        int pos = 0;
-        for (int jj = 0; jj < j; ++jj) pos += keep_lds[jj];
+        const int lane = tid & 63;
+        const unsigned long long below = lane ? (m & ((1ull << lane) - 1ull)) : 0ull;
+        const int pos = __popcll(below) + (tid >= 64 ? __popcll(mask0) : 0);
         if (pos < n_keep) sel_idx[((size_t)b * hkv + g) * n_keep + pos] = j;  // NaN inputs cannot overrun
     }
 }
@@ -73,8 +113,8 @@ hipError_t launch_select(const uint16_t *q, const float *t_q, int batch, int hq,
                          int32_t *sel_idx, hipStream_t s) {
     const int grp = hq / hkv;
     dim3 grid(hkv, batch);
-    const size_t lds = (size_t)grp * D * sizeof(float);
-    hipLaunchKernelGGL(select_kernel, grid, dim3(D), lds, s, q, t_q, hq, hkv, n_keep, q_prime, sel_idx);
+    const size_t lds = 2 * (size_t)grp * D * sizeof(float);
+    hipLaunchKernelGGL(select_kernel, grid, dim3(THREADS), lds, s, q, t_q, hq, hkv, n_keep, q_prime, sel_idx);
     return hipGetLastError();
 }
 
