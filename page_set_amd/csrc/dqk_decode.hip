@@ -303,24 +303,72 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const uint16_t *__rest
 
 // Log-sum-exp merge of the split partials: one workgroup (128 lanes) per
 // (sequence, query head), lane = channel.
-__global__ __launch_bounds__(128) void merge_kernel(const float *__restrict__ partials, int nsplit,
-                                                    float *__restrict__ out, float *__restrict__ lse) {
-    const int bh = blockIdx.x, cch = threadIdx.x;
+constexpr int MERGE_FAST = 32;  // splits whose partials one lane keeps in registers
+
+__global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ partials, int nsplit,
+                                                  float *__restrict__ out, float *__restrict__ lse) {
+    // one block of 128 lanes per (sequence, query head); lane c owns output channel c
+    __shared__ float w_lds[D];
+    __shared__ float red[2][D / 64];
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const float *P = partials + (size_t)bh * nsplit * PART_FLOATS;
-    float M = -__builtin_huge_valf();
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, P[(size_t)s * PART_FLOATS + D]);
-    float Lsum = 0.0f, acc = 0.0f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float m = P[(size_t)s * PART_FLOATS + D];
-        const float l = P[(size_t)s * PART_FLOATS + D + 1];
-        if (l > 0.0f) {
-            const float w = __expf(m - M);
-            Lsum = __builtin_fmaf(l, w, Lsum);
-            acc = __builtin_fmaf(P[(size_t)s * PART_FLOATS + cch], w, acc);
+    // every load that does not depend on the maximum is issued up front
+    float xf[MERGE_FAST];
+    if (nsplit <= MERGE_FAST) {
+#pragma unroll
+        for (int s = 0; s < MERGE_FAST; ++s) xf[s] = s < nsplit ? P[(size_t)s * PART_FLOATS + tid] : 0.0f;
+    }
+    float M = -__builtin_huge_valf(), m_own = -__builtin_huge_valf(), l_own = 0.0f;
+    if (tid < nsplit) {
+        m_own = P[(size_t)tid * PART_FLOATS + D];
+        l_own = P[(size_t)tid * PART_FLOATS + D + 1];
+    }
+    M = m_own;
+    for (int s = tid + D; s < nsplit; s += D) M = fmaxf(M, P[(size_t)s * PART_FLOATS + D]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (lane == 0) red[0][wv] = M;
+    __syncthreads();
+    M = fmaxf(red[0][0], red[0][1]);
+    float lpart = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += D) {
+        const int n = min(D, nsplit - s0);
+        if (s0 > 0) __syncthreads();  // previous chunk's weights are consumed
+        if (tid < n) {
+            float m = m_own, l = l_own;
+            if (s0 > 0) {
+                m = P[(size_t)(s0 + tid) * PART_FLOATS + D];
+                l = P[(size_t)(s0 + tid) * PART_FLOATS + D + 1];
+            }
+            const float w = l > 0.0f ? __expf(m - M) : 0.0f;
+            w_lds[tid] = w;
+            lpart = __builtin_fmaf(l, w, lpart);
+        }
+        __syncthreads();
+        if (nsplit <= MERGE_FAST) {
+#pragma unroll
+            for (int s = 0; s < MERGE_FAST; ++s)
+                if (s < n) acc = __builtin_fmaf(xf[s], w_lds[s], acc);
+        } else {
+            const float *Pc = P + (size_t)s0 * PART_FLOATS + tid;
+            int s = 0;
+            for (; s + 8 <= n; s += 8) {  // eight independent loads in flight, sums kept in split order
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = Pc[(size_t)(s + e) * PART_FLOATS];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], w_lds[s + e], acc);
+            }
+            for (; s < n; ++s) acc = __builtin_fmaf(Pc[(size_t)s * PART_FLOATS], w_lds[s], acc);
         }
     }
-    out[(size_t)bh * D + cch] = acc / Lsum;
-    if (lse && cch == 0) lse[bh] = M + __logf(Lsum);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lpart += __shfl_xor(lpart, o);
+    if (lane == 0) red[1][wv] = lpart;
+    __syncthreads();
+    const float Lsum = red[1][0] + red[1][1];
+    out[(size_t)bh * D + tid] = acc / Lsum;
+    if (lse && tid == 0) lse[bh] = M + __logf(Lsum);
 }
 
 }  // namespace

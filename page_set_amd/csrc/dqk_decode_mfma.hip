@@ -4,30 +4,28 @@
 // copy, INT2 channel-major key rows and token-major values, §3.3; one
 // softmax over the context, §3.4).
 //
-// Workgroup = 4 waves per (split, sequence x KV head); each wave streams its
-// own 4-page blocks ("quads") with an online softmax, and the waves are
-// combined in LDS at the end.  Per quad:
+// Every wave works on its own: a workgroup is one wave, which streams the
+// page pairs of its split through two LDS stages filled by direct
+// global -> LDS loads, keeps its own online softmax and writes one partial
+// (no workgroup barriers anywhere).  Per page pair:
 //
-//  * Scores S^T = codes x q~ on v_mfma_f32_16x16x32_f16, block-diagonal over
-//    the quad's 4 pages: the 16 MFMA columns are (page slot p, head h), the
-//    32-deep k dimension is (page slot, 8 selected channels), so every
-//    column is a real (page, head) pair.  q~ = q' * scale_j (fp16) per page
-//    and channel; the zero points fold into one bias per (page, head).
-//    Token tile m, row i holds token 8i + m, so lane i reads the 16-bit word
-//    i of each selected 32-byte key row: the 8 tokens it needs for all
-//    tiles.
+//  * Scores on v_mfma_f32_16x16x32_f16, block-diagonal over the two pages:
+//    the 32-deep k dimension is (page, 16 selected channels), the 16 columns
+//    are (page, head, limb), where the two limbs are the fp16 hi and lo parts
+//    of q~ = log2(e)/sqrt(d) * q' * scale_j, so one MFMA yields both and a
+//    DPP add of the neighbouring column joins them.  Token tile m, row i
+//    holds token 8i + m: lane i reads the 16-bit word i of each selected
+//    32-byte key row.  The zero points fold into one bias per (page, head).
 //  * 2-bit codes enter MFMA as binary16 subnormals: one AND of a (possibly
-//    shifted) packed word gives code * 2^(offset - 24) exactly for two
-//    tokens at once; the power of two is undone per tile after the MFMA.
-//  * Online softmax in the log2 domain on the score layout (lane = page/head
-//    column, 32 tokens per lane), wave-uniform running max per head.
+//    shifted) packed word gives code * 2^(offset - 24) exactly for two codes
+//    at once; the power of two is undone per tile after the MFMA.
+//  * Online softmax in the log2 domain; the two lanes of a column pair
+//    (the two limbs) split the 8 token tiles between them.
 //  * Values: per page, O[(group q, head h)][channel] += (P*scale_q)[.][token]
-//    x codes[token][channel] on MFMA (M = 4 groups x 4 heads, all rows
-//    real); P is moved to the operand layout with ds_swizzle; the zero
-//    points accumulate as sum_t P z_{t,q} with v_dot2_f32_f16.
+//    x codes[token][channel] on MFMA (M = 4 groups x 4 heads); P moves to the
+//    operand layout through LDS; the zero points accumulate as
+//    sum_t P (z + 1.5 s) - 1.5 sum_t P s with v_dot2_f32_f16 (centred codes).
 #include "dqk_internal.h"
-
-#include <utility>
 
 namespace dqk {
 
@@ -37,9 +35,9 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int GRP = 4;    // query heads per KV head handled here
-constexpr int WAVES = 4;  // waves per workgroup
+constexpr int GRP = 4;  // query heads per KV head handled here
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -73,31 +71,40 @@ __device__ __forceinline__ u32x4 tile_codes(const Packed &P) {
     return (m <= 1 ? P.L : m <= 4 ? P.X : P.R) & mask;
 }
 
-__device__ __forceinline__ uint32_t ld_u16(const uint8_t *p) { return *reinterpret_cast<const uint16_t *>(p); }
-
-template <int PAT>
-__device__ __forceinline__ uint32_t swz(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, PAT);
+// ---------------------------------------------------------------- LDS access
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+__device__ __forceinline__ uint32_t lds_u16(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t *>((uintptr_t)a);
+}
+__device__ __forceinline__ u32x2 lds_u64(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x2 *>((uintptr_t)a);
+}
+__device__ __forceinline__ u32x4 lds_u128(uint32_t a) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)a);
+}
+__device__ __forceinline__ void lds_st64(uint32_t a, u32x2 v) {
+    *reinterpret_cast<__attribute__((address_space(3))) u32x2 *>((uintptr_t)a) = v;
+}
+// Two 16-bit LDS words -> one dword (lo, hi).
+__device__ __forceinline__ uint32_t lds_pair(uint32_t a_lo, uint32_t a_hi) {
+    return __builtin_amdgcn_perm(lds_u16(a_hi), lds_u16(a_lo), 0x05040100u);
 }
 
-__device__ __forceinline__ float sel4(const float (&a)[4], int i) {
-    return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
-}
-__device__ __forceinline__ int64_t sel4i(const int64_t (&a)[4], int i) {
-    return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
-}
-__device__ __forceinline__ int sel4n(const int (&a)[4], int i) {
-    return i == 0 ? a[0] : i == 1 ? a[1] : i == 2 ? a[2] : a[3];
-}
-
-// ---------------------------------------------------------------- staging through LDS
-// Direct global -> LDS loads (16 or 4 bytes per lane, written at M0 + lane * size).
-// They are issued from asm so that the compiler's conservative wait-for-all
-// before every LDS read does not apply; completion is awaited explicitly with
-// s_waitcnt vmcnt(N), N = DMA instructions this wave issued afterwards (any
-// other vector memory op only makes that wait stricter).
+// ---------------------------------------------------------------- direct global -> LDS loads
+// 16 or 4 bytes per lane, written at M0 + lane * size.  Issued from asm so
+// that the compiler's conservative wait-for-all before every LDS read does
+// not apply; completion is awaited explicitly with s_waitcnt vmcnt(N), N =
+// vector memory instructions this wave issued afterwards (any other vector
+// memory op only makes that wait stricter).
+// sbase must be wave-uniform (it is moved into SGPRs).
 __device__ __forceinline__ void dma16_s(const void *sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %0" ::"s"(sbase), "v"(voff), "s"(lds)
+    const uint64_t a = (uint64_t)(uintptr_t)sbase;
+    const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %0" ::"s"((const void *)(uintptr_t)u), "v"(voff),
+                 "s"(lds)
                  : "memory", "m0");
 }
 __device__ __forceinline__ void dma16_v(const void *addr, uint32_t lds) {
@@ -110,382 +117,399 @@ template <int N>
 __device__ __forceinline__ void wait_dma() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// Workgroup barrier that waits only for this wave's LDS operations.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+// ---------------------------------------------------------------- cross-lane moves
+__device__ __forceinline__ float bcast_lane(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float dpp_xor1(float v) {  // quad_perm [1, 0, 3, 2]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor8(float v) {  // row_ror:8 within 16 lanes
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+// v_permlane16_swap with both operands v leaves (row 0, row 0, row 2, row 2) in
+// the first result and (row 1, row 1, row 3, row 3) in the second (rows of 16
+// lanes); v_permlane32_swap does the same for the two halves.  Combining the
+// two results reduces over lane ^ 16 (lane ^ 32), identically in both lanes.
+__device__ __forceinline__ float sum_x16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_x16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int KSM>
-struct Lay {
-    static constexpr int NCH = 8 * KSM;            // compacted channel slots
-    static constexpr int KHR = 2 * NCH;            // 16-byte key half rows per page
-    static constexpr int KPS = 32 * NCH + 32;      // key page stride: row groups of the 4 pages start 8 banks apart
-    static constexpr int KINS = (KHR + 63) / 64;   // DMA instructions per key page
-    static constexpr int KMI = (4 * NCH + 63) / 64;  // 4-byte DMA instructions for key metadata
-    static constexpr int VBS = 32 * ROW_BYTES + 32;  // value block (32 tokens) stride, 8 banks apart
-    static constexpr int VPS = 4 * VBS;
-    static constexpr int OFF_K = 0;
-    static constexpr int KAREA = 4 * KPS > 4 * GRP * PG * 2 ? 4 * KPS : 4 * GRP * PG * 2;  // key rows, later P
-    static constexpr int OFF_KM = OFF_K + KAREA;       // u32 (scale | zero << 16) [4][NCH]
-    static constexpr int OFF_K0 = OFF_KM + 16 * NCH;   // bf16 [4][128]
-    static constexpr int OFF_VC = OFF_K0 + 4 * 256;    // value codes [4][4 blocks][32 rows][32 B]
-    static constexpr int OFF_VM = OFF_VC + 4 * VPS;    // fp16 [4][2][4][128]
-    static constexpr int QB = OFF_VM + 4 * 2048;       // one 4-page block
-    static constexpr int NDMA = 4 * KINS + KMI + 1 + 16 + 8;
-    static constexpr int NW = (NDMA + WAVES - 1) / WAVES;  // DMA instructions per wave per block
-    static_assert(OFF_K0 % 16 == 0 && OFF_VC % 16 == 0 && OFF_VM % 16 == 0 && QB % 16 == 0, "alignment");
+// ---------------------------------------------------------------- stage layout
+// One stage holds a page pair.  Key rows: 16 KS row slots per page (the
+// selected INT2 channels in ascending order, padded with the all-zero row 0),
+// slot s holding row s ^ ((s >> 3) & 1), page 1 starting 64 bytes later
+// modulo 256, so that the four rows one k-step reads at a time fall in
+// distinct banks.  The probabilities of the pair reuse the key-row area once
+// the scores are done.
+template <int KS>
+struct Stage {
+    static constexpr int NR = 16 * KS;                             // key row slots per page
+    static constexpr int KRP = NR * ROW_BYTES + 64;                // key page stride
+    static constexpr int KAREA = 2 * KRP > 2048 ? 2 * KRP : 2048;  // key rows, then P [2][4][128] fp16
+    static constexpr int OFF_KM = KAREA;                           // (scale | zero << 16) [2][NR]
+    static constexpr int OFF_K0 = OFF_KM + 2 * NR * 4;             // channel 0, bf16 [2][128]
+    static constexpr int VBS = 32 * ROW_BYTES + 32;                // value block (32 tokens) stride
+    static constexpr int VPS = 4 * VBS;                            // value page stride
+    static constexpr int OFF_VC = OFF_K0 + 2 * PG * 2;             // value codes [2][4][32][32 B]
+    static constexpr int OFF_VM = OFF_VC + 2 * VPS;                // value (scale, zero) [2][2][4][128]
+    static constexpr int BYTES = OFF_VM + 2 * 2048;
+    static constexpr int KRI = (2 * NR + 63) / 64;  // 16-byte key-row DMAs per page
+    static constexpr int KMI = (2 * NR + 63) / 64;  // 4-byte key-metadata DMAs for the pair
+    static constexpr int NDMA = 2 * KRI + KMI + 1 + 8 + 4;
+    static_assert(KAREA % 16 == 0 && OFF_KM % 16 == 0 && OFF_K0 % 16 == 0 && OFF_VC % 16 == 0 &&
+                      OFF_VM % 16 == 0 && BYTES % 16 == 0,
+                  "alignment");
+    static_assert(NDMA <= 63, "vmcnt range");
 };
 
-struct Quad {
-    int64_t pg[4];  // physical page * hkv + g
-    int nv[4];      // valid tokens (0 for slots past the range)
+struct Pair {
+    int64_t pg0, pg1;  // physical page * hkv + g of the two slots (slot 1 repeats slot 0 when absent)
 };
 
-// Pages of logical pages lp0 .. lp0+3; slots past P1 reuse page lp0 (always valid).
-__device__ __forceinline__ Quad quad_pages(const int32_t *__restrict__ ptab, int lp0, int P1, int L, int hkv, int g) {
-    Quad q;
+__device__ __forceinline__ Pair pair_pages(const int32_t *__restrict__ ptab, int lp0, int P1, int hkv, int g) {
+    Pair p;
+    p.pg0 = (int64_t)ptab[lp0] * hkv + g;
+    p.pg1 = lp0 + 1 < P1 ? (int64_t)ptab[lp0 + 1] * hkv + g : p.pg0;
+    return p;
+}
+
+// Per-lane DMA source offsets, fixed for the whole split.
+template <int KS>
+struct DmaPlan {
+    uint32_t kro[Stage<KS>::KRI];  // key half-row source offsets within a page
+    uint32_t kmo[Stage<KS>::KMI];  // key metadata offsets within a page
+    uint32_t kmp;                  // bit t: key-metadata DMA t reads page slot 1
+    uint32_t vmo;                  // value metadata chunk offset (permuted, see the plan)
+};
+
+// Fill one stage with a page pair: this wave issues exactly Stage<KS>::NDMA
+// vector memory instructions, each with at least lane 0 active.
+template <int KS>
+__device__ __forceinline__ void issue_pair(const dqk_cache &c, const Pair &pr, uint32_t st, int lane,
+                                           const DmaPlan<KS> &pl) {
+    using S = Stage<KS>;
+    // key rows (64 half rows per instruction)
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const int lp = lp0 + p;
-        const bool ok = lp < P1;
-        q.pg[p] = (int64_t)ptab[ok ? lp : lp0] * hkv + g;
-        q.nv[p] = ok ? min(PG, L - lp * PG) : 0;
+    for (int p = 0; p < 2; ++p) {
+        const uint8_t *base = c.k_codes + (p ? pr.pg1 : pr.pg0) * (D * ROW_BYTES);
+#pragma unroll
+        for (int j = 0; j < S::KRI; ++j)
+            if (64 * j + lane < 2 * S::NR) dma16_s(base, pl.kro[j], st + p * S::KRP + 64 * j * 16);
     }
-    return q;
-}
-
-__device__ __forceinline__ int64_t sel4l(const int64_t (&a)[4], int i) {
-    const int64_t lo = (i & 1) ? a[1] : a[0];
-    const int64_t hi = (i & 1) ? a[3] : a[2];
-    return (i & 2) ? hi : lo;
-}
-
-// 16-byte chunks (row r of 4, chunk c of 16: tokens 8c .. 8c+7) of a 1 KB
-// [4][128] fp16 table are stored at slot 16 (c & 3) + 4 (c >> 2) + r, so that
-// the 16 chunks (r, 4G + k) read together for a k-step fall in distinct banks.
-// LDS slot l of a DMA receives the chunk read from this byte offset:
-__device__ __forceinline__ uint32_t vm_chunk(int l) {
-    const int r = l & 3, c = 4 * ((l >> 2) & 3) + (l >> 4);
-    return (uint32_t)(r * 256 + c * 16);
-}
-__device__ __forceinline__ constexpr int chunk_slot(int r, int c) { return 16 * (c & 3) + 4 * (c >> 2) + r; }
-
-// One DMA instruction of a block fill; D_ is its compile-time index.
-template <int KSM, int D_>
-__device__ __forceinline__ void block_dma(const dqk_cache &c, const Quad &Q, uint32_t qb, int lane,
-                                          const uint32_t (&kro)[Lay<KSM>::KINS],
-                                          const uint32_t (&kmo)[Lay<KSM>::KMI], const int (&kmp)[Lay<KSM>::KMI]) {
-    using Ly = Lay<KSM>;
-    constexpr int NK = 4 * Ly::KINS, NKM = NK + Ly::KMI, NK0 = NKM + 1, NVC = NK0 + 16;
-    constexpr int d = D_ < Ly::NDMA ? D_ : NKM;  // spare slots repeat the channel-0 load (same bytes)
-    if constexpr (d < NK) {  // selected key rows of page p, 64 half rows per instruction
-        constexpr int p = d / Ly::KINS, j = d % Ly::KINS;
-        if (64 * j + lane < Ly::KHR)
-            dma16_s(c.k_codes + Q.pg[p] * (D * ROW_BYTES), kro[j], qb + Ly::OFF_K + p * Ly::KPS + 64 * j * 16);
-    } else if constexpr (d < NKM) {  // (scale, zero) of the selected channels of the 4 pages
-        constexpr int t = d - NK;
-        if (64 * t + lane < 4 * Ly::NCH)
-            dma4_v(reinterpret_cast<const uint8_t *>(c.k_meta) + sel4l(Q.pg, kmp[t]) * (D * 4) + kmo[t],
-                   qb + Ly::OFF_KM + 64 * t * 4);
-    } else if constexpr (d < NK0) {  // channel 0 of the 4 pages
-        dma16_v(reinterpret_cast<const uint8_t *>(c.k_ch0) + sel4l(Q.pg, lane >> 4) * (PG * 2) + (lane & 15) * 16,
-                qb + Ly::OFF_K0);
-    } else if constexpr (d < NVC) {  // value codes: page p, 32-token block bb
-        constexpr int p = (d - NK0) >> 2, bb = (d - NK0) & 3;
-        dma16_s(c.v_codes + Q.pg[p] * (PG * ROW_BYTES) + bb * 1024, (uint32_t)lane * 16u,
-                qb + Ly::OFF_VC + p * Ly::VPS + bb * Ly::VBS);
-    } else {  // value metadata: page p, half hf (scales / zeros), chunks permuted (see vm_chunk)
-        constexpr int p = (d - NVC) >> 1, hf = (d - NVC) & 1;
-        dma16_s(reinterpret_cast<const uint8_t *>(c.v_meta) + Q.pg[p] * (2 * VGROUPS * PG * 2) + hf * 1024,
-                vm_chunk(lane), qb + Ly::OFF_VM + p * 2048 + hf * 1024);
+    // (scale, zero) of the selected channels, both pages
+    const uint8_t *km0 = reinterpret_cast<const uint8_t *>(c.k_meta) + pr.pg0 * (D * 4);
+    const uint8_t *km1 = reinterpret_cast<const uint8_t *>(c.k_meta) + pr.pg1 * (D * 4);
+#pragma unroll
+    for (int t = 0; t < S::KMI; ++t)
+        if (64 * t + lane < 2 * S::NR) dma4_v(((pl.kmp >> t) & 1u ? km1 : km0) + pl.kmo[t], st + S::OFF_KM + 64 * t * 4);
+    // channel 0 of both pages (32 lanes x 16 bytes)
+    if (lane < 32) {
+        const uint8_t *k0 = reinterpret_cast<const uint8_t *>(c.k_ch0) + (lane < 16 ? pr.pg0 : pr.pg1) * (PG * 2);
+        dma16_v(k0 + (lane & 15) * 16, st + S::OFF_K0);
+    }
+    // value codes: page p, 32-token block bb
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const uint8_t *base = c.v_codes + (p ? pr.pg1 : pr.pg0) * (PG * ROW_BYTES);
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+            dma16_s(base + bb * 1024, (uint32_t)lane * 16u, st + S::OFF_VC + p * S::VPS + bb * S::VBS);
+    }
+    // value metadata: page p, half hf (scales, zeros)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const uint8_t *base =
+            reinterpret_cast<const uint8_t *>(c.v_meta) + (p ? pr.pg1 : pr.pg0) * (2 * VGROUPS * PG * 2);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) dma16_s(base + hf * 1024, pl.vmo, st + S::OFF_VM + p * 2048 + hf * 1024);
     }
 }
 
-template <int KSM, int... Ds>
-__device__ __forceinline__ void issue_all(const dqk_cache &c, const Quad &Q, uint32_t qb, int w, int lane,
-                                          const uint32_t (&kro)[Lay<KSM>::KINS],
-                                          const uint32_t (&kmo)[Lay<KSM>::KMI], const int (&kmp)[Lay<KSM>::KMI],
-                                          std::integer_sequence<int, Ds...>) {
-    ((w == (Ds & (WAVES - 1)) ? block_dma<KSM, Ds>(c, Q, qb, lane, kro, kmo, kmp) : (void)0), ...);
-}
-
-// Issue this wave's share (NW instructions) of the DMAs that fill one block buffer.
-template <int KSM>
-__device__ __forceinline__ void issue_block(const dqk_cache &c, const Quad &Q, uint32_t qb, int w, int lane,
-                                            const uint32_t (&kro)[Lay<KSM>::KINS],
-                                            const uint32_t (&kmo)[Lay<KSM>::KMI], const int (&kmp)[Lay<KSM>::KMI]) {
-    issue_all<KSM>(c, Q, qb, w, lane, kro, kmo, kmp, std::make_integer_sequence<int, WAVES * Lay<KSM>::NW>{});
-}
-
-__device__ __forceinline__ uint32_t lds_u16(uint32_t a) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t *>((uintptr_t)a);
-}
-__device__ __forceinline__ uint32_t lds_u32(uint32_t a) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t *>((uintptr_t)a);
-}
-__device__ __forceinline__ u32x4 lds_u128(uint32_t a) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>((uintptr_t)a);
-}
-__device__ __forceinline__ void lds_st32(uint32_t a, uint32_t v) {
-    *reinterpret_cast<__attribute__((address_space(3))) uint32_t *>((uintptr_t)a) = v;
-}
-__device__ __forceinline__ void lds_stf(uint32_t a, float v) {
-    *reinterpret_cast<__attribute__((address_space(3))) float *>((uintptr_t)a) = v;
-}
-__device__ __forceinline__ float lds_f(uint32_t a) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) float *>((uintptr_t)a);
-}
-
-// Score tiles 2W, 2W+1 of one k-step (hi and lo halves of q~).
-template <int W>
-__device__ __forceinline__ void qk_step(f32x4 (&S)[2], const u32x4 &X, const half8 &Bh, const half8 &Bl) {
-    Packed P;
-    if (W == 0) P.L = X << 4;
-    if (W == 2 || W == 3) P.R = X >> 6;
-    P.X = X;
-    const half8 a0 = as_half8(tile_codes<2 * W>(P));
-    const half8 a1 = as_half8(tile_codes<2 * W + 1>(P));
-    S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bh, S[0], 0, 0, 0);
-    S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bh, S[1], 0, 0, 0);
-    S[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, Bl, S[0], 0, 0, 0);
-    S[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, Bl, S[1], 0, 0, 0);
-}
-
-template <int KSM>
-__global__ __launch_bounds__(256) void decode_g4_kernel(dqk_cache c, const float *__restrict__ q_prime,
-                                                        const int32_t *__restrict__ sel_idx, int n_keep, int hq,
-                                                        const int32_t *__restrict__ page_table, int max_pages,
-                                                        const int32_t *__restrict__ seq_lens, float sm_scale,
-                                                        int nsplit, float *__restrict__ partials) {
-    using Ly = Lay<KSM>;
-    constexpr int NCH = Ly::NCH;
-    // two block buffers; the scores' probabilities reuse the key rows of the
-    // current buffer once every wave is past its score MFMAs
-    __shared__ __attribute__((aligned(16))) uint8_t blk[2][Ly::QB];
-    __shared__ __attribute__((aligned(16))) _Float16 qt[2][4][GRP][NCH];  // q~ hi/lo [p][h][jj]
-    __shared__ __attribute__((aligned(16))) float colmax[WAVES][16];
-    __shared__ __attribute__((aligned(16))) float bias_lds[4][GRP];
-    __shared__ __attribute__((aligned(16))) _Float16 zero16[8];
-    static_assert(4 * GRP * PG * 2 <= Ly::KAREA, "probabilities fit in the key-row area");
+template <int KS>
+__global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float *__restrict__ q_prime,
+                                                       const int32_t *__restrict__ sel_idx, int n_keep, int hq,
+                                                       const int32_t *__restrict__ page_table, int max_pages,
+                                                       const int32_t *__restrict__ seq_lens, float sm_scale,
+                                                       int nsplit, float *__restrict__ partials) {
+    using S = Stage<KS>;
+    constexpr int NR = S::NR;
+    __shared__ __attribute__((aligned(16))) uint8_t stg[2][S::BYTES];
 
     const int split = blockIdx.x, bg = blockIdx.y;
     const int hkv = c.num_kv_heads;
     const int b = bg / hkv, g = bg - b * hkv;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform by construction
+    const int lane = threadIdx.x;
     const int G = lane >> 4, n = lane & 15;
     const int L = seq_lens[b];
     const int npages = (L + PG - 1) / PG;
-    const int per = (((npages + nsplit - 1) / nsplit) + 15) & ~15;
+    const int per = (((npages + nsplit - 1) / nsplit) + 1) & ~1;
     const int P0 = min(npages, split * per), P1 = min(npages, P0 + per);
-    const int nq = (P1 - P0 + 3) >> 2;
+    const int npairs = (P1 - P0 + 1) >> 1;
 
     const float C = sm_scale * LOG2E;
-    const int32_t *sel = sel_idx + ((size_t)b * hkv + g) * n_keep;
-    const int has0 = sel[0] == 0;  // the list is ascending
-    const int R = n_keep - has0;   // selected INT2 channels (R <= NCH)
-    const int KS = (R + 7) >> 3;
-    const float *qp = q_prime + ((size_t)b * hq + (size_t)g * GRP) * D;
-    auto chan = [&](int jj) { return jj < R ? sel[jj + has0] : 0; };
-
-    // per-lane DMA source offsets (fixed for the whole split)
-    uint32_t kro[Ly::KINS];
-#pragma unroll
-    for (int j = 0; j < Ly::KINS; ++j) {
-        const int hr = 64 * j + lane;
-        kro[j] = hr < Ly::KHR ? (uint32_t)chan(hr >> 1) * ROW_BYTES + (hr & 1) * 16 : 0u;
+    static_assert(GRP * D * 4 + D * 4 <= S::BYTES, "q' and the selection fit in one stage");
+    // q' of the 4 heads and the selected channels go through LDS (stage 1, before its
+    // first fill) with one round of loads
+    {
+        const float4 *qsrc = reinterpret_cast<const float4 *>(q_prime + ((size_t)b * hq + (size_t)g * GRP) * D);
+        const int32_t *ssrc = sel_idx + ((size_t)b * hkv + g) * n_keep;
+        const float4 qa = qsrc[lane], qb = qsrc[lane + 64];
+        const int sa = ssrc[min(lane, n_keep - 1)], sb = ssrc[min(lane + 64, n_keep - 1)];
+        float4 *qd = reinterpret_cast<float4 *>(&stg[1][0]);
+        int32_t *sd = reinterpret_cast<int32_t *>(&stg[1][GRP * D * 4]);
+        qd[lane] = qa;
+        qd[lane + 64] = qb;
+        sd[lane] = sa;
+        sd[lane + 64] = sb;
     }
-    uint32_t kmo[Ly::KMI];
-    int kmp[Ly::KMI];
-#pragma unroll
-    for (int t = 0; t < Ly::KMI; ++t) {
-        const int idx = min(64 * t + lane, 4 * NCH - 1);
-        kmp[t] = idx / NCH;
-        kmo[t] = (uint32_t)chan(idx - kmp[t] * NCH) * 4u;
-    }
-    // staging lane: channels 2*lane, 2*lane+1 of page slot w; C * q' of them for the 4 heads
-    float qs[GRP][2];
-#pragma unroll
-    for (int h = 0; h < GRP; ++h)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int jj = 2 * lane + e;
-            qs[h][e] = jj < R ? qp[h * D + chan(jj)] * C : 0.0f;
-        }
-    const int pc = n >> 2, hc = n & 3;  // score lane: column (page slot, head)
-    const int qv = n >> 2, hv = n & 3;  // value lane: row (group, head)
-    const float q0c = has0 ? qp[hc * D] * C : 0.0f;
-    if (tid < 8) zero16[tid] = (_Float16)0.0f;
+    __syncthreads();
+    const float *q_l = reinterpret_cast<const float *>(&stg[1][0]);            // [4][128]
+    const int32_t *sel_l = reinterpret_cast<const int32_t *>(&stg[1][GRP * D * 4]);  // [n_keep]
+    const int has0 = sel_l[0] == 0;  // the list is ascending
+    const int R = n_keep - has0;     // selected INT2 channels (R <= NR)
+    // selected INT2 channel of key row r; rows past R read the all-zero row 0
+    auto chan = [&](int r) {
+        const int v = sel_l[min(r + has0, n_keep - 1)];
+        return r < R ? v : 0;
+    };
 
-    const uint32_t blk0 = lds_addr(&blk[0][0]);
+    // ---- DMA plan, and the first pair in flight
+    DmaPlan<KS> pl;
+#pragma unroll
+    for (int j = 0; j < S::KRI; ++j) {
+        const int x = 64 * j + lane, s = x >> 1;
+        const int r = s ^ ((s >> 3) & 1);
+        pl.kro[j] = x < 2 * NR ? (uint32_t)chan(r) * ROW_BYTES + (x & 1) * 16 : 0u;
+    }
+    pl.kmp = 0;
+#pragma unroll
+    for (int t = 0; t < S::KMI; ++t) {
+        const int x = min(64 * t + lane, 2 * NR - 1);
+        const int p = x >= NR;
+        pl.kmp |= (uint32_t)p << t;
+        pl.kmo[t] = (uint32_t)chan(x - p * NR) * 4u;
+    }
+    // value metadata: LDS slot l of each 1 KB half holds chunk (l & 15) ^ (l >> 4) of group l >> 4
+    pl.vmo = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ (lane >> 4)));
+
+    const uint32_t st0 = lds_addr(&stg[0][0]);
     const int32_t *ptab = page_table + (size_t)b * max_pages;
-    if (nq > 0) issue_block<KSM>(c, quad_pages(ptab, P0, P1, L, hkv, g), blk0, w, lane, kro, kmo, kmp);
-    if (nq > 1) issue_block<KSM>(c, quad_pages(ptab, P0 + 4, P1, L, hkv, g), blk0 + Ly::QB, w, lane, kro, kmo, kmp);
+    if (npairs > 0) issue_pair<KS>(c, pair_pages(ptab, P0, P1, hkv, g), st0, lane, pl);
 
-    float m_lane = -__builtin_huge_valf();  // running max (log2 domain) of head n & 3
-    float l_lane = 0.0f, z_lane = 0.0f;
+    // ---- score lanes.  Lane (G, n): k range = page G >> 1, channels
+    //      16 ks + 8 (G & 1) + 0..7; column n = (page pp, head hh, limb ll).
+    const int pp = n >> 3, hh = (n >> 1) & 3, ll = n & 1;
+    const int kpage = G >> 1, kh = G & 1;
+    // C q' as fp16 pairs: limb-1 lanes hold (hi, lo), limb-0 lanes (0, hi), so
+    // fma(QL, s, fma(QH, s, -QH s)) is the lane's limb of C q' s either way
+    uint32_t QH[KS][4], QL[KS][4];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+            half2v h, l;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int jj = 16 * ks + 8 * kh + 2 * e2 + u;
+                const float qj = q_l[hh * D + chan(jj)];
+                const float v = (pp == kpage && jj < R) ? qj * C : 0.0f;
+                const _Float16 vh = (_Float16)v;
+                const _Float16 vl = (_Float16)(v - (float)vh);
+                h[u] = ll ? vh : (_Float16)0.0f;
+                l[u] = ll ? vl : vh;
+            }
+            QH[ks][e2] = as_u32(h);
+            QL[ks][e2] = as_u32(l);
+        }
+    const float q0 = q_l[hh * D];
+    const float q0c = has0 ? q0 * C : 0.0f;
+    // stage 1 is free again once every LDS read above has returned
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (npairs > 1) issue_pair<KS>(c, pair_pages(ptab, P0 + 2, P1, hkv, g), st0 + S::BYTES, lane, pl);
+    float comp[4];  // this lane keeps tiles 4 ll + j after the limb split
+#pragma unroll
+    for (int j = 0; j < 4; ++j) comp[j] = ll ? tile_comp(4 + j) : tile_comp(j);
+
+    // ---- per-lane LDS offsets within a stage
+    // key row 16 ks + 8 kh + e sits in slot 16 ks + 8 kh + (e ^ kh)
+    const uint32_t kr_even = kpage * S::KRP + (9 * kh) * ROW_BYTES + 2 * n;  // e even: slot e + kh
+    const uint32_t kr_odd = kpage * S::KRP + (7 * kh) * ROW_BYTES + 2 * n;   // e odd: slot e - kh
+    const uint32_t km_lane = S::OFF_KM + (kpage * NR + 8 * kh) * 4;
+    const uint32_t k0_lane = S::OFF_K0 + pp * 256 + 64 * G + 8 * ll;
+    uint32_t pw[4];  // P writes: chunk 4G + r of (pp, hh) at slot (4G + r) ^ hh, half ll
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = pp * 1024 + hh * 256 + 16 * ((4 * G + r) ^ hh) + 8 * ll;
+    // value lanes: row (q, h) = (n >> 2, n & 3), tokens 32 G + 8 kv + 0..7
+    const int qv = n >> 2, hv = n & 3;
+    uint32_t pr_ofs[4], vm_ofs[4];
+#pragma unroll
+    for (int kv = 0; kv < 4; ++kv) {
+        pr_ofs[kv] = hv * 256 + 16 * ((4 * G + kv) ^ hv);
+        vm_ofs[kv] = S::OFF_VM + qv * 256 + 16 * ((4 * G + kv) ^ qv);
+    }
+    const uint32_t vc_lane = S::OFF_VC + G * S::VBS + 2 * n;
+
+    float m_run = -__builtin_huge_valf();  // running max (log2 domain) of head hh
+    float l_acc = 0.0f, z_acc = 0.0f;
     f32x4 O[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) O[t] = {0.f, 0.f, 0.f, 0.f};
 
-    for (int u = 0; u < nq; ++u) {
-        const uint32_t qb = blk0 + (uint32_t)(u & 1) * Ly::QB;
-        if (u + 1 < nq)
-            wait_dma<Ly::NW>();
+    for (int u = 0; u < npairs; ++u) {
+        const uint32_t st = st0 + (uint32_t)(u & 1) * S::BYTES;
+        const int lp0 = P0 + 2 * u;
+        const int nv0 = min(PG, L - lp0 * PG);
+        const int nv1 = lp0 + 1 < P1 ? min(PG, L - (lp0 + 1) * PG) : 0;
+        const bool more = u + 2 < npairs;
+        Pair nxt = {0, 0};
+        if (more) nxt = pair_pages(ptab, lp0 + 4, P1, hkv, g);
+        if (u + 1 < npairs)
+            wait_dma<S::NDMA>();
         else
             wait_dma<0>();
-        lds_barrier();
 
-        // ---- stage q~ (fp16 hi/lo) for page slot w, channels 2 lane, 2 lane + 1; bias partials
-        {
-            float bp[GRP] = {0.f, 0.f, 0.f, 0.f};
-            if (2 * lane < NCH) {
-                const bool pv = P0 + 4 * u + w < P1;
-                const uint32_t sz0 = lds_u32(qb + Ly::OFF_KM + (w * NCH + 2 * lane) * 4);
-                const uint32_t sz1 = lds_u32(qb + Ly::OFF_KM + (w * NCH + 2 * lane + 1) * 4);
-                const float s0 = pv ? h2f((uint16_t)sz0) : 0.f, z0 = pv ? h2f((uint16_t)(sz0 >> 16)) : 0.f;
-                const float s1 = pv ? h2f((uint16_t)sz1) : 0.f, z1 = pv ? h2f((uint16_t)(sz1 >> 16)) : 0.f;
+        // ---- scores and the zero-point bias
+        f32x4 Sc[8];
 #pragma unroll
-                for (int h = 0; h < GRP; ++h) {
-                    const float t0 = qs[h][0] * s0, t1 = qs[h][1] * s1;
-                    half2v hi, lo;
-                    hi[0] = (_Float16)t0;
-                    hi[1] = (_Float16)t1;
-                    lo[0] = (_Float16)(t0 - (float)hi[0]);
-                    lo[1] = (_Float16)(t1 - (float)hi[1]);
-                    *reinterpret_cast<half2v *>(&qt[0][w][h][2 * lane]) = hi;
-                    *reinterpret_cast<half2v *>(&qt[1][w][h][2 * lane]) = lo;
-                    bp[h] = __builtin_fmaf(qs[h][1], z1, qs[h][0] * z0);
-                }
+        for (int t = 0; t < 8; ++t) Sc[t] = {0.f, 0.f, 0.f, 0.f};
+        float bias = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 d0 = lds_u128(st + km_lane + 64 * ks);
+            const u32x4 d1 = lds_u128(st + km_lane + 64 * ks + 16);
+            const uint32_t dd[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+            u32x4 Bv;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const half2v s2 = as_half2(__builtin_amdgcn_perm(dd[2 * e2 + 1], dd[2 * e2], 0x05040100u));
+                const half2v z2 = as_half2(__builtin_amdgcn_perm(dd[2 * e2 + 1], dd[2 * e2], 0x07060302u));
+                const half2v qh = as_half2(QH[ks][e2]), ql = as_half2(QL[ks][e2]);
+                const half2v t1 = qh * s2;
+                const half2v t2 = __builtin_elementwise_fma(qh, s2, -t1);
+                Bv[e2] = as_u32(__builtin_elementwise_fma(ql, s2, t2));
+                bias = __builtin_amdgcn_fdot2(qh, z2, bias, false);
+                bias = __builtin_amdgcn_fdot2(ql, z2, bias, false);
             }
+            const half8 Bh = as_half8(Bv);
+            u32x4 X;
+            const uint32_t kb = st + 16 * ks * ROW_BYTES;
 #pragma unroll
-            for (int h = 0; h < GRP; ++h) {
+            for (int e2 = 0; e2 < 4; ++e2) X[e2] = lds_pair(kb + kr_even + 64 * e2, kb + kr_odd + 64 * e2 + ROW_BYTES);
+            const Packed XP = pack_shifts(X);
+            Sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<0>(XP)), Bh, Sc[0], 0, 0, 0);
+            Sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<1>(XP)), Bh, Sc[1], 0, 0, 0);
+            Sc[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<2>(XP)), Bh, Sc[2], 0, 0, 0);
+            Sc[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<3>(XP)), Bh, Sc[3], 0, 0, 0);
+            Sc[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<4>(XP)), Bh, Sc[4], 0, 0, 0);
+            Sc[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<5>(XP)), Bh, Sc[5], 0, 0, 0);
+            Sc[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<6>(XP)), Bh, Sc[6], 0, 0, 0);
+            Sc[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<7>(XP)), Bh, Sc[7], 0, 0, 0);
+        }
+        // bias of column (pp, hh): the limb-1 lanes hold C q' in full; sum over the k ranges
+        bias = ll ? bias : 0.0f;
+        bias += dpp_xor1(bias);
+        bias = sum_x32(sum_x16(bias));
+
+        // ---- logits (log2 domain): lane keeps tiles 4 ll + j of its column, rows r:
+        //      token 32 G + 8 r + 4 ll + j of page pp, head hh
+        float x[4][4];
 #pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) bp[h] += __shfl_xor(bp[h], o);
-            }
-            if (lane == 0) {
+        for (int r = 0; r < 4; ++r) {
+            u32x2 k0 = {0u, 0u};
+            if (has0) k0 = lds_u64(st + k0_lane + 16 * r);
 #pragma unroll
-                for (int h = 0; h < GRP; ++h) bias_lds[w][h] = bp[h];
+            for (int j = 0; j < 4; ++j) {
+                const float mine = ll ? Sc[4 + j][r] : Sc[j][r];
+                const float give = ll ? Sc[j][r] : Sc[4 + j][r];
+                float v = __builtin_fmaf(mine + dpp_xor1(give), comp[j], bias);
+                const uint32_t kw = k0[j >> 1];
+                v = __builtin_fmaf(q0c, __uint_as_float((j & 1) ? (kw & 0xFFFF0000u) : (kw << 16)), v);
+                x[r][j] = v;
             }
         }
-        lds_barrier();
-
-        // ---- scores: tiles 2w, 2w+1 of all 4 pages (block-diagonal over the page slots)
-        f32x4 S[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-        {
-            const _Float16 *bhi = pc == G ? &qt[0][pc][hc][0] : &zero16[0];
-            const _Float16 *blo = pc == G ? &qt[1][pc][hc][0] : &zero16[0];
-            const int bstep = pc == G ? 8 : 0;
-            const uint32_t krow = qb + Ly::OFF_K + G * Ly::KPS + 2 * n;
+        if (nv0 < PG || nv1 < PG) {
+            const int nvp = pp ? nv1 : nv0;
 #pragma unroll
-            for (int kk = 0; kk < KSM; ++kk) {
-                if (kk < KS) {
-                    const half8 Bh = *reinterpret_cast<const half8 *>(bhi + bstep * kk);
-                    const half8 Bl = *reinterpret_cast<const half8 *>(blo + bstep * kk);
-                    u32x4 X;
+            for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2)
-                        X[e2] = lds_u16(krow + (8 * kk + 2 * e2) * ROW_BYTES) |
-                                (lds_u16(krow + (8 * kk + 2 * e2 + 1) * ROW_BYTES) << 16);
-                    switch (w) {
-                        case 0: qk_step<0>(S, X, Bh, Bl); break;
-                        case 1: qk_step<1>(S, X, Bh, Bl); break;
-                        case 2: qk_step<2>(S, X, Bh, Bl); break;
-                        default: qk_step<3>(S, X, Bh, Bl); break;
-                    }
-                }
-            }
+                for (int j = 0; j < 4; ++j)
+                    if (32 * G + 8 * r + 4 * ll + j >= nvp) x[r][j] = -__builtin_huge_valf();
         }
-        // ---- logits (log2 domain): tokens 32G + 8r + 2w + t of page slot pc, head hc
-        const int lpc = P0 + 4 * u + pc;
-        const int nvl = lpc < P1 ? min(PG, L - lpc * PG) : 0;
-        const float bias = bias_lds[pc][hc];
-        float x[2][4];
-        {
-            const float cmp0 = w == 0 ? tile_comp(0) : w == 1 ? tile_comp(2) : w == 2 ? tile_comp(4) : tile_comp(6);
-            const float cmp1 = w == 0 ? tile_comp(1) : w == 1 ? tile_comp(3) : w == 2 ? tile_comp(5) : tile_comp(7);
+        // ---- running max of head hh over the pair
+        float bm = -__builtin_huge_valf();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = 32 * G + 8 * r + 2 * w;
-                const uint32_t k0p = has0 ? lds_u32(qb + Ly::OFF_K0 + (pc * PG + tok) * 2) : 0u;
-                float v0 = __builtin_fmaf(S[0][r], cmp0, bias);
-                float v1 = __builtin_fmaf(S[1][r], cmp1, bias);
-                v0 = __builtin_fmaf(q0c, __uint_as_float(k0p << 16), v0);
-                v1 = __builtin_fmaf(q0c, __uint_as_float(k0p & 0xFFFF0000u), v1);
-                x[0][r] = tok < nvl ? v0 : -__builtin_huge_valf();
-                x[1][r] = tok + 1 < nvl ? v1 : -__builtin_huge_valf();
-            }
-        }
-        float xm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-        xm = fmaxf(xm, __shfl_xor(xm, 16));
-        xm = fmaxf(xm, __shfl_xor(xm, 32));
-        if (lane < 16) colmax[w][lane] = xm;
-        lds_barrier();
-
-        // ---- running max per head over the block (identical in every wave); each
-        //      lane tracks the head n & 3 its score column and value row belong to
-        float cm = lane < 16 ? fmaxf(fmaxf(colmax[0][n], colmax[1][n]), fmaxf(colmax[2][n], colmax[3][n]))
-                             : -__builtin_huge_valf();
-        cm = fmaxf(cm, __shfl_xor(cm, 4));
-        cm = fmaxf(cm, __shfl_xor(cm, 8));  // lane h (< 4) holds the block max of head h
-        const float m_new = fmaxf(m_lane, __shfl(cm, hc));
-        const float alpha_lane = __builtin_amdgcn_exp2f(m_lane - m_new);
-        if (__builtin_amdgcn_ballot_w64(m_new != m_lane)) {
-            float alpha[GRP];
+        for (int r = 0; r < 4; ++r) bm = fmaxf(bm, fmaxf(fmaxf(x[r][0], x[r][1]), fmaxf(x[r][2], x[r][3])));
+        bm = fmaxf(bm, dpp_xor1(bm));
+        bm = fmaxf(bm, dpp_xor8(bm));
+        bm = max_x32(max_x16(bm));
+        const float m_new = fmaxf(m_run, bm);
+        if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // head hh
+            float a[GRP];
 #pragma unroll
-            for (int h = 0; h < GRP; ++h)
-                alpha[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha_lane), h));
+            for (int h = 0; h < GRP; ++h) a[h] = bcast_lane(alpha, 2 * h);  // lane 2h: column (0, h, 0)
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) O[t][r] *= alpha[r];
-            z_lane *= alpha_lane;
-            l_lane *= alpha_lane;
+                for (int r = 0; r < 4; ++r) O[t][r] *= a[r];
+            z_acc *= (hv & 2) ? ((hv & 1) ? a[3] : a[2]) : ((hv & 1) ? a[1] : a[0]);
+            l_acc *= alpha;
         }
-        m_lane = m_new;
-        // probabilities to LDS (key-row area of this buffer): P[p][h][token] fp16
+        m_run = m_new;
+        // ---- probabilities -> fp16 -> LDS (key-row area of this stage)
         {
-            const float mh = m_lane;
-            const uint32_t pbase = qb + Ly::OFF_K + pc * 1024;  // [p] 1 KB, chunks as in vm_chunk
             float ls = 0.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float pa = __builtin_amdgcn_exp2f(x[0][r] - mh);
-                const float pb = __builtin_amdgcn_exp2f(x[1][r] - mh);
-                ls += pa + pb;
-                half2v hp;
-                hp[0] = (_Float16)pa;
-                hp[1] = (_Float16)pb;
-                lds_st32(pbase + chunk_slot(hc, 4 * G + r) * 16 + 4 * w, as_u32(hp));
+                float p[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    p[j] = __builtin_amdgcn_exp2f(x[r][j] - m_new);
+                    ls += p[j];
+                }
+                half2v h01, h23;
+                h01[0] = (_Float16)p[0];
+                h01[1] = (_Float16)p[1];
+                h23[0] = (_Float16)p[2];
+                h23[1] = (_Float16)p[3];
+                lds_st64(st + pw[r], u32x2{as_u32(h01), as_u32(h23)});
             }
-            l_lane += ls;
+            l_acc += ls;
         }
-        lds_barrier();
 
-        // ---- values of page slot w
-        const int lpw = P0 + 4 * u + w;
-        const int nvp = lpw < P1 ? min(PG, L - lpw * PG) : 0;
-        if (nvp > 0) {
-            const bool partial = nvp < PG;
-            const uint32_t pb = qb + Ly::OFF_K + w * 1024 + chunk_slot(hv, 4 * G) * 16;   // + 256 per k-step
-            const uint32_t sb = qb + Ly::OFF_VM + w * 2048 + chunk_slot(qv, 4 * G) * 16;
-            const uint32_t vb = qb + Ly::OFF_VC + w * Ly::VPS + G * Ly::VBS + 2 * n;
-            const half2v c15 = {(_Float16)1.5f, (_Float16)1.5f};
-            const half2v m15 = {(_Float16)-1.5f, (_Float16)-1.5f};
+        // ---- values of both pages
+        const half2v c15 = {(_Float16)1.5f, (_Float16)1.5f};
+        const half2v m15 = {(_Float16)-1.5f, (_Float16)-1.5f};
+#pragma unroll
+        for (int vp = 0; vp < 2; ++vp) {
+            const int nv = vp ? nv1 : nv0;
+            if (nv <= 0) continue;
 #pragma unroll
             for (int kv = 0; kv < 4; ++kv) {
-                u32x4 Pp = lds_u128(pb + 256 * kv);
-                u32x4 sp = lds_u128(sb + 256 * kv);
-                u32x4 zp = lds_u128(sb + 1024 + 256 * kv);
-                if (partial) {
+                u32x4 Pp = lds_u128(st + vp * 1024 + pr_ofs[kv]);
+                u32x4 sp = lds_u128(st + vp * 2048 + vm_ofs[kv]);
+                u32x4 zp = lds_u128(st + vp * 2048 + vm_ofs[kv] + 1024);
+                if (nv < PG) {
                     const int tok0 = 32 * G + 8 * kv;
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
-                        const uint32_t keep = (tok0 + 2 * e2 < nvp ? 0x0000FFFFu : 0u) |
-                                              (tok0 + 2 * e2 + 1 < nvp ? 0xFFFF0000u : 0u);
+                        const uint32_t keep = (tok0 + 2 * e2 < nv ? 0x0000FFFFu : 0u) |
+                                              (tok0 + 2 * e2 + 1 < nv ? 0xFFFF0000u : 0u);
                         sp[e2] &= keep;
                         zp[e2] &= keep;
                         Pp[e2] &= keep;
@@ -498,14 +522,13 @@ __global__ __launch_bounds__(256) void decode_g4_kernel(dqk_cache c, const float
                     A[e2] = as_u32(a2);
                     // centred codes: v = (c - 1.5) s + (z + 1.5 s)
                     const half2v zc = __builtin_elementwise_fma(as_half2(sp[e2]), c15, as_half2(zp[e2]));
-                    z_lane = __builtin_amdgcn_fdot2(as_half2(Pp[e2]), zc, z_lane, false);
-                    z_lane = __builtin_amdgcn_fdot2(a2, m15, z_lane, false);
+                    z_acc = __builtin_amdgcn_fdot2(as_half2(Pp[e2]), zc, z_acc, false);
+                    z_acc = __builtin_amdgcn_fdot2(a2, m15, z_acc, false);
                 }
                 u32x4 X;
+                const uint32_t vb = st + vc_lane + vp * S::VPS + 8 * kv * ROW_BYTES;
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2)
-                    X[e2] = lds_u16(vb + (8 * kv + 2 * e2) * ROW_BYTES) |
-                            (lds_u16(vb + (8 * kv + 2 * e2 + 1) * ROW_BYTES) << 16);
+                for (int e2 = 0; e2 < 4; ++e2) X[e2] = lds_pair(vb + 64 * e2, vb + 64 * e2 + ROW_BYTES);
                 const half8 Ah = as_half8(A);
                 const Packed XP = pack_shifts(X);
                 O[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<0>(XP)), O[0], 0, 0, 0);
@@ -518,50 +541,32 @@ __global__ __launch_bounds__(256) void decode_g4_kernel(dqk_cache c, const float
                 O[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<7>(XP)), O[7], 0, 0, 0);
             }
         }
-        lds_barrier();  // every wave is done with this buffer
-        if (u + 2 < nq)
-            issue_block<KSM>(c, quad_pages(ptab, P0 + 4 * (u + 2), P1, L, hkv, g), qb, w, lane, kro, kmo, kmp);
+        // this stage is consumed: refill it with pair u + 2
+        if (more) issue_pair<KS>(c, nxt, st, lane, pl);
     }
-
-    // ---- totals: each wave holds page slot w's value sums; all share m_run
     wait_dma<0>();
-    l_lane += __shfl_xor(l_lane, 4);
-    l_lane += __shfl_xor(l_lane, 8);
-    l_lane += __shfl_xor(l_lane, 16);
-    l_lane += __shfl_xor(l_lane, 32);  // lanes with hc = h: this wave's share of l of head h
-    z_lane += __shfl_xor(z_lane, 16);
-    z_lane += __shfl_xor(z_lane, 32);  // lane (., 4q + h): zero-point term of (q, h)
+
+    // ---- totals
+    l_acc += dpp_xor1(l_acc);
+    l_acc += dpp_xor8(l_acc);
+    l_acc = sum_x32(sum_x16(l_acc));  // every lane of head hh: l of head hh
+    z_acc = sum_x32(sum_x16(z_acc));  // lanes n = 4q + h: zero-point term of row (q, h)
     float zq[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) zq[r] = __shfl(z_lane, 16 * G + 4 * G + r);  // (q = G, h = r)
-    float m_fin[GRP];
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) m_fin[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_lane), h));
-    float *comb = reinterpret_cast<float *>(&blk[0][0]);  // [WAVES][GRP][D + 1]
-    lds_barrier();
-    if ((n >> 2) == G) {
+    for (int r = 0; r < 4; ++r) zq[r] = __shfl(z_acc, 4 * G + r);  // row (q = G, h = r)
+    float *dst0 = partials + (((size_t)b * hq + (size_t)g * GRP) * nsplit + split) * PART_FLOATS;
+    const size_t hstride = (size_t)nsplit * PART_FLOATS;
+    if ((n >> 2) == G) {  // channel 8n + t belongs to group q = G
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                comb[(w * GRP + r) * (D + 1) + 8 * n + t] = __builtin_fmaf(O[t][r], tile_comp(t), zq[r]);
+                dst0[r * hstride + 8 * n + t] = npairs > 0 ? __builtin_fmaf(O[t][r], tile_comp(t), zq[r]) : 0.0f;
     }
-    if (lane < GRP) comb[(w * GRP + lane) * (D + 1) + D] = l_lane;
-    lds_barrier();
-    for (int i = tid; i < GRP * D; i += 256) {
-        const int h = i >> 7, ch = i & (D - 1);
-        float acc = 0.0f, lsum = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < WAVES; ++ww) {
-            acc += comb[(ww * GRP + h) * (D + 1) + ch];
-            lsum += comb[(ww * GRP + h) * (D + 1) + D];
-        }
-        float *dst = partials + (((size_t)b * hq + (size_t)g * GRP + h) * nsplit + split) * PART_FLOATS;
-        dst[ch] = nq > 0 ? acc : 0.0f;
-        if (ch == 0) {
-            dst[D] = nq > 0 ? m_fin[h] * LN2 : -__builtin_huge_valf();
-            dst[D + 1] = nq > 0 ? lsum : 0.0f;
-        }
+    if (lane < 8 && (lane & 1) == 0) {  // lane 2h: column (0, h, 0)
+        const int h = lane >> 1;
+        dst0[h * hstride + D] = npairs > 0 ? m_run * LN2 : -__builtin_huge_valf();
+        dst0[h * hstride + D + 1] = npairs > 0 ? l_acc : 0.0f;
     }
 }
 
@@ -570,31 +575,34 @@ __global__ __launch_bounds__(256) void decode_g4_kernel(dqk_cache c, const float
 bool use_mfma_decode(int hq, int hkv) { return hkv > 0 && hq == GRP * hkv; }
 
 int decode_splits_mfma(int batch, int hkv, int max_pages) {
-    // about two workgroups of 4 waves per CU on 256 CUs, at least 16 pages per workgroup
+    // about four single-wave workgroups per CU on 256 CUs, at least 8 pages each
     const int units = batch * hkv;
-    int s = (512 + units - 1) / units;
-    const int cap = (max_pages + 15) / 16;
+    int s = (1024 + units - 1) / units;
+    const int cap = (max_pages + 7) / 8;
     if (s > cap) s = cap;
     return s < 1 ? 1 : s;
 }
 
-template <int KSM>
-static hipError_t launch_ksm(const DecodeArgs &a, hipStream_t s) {
+template <int KS>
+static hipError_t launch_ks(const DecodeArgs &a, hipStream_t s) {
     dim3 grid(a.num_splits, a.batch * a.hkv);
-    hipLaunchKernelGGL(decode_g4_kernel<KSM>, grid, dim3(256), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep, a.hq,
+    hipLaunchKernelGGL(decode_g4_kernel<KS>, grid, dim3(64), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep, a.hq,
                        a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
-    // key k-steps of 8 channels needed for n_keep selected channels
-    const int ks = (a.n_keep + 7) / 8;
-    if (ks <= 2) return launch_ksm<2>(a, s);
-    if (ks <= 4) return launch_ksm<4>(a, s);
-    if (ks <= 7) return launch_ksm<7>(a, s);
-    if (ks <= 10) return launch_ksm<10>(a, s);
-    if (ks <= 13) return launch_ksm<13>(a, s);
-    return launch_ksm<16>(a, s);
+    // 16-channel k-steps per page for up to n_keep INT2 channels
+    switch ((a.n_keep + 15) / 16) {
+        case 1: return launch_ks<1>(a, s);
+        case 2: return launch_ks<2>(a, s);
+        case 3: return launch_ks<3>(a, s);
+        case 4: return launch_ks<4>(a, s);
+        case 5: return launch_ks<5>(a, s);
+        case 6: return launch_ks<6>(a, s);
+        case 7: return launch_ks<7>(a, s);
+        default: return launch_ks<8>(a, s);
+    }
 }
 
 }  // namespace dqk

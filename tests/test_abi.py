@@ -80,9 +80,9 @@ def test_decode_validation():
     assert _dec(hq=8 * 32) == pa.DQK_ERR_UNSUPPORTED          # group of 32 query heads
     assert _dec(c=_cache(v_meta=4096 + 2)) == pa.DQK_ERR_ALIGN
     assert _dec(lse=MIS) == pa.DQK_ERR_ALIGN
-    need = pa.dqk_decode_workspace_size(4, 32, 8, 16, 0)
-    assert need > 0
-    assert _dec(wsb=need - 4) == pa.DQK_ERR_WORKSPACE
+    need = pa.dqk_decode_workspace_size(4, 32, 8, 16, 4)
+    assert need == 4 * 32 * 4 * 130 * 4
+    assert _dec(ns=4, wsb=need - 4) == pa.DQK_ERR_WORKSPACE
 
 
 def test_workspace_size():

@@ -132,11 +132,13 @@ def test_decode_config1_full():
     assert (rel <= gu.TOL).all()
 
 
-@pytest.mark.parametrize("hq,hkv,tol", [(32, 8, 5e-4), (16, 8, 1e-5)], ids=["mfma-g4", "generic-g2"])
+@pytest.mark.parametrize("hq,hkv,tol", [(32, 8, 1e-3), (16, 8, 1e-5)], ids=["mfma-g4", "generic-g2"])
 def test_decode_split_invariance_and_permutation(hq, hkv, tol):
     """Split count changes only rounding: the group-4 MFMA path rounds the
-    probabilities to fp16 relative to each split's running maximum, the
-    generic path keeps fp32 throughout."""
+    probabilities and P * scale to fp16 relative to each split's running
+    maximum (two roundings of at most 2^-12 relative each, so the outputs of
+    two split counts may differ by about 2^-10 of a row's scale), the generic
+    path keeps fp32 throughout."""
     _say("decode splits/permutation", hq, hkv)
     shape = synth.Shape(2, hq, hkv, [4000, 2500], 77)
     outs = []
