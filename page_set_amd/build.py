@@ -15,6 +15,9 @@ LIB = os.path.join(HERE, "libdqk.so")
 ARCH = os.environ.get("DQK_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["dqk_api.cpp", "dqk_select.hip", "dqk_append.hip", "dqk_decode.hip", "dqk_decode_mfma.hip"]
+# MFMA accumulators in ordinary VGPRs: the decode loop reads and rescales them
+# with VALU instructions, which would otherwise copy them out of AGPRs
+EXTRA = {"dqk_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
@@ -39,7 +42,7 @@ def build(verbose: bool = False) -> str:
             obj = os.path.join(tmp, src + ".o")
             objs.append(obj)
             lang = ["-x", "hip"] if src.endswith(".hip") else ["-x", "hip"]
-            cmd = [hipcc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *COMMON, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

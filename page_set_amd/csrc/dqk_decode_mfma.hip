@@ -23,8 +23,9 @@
 //    (the two limbs) split the 8 token tiles between them.
 //  * Values: per page, O[(group q, head h)][channel] += (P*scale_q)[.][token]
 //    x codes[token][channel] on MFMA (M = 4 groups x 4 heads); P moves to the
-//    operand layout through LDS; the zero points accumulate as
-//    sum_t P (z + 1.5 s) - 1.5 sum_t P s with v_dot2_f32_f16 (centred codes).
+//    operand layout through LDS; the zero points (as sum_t P (z + 1.5 s) -
+//    1.5 sum_t P s, centred codes) and the softmax denominator sum_t P
+//    accumulate on two more MFMAs per 32 tokens.
 #include "dqk_internal.h"
 
 namespace dqk {
@@ -150,31 +151,32 @@ __device__ __forceinline__ float max_x32(float v) {
 }
 
 // ---------------------------------------------------------------- stage layout
-// One stage holds a page pair.  Key rows: 16 KS row slots per page (the
-// selected INT2 channels in ascending order, padded with the all-zero row 0),
-// slot s holding row s ^ ((s >> 3) & 1), page 1 starting 64 bytes later
-// modulo 256, so that the four rows one k-step reads at a time fall in
-// distinct banks.  The probabilities of the pair reuse the key-row area once
-// the scores are done.
+// Two stages per wave.  Stage u & 1 holds the keys of page pair u (needed by
+// its scores) and the values of pair u (needed one step later, by its value
+// products), so keys of pair u + 2 and values of pair u + 1 can be loaded
+// while pair u is scored.  Key rows: 16 KS row slots per page (the selected
+// INT2 channels in ascending order, padded with the all-zero row 0), slot s
+// holding row s ^ ((s >> 3) & 1), page 1 starting 64 bytes later modulo 256,
+// so that the four rows one k-step reads at a time fall in distinct banks.
 template <int KS>
 struct Stage {
-    static constexpr int NR = 16 * KS;                             // key row slots per page
-    static constexpr int KRP = NR * ROW_BYTES + 64;                // key page stride
-    static constexpr int KAREA = 2 * KRP > 2048 ? 2 * KRP : 2048;  // key rows, then P [2][4][128] fp16
-    static constexpr int OFF_KM = KAREA;                           // (scale | zero << 16) [2][NR]
-    static constexpr int OFF_K0 = OFF_KM + 2 * NR * 4;             // channel 0, bf16 [2][128]
-    static constexpr int VBS = 32 * ROW_BYTES + 32;                // value block (32 tokens) stride
-    static constexpr int VPS = 4 * VBS;                            // value page stride
-    static constexpr int OFF_VC = OFF_K0 + 2 * PG * 2;             // value codes [2][4][32][32 B]
-    static constexpr int OFF_VM = OFF_VC + 2 * VPS;                // value (scale, zero) [2][2][4][128]
+    static constexpr int NR = 16 * KS;                  // key row slots per page
+    static constexpr int KRP = NR * ROW_BYTES + 64;     // key page stride
+    static constexpr int OFF_KM = 2 * KRP;              // (scale | zero << 16) [2][NR]
+    static constexpr int OFF_K0 = OFF_KM + 2 * NR * 4;  // channel 0, bf16 [2][128]
+    static constexpr int VBS = 32 * ROW_BYTES + 32;     // value block (32 tokens) stride
+    static constexpr int VPS = 4 * VBS;                 // value page stride
+    static constexpr int OFF_VC = OFF_K0 + 2 * PG * 2;  // value codes [2][4][32][32 B]
+    static constexpr int OFF_VM = OFF_VC + 2 * VPS;     // value (scale, zero) [2][2][4][128]
     static constexpr int BYTES = OFF_VM + 2 * 2048;
     static constexpr int KRI = (2 * NR + 63) / 64;  // 16-byte key-row DMAs per page
     static constexpr int KMI = (2 * NR + 63) / 64;  // 4-byte key-metadata DMAs for the pair
-    static constexpr int NDMA = 2 * KRI + KMI + 1 + 8 + 4;
-    static_assert(KAREA % 16 == 0 && OFF_KM % 16 == 0 && OFF_K0 % 16 == 0 && OFF_VC % 16 == 0 &&
-                      OFF_VM % 16 == 0 && BYTES % 16 == 0,
+    static constexpr int KN = 2 * KRI + KMI + 1;    // key DMAs of a pair
+    static constexpr int VN = 8 + 4;                // value DMAs of a pair
+    static_assert(OFF_KM % 16 == 0 && OFF_K0 % 16 == 0 && OFF_VC % 16 == 0 && OFF_VM % 16 == 0 &&
+                      BYTES % 16 == 0,
                   "alignment");
-    static_assert(NDMA <= 63, "vmcnt range");
+    static_assert(2 * (KN + VN) <= 63, "vmcnt range");
 };
 
 struct Pair {
@@ -197,15 +199,14 @@ struct DmaPlan {
     uint32_t vmo;                  // value metadata chunk offset (permuted, see the plan)
 };
 
-// Fill one stage with a page pair: this wave issues exactly Stage<KS>::NDMA
-// vector memory instructions, each with at least lane 0 active.
+// Keys of a page pair into stage st: exactly Stage<KS>::KN vector memory
+// instructions, each with at least lane 0 active.
 template <int KS>
-__device__ __forceinline__ void issue_pair(const dqk_cache &c, const Pair &pr, uint32_t st, int lane,
+__device__ __forceinline__ void issue_keys(const dqk_cache &c, const Pair &pr, uint32_t st, int lane,
                                            const DmaPlan<KS> &pl) {
     using S = Stage<KS>;
-    // key rows (64 half rows per instruction)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 2; ++p) {  // key rows, 64 half rows per instruction
         const uint8_t *base = c.k_codes + (p ? pr.pg1 : pr.pg0) * (D * ROW_BYTES);
 #pragma unroll
         for (int j = 0; j < S::KRI; ++j)
@@ -217,26 +218,132 @@ __device__ __forceinline__ void issue_pair(const dqk_cache &c, const Pair &pr, u
 #pragma unroll
     for (int t = 0; t < S::KMI; ++t)
         if (64 * t + lane < 2 * S::NR) dma4_v(((pl.kmp >> t) & 1u ? km1 : km0) + pl.kmo[t], st + S::OFF_KM + 64 * t * 4);
-    // channel 0 of both pages (32 lanes x 16 bytes)
-    if (lane < 32) {
+    if (lane < 32) {  // channel 0 of both pages (32 lanes x 16 bytes)
         const uint8_t *k0 = reinterpret_cast<const uint8_t *>(c.k_ch0) + (lane < 16 ? pr.pg0 : pr.pg1) * (PG * 2);
         dma16_v(k0 + (lane & 15) * 16, st + S::OFF_K0);
     }
-    // value codes: page p, 32-token block bb
+}
+
+// Values of a page pair into stage st: exactly Stage<KS>::VN instructions.
+template <int KS>
+__device__ __forceinline__ void issue_vals(const dqk_cache &c, const Pair &pr, uint32_t st, int lane,
+                                           const DmaPlan<KS> &pl) {
+    using S = Stage<KS>;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 2; ++p) {  // value codes: page p, 32-token block bb
         const uint8_t *base = c.v_codes + (p ? pr.pg1 : pr.pg0) * (PG * ROW_BYTES);
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb)
             dma16_s(base + bb * 1024, (uint32_t)lane * 16u, st + S::OFF_VC + p * S::VPS + bb * S::VBS);
     }
-    // value metadata: page p, half hf (scales, zeros)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 2; ++p) {  // value metadata: page p, half hf (scales, zeros)
         const uint8_t *base =
             reinterpret_cast<const uint8_t *>(c.v_meta) + (p ? pr.pg1 : pr.pg0) * (2 * VGROUPS * PG * 2);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) dma16_s(base + hf * 1024, pl.vmo, st + S::OFF_VM + p * 2048 + hf * 1024);
+    }
+}
+
+// ---------------------------------------------------------------- per-lane constants
+template <int KS>
+struct Lane {
+    // score lanes: k range = page G >> 1, channels 16 ks + 8 (G & 1) + 0..7;
+    // column n = (page pp, head hh, limb ll)
+    int pp, hh, ll;
+    uint32_t QH[KS][4], QL[KS][4];  // C q' fp16 pairs: limb-1 lanes (hi, lo), limb-0 lanes (0, hi)
+    float q0c;                      // C q'_0 (0 when channel 0 is pruned)
+    float comp[4];                  // tiles 4 ll + j after the limb split
+    uint32_t kr_even, kr_odd, km, k0;
+    uint32_t pw[4];  // P writes
+    // value lanes: row (q, h) = (n >> 2, n & 3), tokens 32 G + 8 kv + 0..7
+    uint32_t pr_ofs[4], vm_ofs[4], vc;
+    half2v zc_s, zc_z, zc_c;
+    half8 M15;
+};
+
+// One score k-step: 16 selected channels of each page of the pair.
+template <int KS>
+__device__ __forceinline__ void qk_step(int ks, uint32_t st, const Lane<KS> &ln, f32x4 (&Sc)[8], f32x4 &Sb) {
+    const u32x4 d0 = lds_u128(st + ln.km + 64 * ks);
+    const u32x4 d1 = lds_u128(st + ln.km + 64 * ks + 16);
+    const uint32_t dd[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+    u32x4 Bv, Zv, QLv;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        const half2v s2 = as_half2(__builtin_amdgcn_perm(dd[2 * e2 + 1], dd[2 * e2], 0x05040100u));
+        Zv[e2] = __builtin_amdgcn_perm(dd[2 * e2 + 1], dd[2 * e2], 0x07060302u);
+        const half2v qh = as_half2(ln.QH[ks][e2]), ql = as_half2(ln.QL[ks][e2]);
+        const half2v t1 = qh * s2;
+        const half2v t2 = __builtin_elementwise_fma(qh, s2, -t1);
+        Bv[e2] = as_u32(__builtin_elementwise_fma(ql, s2, t2));
+        QLv[e2] = ln.QL[ks][e2];
+    }
+    const half8 Bh = as_half8(Bv);
+    // rows of A all equal z_k (k = this lane's channels), B = the lane's limb of C q'
+    Sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(Zv), as_half8(QLv), Sb, 0, 0, 0);
+    u32x4 X;
+    const uint32_t kb = st + 16 * ks * ROW_BYTES;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) X[e2] = lds_pair(kb + ln.kr_even + 64 * e2, kb + ln.kr_odd + 64 * e2 + ROW_BYTES);
+    const Packed XP = pack_shifts(X);
+    Sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<0>(XP)), Bh, Sc[0], 0, 0, 0);
+    Sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<1>(XP)), Bh, Sc[1], 0, 0, 0);
+    Sc[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<2>(XP)), Bh, Sc[2], 0, 0, 0);
+    Sc[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<3>(XP)), Bh, Sc[3], 0, 0, 0);
+    Sc[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<4>(XP)), Bh, Sc[4], 0, 0, 0);
+    Sc[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<5>(XP)), Bh, Sc[5], 0, 0, 0);
+    Sc[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<6>(XP)), Bh, Sc[6], 0, 0, 0);
+    Sc[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<7>(XP)), Bh, Sc[7], 0, 0, 0);
+}
+
+// One value step: 32 tokens (32 G + 8 kv + 0..7) of page vp; P from pbase.
+template <int KS>
+__device__ __forceinline__ void pv_step(int vp, int kv, uint32_t st, uint32_t pbase, const Lane<KS> &ln,
+                                        f32x4 (&O)[8], f32x4 &Oz) {
+    using S = Stage<KS>;
+    const u32x4 Pp = lds_u128(pbase + vp * 1024 + ln.pr_ofs[kv]);
+    const u32x4 sp = lds_u128(st + vp * 2048 + ln.vm_ofs[kv]);
+    const u32x4 zp = lds_u128(st + vp * 2048 + ln.vm_ofs[kv] + 1024);
+    // centred codes: v = (c - 1.5) s + (z + 1.5 s)
+    u32x4 A, Bz;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+        A[e2] = as_u32(as_half2(Pp[e2]) * as_half2(sp[e2]));
+        Bz[e2] = as_u32(__builtin_elementwise_fma(as_half2(sp[e2]), ln.zc_s,
+                                                  __builtin_elementwise_fma(as_half2(zp[e2]), ln.zc_z, ln.zc_c)));
+    }
+    u32x4 X;
+    const uint32_t vb = st + ln.vc + vp * S::VPS + 8 * kv * ROW_BYTES;
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) X[e2] = lds_pair(vb + 64 * e2, vb + 64 * e2 + ROW_BYTES);
+    const half8 Ah = as_half8(A);
+    Oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(Pp), as_half8(Bz), Oz, 0, 0, 0);
+    Oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, ln.M15, Oz, 0, 0, 0);
+    const Packed XP = pack_shifts(X);
+    O[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<0>(XP)), O[0], 0, 0, 0);
+    O[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<1>(XP)), O[1], 0, 0, 0);
+    O[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<2>(XP)), O[2], 0, 0, 0);
+    O[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<3>(XP)), O[3], 0, 0, 0);
+    O[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<4>(XP)), O[4], 0, 0, 0);
+    O[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<5>(XP)), O[5], 0, 0, 0);
+    O[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<6>(XP)), O[6], 0, 0, 0);
+    O[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<7>(XP)), O[7], 0, 0, 0);
+}
+
+// Value scales and zero points of tokens at or past nv (0 <= nv < 128) of a page
+// set to zero, so that unspecified bytes past the end of a sequence cannot
+// reach the products (their probabilities are already zero).
+__device__ __forceinline__ void clear_tail_meta(uint32_t vm_page, int nv, int lane) {
+    // entry (hf, q, t) of the page sits in chunk t >> 3 of group q, at slot (t >> 3) ^ q
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int e = 64 * i + lane;  // 1024 entries: hf (1), q (2), t (7)
+        const int hf = e >> 9, q = (e >> 7) & 3, t = e & 127;
+        if (t >= nv) {
+            const uint32_t a = vm_page + hf * 1024 + q * 256 + 16 * ((t >> 3) ^ q) + 2 * (t & 7);
+            *reinterpret_cast<__attribute__((address_space(3))) uint16_t *>((uintptr_t)a) = 0;
+        }
     }
 }
 
@@ -249,6 +356,7 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
     using S = Stage<KS>;
     constexpr int NR = S::NR;
     __shared__ __attribute__((aligned(16))) uint8_t stg[2][S::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2 * GRP * PG * 2];  // P [2][4][128] fp16
 
     const int split = blockIdx.x, bg = blockIdx.y;
     const int hkv = c.num_kv_heads;
@@ -260,6 +368,21 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
     const int per = (((npages + nsplit - 1) / nsplit) + 1) & ~1;
     const int P0 = min(npages, split * per), P1 = min(npages, P0 + per);
     const int npairs = (P1 - P0 + 1) >> 1;
+    const int32_t *ptab = page_table + (size_t)b * max_pages;
+    const uint32_t st0 = lds_addr(&stg[0][0]);
+    const uint32_t pb = lds_addr(&pbuf[0]);
+    auto stage = [&](int u) { return st0 + (uint32_t)(u & 1) * S::BYTES; };
+    auto nvalid = [&](int lp) { return lp < P1 ? min(PG, L - lp * PG) : 0; };
+
+    DmaPlan<KS> pl;
+    // value metadata: LDS slot l of each 1 KB half holds chunk (l & 15) ^ (l >> 4) of group l >> 4
+    pl.vmo = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ (lane >> 4)));
+    // values of pair 0 do not depend on the selection: in flight first
+    Pair pr_v = {0, 0};  // pages whose values load next
+    if (npairs > 0) {
+        pr_v = pair_pages(ptab, P0, P1, hkv, g);
+        issue_vals<KS>(c, pr_v, stage(0), lane, pl);
+    }
 
     const float C = sm_scale * LOG2E;
     static_assert(GRP * D * 4 + D * 4 <= S::BYTES, "q' and the selection fit in one stage");
@@ -278,7 +401,7 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
         sd[lane + 64] = sb;
     }
     __syncthreads();
-    const float *q_l = reinterpret_cast<const float *>(&stg[1][0]);            // [4][128]
+    const float *q_l = reinterpret_cast<const float *>(&stg[1][0]);                  // [4][128]
     const int32_t *sel_l = reinterpret_cast<const int32_t *>(&stg[1][GRP * D * 4]);  // [n_keep]
     const int has0 = sel_l[0] == 0;  // the list is ascending
     const int R = n_keep - has0;     // selected INT2 channels (R <= NR)
@@ -288,8 +411,7 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
         return r < R ? v : 0;
     };
 
-    // ---- DMA plan, and the first pair in flight
-    DmaPlan<KS> pl;
+    // ---- key DMA plan
 #pragma unroll
     for (int j = 0; j < S::KRI; ++j) {
         const int x = 64 * j + lane, s = x >> 1;
@@ -304,20 +426,15 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
         pl.kmp |= (uint32_t)p << t;
         pl.kmo[t] = (uint32_t)chan(x - p * NR) * 4u;
     }
-    // value metadata: LDS slot l of each 1 KB half holds chunk (l & 15) ^ (l >> 4) of group l >> 4
-    pl.vmo = (uint32_t)((lane >> 4) * 256 + 16 * ((lane & 15) ^ (lane >> 4)));
 
-    const uint32_t st0 = lds_addr(&stg[0][0]);
-    const int32_t *ptab = page_table + (size_t)b * max_pages;
-    if (npairs > 0) issue_pair<KS>(c, pair_pages(ptab, P0, P1, hkv, g), st0, lane, pl);
-
-    // ---- score lanes.  Lane (G, n): k range = page G >> 1, channels
-    //      16 ks + 8 (G & 1) + 0..7; column n = (page pp, head hh, limb ll).
-    const int pp = n >> 3, hh = (n >> 1) & 3, ll = n & 1;
+    // ---- per-lane constants
+    Lane<KS> ln;
+    ln.pp = n >> 3;
+    ln.hh = (n >> 1) & 3;
+    ln.ll = n & 1;
     const int kpage = G >> 1, kh = G & 1;
-    // C q' as fp16 pairs: limb-1 lanes hold (hi, lo), limb-0 lanes (0, hi), so
-    // fma(QL, s, fma(QH, s, -QH s)) is the lane's limb of C q' s either way
-    uint32_t QH[KS][4], QL[KS][4];
+    // limb-1 lanes hold (hi, lo), limb-0 lanes (0, hi), so fma(QL, s, fma(QH, s, -QH s))
+    // is the lane's limb of C q' s either way
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -326,129 +443,157 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int jj = 16 * ks + 8 * kh + 2 * e2 + u;
-                const float qj = q_l[hh * D + chan(jj)];
-                const float v = (pp == kpage && jj < R) ? qj * C : 0.0f;
+                const float qj = q_l[ln.hh * D + chan(jj)];
+                const float v = (ln.pp == kpage && jj < R) ? qj * C : 0.0f;
                 const _Float16 vh = (_Float16)v;
                 const _Float16 vl = (_Float16)(v - (float)vh);
-                h[u] = ll ? vh : (_Float16)0.0f;
-                l[u] = ll ? vl : vh;
+                h[u] = ln.ll ? vh : (_Float16)0.0f;
+                l[u] = ln.ll ? vl : vh;
             }
-            QH[ks][e2] = as_u32(h);
-            QL[ks][e2] = as_u32(l);
+            ln.QH[ks][e2] = as_u32(h);
+            ln.QL[ks][e2] = as_u32(l);
         }
-    const float q0 = q_l[hh * D];
-    const float q0c = has0 ? q0 * C : 0.0f;
+    {
+        const float q0 = q_l[ln.hh * D];
+        ln.q0c = has0 ? q0 * C : 0.0f;
+    }
     // stage 1 is free again once every LDS read above has returned
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (npairs > 1) issue_pair<KS>(c, pair_pages(ptab, P0 + 2, P1, hkv, g), st0 + S::BYTES, lane, pl);
-    float comp[4];  // this lane keeps tiles 4 ll + j after the limb split
+    Pair pr_k = {0, 0};  // pages whose keys load next
+    if (npairs > 0) issue_keys<KS>(c, pr_v, stage(0), lane, pl);
+    if (npairs > 1) {
+        pr_k = pair_pages(ptab, P0 + 2, P1, hkv, g);
+        issue_keys<KS>(c, pr_k, stage(1), lane, pl);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) comp[j] = ll ? tile_comp(4 + j) : tile_comp(j);
-
-    // ---- per-lane LDS offsets within a stage
+    for (int j = 0; j < 4; ++j) ln.comp[j] = ln.ll ? tile_comp(4 + j) : tile_comp(j);
     // key row 16 ks + 8 kh + e sits in slot 16 ks + 8 kh + (e ^ kh)
-    const uint32_t kr_even = kpage * S::KRP + (9 * kh) * ROW_BYTES + 2 * n;  // e even: slot e + kh
-    const uint32_t kr_odd = kpage * S::KRP + (7 * kh) * ROW_BYTES + 2 * n;   // e odd: slot e - kh
-    const uint32_t km_lane = S::OFF_KM + (kpage * NR + 8 * kh) * 4;
-    const uint32_t k0_lane = S::OFF_K0 + pp * 256 + 64 * G + 8 * ll;
-    uint32_t pw[4];  // P writes: chunk 4G + r of (pp, hh) at slot (4G + r) ^ hh, half ll
+    ln.kr_even = kpage * S::KRP + (9 * kh) * ROW_BYTES + 2 * n;  // e even: slot e + kh
+    ln.kr_odd = kpage * S::KRP + (7 * kh) * ROW_BYTES + 2 * n;   // e odd: slot e - kh
+    ln.km = S::OFF_KM + (kpage * NR + 8 * kh) * 4;
+    ln.k0 = S::OFF_K0 + ln.pp * 256 + 64 * G + 8 * ln.ll;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pw[r] = pp * 1024 + hh * 256 + 16 * ((4 * G + r) ^ hh) + 8 * ll;
-    // value lanes: row (q, h) = (n >> 2, n & 3), tokens 32 G + 8 kv + 0..7
+    for (int r = 0; r < 4; ++r)  // chunk 4G + r of (pp, hh) at slot (4G + r) ^ hh, half ll
+        ln.pw[r] = ln.pp * 1024 + ln.hh * 256 + 16 * ((4 * G + r) ^ ln.hh) + 8 * ln.ll;
     const int qv = n >> 2, hv = n & 3;
-    uint32_t pr_ofs[4], vm_ofs[4];
 #pragma unroll
     for (int kv = 0; kv < 4; ++kv) {
-        pr_ofs[kv] = hv * 256 + 16 * ((4 * G + kv) ^ hv);
-        vm_ofs[kv] = S::OFF_VM + qv * 256 + 16 * ((4 * G + kv) ^ qv);
+        ln.pr_ofs[kv] = hv * 256 + 16 * ((4 * G + kv) ^ hv);
+        ln.vm_ofs[kv] = S::OFF_VM + qv * 256 + 16 * ((4 * G + kv) ^ qv);
     }
-    const uint32_t vc_lane = S::OFF_VC + G * S::VBS + 2 * n;
+    ln.vc = S::OFF_VC + G * S::VBS + 2 * n;
+    // zero-point MFMA B operand: z + 1.5 s of group n >> 2 in columns 4q (its row
+    // (q, h) sum is sum_t P (z + 1.5 s)), 1 in columns 4q + 1 (sum_t P, the softmax
+    // denominator), 0 elsewhere; -1.5 in columns 4q of the second one adds -1.5 sum_t P s
+    {
+        const int zcol = n & 3;
+        const _Float16 a = (_Float16)(zcol == 0 ? 1.5f : 0.f), o = (_Float16)(zcol == 0 ? 1.f : 0.f);
+        const _Float16 cc = (_Float16)(zcol == 1 ? 1.f : 0.f), m = (_Float16)(zcol == 0 ? -1.5f : 0.f);
+        ln.zc_s = half2v{a, a};
+        ln.zc_z = half2v{o, o};
+        ln.zc_c = half2v{cc, cc};
+        ln.M15 = half8{m, m, m, m, m, m, m, m};
+    }
 
     float m_run = -__builtin_huge_valf();  // running max (log2 domain) of head hh
-    float l_acc = 0.0f, z_acc = 0.0f;
     f32x4 O[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) O[t] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 Oz = {0.f, 0.f, 0.f, 0.f};  // zero-point terms (columns 4q) and denominators (4q + 1)
 
-    for (int u = 0; u < npairs; ++u) {
-        const uint32_t st = st0 + (uint32_t)(u & 1) * S::BYTES;
-        const int lp0 = P0 + 2 * u;
-        const int nv0 = min(PG, L - lp0 * PG);
-        const int nv1 = lp0 + 1 < P1 ? min(PG, L - (lp0 + 1) * PG) : 0;
-        const bool more = u + 2 < npairs;
-        Pair nxt = {0, 0};
-        if (more) nxt = pair_pages(ptab, lp0 + 4, P1, hkv, g);
-        if (u + 1 < npairs)
-            wait_dma<S::NDMA>();
+    // Step u scores pair u (u < npairs) and multiplies the values of pair u - 1
+    // (u >= 1).  At its start the loads issued two steps back have to be
+    // complete: keys of pair u and values of pair u - 1.
+    int issued = 0;  // vector memory instructions issued by the previous step
+    if (npairs > 1) issued = S::KN;  // keys of pair 1 behind those of pair 0
+    for (int u = 0; u <= npairs; ++u) {
+        if (issued == S::KN + S::VN)
+            wait_dma<S::KN + S::VN>();
+        else if (issued == S::KN)
+            wait_dma<S::KN>();
+        else if (issued == S::VN)
+            wait_dma<S::VN>();
         else
             wait_dma<0>();
+        const bool score = u < npairs, mult = u >= 1;
+        const uint32_t stq = stage(u), stv = stage(u - 1);
+        if (mult) {  // unspecified metadata past the end of a sequence must not reach the products
+            const int lp = P0 + 2 * (u - 1);
+            const int v0 = nvalid(lp), v1 = nvalid(lp + 1);
+            if (v0 < PG) clear_tail_meta(stv + S::OFF_VM, v0, lane);
+            if (v1 < PG) clear_tail_meta(stv + S::OFF_VM + 2048, v1, lane);  // an absent page too
+        }
+        // next loads: keys of pair u + 2 (into this stage, once scored), values of
+        // pair u + 1 (into the other stage, once multiplied)
+        const bool ld_k = u + 2 < npairs, ld_v = u + 1 < npairs;
+        Pair nk = {0, 0}, nv = {0, 0};
+        if (ld_k) nk = pair_pages(ptab, P0 + 2 * (u + 2), P1, hkv, g);
+        if (ld_v) nv = pr_k;  // keys of pair u + 1 were loaded last step with these pages
 
-        // ---- scores and the zero-point bias
-        f32x4 Sc[8];
+        // channel 0 of pair u, read before this stage's key area is refilled below
+        u32x2 k0v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) k0v[r] = score ? lds_u64(stq + ln.k0 + 16 * r) : u32x2{0u, 0u};
+        f32x4 Sc[8], Sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 8; ++t) Sc[t] = {0.f, 0.f, 0.f, 0.f};
-        float bias = 0.0f;
+        if (score && mult) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 d0 = lds_u128(st + km_lane + 64 * ks);
-            const u32x4 d1 = lds_u128(st + km_lane + 64 * ks + 16);
-            const uint32_t dd[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-            u32x4 Bv;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const half2v s2 = as_half2(__builtin_amdgcn_perm(dd[2 * e2 + 1], dd[2 * e2], 0x05040100u));
-                const half2v z2 = as_half2(__builtin_amdgcn_perm(dd[2 * e2 + 1], dd[2 * e2], 0x07060302u));
-                const half2v qh = as_half2(QH[ks][e2]), ql = as_half2(QL[ks][e2]);
-                const half2v t1 = qh * s2;
-                const half2v t2 = __builtin_elementwise_fma(qh, s2, -t1);
-                Bv[e2] = as_u32(__builtin_elementwise_fma(ql, s2, t2));
-                bias = __builtin_amdgcn_fdot2(qh, z2, bias, false);
-                bias = __builtin_amdgcn_fdot2(ql, z2, bias, false);
+            for (int i = 0; i < 8; ++i) {
+                pv_step<KS>(i >> 2, i & 3, stv, pb, ln, O, Oz);
+                if (i < KS) qk_step<KS>(i, stq, ln, Sc, Sb);
             }
-            const half8 Bh = as_half8(Bv);
-            u32x4 X;
-            const uint32_t kb = st + 16 * ks * ROW_BYTES;
+        } else if (score) {
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) X[e2] = lds_pair(kb + kr_even + 64 * e2, kb + kr_odd + 64 * e2 + ROW_BYTES);
-            const Packed XP = pack_shifts(X);
-            Sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<0>(XP)), Bh, Sc[0], 0, 0, 0);
-            Sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<1>(XP)), Bh, Sc[1], 0, 0, 0);
-            Sc[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<2>(XP)), Bh, Sc[2], 0, 0, 0);
-            Sc[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<3>(XP)), Bh, Sc[3], 0, 0, 0);
-            Sc[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<4>(XP)), Bh, Sc[4], 0, 0, 0);
-            Sc[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<5>(XP)), Bh, Sc[5], 0, 0, 0);
-            Sc[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<6>(XP)), Bh, Sc[6], 0, 0, 0);
-            Sc[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(tile_codes<7>(XP)), Bh, Sc[7], 0, 0, 0);
+            for (int ks = 0; ks < KS; ++ks) qk_step<KS>(ks, stq, ln, Sc, Sb);
+        } else if (mult) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv_step<KS>(i >> 2, i & 3, stv, pb, ln, O, Oz);
         }
-        // bias of column (pp, hh): the limb-1 lanes hold C q' in full; sum over the k ranges
-        bias = ll ? bias : 0.0f;
-        bias += dpp_xor1(bias);
-        bias = sum_x32(sum_x16(bias));
+        // every LDS read of the two stages has returned: refill them
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issued = 0;
+        if (ld_k) {
+            issue_keys<KS>(c, nk, stq, lane, pl);
+            issued += S::KN;
+        }
+        if (ld_v) {
+            issue_vals<KS>(c, nv, stage(u + 1), lane, pl);
+            issued += S::VN;
+        }
+        if (ld_k) pr_k = nk;
+        if (!score) break;
 
-        // ---- logits (log2 domain): lane keeps tiles 4 ll + j of its column, rows r:
-        //      token 32 G + 8 r + 4 ll + j of page pp, head hh
+        // ---- logits (log2 domain) of pair u: lane keeps tiles 4 ll + j of its
+        //      column, rows r: token 32 G + 8 r + 4 ll + j of page pp, head hh
+        const int lp0 = P0 + 2 * u;
+        const int nv0 = nvalid(lp0), nv1 = nvalid(lp0 + 1);
+        const float bias = Sb[0] + dpp_xor1(Sb[0]);  // both limbs
+        const uint32_t llmask = ln.ll ? 0xFFFFFFFFu : 0u;
         float x[4][4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            u32x2 k0 = {0u, 0u};
-            if (has0) k0 = lds_u64(st + k0_lane + 16 * r);
+            const u32x2 k0 = k0v[r];  // q0c = 0 when channel 0 is pruned
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float mine = ll ? Sc[4 + j][r] : Sc[j][r];
-                const float give = ll ? Sc[j][r] : Sc[4 + j][r];
-                float v = __builtin_fmaf(mine + dpp_xor1(give), comp[j], bias);
+                // bitwise selects: a conditional pick between the two tiles would be
+                // turned into an indexed access of the accumulator array
+                const uint32_t lo = __float_as_uint(Sc[j][r]), hi = __float_as_uint(Sc[4 + j][r]);
+                const float mine = __uint_as_float((hi & llmask) | (lo & ~llmask));
+                const float give = __uint_as_float((lo & llmask) | (hi & ~llmask));
+                float v = __builtin_fmaf(mine + dpp_xor1(give), ln.comp[j], bias);
                 const uint32_t kw = k0[j >> 1];
-                v = __builtin_fmaf(q0c, __uint_as_float((j & 1) ? (kw & 0xFFFF0000u) : (kw << 16)), v);
+                v = __builtin_fmaf(ln.q0c, __uint_as_float((j & 1) ? (kw & 0xFFFF0000u) : (kw << 16)), v);
                 x[r][j] = v;
             }
         }
         if (nv0 < PG || nv1 < PG) {
-            const int nvp = pp ? nv1 : nv0;
+            const int nvp = ln.pp ? nv1 : nv0;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (32 * G + 8 * r + 4 * ll + j >= nvp) x[r][j] = -__builtin_huge_valf();
+                    if (32 * G + 8 * r + 4 * ln.ll + j >= nvp) x[r][j] = -__builtin_huge_valf();
         }
         // ---- running max of head hh over the pair
         float bm = -__builtin_huge_valf();
@@ -458,7 +603,7 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
         bm = fmaxf(bm, dpp_xor8(bm));
         bm = max_x32(max_x16(bm));
         const float m_new = fmaxf(m_run, bm);
-        if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {
+        if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {  // O already holds pair u - 1
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // head hh
             float a[GRP];
 #pragma unroll
@@ -467,93 +612,35 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
             for (int t = 0; t < 8; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) O[t][r] *= a[r];
-            z_acc *= (hv & 2) ? ((hv & 1) ? a[3] : a[2]) : ((hv & 1) ? a[1] : a[0]);
-            l_acc *= alpha;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Oz[r] *= a[r];
         }
         m_run = m_new;
-        // ---- probabilities -> fp16 -> LDS (key-row area of this stage)
-        {
-            float ls = 0.0f;
+        // ---- probabilities -> fp16 -> LDS (read by the next step's value products)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float p[4];
+        for (int r = 0; r < 4; ++r) {
+            float p[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    p[j] = __builtin_amdgcn_exp2f(x[r][j] - m_new);
-                    ls += p[j];
-                }
-                half2v h01, h23;
-                h01[0] = (_Float16)p[0];
-                h01[1] = (_Float16)p[1];
-                h23[0] = (_Float16)p[2];
-                h23[1] = (_Float16)p[3];
-                lds_st64(st + pw[r], u32x2{as_u32(h01), as_u32(h23)});
-            }
-            l_acc += ls;
+            for (int j = 0; j < 4; ++j) p[j] = __builtin_amdgcn_exp2f(x[r][j] - m_new);
+            half2v h01, h23;
+            h01[0] = (_Float16)p[0];
+            h01[1] = (_Float16)p[1];
+            h23[0] = (_Float16)p[2];
+            h23[1] = (_Float16)p[3];
+            lds_st64(pb + ln.pw[r], u32x2{as_u32(h01), as_u32(h23)});
         }
-
-        // ---- values of both pages
-        const half2v c15 = {(_Float16)1.5f, (_Float16)1.5f};
-        const half2v m15 = {(_Float16)-1.5f, (_Float16)-1.5f};
-#pragma unroll
-        for (int vp = 0; vp < 2; ++vp) {
-            const int nv = vp ? nv1 : nv0;
-            if (nv <= 0) continue;
-#pragma unroll
-            for (int kv = 0; kv < 4; ++kv) {
-                u32x4 Pp = lds_u128(st + vp * 1024 + pr_ofs[kv]);
-                u32x4 sp = lds_u128(st + vp * 2048 + vm_ofs[kv]);
-                u32x4 zp = lds_u128(st + vp * 2048 + vm_ofs[kv] + 1024);
-                if (nv < PG) {
-                    const int tok0 = 32 * G + 8 * kv;
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        const uint32_t keep = (tok0 + 2 * e2 < nv ? 0x0000FFFFu : 0u) |
-                                              (tok0 + 2 * e2 + 1 < nv ? 0xFFFF0000u : 0u);
-                        sp[e2] &= keep;
-                        zp[e2] &= keep;
-                        Pp[e2] &= keep;
-                    }
-                }
-                u32x4 A;
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const half2v a2 = as_half2(Pp[e2]) * as_half2(sp[e2]);
-                    A[e2] = as_u32(a2);
-                    // centred codes: v = (c - 1.5) s + (z + 1.5 s)
-                    const half2v zc = __builtin_elementwise_fma(as_half2(sp[e2]), c15, as_half2(zp[e2]));
-                    z_acc = __builtin_amdgcn_fdot2(as_half2(Pp[e2]), zc, z_acc, false);
-                    z_acc = __builtin_amdgcn_fdot2(a2, m15, z_acc, false);
-                }
-                u32x4 X;
-                const uint32_t vb = st + vc_lane + vp * S::VPS + 8 * kv * ROW_BYTES;
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) X[e2] = lds_pair(vb + 64 * e2, vb + 64 * e2 + ROW_BYTES);
-                const half8 Ah = as_half8(A);
-                const Packed XP = pack_shifts(X);
-                O[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<0>(XP)), O[0], 0, 0, 0);
-                O[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<1>(XP)), O[1], 0, 0, 0);
-                O[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<2>(XP)), O[2], 0, 0, 0);
-                O[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<3>(XP)), O[3], 0, 0, 0);
-                O[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<4>(XP)), O[4], 0, 0, 0);
-                O[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<5>(XP)), O[5], 0, 0, 0);
-                O[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<6>(XP)), O[6], 0, 0, 0);
-                O[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(tile_codes<7>(XP)), O[7], 0, 0, 0);
-            }
-        }
-        // this stage is consumed: refill it with pair u + 2
-        if (more) issue_pair<KS>(c, nxt, st, lane, pl);
     }
     wait_dma<0>();
 
-    // ---- totals
-    l_acc += dpp_xor1(l_acc);
-    l_acc += dpp_xor8(l_acc);
-    l_acc = sum_x32(sum_x16(l_acc));  // every lane of head hh: l of head hh
-    z_acc = sum_x32(sum_x16(z_acc));  // lanes n = 4q + h: zero-point term of row (q, h)
+    // ---- totals: row (q = G, h = r) of Oz holds the zero-point term in column 4G
+    //      (broadcast over the quad of lanes 4G..4G+3) and l_h in column 4q + 1
     float zq[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) zq[r] = __shfl(z_acc, 4 * G + r);  // row (q = G, h = r)
+    for (int r = 0; r < 4; ++r)
+        zq[r] = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(Oz[r]), 0x00, 0xF, 0xF, false));
+    float l_h[GRP];
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) l_h[h] = bcast_lane(Oz[h], 1);  // lane 1: column 1, rows (0, h)
     float *dst0 = partials + (((size_t)b * hq + (size_t)g * GRP) * nsplit + split) * PART_FLOATS;
     const size_t hstride = (size_t)nsplit * PART_FLOATS;
     if ((n >> 2) == G) {  // channel 8n + t belongs to group q = G
@@ -565,8 +652,9 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
     }
     if (lane < 8 && (lane & 1) == 0) {  // lane 2h: column (0, h, 0)
         const int h = lane >> 1;
+        const float lh = (h & 2) ? ((h & 1) ? l_h[3] : l_h[2]) : ((h & 1) ? l_h[1] : l_h[0]);
         dst0[h * hstride + D] = npairs > 0 ? m_run * LN2 : -__builtin_huge_valf();
-        dst0[h * hstride + D + 1] = npairs > 0 ? l_acc : 0.0f;
+        dst0[h * hstride + D + 1] = npairs > 0 ? lh : 0.0f;
     }
 }
 
