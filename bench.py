@@ -61,6 +61,43 @@ def committed_traffic(kernel_hash):
     return rec
 
 
+def _counter_means(path, counter):
+    """Per-dispatch mean of one counter for every kernel name in a rocprofv3 counter CSV."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def write_traffic(fetch_csv, write_csv, out_json):
+    """HBM bytes per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the 1 GiB copy of --calib-copy
+    (1 GiB read, 1 GiB written)."""
+    fetch, write = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "elementwise" in k and "Mul" in k]
+    if not copy:
+        copy = [k for k in fetch if "elementwise" in k]
+    copy_f = max(fetch[k] for k in copy)
+    copy_w = max(write.get(k, 0.0) for k in copy)
+    gib_kib = float(1 << 20)
+    ff, fw = gib_kib / copy_f, gib_kib / copy_w
+    rec = {"kernel_hash": source_hash(), "fetch_scale": round(ff, 4), "write_scale": round(fw, 4),
+           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "kernels": {}}
+    total = 0.0
+    for k in fetch:
+        if "decode_g4_kernel" in k or "merge_kernel" in k:
+            b = fetch[k] * 1024 * ff + write.get(k, 0.0) * 1024 * fw
+            rec["kernels"][k[:60]] = {"fetch_kib": fetch[k], "write_kib": write.get(k, 0.0), "hbm_bytes": b}
+            total += b
+    rec["hbm_bytes_per_launch"] = total
+    with open(out_json, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def build_cache(prob, shape, d, pa, torch):
     """Pack the whole batch into the INT2 cache on the GPU, sequence by sequence."""
     cache = pa.Cache(prob.num_pages, shape.hkv)
@@ -117,10 +154,16 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps (MALL eviction)")
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--cpu-reps", type=int, default=15)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy kernel (PMC calibration)")
+    ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
+                    help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a --calib-copy run "
+                         "into the per-launch HBM traffic record and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
