@@ -109,7 +109,7 @@ def build_cache(prob, shape, d, pa, torch):
             k_d = torch.from_numpy(kb.view(np.int16)).to("cuda")
             v_d = torch.from_numpy(vb.view(np.int16)).to("cuda")
             cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
-            pa.dqk_quantize_append(cache, k_d, v_d, d["t_k"], cu, d["page_table"][b:b + 1].contiguous())
+            pa.dqk_quantize_append(cache, k_d, v_d, d["t_k"], cu, d["page_table"][b:b + 1].clone())
             torch.cuda.synchronize()
             del k_d, v_d
     return cache

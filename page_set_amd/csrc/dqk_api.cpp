@@ -29,10 +29,10 @@ int check_cache(const dqk_cache *c) {
     return DQK_OK;
 }
 
-int resolve_splits(int batch, int hq, int hkv, int max_pages, int num_splits) {
-    (void)hq;
+// n_keep = 0: the largest count any n_keep can resolve to (workspace sizing)
+int resolve_splits(int batch, int hq, int hkv, int max_pages, int num_splits, int n_keep) {
     if (num_splits > 0) return num_splits;
-    if (dqk::use_mfma_decode(hq, hkv)) return dqk::decode_splits_mfma(batch, hkv, max_pages);
+    if (dqk::use_mfma_decode(hq, hkv)) return dqk::decode_splits_mfma(batch, hkv, max_pages, n_keep);
     return dqk::decode_splits_generic(batch, hkv, max_pages);
 }
 
@@ -85,7 +85,7 @@ int dqk_quantize_append(const dqk_cache *c, const void *k_bf16, const void *v_bf
 size_t dqk_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t max_pages, int32_t num_splits) {
     if (batch < 1 || hq < 1 || hkv < 1 || max_pages < 1 || num_splits < 0) return 0;
     // enough for either decode entry point
-    int s = resolve_splits(batch, hq, hkv, max_pages, num_splits);
+    int s = resolve_splits(batch, hq, hkv, max_pages, num_splits, 0);
     const int s_gen = num_splits > 0 ? num_splits : dqk::decode_splits_generic(batch, hkv, max_pages);
     if (s_gen > s) s = s_gen;
     return (size_t)batch * hq * s * dqk::PART_FLOATS * sizeof(float);
@@ -108,7 +108,7 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
     if (!aligned16(q_prime) || !aligned16(sel_idx) || !aligned16(page_table) || !aligned16(seq_lens) ||
         !aligned16(workspace) || !aligned16(out) || (lse && !aligned16(lse)))
         return DQK_ERR_ALIGN;
-    const int splits = resolve_splits(batch, hq, hkv, max_pages, num_splits);
+    const int splits = resolve_splits(batch, hq, hkv, max_pages, num_splits, n_keep);
     if (ws_bytes < (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float)) return DQK_ERR_WORKSPACE;
     dqk::DecodeArgs a{c,         q_prime,  sel_idx, n_keep, batch,  hq, hkv, page_table, max_pages, seq_lens,
                       sm_scale, splits, static_cast<float *>(workspace), out, lse};

@@ -662,10 +662,22 @@ __global__ __launch_bounds__(64) void decode_g4_kernel(dqk_cache c, const float 
 
 bool use_mfma_decode(int hq, int hkv) { return hkv > 0 && hq == GRP * hkv; }
 
-int decode_splits_mfma(int batch, int hkv, int max_pages) {
-    // about four single-wave workgroups per CU on 256 CUs, at least 8 pages each
+template <int KS>
+static constexpr int wave_lds_bytes() {
+    return 2 * Stage<KS>::BYTES + 2 * GRP * PG * 2;
+}
+
+int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep) {
+    // enough single-wave workgroups to fill every CU once (256 CUs, as many
+    // per CU as fit in 160 KB of LDS), at least 8 pages each; n_keep = 0 asks
+    // for the largest count any n_keep can use (workspace sizing)
+    static constexpr int lds[9] = {0,
+                                   wave_lds_bytes<1>(), wave_lds_bytes<2>(), wave_lds_bytes<3>(), wave_lds_bytes<4>(),
+                                   wave_lds_bytes<5>(), wave_lds_bytes<6>(), wave_lds_bytes<7>(), wave_lds_bytes<8>()};
+    const int ks = n_keep > 0 ? (n_keep + 15) / 16 : 1;
+    const int per_cu = (160 * 1024) / lds[ks < 1 ? 1 : ks > 8 ? 8 : ks];
     const int units = batch * hkv;
-    int s = (1024 + units - 1) / units;
+    int s = (256 * per_cu + units - 1) / units;
     const int cap = (max_pages + 7) / 8;
     if (s > cap) s = cap;
     return s < 1 ? 1 : s;

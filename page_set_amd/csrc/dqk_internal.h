@@ -131,7 +131,7 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 
 // MFMA path (group size 4, the GQA 32/8 shape).
 bool use_mfma_decode(int hq, int hkv);
-int decode_splits_mfma(int batch, int hkv, int max_pages);
+int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep);  // n_keep 0: the largest
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 
 struct DecodeBf16Args {
