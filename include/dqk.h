@@ -166,6 +166,17 @@ int dqk_decode_attn_bf16(const void *k_pages, const void *v_pages, int32_t hkv, 
                          const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
                          size_t ws_bytes, float *out, float *lse, hipStream_t stream);
 
+/*
+ * dqk_stream_read -- measurement helper, not part of the attention path: a
+ * plain streaming read of `bytes` bytes (a multiple of 16 KiB) at `src`,
+ * 16 bytes per lane through LDS, as the reference point for the decode
+ * kernel's achieved HBM bandwidth.  `sink` (device, 4 bytes per 64-lane
+ * workgroup: bytes / 16 KiB rounded to the grid the call picks, at most
+ * 4096 * 4 bytes) receives a checksum so the reads cannot be elided.
+ * Returns DQK_ERR_SHAPE if bytes is 0 or not a multiple of 16 KiB.
+ */
+int dqk_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Static text for a DQK_* status code. */
 const char *dqk_status_string(int status);
 

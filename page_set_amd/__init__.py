@@ -64,6 +64,8 @@ def lib():
         L.dqk_decode_attn_bf16.argtypes = [P, P, i32, i32, P, i32, i32, P, i32, P, ctypes.c_float, i32, P, sz, P, P,
                                            P]
         L.dqk_decode_attn_bf16.restype = ctypes.c_int
+        L.dqk_stream_read.argtypes = [P, sz, P, P]
+        L.dqk_stream_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -179,3 +181,10 @@ def dqk_decode_attn_bf16(k_pages, v_pages, q, page_table, seq_lens, sm_scale: fl
                                     _stream(stream))
     _check(rc, "dqk_decode_attn_bf16")
     return out, lse
+
+
+def dqk_stream_read(src, sink, stream=None):
+    """Measurement helper: plain streaming read of all of `src` (device tensor,
+    a multiple of 16 KiB); `sink` is a device uint32/int32 tensor of 4096 entries."""
+    rc = lib().dqk_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream))
+    _check(rc, "dqk_stream_read")

@@ -55,6 +55,13 @@ const char *dqk_status_string(int status) {
 
 int dqk_last_hip_error(void) { return g_last_hip; }
 
+int dqk_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t stream) {
+    if (!src || !sink) return DQK_ERR_NULL;
+    if (bytes == 0 || bytes % 16384 != 0) return DQK_ERR_SHAPE;
+    if (!aligned16(src) || !aligned16(sink)) return DQK_ERR_ALIGN;
+    return hip_status(dqk::launch_stream_read(src, bytes, sink, stream));
+}
+
 int dqk_select_channels(const void *q_bf16, const float *t_q, int32_t batch, int32_t hq, int32_t hkv,
                         int32_t n_keep, float *q_prime, int32_t *sel_idx, hipStream_t stream) {
     if (!q_bf16 || !t_q || !q_prime || !sel_idx) return DQK_ERR_NULL;

@@ -371,7 +371,51 @@ __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part
     if (lse && tid == 0) lse[bh] = M + __logf(Lsum);
 }
 
+// Plain streaming read (measurement reference): block i reads chunk i of
+// `per` bytes, 8 KB stages through LDS, two stages in flight.
+__global__ __launch_bounds__(64) void stream_read_kernel(const uint8_t *__restrict__ src, size_t per,
+                                                         uint32_t *__restrict__ sink) {
+    __shared__ __attribute__((aligned(16))) uint8_t buf[2][8192];
+    const uint8_t *p = src + (size_t)blockIdx.x * per;
+    const int lane = threadIdx.x;
+    const int nst = (int)(per / 8192);
+    const uint32_t b0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)&buf[0][0];
+    auto issue = [&](int s) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint8_t *a = p + (size_t)s * 8192 + k * 1024 + lane * 16;
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(a),
+                         "s"(b0 + (uint32_t)(s & 1) * 8192 + k * 1024)
+                         : "memory", "m0");
+        }
+    };
+    issue(0);
+    uint32_t acc = 0;
+    for (int s = 0; s < nst; ++s) {
+        if (s + 1 < nst) {
+            issue(s + 1);
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        acc ^= *(volatile __attribute__((address_space(3))) uint32_t *)(uintptr_t)(b0 + (uint32_t)(s & 1) * 8192 + lane * 4);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    acc += __shfl_xor(acc, 1);
+    if (lane == 0) sink[blockIdx.x] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s) {
+    // up to 4096 single-wave blocks, each a whole number of 16 KiB
+    const size_t units = bytes / 16384;
+    int blocks = (int)(units < 4096 ? units : 4096);
+    while (units % (size_t)blocks) --blocks;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(64), 0, s, static_cast<const uint8_t *>(src),
+                       bytes / (size_t)blocks, sink);
+    return hipGetLastError();
+}
 
 int decode_splits_generic(int batch, int hkv, int max_pages) {
     const int units = batch * hkv;

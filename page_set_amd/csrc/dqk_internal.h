@@ -150,6 +150,8 @@ struct DecodeBf16Args {
 
 hipError_t launch_decode_bf16(const DecodeBf16Args &a, hipStream_t s);
 
+hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hipStream_t s);
+
 hipError_t launch_merge(const float *partials, int batch, int hq, int num_splits, float *out, float *lse,
                         hipStream_t s);
 

@@ -128,3 +128,11 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(pa, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError):
         pa.lib()
+
+
+def test_stream_read_validation():
+    L = pa.lib()
+    assert L.dqk_stream_read(None, 16384, A, None) == pa.DQK_ERR_NULL
+    assert L.dqk_stream_read(A, 0, A, None) == pa.DQK_ERR_SHAPE
+    assert L.dqk_stream_read(A, 16384 + 16, A, None) == pa.DQK_ERR_SHAPE
+    assert L.dqk_stream_read(MIS, 16384, A, None) == pa.DQK_ERR_ALIGN
