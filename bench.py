@@ -98,39 +98,71 @@ def write_traffic(fetch_csv, write_csv, out_json):
     print(json.dumps(rec, indent=1))
 
 
-def build_cache(prob, shape, d, pa, torch):
-    """Pack the whole batch into the INT2 cache on the GPU, sequence by sequence;
-    each append call is timed with HIP events on its stream (inputs resident)."""
+def build_cache(prob, shape, d, pa, torch, one_call=False):
+    """Pack the whole batch into the INT2 cache on the GPU (dqk_quantize_append,
+    inputs resident in HBM); each append call is timed with HIP events on its
+    stream.  Sequence by sequence by default; `one_call` appends the whole
+    ragged batch in a single call (cu_tokens over all sequences)."""
     cache = pa.Cache(prob.num_pages, shape.hkv)
     times, tokens = [], 0
     stream = torch.cuda.current_stream()
+
+    def timed(k_d, v_d, cu, pt, warm):
+        if warm:  # untimed first call (loads the code object); rewrites the same pages
+            pa.dqk_quantize_append(cache, k_d, v_d, d["t_k"], cu, pt, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pa.dqk_quantize_append(cache, k_d, v_d, d["t_k"], cu, pt, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e-3)
+
     with cf.ThreadPoolExecutor(max_workers=4) as ex:
         futs = [ex.submit(synth.make_kv_seq, shape, prob.seed, b, prob.outliers) for b in range(shape.batch)]
+        if one_call:
+            kk, vv = zip(*[f.result() for f in futs])
+            k_d = torch.from_numpy(np.concatenate(kk).view(np.int16)).to("cuda")
+            v_d = torch.from_numpy(np.concatenate(vv).view(np.int16)).to("cuda")
+            del kk, vv
+            timed(k_d, v_d, d["cu"], d["page_table"], True)
+            tokens = int(k_d.shape[0])
+            del k_d, v_d
+            return cache, sum(times), tokens
         for b, f in enumerate(futs):
             kb, vb = f.result()
             L = kb.shape[0]
             k_d = torch.from_numpy(kb.view(np.int16)).to("cuda")
             v_d = torch.from_numpy(vb.view(np.int16)).to("cuda")
             cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
-            pt = d["page_table"][b:b + 1].clone()
-            if b == 0:  # untimed first call (loads the code object); rewrites the same pages
-                pa.dqk_quantize_append(cache, k_d, v_d, d["t_k"], cu, pt, stream=stream)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            pa.dqk_quantize_append(cache, k_d, v_d, d["t_k"], cu, pt, stream=stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e-3)
+            timed(k_d, v_d, cu, d["page_table"][b:b + 1].clone(), b == 0)
             tokens += L
             del k_d, v_d
     return cache, sum(times), tokens
 
 
-def append_roofline(seconds, tokens, hkv):
+def build_bf16_pages(prob, shape, torch):
+    """The unpruned BF16 cache of the baseline: raw keys and values laid out in
+    128-token pages [page][Hkv][128 tok][128 ch] on the GPU (page table as in
+    the INT2 cache)."""
+    kp = torch.zeros((prob.num_pages, shape.hkv, 128, 128), dtype=torch.int16, device="cuda")
+    vp = torch.zeros_like(kp)
+    for b in range(shape.batch):
+        kb, vb = synth.make_kv_seq(shape, prob.seed, b, prob.outliers)
+        L = kb.shape[0]
+        npg = (L + 127) // 128
+        pages = torch.from_numpy(prob.page_table[b, :npg].astype(np.int64)).to("cuda")
+        for src, dst in ((kb, kp), (vb, vp)):
+            x = torch.zeros((npg * 128, shape.hkv, 128), dtype=torch.int16, device="cuda")
+            x[:L] = torch.from_numpy(src.view(np.int16)).to("cuda")
+            dst[pages] = x.view(npg, 128, shape.hkv, 128).permute(0, 2, 1, 3)
+            del x
+    return kp, vp
+
+
+def append_roofline(seconds, tokens, pages, hkv):
     """Quantize-append: bf16 K and V read, INT2 pages written; K x T_K on MFMA."""
     rd = tokens * hkv * 128 * 2 * 2 + hkv * 128 * 128 * 2
-    pages = -(-tokens // 128)
     wr = pages * hkv * (128 * 32 + 128 * 4 + 128 * 2 + 128 * 32 + 2048)
     flops = 2.0 * tokens * hkv * 128 * 128
     gbs = (rd + wr) / seconds / 1e9
@@ -163,33 +195,164 @@ def stream_read_gbs(torch, pa, nbytes):
     return n / t / 1e9
 
 
-def cpu_baseline(shape, seed, n_keep, reps):
-    """The CPU oracle (single thread, as written) on one (sequence, KV head)
-    unit of the same workload: select + decode repeated `reps` times, scaled to
-    the batch's units per step."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(shape, seed, n_keep, max_workers=16):
+    """The CPU oracle (as written: single-threaded C, fp64) on the same workload,
+    on a bounded sample of its (sequence, KV head) units.  Each unit's cache is
+    built by the oracle from the same seeded inputs; then `w` units are decoded
+    at once on `w` host threads (ctypes releases the GIL, so the oracle calls
+    run in parallel), and one unit is decoded alone for the single-core figure.
+    Step time = units per step x the per-unit time / threads."""
     import oracle
     prob = synth.make_problem(shape, seed, materialize_kv=False)
-    L = shape.seq_lens[0]
-    g = 0
     grp = shape.hq // shape.hkv
-    kb, vb = synth.make_kv_seq(shape, seed, 0, prob.outliers)
-    kk = np.ascontiguousarray(kb[:, g:g + 1])
-    vv = np.ascontiguousarray(vb[:, g:g + 1])
-    npg = (L + 127) // 128
-    pt = np.arange(npg, dtype=np.int32)[None]
-    cache, _ = oracle.quantize_append(kk, vv, prob.t_k[g:g + 1], np.array([0, L], np.int32), pt, npg)
-    q = np.ascontiguousarray(prob.q[0:1, g * grp:(g + 1) * grp])
-    lens = np.array([L], np.int32)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        qp, sel = oracle.select_channels(q, prob.t_q[g:g + 1], 1, n_keep)
+    units_all = shape.batch * shape.hkv
+    w = max(1, min(max_workers, os.cpu_count() or 1, units_all))
+    units = [(u // shape.hkv, u % shape.hkv) for u in range(w)]
+
+    kv = {}
+    for b in sorted({b for b, _ in units}):
+        kb, vb = synth.make_kv_seq(shape, seed, b, prob.outliers)
+        for bb, g in units:
+            if bb == b:
+                kv[(b, g)] = (np.ascontiguousarray(kb[:, g:g + 1]), np.ascontiguousarray(vb[:, g:g + 1]))
+        del kb, vb
+
+    def build(unit):
+        b, g = unit
+        kk, vv = kv[unit]
+        L = kk.shape[0]
+        npg = (L + 127) // 128
+        pt = np.arange(npg, dtype=np.int32)[None]
+        cache, _ = oracle.quantize_append(kk, vv, prob.t_k[g:g + 1], np.array([0, L], np.int32), pt, npg)
+        q = np.ascontiguousarray(prob.q[b:b + 1, g * grp:(g + 1) * grp])
+        return cache, q, pt, np.array([L], np.int32), prob.t_q[g:g + 1]
+
+    def run(args):
+        cache, q, pt, lens, tq = args
+        t0 = time.perf_counter()
+        qp, sel = oracle.select_channels(q, tq, 1, n_keep)
         oracle.decode_attn(cache, qp, sel, pt, lens, prob.sm_scale)
-    dt = (time.perf_counter() - t0) / reps
-    units = shape.batch * shape.hkv
-    t_step = dt * units
-    return {"value": shape.batch / t_step, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"1 of {units} (sequence, KV head) units ({grp} query heads x {L} tokens), select + decode, "
-                      f"{reps} repetitions, {dt:.3f} s each; step time = {units} x unit time"}
+        return time.perf_counter() - t0
+
+    with cf.ThreadPoolExecutor(max_workers=w) as ex:
+        built = list(ex.map(build, units))
+        kv.clear()
+        t0 = time.perf_counter()
+        per_unit = list(ex.map(run, built))
+        wall = time.perf_counter() - t0
+    single = min(run(built[0]) for _ in range(2))
+    t_step_all = units_all * wall / w
+    t_step_one = units_all * single
+    L = shape.seq_lens[0]
+    return {"value": round(shape.batch / t_step_all, 4), "unit": "tokens/s", "cores": w, "kind": "oracle",
+            "single_core_value": round(shape.batch / t_step_one, 4), "nproc": os.cpu_count(),
+            "cpu_model": _cpu_model(),
+            "sample": f"{w} of the {units_all} (sequence, KV head) units of the workload ({grp} query heads x "
+                      f"{L} tokens each), select + decode by the oracle: {w} units at once on {w} threads took "
+                      f"{wall:.2f} s (per unit {min(per_unit):.2f}-{max(per_unit):.2f} s), one unit alone "
+                      f"{single:.2f} s; step time = {units_all} units x unit time / threads"}
+
+
+def _copies_for(nbytes, target=1 << 30, cap=48):
+    """Cache copies rotated across steps so that one pass over all of them
+    exceeds the 256 MB Infinity Cache several times over."""
+    return int(max(2, min(cap, -(-target // max(1, nbytes)))))
+
+
+class Int2Workload:
+    """One INT2 decode workload resident on the GPU: inputs, cache copies and
+    output buffers of a config."""
+
+    def __init__(self, shape, seed, pa, torch, one_call=False):
+        self.shape, self.pa, self.torch = shape, pa, torch
+        self.prob = synth.make_problem(shape, seed, materialize_kv=False)
+        p = self.prob
+        self.d = {"q": torch.from_numpy(p.q.view(np.int16)).to("cuda"),
+                  "t_q": torch.from_numpy(p.t_q).to("cuda"),
+                  "t_k": torch.from_numpy(p.t_k.view(np.int16)).to("cuda"),
+                  "page_table": torch.from_numpy(p.page_table).to("cuda"),
+                  "seq_lens": torch.from_numpy(p.seq_lens).to("cuda"),
+                  "cu": torch.from_numpy(p.cu_tokens).to("cuda")}
+        cache, self.append_s, self.append_tokens = build_cache(p, shape, self.d, pa, torch, one_call=one_call)
+        self.caches = [cache]
+        for _ in range(_copies_for(cache.nbytes()) - 1):
+            c2 = pa.Cache(cache.num_pages, cache.num_kv_heads)
+            for a, b in zip(cache.arrays(), c2.arrays()):
+                b.copy_(a)
+            self.caches.append(c2)
+        torch.cuda.synchronize()
+        self.max_pages = int(p.page_table.shape[1])
+
+    def time_steps(self, n_keep, steps, warmup, num_splits=0):
+        """Wall time per step over `steps` steps (synchronised on both sides),
+        plus HIP-event averages of the select and decode calls on their stream."""
+        torch, pa, sh = self.torch, self.pa, self.shape
+        B, hq, hkv = sh.batch, sh.hq, sh.hkv
+        q_prime = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+        sel = torch.empty((B, hkv, n_keep), dtype=torch.int32, device="cuda")
+        out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+        ws_bytes = pa.dqk_decode_workspace_size(B, hq, hkv, self.max_pages, num_splits)
+        ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
+        stream = torch.cuda.current_stream()
+        d = self.d
+
+        def step(i, ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            pa.dqk_select_channels(d["q"], d["t_q"], hkv, n_keep, q_prime=q_prime, sel_idx=sel, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            pa.dqk_decode_attn(self.caches[i % len(self.caches)], q_prime, sel, d["page_table"], d["seq_lens"],
+                               self.prob.sm_scale, num_splits=num_splits, workspace=ws, out=out, want_lse=False,
+                               stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+
+        for i in range(warmup):
+            step(i)
+        evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        sel_us = [a.elapsed_time(b) * 1e3 for a, b, _ in evs]
+        dec_us = [b.elapsed_time(c) * 1e3 for _, b, c in evs]
+        sel_h = sel.cpu().numpy()
+        from page_set_amd import traffic
+        cache_bytes = traffic.decode_cache_bytes(self.prob.seq_lens, sel_h)
+        fixed = traffic.decode_fixed_bytes(B, hq, hkv, n_keep, self.max_pages)
+        return {"t_step_us": wall * 1e6, "select_us": float(np.mean(sel_us)), "decode_us": float(np.mean(dec_us)),
+                "decode_p10_us": float(np.percentile(dec_us, 10)), "decode_p90_us": float(np.percentile(dec_us, 90)),
+                "cache_bytes": cache_bytes, "decode_bytes": cache_bytes + fixed["decode"],
+                "step_bytes": cache_bytes + fixed["decode"] + fixed["select"],
+                "bytes_per_token_head": cache_bytes / (hkv * float(np.sum(self.prob.seq_lens)))}
+
+
+def _summary(name, w, r, n_keep):
+    B = w.shape.batch
+    rec = {"workload": name, "batch": B, "context": (max(w.shape.seq_lens) if len(set(w.shape.seq_lens)) == 1
+                                                     else "ragged"),
+           "n_keep": n_keep, "t_step_us": round(r["t_step_us"], 2), "tokens_per_s": round(B / (r["t_step_us"] * 1e-6), 1),
+           "select_us": round(r["select_us"], 2), "decode_call_us": round(r["decode_us"], 2),
+           "algorithmic_bytes_per_step": int(r["step_bytes"]),
+           "bytes_per_token_head": round(r["bytes_per_token_head"], 3),
+           "achieved_step_gbs": round(r["step_bytes"] / (r["t_step_us"] * 1e-6) / 1e9, 1),
+           "frac_step": round(r["step_bytes"] / (r["t_step_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+           "achieved_decode_gbs": round(r["decode_bytes"] / (r["decode_us"] * 1e-6) / 1e9, 1),
+           "cache_copies": len(w.caches)}
+    return rec
 
 
 def main():
@@ -200,10 +363,10 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--sparsity", type=float, default=0.4)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--copies", type=int, default=4, help="cache copies rotated across steps (MALL eviction)")
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-reps", type=int, default=15)
+    ap.add_argument("--sub-steps", type=int, default=20, help="timed steps of each secondary workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="headline workload only (no per-config records)")
     ap.add_argument("--calib-copy", action="store_true", help="also run a plain 1 GiB copy kernel (PMC calibration)")
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a --calib-copy run "
@@ -220,79 +383,40 @@ def main():
 
     import torch
     import page_set_amd as pa
-    from page_set_amd import traffic
 
     shape = synth.config_shape(args.config, args.seed, args.sparsity)
     n_keep = shape.n_keep
     log(f"[bench] workload {shape.name}: B={shape.batch} Hq/Hkv={shape.hq}/{shape.hkv} ctx={max(shape.seq_lens)} "
         f"n_keep={n_keep}")
-    prob = synth.make_problem(shape, args.seed, materialize_kv=False)
-    d = {"q": torch.from_numpy(prob.q.view(np.int16)).to("cuda"),
-         "t_q": torch.from_numpy(prob.t_q).to("cuda"),
-         "t_k": torch.from_numpy(prob.t_k.view(np.int16)).to("cuda"),
-         "page_table": torch.from_numpy(prob.page_table).to("cuda"),
-         "seq_lens": torch.from_numpy(prob.seq_lens).to("cuda")}
     t0 = time.time()
-    cache, app_s, app_tokens = build_cache(prob, shape, d, pa, torch)
-    log(f"[bench] cache built on GPU in {time.time() - t0:.1f}s ({cache.nbytes() / 1e6:.1f} MB)")
-    caches = [cache]
-    for _ in range(args.copies - 1):
-        c2 = pa.Cache(cache.num_pages, cache.num_kv_heads)
-        for a, b in zip(cache.arrays(), c2.arrays()):
-            b.copy_(a)
-        caches.append(c2)
-    torch.cuda.synchronize()
+    w = Int2Workload(shape, args.seed, pa, torch)
+    log(f"[bench] cache built on GPU in {time.time() - t0:.1f}s ({w.caches[0].nbytes() / 1e6:.1f} MB, "
+        f"{len(w.caches)} copies)")
+    r = w.time_steps(n_keep, args.steps, args.warmup, args.num_splits)
+    B = shape.batch
+    ms_per_step = r["t_step_us"] * 1e-3
+    log(f"[bench] {r['t_step_us']:.1f} us/step; select {r['select_us']:.1f} us; decode call {r['decode_us']:.1f} us "
+        f"(p10 {r['decode_p10_us']:.1f}, p90 {r['decode_p90_us']:.1f})")
 
-    B, hq, hkv = shape.batch, shape.hq, shape.hkv
-    max_pages = int(prob.page_table.shape[1])
-    q_prime = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
-    sel = torch.empty((B, hkv, n_keep), dtype=torch.int32, device="cuda")
-    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
-    ws_bytes = pa.dqk_decode_workspace_size(B, hq, hkv, max_pages, args.num_splits)
-    ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        pa.dqk_select_channels(d["q"], d["t_q"], hkv, n_keep, q_prime=q_prime, sel_idx=sel, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        pa.dqk_decode_attn(caches[i % len(caches)], q_prime, sel, d["page_table"], d["seq_lens"], prob.sm_scale,
-                           num_splits=args.num_splits, workspace=ws, out=out, want_lse=False, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_ms_avg = float(np.mean(dec_ms))
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step; decode call {dec_ms_avg * 1e3:.1f} us "
-        f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})")
-
-    sel_h = sel.cpu().numpy()
-    cache_bytes = traffic.decode_cache_bytes(prob.seq_lens, sel_h)
-    fixed = traffic.decode_fixed_bytes(B, hq, hkv, n_keep, max_pages)
-    alg_bytes = cache_bytes + fixed["decode"]
-    achieved = alg_bytes / (dec_ms_avg * 1e-3) / 1e9
+    achieved = r["decode_bytes"] / (r["decode_us"] * 1e-6) / 1e9
+    achieved_step = r["step_bytes"] / (r["t_step_us"] * 1e-6) / 1e9
     khash = source_hash()
     tr = committed_traffic(khash)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": (tr["hbm_bytes_per_launch"] if tr else None),
-            "kernel": "dqk_decode_attn (split decode + merge)", "algorithmic_bytes_per_launch": int(alg_bytes),
-            "bytes_per_token_head": round(cache_bytes / (B * hkv * max(shape.seq_lens)), 3),
-            "avg_launch_us": round(dec_ms_avg * 1e3, 2), "kernel_source_hash": khash}
-
-    roof["stream_read_gbs"] = round(stream_read_gbs(torch, pa, int(alg_bytes)), 1)
+            "kernel": "dqk_decode_attn (split decode + merge), HIP events on its stream",
+            "algorithmic_bytes_per_launch": int(r["decode_bytes"]),
+            "bytes_per_token_head": round(r["bytes_per_token_head"], 3),
+            "avg_launch_us": round(r["decode_us"], 2),
+            "step_definition": "select + decode + merge, wall clock per step",
+            "algorithmic_bytes_per_step": int(r["step_bytes"]),
+            "achieved_step": round(achieved_step, 1), "frac_step": round(achieved_step / PEAK_HBM_GBS, 4),
+            "select_us": round(r["select_us"], 2), "kernel_source_hash": khash}
+    roof["stream_read_gbs"] = round(stream_read_gbs(torch, pa, int(r["decode_bytes"])), 1)
     roof["frac_of_stream_read"] = round(achieved / roof["stream_read_gbs"], 4)
+    app = append_roofline(w.append_s, w.append_tokens, w.prob.num_pages, shape.hkv)
+    app["workload"] = f"prefill of {shape.seq_lens[0]} tokens x {shape.hkv} KV heads per call, {shape.batch} calls"
 
     if args.calib_copy:
         x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -306,13 +430,77 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int2-kv/fp32-accumulate",
            "data": "synthetic (seeded Gaussian q/k/v, 4 outlier key channels x10, channel-0 offset +3)",
-           "config": {"workload": shape.name, "batch": B, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
-                      "context": max(shape.seq_lens), "n_keep": n_keep, "sparsity": args.sparsity,
-                      "cache_copies": len(caches), "num_splits": args.num_splits or "auto"},
-           "roofline": roof, "append_roofline": append_roofline(app_s, app_tokens, hkv)}
+           "config": {"workload": shape.name, "batch": B, "q_heads": shape.hq, "kv_heads": shape.hkv,
+                      "head_dim": 128, "context": max(shape.seq_lens), "n_keep": n_keep, "sparsity": args.sparsity,
+                      "cache_copies": len(w.caches), "num_splits": args.num_splits or "auto"},
+           "roofline": roof, "append_roofline": app}
+
+    if not args.no_configs and args.config == 3:
+        configs = {}
+        sub = args.sub_steps
+        sweep = {}
+        for nk in (128, 103, 77, 52):
+            rs = w.time_steps(nk, sub, 5)
+            sweep[str(nk)] = _summary(shape.name, w, rs, nk)
+            log(f"[bench] sweep n_keep {nk}: {rs['t_step_us']:.1f} us/step")
+        configs["3_sparsity_sweep"] = sweep
+        del w
+        torch.cuda.empty_cache()
+        s1 = synth.config_shape(1, args.seed)
+        w1 = Int2Workload(s1, args.seed, pa, torch)
+        configs["1"] = _summary(s1.name, w1, w1.time_steps(s1.n_keep, sub, 5), s1.n_keep)
+        log(f"[bench] config 1: {configs['1']['t_step_us']} us/step")
+        del w1
+        s2 = synth.config_shape(2, args.seed)
+        w2 = Int2Workload(s2, args.seed, pa, torch)
+        c2 = {"int2_40": _summary(s2.name, w2, w2.time_steps(77, sub, 5), 77),
+              "int2_0": _summary(s2.name, w2, w2.time_steps(128, sub, 5), 128)}
+        prob2 = w2.prob
+        del w2
+        torch.cuda.empty_cache()
+        kp, vp = build_bf16_pages(prob2, s2, torch)
+        qd = torch.from_numpy(prob2.q.view(np.int16)).to("cuda")
+        ptd = torch.from_numpy(prob2.page_table).to("cuda")
+        sld = torch.from_numpy(prob2.seq_lens).to("cuda")
+        out = torch.empty((s2.batch, s2.hq, 128), dtype=torch.float32, device="cuda")
+        ws = torch.empty(pa.dqk_decode_workspace_size(s2.batch, s2.hq, s2.hkv, ptd.shape[1], 0) // 4 + 4,
+                         dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            pa.dqk_decode_attn_bf16(kp, vp, qd, ptd, sld, prob2.sm_scale, workspace=ws, out=out, want_lse=False)
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        for _ in range(sub):
+            pa.dqk_decode_attn_bf16(kp, vp, qd, ptd, sld, prob2.sm_scale, workspace=ws, out=out, want_lse=False)
+        torch.cuda.synchronize()
+        t_bf = (time.perf_counter() - tb) / sub
+        from page_set_amd import traffic
+        bf_bytes = traffic.bf16_cache_bytes(prob2.seq_lens, s2.hkv)
+        c2["bf16_dense"] = {"workload": s2.name, "t_step_us": round(t_bf * 1e6, 2),
+                            "tokens_per_s": round(s2.batch / t_bf, 1), "algorithmic_bytes_per_step": int(bf_bytes),
+                            "achieved_step_gbs": round(bf_bytes / t_bf / 1e9, 1),
+                            "frac_step": round(bf_bytes / t_bf / 1e9 / PEAK_HBM_GBS, 4),
+                            "kernel": "dqk_decode_attn_bf16 (unpruned BF16, split decode + merge)"}
+        c2["int2_40_vs_bf16_speedup"] = round(t_bf * 1e6 / c2["int2_40"]["t_step_us"], 3)
+        c2["int2_0_vs_bf16_speedup"] = round(t_bf * 1e6 / c2["int2_0"]["t_step_us"], 3)
+        c2["bf16_vs_int2_40_read_ratio"] = round(bf_bytes / c2["int2_40"]["algorithmic_bytes_per_step"], 3)
+        configs["2"] = c2
+        log(f"[bench] config 2: INT2 40% {c2['int2_40']['t_step_us']} us, BF16 {c2['bf16_dense']['t_step_us']} us")
+        del kp, vp
+        torch.cuda.empty_cache()
+        s4 = synth.config_shape(4, args.seed)
+        w4 = Int2Workload(s4, args.seed, pa, torch, one_call=True)
+        c4 = _summary(s4.name, w4, w4.time_steps(s4.n_keep, sub, 5), s4.n_keep)
+        c4["total_tokens"] = int(np.sum(s4.seq_lens))
+        c4["append"] = append_roofline(w4.append_s, w4.append_tokens, w4.prob.num_pages, s4.hkv)
+        c4["append"]["workload"] = f"one call over the ragged batch ({c4['total_tokens']} tokens, shuffled pages)"
+        configs["4"] = c4
+        log(f"[bench] config 4: {c4['t_step_us']} us/step")
+        del w4
+        rec["configs"] = configs
+
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        rec["cpu_baseline"] = cpu_baseline(shape, args.seed, n_keep, args.cpu_reps)
+        rec["cpu_baseline"] = cpu_baseline(shape, args.seed, n_keep)
     print(json.dumps(rec), flush=True)
 
 

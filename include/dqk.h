@@ -90,7 +90,8 @@ typedef struct dqk_cache {
 
 /*
  * Quantize-append: transform keys with T_K and pack keys and values into
- * pages ("each new key is transformed ... and stored", §3.4; layout §3.3).
+ * pages (§3.4: a key enters the cache only after the key transform; layout
+ * §3.3).
  *   c           host pointer to the cache description.
  *   k_bf16      bf16 [total_tokens][Hkv][128] raw keys (post-RoPE).
  *   v_bf16      bf16 [total_tokens][Hkv][128] raw values.

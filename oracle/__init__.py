@@ -25,8 +25,12 @@ decode_attn            textbook softmax attention (numpy, fp64) on the decoded
                        cache with unselected channels zeroed; tiny brute force;
                        n_keep = 128 dense reduction; unquantized transform
                        identity; App. C.2 pruning-variance statistics
-decode_bf16            textbook attention (numpy, fp64)
-bytes (bytes.py)       the bits-per-element figures printed in Table 1
+decode_bf16            attention computed from the raw unpaged bf16 keys and
+                       values (numpy, fp64); 3-token pure-Python brute force;
+                       scale 0 gives the value mean; page permutation and
+                       tail-garbage invariance (tests/test_oracle_bf16.py)
+paged_bf16             token t of sequence b lands at [page_table[b][t//128]][g]
+                       [t%128], checked element by element
 =====================  ==========================================================
 
 Parity unpinned: the accuracy tables of the paper (need models and datasets).

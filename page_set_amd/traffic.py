@@ -5,11 +5,11 @@ against the figures the paper prints) and by the benchmark (to turn a
 measured time into algorithmic bytes per second).
 
 Closed form of the effective bits per KV element that "Dual-QK: Sharp Queries
-and Flat Keys for Prunable 2-bit KV Caches" reports in Table 1 and Table 9
-(§4.1 "Capacity BPE describes the stored cache, while bandwidth BPE estimates
-the KV data read per decoding step with channel selection.  Both account for
-quantization metadata and high-precision entries, including the protected sink
-and recent tokens"):
+and Flat Keys for Prunable 2-bit KV Caches" reports in Table 1 and Table 9.
+Per §4.1 the paper gives two figures: a capacity figure for what the cache
+stores, and a bandwidth figure for what one decode step reads once channels
+are pruned; both include the quantization metadata and the BF16-kept tokens
+(the sink and the recent window):
 
     bits/element = [(N - n_prot) * b_tok + n_prot * b_prot] / (N * 2 d)
 

@@ -13,8 +13,8 @@ benchmark suites that are not available here; seeded Gaussians stand in:
 * q, k, v ~ N(0, 1), rounded to bf16 (round to nearest even).
 * k gets 4 outlier channels per KV head (drawn from 1..127 without
   replacement) scaled by 10, and channel 0 offset by +3, before rounding.
-* One transform pair per KV head (§3.1: "each layer and KV head uses a fixed
-  transform pair"): T_K = bf16(R diag(u)) with R Haar-orthogonal (QR of a
+* One transform pair per KV head (§3.1 fixes one pair per layer and KV
+  head): T_K = bf16(R diag(u)) with R Haar-orthogonal (QR of a
   Gaussian, sign-fixed) and u ~ U[0.5, 2]; T_Q = (T_K as stored)^{-T}, computed
   in fp64 and rounded to fp32, so that (q T_Q)(k T_K)^T = q k^T (§3.1, Eq. 1).
 * 128-token pages.  Identity page table unless ``shuffle_pages``.

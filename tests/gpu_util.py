@@ -53,3 +53,34 @@ def row_rel_err(got, want):
     num = np.abs(got - want).max(axis=-1)
     den = np.abs(want).max(axis=-1)
     return num / np.maximum(den, 1e-30)
+
+
+def lse_bound(cache, qp, sel, page_table, seq_lens, sm_scale, lse_ref):
+    """Allowed |lse_gpu - lse_oracle| per (b, h) row.
+
+    The kernels form each logit as an fp32 sum over the selected channels of
+    products whose query-side operand carries at least 21 significant bits
+    (q' * scale split into two binary16 limbs), so every logit is off by at
+    most about n * 2^-24 + 2^-21 <= 2^-16 times the sum of the absolute
+    values of its terms (n <= 128).  The log-sum-exp is a softmax-weighted
+    mean of the logits, so its error is bounded by the largest logit error,
+    plus the fp32 rounding of exp2/log2 and of the merge (2^-20 |lse|)."""
+    from tests import cachefmt as cf
+    B, hq = qp.shape[0], qp.shape[1]
+    hkv = sel.shape[1]
+    grp = hq // hkv
+    out = np.zeros((B, hq))
+    for b in range(B):
+        L = int(seq_lens[b])
+        for g in range(hkv):
+            kh, _ = cf.gather_seq(cache, page_table, b, L, g)
+            mask = np.zeros(128)
+            mask[sel[b, g]] = 1.0
+            qa = np.abs(qp[b, g * grp:(g + 1) * grp].astype(np.float64)) * mask
+            out[b, g * grp:(g + 1) * grp] = (np.abs(kh.astype(np.float64)) @ qa.T).max(0) * sm_scale
+    return 2.0 ** -16 * out + 2.0 ** -20 * np.abs(lse_ref)
+
+
+def assert_lse(lse, lse_ref, bound):
+    err = np.abs(np.asarray(lse, np.float64) - lse_ref)
+    assert (err <= bound).all(), f"lse error {err.max():.3e} above the derived bound (worst ratio {(err / bound).max():.2f})"

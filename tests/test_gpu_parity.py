@@ -120,8 +120,8 @@ def test_decode_parity(name, shape):
     rel = gu.row_rel_err(out, ref)
     _say(f"  max row rel err {rel.max():.3e}")
     assert (rel <= gu.TOL).all(), rel.max()
-    # logits carry q' * scale as an fp16 hi/lo pair (~2^-22 relative)
-    np.testing.assert_allclose(lse, ref_lse, rtol=2e-5, atol=2e-5)
+    gu.assert_lse(lse, ref_lse, gu.lse_bound(cache, qp, sel, prob.page_table, prob.seq_lens, prob.sm_scale,
+                                             ref_lse))
 
 
 def test_decode_config1_full():
