@@ -33,7 +33,7 @@ import synth  # noqa: E402
 
 METRIC = "decode-attn tokens/s @128K, INT2 KV, 40% q-prune; achieved HBM GB/s %"
 PEAK_HBM_GBS = 8000.0
-DECODE_SOURCES = ["page_set_amd/csrc/dqk_decode_mfma.hip", "page_set_amd/csrc/dqk_decode.hip",
+DECODE_SOURCES = ["page_set_amd/csrc/dqk_decode_blk.hip", "page_set_amd/csrc/dqk_decode.hip",
                   "page_set_amd/csrc/dqk_internal.h"]
 
 
@@ -88,7 +88,7 @@ def write_traffic(fetch_csv, write_csv, out_json):
            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "kernels": {}}
     total = 0.0
     for k in fetch:
-        if "decode_g4_kernel" in k or "merge_kernel" in k:
+        if "decode_blk_kernel" in k or "merge_kernel" in k:
             b = fetch[k] * 1024 * ff + write.get(k, 0.0) * 1024 * fw
             rec["kernels"][k[:60]] = {"fetch_kib": fetch[k], "write_kib": write.get(k, 0.0), "hbm_bytes": b}
             total += b

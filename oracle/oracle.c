@@ -16,12 +16,16 @@
  * T[i][j] with i the input and j the output channel.  d = 128, pages of 128
  * tokens.  Query head h uses KV head h / (Hq/Hkv).
  *
- * Cache format (all little-endian, per physical page p and KV head g):
- *   k_codes u8   [P][Hkv][128 ch][32]  channel-major rows (§3.3: one channel
- *                                       per contiguous 32-byte row); token t at
+ * Cache format (all little-endian).  Physical pages come in aligned blocks
+ * of four (page p is slot p & 3 of block p >> 2); per block B, KV head g:
+ *   k_codes u8   [P/4][Hkv][128 ch][4 slot][32]  channel-major rows (§3.3: one
+ *                                       channel of one page per contiguous
+ *                                       32-byte row); the four pages' rows of
+ *                                       a channel are adjacent.  Token t at
  *                                       byte t>>2, bits 2*(t&3).  Row 0 zero.
- *   k_meta  f16  [P][Hkv][128 ch][2]   (scale, zero) per channel and page;
- *                                       entry 0 zero.
+ *   k_meta  f16  [P/4][Hkv][128 ch][4 slot][2]  (scale, zero) per channel and
+ *                                       page; channel 0 entries zero.
+ * and per physical page p:
  *   k_ch0   bf16 [P][Hkv][128 tok]     channel 0 of k' kept in bf16 (§3.3).
  *   v_codes u8   [P][Hkv][128 tok][32] token-major (§3.3); channel c at byte
  *                                       c>>2, bits 2*(c&3).
@@ -38,6 +42,13 @@
 #define HD 128
 #define PG 128
 #define VGROUP 32
+
+/* Index of the 32-byte key row (and of the 2-entry key metadata) of channel j
+ * of physical page p, KV head g: block p >> 2, slot p & 3. */
+static size_t krow(int64_t p, int g, int hkv, int j)
+{
+    return ((((size_t)(p >> 2) * (size_t)hkv + (size_t)g) * HD + (size_t)j) * 4) + (size_t)(p & 3);
+}
 
 /* ------------------------------------------------------------------------ */
 /* Number formats, from their IEEE 754 definitions (binary16; bfloat16 is the
@@ -251,13 +262,14 @@ void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs,
             int64_t base_tok = t0 + pi * PG;
             for (int g = 0; g < hkv; ++g) {
                 size_t pg = (size_t)p * hkv + g;
-                uint8_t *kc = k_codes + pg * HD * 32;
-                uint16_t *km = k_meta + pg * HD * 2;
                 uint16_t *k0 = k_ch0 + pg * PG;
                 uint8_t *vc = v_codes + pg * PG * 32;
                 uint16_t *vm = v_meta + pg * 2 * 4 * PG;
-                memset(kc, 0, HD * 32);
-                memset(km, 0, HD * 2 * sizeof(uint16_t));
+                for (int j = 0; j < HD; ++j) {
+                    memset(k_codes + krow(p, g, hkv, j) * 32, 0, 32);
+                    k_meta[krow(p, g, hkv, j) * 2 + 0] = 0;
+                    k_meta[krow(p, g, hkv, j) * 2 + 1] = 0;
+                }
                 memset(k0, 0, PG * sizeof(uint16_t));
                 memset(vc, 0, PG * 32);
                 memset(vm, 0, 2 * 4 * PG * sizeof(uint16_t));
@@ -265,12 +277,14 @@ void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs,
                 for (int s = 0; s < nvalid; ++s)
                     k0[s] = orc_bf16_round_nearest(kp[(size_t)s * hkv * HD + 0]);
                 for (int j = 1; j < HD; ++j) {
+                    uint8_t *kc = k_codes + krow(p, g, hkv, j) * 32;
+                    uint16_t *km = k_meta + krow(p, g, hkv, j) * 2;
                     grid_t gr = make_grid(kp + j, nvalid, hkv * HD);
-                    km[j * 2 + 0] = gr.s_bits;
-                    km[j * 2 + 1] = gr.z_bits;
+                    km[0] = gr.s_bits;
+                    km[1] = gr.z_bits;
                     for (int s = 0; s < nvalid; ++s) {
                         int c = code_of(kp[(size_t)s * hkv * HD + j], &gr);
-                        kc[j * 32 + (s >> 2)] |= (uint8_t)(c << (2 * (s & 3)));
+                        kc[s >> 2] |= (uint8_t)(c << (2 * (s & 3)));
                     }
                 }
                 for (int s = 0; s < nvalid; ++s) {
@@ -379,8 +393,9 @@ int orc_decode_attn(const uint8_t *k_codes, const uint16_t *k_meta, const uint16
                     if (j == 0) {
                         kv = orc_bf16_value(k_ch0[pg * PG + s]);
                     } else {
-                        int c = (k_codes[(pg * HD + j) * 32 + (s >> 2)] >> (2 * (s & 3))) & 3;
-                        kv = orc_dequant(c, k_meta[(pg * HD + j) * 2], k_meta[(pg * HD + j) * 2 + 1]);
+                        size_t r = krow(p, g, hkv, j);
+                        int c = (k_codes[r * 32 + (s >> 2)] >> (2 * (s & 3))) & 3;
+                        kv = orc_dequant(c, k_meta[r * 2], k_meta[r * 2 + 1]);
                     }
                     acc += (double)qp[j] * (double)kv;
                 }

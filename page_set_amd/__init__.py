@@ -87,14 +87,15 @@ def _check(rc: int, where: str):
 
 
 class Cache:
-    """Device buffers of the paged INT2 cache (layout in include/dqk.h)."""
+    """Device buffers of the paged INT2 cache (layout in include/dqk.h).  The
+    page pool is a whole number of aligned 4-page blocks (rounded up here)."""
 
     def __init__(self, num_pages: int, num_kv_heads: int, device="cuda"):
         import torch
-        self.num_pages, self.num_kv_heads = int(num_pages), int(num_kv_heads)
+        self.num_pages, self.num_kv_heads = -(-int(num_pages) // 4) * 4, int(num_kv_heads)
         P, H = self.num_pages, self.num_kv_heads
-        self.k_codes = torch.zeros((P, H, HEAD_DIM, 32), dtype=torch.uint8, device=device)
-        self.k_meta = torch.zeros((P, H, HEAD_DIM, 2), dtype=torch.int16, device=device)
+        self.k_codes = torch.zeros((P // 4, H, HEAD_DIM, 4, 32), dtype=torch.uint8, device=device)
+        self.k_meta = torch.zeros((P // 4, H, HEAD_DIM, 4, 2), dtype=torch.int16, device=device)
         self.k_ch0 = torch.zeros((P, H, PAGE), dtype=torch.int16, device=device)
         self.v_codes = torch.zeros((P, H, PAGE, 32), dtype=torch.uint8, device=device)
         self.v_meta = torch.zeros((P, H, 2, 4, PAGE), dtype=torch.int16, device=device)
@@ -107,6 +108,14 @@ class Cache:
 
     def nbytes(self) -> int:
         return sum(a.numel() * a.element_size() for a in self.arrays())
+
+    def page_major(self):
+        """Copies of the five buffers indexed by physical page first (key rows
+        [P][Hkv][128][32], key metadata [P][Hkv][128][2]); for tests."""
+        P, H = self.num_pages, self.num_kv_heads
+        kc = self.k_codes.permute(0, 3, 1, 2, 4).reshape(P, H, HEAD_DIM, 32)
+        km = self.k_meta.permute(0, 3, 1, 2, 4).reshape(P, H, HEAD_DIM, 2)
+        return kc, km, self.k_ch0, self.v_codes, self.v_meta
 
 
 def dqk_quantize_append(cache: Cache, k, v, t_k, cu_tokens, page_table, kprime_dbg=None, stream=None):

@@ -21,7 +21,7 @@ int hip_status(hipError_t e) {
 
 int check_cache(const dqk_cache *c) {
     if (!c || !c->k_codes || !c->k_meta || !c->k_ch0 || !c->v_codes || !c->v_meta) return DQK_ERR_NULL;
-    if (c->num_kv_heads < 1 || c->num_pages < 1) return DQK_ERR_SHAPE;
+    if (c->num_kv_heads < 1 || c->num_pages < 1 || c->num_pages % dqk::KBLK != 0) return DQK_ERR_SHAPE;
     if (c->num_kv_heads > 65535) return DQK_ERR_UNSUPPORTED;
     if (!aligned16(c->k_codes) || !aligned16(c->k_meta) || !aligned16(c->k_ch0) || !aligned16(c->v_codes) ||
         !aligned16(c->v_meta))

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void append_kernel(dqk_cache c, const uint16_t
                     if (tok < nvalid) kprime_dbg[((size_t)(t0 + tok) * hkv + g) * D + ch] = acc[mt][nt][r];
                 }
         }
-        uint8_t *row = c.k_codes + (pg * D + ch) * ROW_BYTES + 8 * G;
+        uint8_t *row = c.k_codes + krow(p, g, hkv, ch) * ROW_BYTES + 8 * G;
         if (ch == 0) {
             uint16_t *k0 = c.k_ch0 + pg * PG + 32 * G;
 #pragma unroll
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void append_kernel(dqk_cache c, const uint16_t
                     k0[4 * mt + r] = tok < nvalid ? f2bf_rne(acc[mt][nt][r]) : (uint16_t)0;
                 }
             *reinterpret_cast<uint64_t *>(row) = 0;
-            if (G == 0) *reinterpret_cast<uint32_t *>(c.k_meta + (pg * D + ch) * 2) = 0u;
+            if (G == 0) *reinterpret_cast<uint32_t *>(c.k_meta + krow(p, g, hkv, ch) * 2) = 0u;
             continue;
         }
         float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void append_kernel(dqk_cache c, const uint16_t
             }
         *reinterpret_cast<uint64_t *>(row) = bits;
         if (G == 0)
-            *reinterpret_cast<uint32_t *>(c.k_meta + (pg * D + ch) * 2) = (uint32_t)gr.sb | ((uint32_t)gr.zb << 16);
+            *reinterpret_cast<uint32_t *>(c.k_meta + krow(p, g, hkv, ch) * 2) = (uint32_t)gr.sb | ((uint32_t)gr.zb << 16);
     }
 }
 

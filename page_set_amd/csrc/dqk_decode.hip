@@ -125,9 +125,9 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(dqk_cache c, const flo
             const int jj = r >> 1, hf = r & 1;
             const int j = jrow[jj];
             *reinterpret_cast<uint4 *>(&krows[jj][hf * 16]) =
-                *reinterpret_cast<const uint4 *>(c.k_codes + (pg * D + j) * ROW_BYTES + hf * 16);
+                *reinterpret_cast<const uint4 *>(c.k_codes + krow(p, g, hkv, j) * ROW_BYTES + hf * 16);
             if (hf == 0) {
-                const uint32_t sz = *reinterpret_cast<const uint32_t *>(c.k_meta + (pg * D + j) * 2);
+                const uint32_t sz = *reinterpret_cast<const uint32_t *>(c.k_meta + krow(p, g, hkv, j) * 2);
                 ks_lds[jj] = h2f((uint16_t)(sz & 0xFFFFu));
                 kz_lds[jj] = h2f((uint16_t)(sz >> 16));
             }
@@ -203,6 +203,7 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(dqk_cache c, const flo
             if (t == 0) {
                 dst[D] = m_lds[h];
                 dst[D + 1] = l_lds[h];
+                dst[D + 2] = l_lds[h];  // fp32 probabilities: the same sum
             }
         }
     }
@@ -296,6 +297,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const uint16_t *__rest
             if (t == 0) {
                 dst[D] = m_lds[h];
                 dst[D + 1] = l_lds[h];
+                dst[D + 2] = l_lds[h];  // fp32 probabilities: the same sum
             }
         }
     }
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part
                                                   float *__restrict__ out, float *__restrict__ lse) {
     // one block of 128 lanes per (sequence, query head); lane c owns output channel c
     __shared__ float w_lds[D];
-    __shared__ float red[2][D / 64];
+    __shared__ float red[3][D / 64];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const float *P = partials + (size_t)bh * nsplit * PART_FLOATS;
     // every load that does not depend on the maximum is issued up front
@@ -318,10 +320,11 @@ __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part
 #pragma unroll
         for (int s = 0; s < MERGE_FAST; ++s) xf[s] = s < nsplit ? P[(size_t)s * PART_FLOATS + tid] : 0.0f;
     }
-    float M = -__builtin_huge_valf(), m_own = -__builtin_huge_valf(), l_own = 0.0f;
+    float M = -__builtin_huge_valf(), m_own = -__builtin_huge_valf(), l_own = 0.0f, l32_own = 0.0f;
     if (tid < nsplit) {
         m_own = P[(size_t)tid * PART_FLOATS + D];
         l_own = P[(size_t)tid * PART_FLOATS + D + 1];
+        l32_own = P[(size_t)tid * PART_FLOATS + D + 2];
     }
     M = m_own;
     for (int s = tid + D; s < nsplit; s += D) M = fmaxf(M, P[(size_t)s * PART_FLOATS + D]);
@@ -330,19 +333,21 @@ __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part
     if (lane == 0) red[0][wv] = M;
     __syncthreads();
     M = fmaxf(red[0][0], red[0][1]);
-    float lpart = 0.0f, acc = 0.0f;
+    float lpart = 0.0f, l32part = 0.0f, acc = 0.0f;
     for (int s0 = 0; s0 < nsplit; s0 += D) {
         const int n = min(D, nsplit - s0);
         if (s0 > 0) __syncthreads();  // previous chunk's weights are consumed
         if (tid < n) {
-            float m = m_own, l = l_own;
+            float m = m_own, l = l_own, l32 = l32_own;
             if (s0 > 0) {
                 m = P[(size_t)(s0 + tid) * PART_FLOATS + D];
                 l = P[(size_t)(s0 + tid) * PART_FLOATS + D + 1];
+                l32 = P[(size_t)(s0 + tid) * PART_FLOATS + D + 2];
             }
             const float w = l > 0.0f ? __expf(m - M) : 0.0f;
             w_lds[tid] = w;
             lpart = __builtin_fmaf(l, w, lpart);
+            l32part = __builtin_fmaf(l32, w, l32part);
         }
         __syncthreads();
         if (nsplit <= MERGE_FAST) {
@@ -363,12 +368,18 @@ __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part
         }
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lpart += __shfl_xor(lpart, o);
-    if (lane == 0) red[1][wv] = lpart;
+    for (int o = 32; o >= 1; o >>= 1) {
+        lpart += __shfl_xor(lpart, o);
+        l32part += __shfl_xor(l32part, o);
+    }
+    if (lane == 0) {
+        red[1][wv] = lpart;
+        red[2][wv] = l32part;
+    }
     __syncthreads();
     const float Lsum = red[1][0] + red[1][1];
     out[(size_t)bh * D + tid] = acc / Lsum;
-    if (lse && tid == 0) lse[bh] = M + __logf(Lsum);
+    if (lse && tid == 0) lse[bh] = M + __logf(red[2][0] + red[2][1]);
 }
 
 // Plain streaming read (measurement reference): block i reads chunk i of

@@ -13,8 +13,20 @@ constexpr int PG = DQK_PAGE;
 constexpr int ROW_BYTES = 32;     // 128 two-bit codes
 constexpr int VGROUPS = 4;        // value groups of 32 channels
 
-// Partial of one (b, h, split): o[128] (unnormalised, relative to m), m, l.
-constexpr int PART_FLOATS = D + 2;
+// Physical pages come in aligned blocks of four: key rows and key metadata of
+// a channel sit side by side for the block's four pages.
+constexpr int KBLK = 4;
+
+// Index of the 32-byte key row (and of the (scale, zero) pair) of channel j of
+// physical page p, KV head g.
+__host__ __device__ __forceinline__ size_t krow(int64_t p, int g, int hkv, int j) {
+    return ((((size_t)(p >> 2) * (size_t)hkv + (size_t)g) * D + (size_t)j) * KBLK) + (size_t)(p & 3);
+}
+
+// Partial of one (b, h, split): o[128] (unnormalised, relative to m), m (natural
+// log units), l (the denominator matching o), l32 (fp32 sum of the unrounded
+// probabilities, for the log-sum-exp), pad.
+constexpr int PART_FLOATS = D + 4;
 
 // ---------------------------------------------------------------- formats
 // binary16 bits -> fp32 (exact).

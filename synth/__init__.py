@@ -17,7 +17,8 @@ benchmark suites that are not available here; seeded Gaussians stand in:
   head): T_K = bf16(R diag(u)) with R Haar-orthogonal (QR of a
   Gaussian, sign-fixed) and u ~ U[0.5, 2]; T_Q = (T_K as stored)^{-T}, computed
   in fp64 and rounded to fp32, so that (q T_Q)(k T_K)^T = q k^T (§3.1, Eq. 1).
-* 128-token pages.  Identity page table unless ``shuffle_pages``.
+* 128-token pages handed out in aligned blocks of four; identity page table
+  unless ``shuffle_pages`` (a seeded permutation of the blocks).
 
 bf16 values are carried as ``numpy.uint16`` bit patterns.
 """
@@ -158,18 +159,26 @@ def make_kv_seq(shape: Shape, seed: int, b: int, outl: Optional[np.ndarray] = No
 
 
 def make_page_table(shape: Shape, seed: int):
-    """int32 [batch][max_pages] page table (unused slots = -1) and pool size."""
+    """int32 [batch][max_pages] page table (unused slots = -1) and pool size.
+
+    The pool is handed out in aligned blocks of four pages (the cache keeps
+    the key rows of a block's four pages side by side): sequence b gets
+    ceil(pages_b / 4) blocks and its logical page i sits in slot i % 4 of its
+    block i // 4.  ``shuffle_pages`` permutes the blocks of the pool."""
     pps = shape.pages_per_seq
-    total = int(sum(pps))
-    phys = np.arange(total, dtype=np.int32)
+    nblk = [(n + 3) // 4 for n in pps]
+    total_blocks = int(sum(nblk))
+    blocks = np.arange(total_blocks, dtype=np.int32)
     if shape.shuffle_pages:
-        phys = _rng(seed, _ID_PERM).permutation(total).astype(np.int32)
+        blocks = _rng(seed, _ID_PERM).permutation(total_blocks).astype(np.int32)
     pt = np.full((shape.batch, shape.max_pages), -1, dtype=np.int32)
     off = 0
     for b, n in enumerate(pps):
-        pt[b, :n] = phys[off:off + n]
-        off += n
-    return pt, total
+        mine = blocks[off:off + nblk[b]]
+        i = np.arange(n)
+        pt[b, :n] = 4 * mine[i // 4] + i % 4
+        off += nblk[b]
+    return pt, 4 * total_blocks
 
 
 @dataclasses.dataclass

@@ -77,18 +77,19 @@ def test_decode_validation():
     assert _dec(nk=0) == pa.DQK_ERR_SHAPE
     assert _dec(ns=17) == pa.DQK_ERR_SHAPE
     assert _dec(c=_cache(num_kv_heads=0)) == pa.DQK_ERR_SHAPE
+    assert _dec(c=_cache(num_pages=62)) == pa.DQK_ERR_SHAPE        # the pool is whole 4-page blocks
     assert _dec(hq=8 * 32) == pa.DQK_ERR_UNSUPPORTED          # group of 32 query heads
     assert _dec(c=_cache(v_meta=4096 + 2)) == pa.DQK_ERR_ALIGN
     assert _dec(lse=MIS) == pa.DQK_ERR_ALIGN
     need = pa.dqk_decode_workspace_size(4, 32, 8, 16, 4)
-    assert need == 4 * 32 * 4 * 130 * 4
+    assert need == 4 * 32 * 4 * 132 * 4
     assert _dec(ns=4, wsb=need - 4) == pa.DQK_ERR_WORKSPACE
 
 
 def test_workspace_size():
     assert pa.dqk_decode_workspace_size(0, 32, 8, 16, 0) == 0
-    assert pa.dqk_decode_workspace_size(2, 8, 8, 16, 3) == 2 * 8 * 3 * 130 * 4
-    assert pa.dqk_decode_workspace_size(4, 32, 8, 1024, 0) >= 4 * 32 * 130 * 4
+    assert pa.dqk_decode_workspace_size(2, 8, 8, 16, 3) == 2 * 8 * 3 * 132 * 4
+    assert pa.dqk_decode_workspace_size(4, 32, 8, 1024, 0) >= 4 * 32 * 132 * 4
 
 
 def test_append_validation():

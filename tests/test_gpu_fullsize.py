@@ -43,12 +43,16 @@ def _build_cache(shape, prob, d, kprime_seq0=None):
     return cache
 
 
-def _unit_cache(cache, pages, g):
-    """The pages of one sequence for KV head g, as a one-head oracle cache."""
+def _unit_cache(pm, pages, g):
+    """The pages of one sequence for KV head g, as a one-head oracle cache
+    (pm: the GPU cache's page-major copies)."""
     idx = torch.from_numpy(np.ascontiguousarray(pages, dtype=np.int64)).to("cuda")
     sub = oracle.Cache(len(pages), 1)
-    for src, dst in zip(cache.arrays(), sub.arrays()):
-        dst[:, 0] = gu.host(src.index_select(0, idx)[:, g].contiguous(), dst.dtype)
+    dst = [np.zeros((sub.num_pages, 1) + tuple(a.shape[2:]), dtype=b)
+           for a, b in zip(pm, (np.uint8, np.uint16, np.uint16, np.uint8, np.uint16))]
+    for src, d in zip(pm, dst):
+        d[:len(pages), 0] = gu.host(src.index_select(0, idx)[:, g].contiguous(), d.dtype)
+    sub.set_page_major(*dst)
     return sub
 
 
@@ -56,8 +60,9 @@ def _meta_lse_bound(sub, qp, sel, sm_scale, lse_ref):
     """The derived lse bound of gpu_util.lse_bound with max_t |k_tj| replaced by
     its per-channel upper bound from the page metadata (max over pages of
     |zero| and |zero + 3 scale|, channel 0 from its bf16 values)."""
-    s = sub.k_meta[:, 0, :, 0].view(np.float16).astype(np.float64)
-    z = sub.k_meta[:, 0, :, 1].view(np.float16).astype(np.float64)
+    km = sub.page_major()[1]
+    s = km[:, 0, :, 0].view(np.float16).astype(np.float64)
+    z = km[:, 0, :, 1].view(np.float16).astype(np.float64)
     kmax = np.maximum(np.abs(z), np.abs(z + 3 * s)).max(0)
     kmax[0] = np.abs(synth.bf16_bits_to_f32(sub.k_ch0[:, 0]).astype(np.float64)).max()
     mask = np.zeros(128)
@@ -99,10 +104,11 @@ def test_full_size_every_unit(cfg):
         return float(rel.max()), bool((err <= bound).all()), float((err / bound).max())
 
     worst, lse_ok, futs = 0.0, True, []
+    pm = cache.page_major()
     with cf.ThreadPoolExecutor(max_workers=THREADS) as ex:
         for b, g in units:
             L = int(prob.seq_lens[b])
-            sub = _unit_cache(cache, prob.page_table[b, :(L + 127) // 128], g)
+            sub = _unit_cache(pm, prob.page_table[b, :(L + 127) // 128], g)
             futs.append(ex.submit(check, (b, g), sub))
         for (b, g), f in zip(units, futs):
             rel, ok, ratio = f.result()
@@ -127,6 +133,7 @@ def test_append_stagewise_at_prefill_size():
     cache = _build_cache(shape, prob, d, kprime_seq0=kdbg)
     kb, vb = synth.make_kv_seq(shape, prob.seed, 0, prob.outliers)
     pages = np.random.default_rng(11).choice(L // 128, size=24, replace=False)
+    pm = cache.page_major()
     gam = 128 * 2.0 ** -24 / (1 - 128 * 2.0 ** -24)
     t64 = np.abs(synth.bf16_bits_to_f32(prob.t_k).astype(np.float64))
     for pi in pages:
@@ -140,9 +147,10 @@ def test_append_stagewise_at_prefill_size():
         err = np.abs(kp_gpu.astype(np.float64) - kp_ref.astype(np.float64))
         assert (err <= gam * absdot + np.spacing(np.abs(kp_ref))).all(), pi
         want = oracle.pack_cache(kp_gpu, vseg, np.array([0, 128], np.int32), np.zeros((1, 1), np.int32), 1)
+        want_pm = want.page_major()
         for g in range(shape.hkv):
-            got = _unit_cache(cache, [p], g)
-            for nm, a, w in zip(["k_codes", "k_meta", "k_ch0", "v_codes", "v_meta"], got.arrays(), want.arrays()):
+            got = _unit_cache(pm, [p], g).page_major()
+            for nm, a, w in zip(["k_codes", "k_meta", "k_ch0", "v_codes", "v_meta"], got, want_pm):
                 np.testing.assert_array_equal(a[0, 0], w[0, g], err_msg=f"{nm} page {pi} head {g}")
     _say(f"  {len(pages)} sampled pages x {shape.hkv} heads: stagewise parity holds")
 

@@ -152,8 +152,12 @@ def test_decode_split_invariance_and_permutation(hq, hkv, tol):
     def permute(cache, prob):
         perm = np.random.default_rng(4).permutation(prob.num_pages)
         c2 = oracle.Cache(prob.num_pages, cache.hkv)
-        for a, b in zip(cache.arrays(), c2.arrays()):
+        moved = []
+        for a in cache.page_major():
+            b = np.empty_like(a)
             b[perm] = a
+            moved.append(b)
+        c2.set_page_major(*moved)
         prob.page_table = np.where(prob.page_table >= 0, perm[np.maximum(prob.page_table, 0)], -1).astype(np.int32)
         return c2
 
@@ -175,8 +179,8 @@ def test_decode_ignores_garbage_past_sequence_end():
                 cache.v_codes[p, :, s:] = rng.integers(0, 256, cache.v_codes[p, :, s:].shape, dtype=np.uint8)
                 cache.v_meta[p, :, :, :, s:] = rng.integers(0, 0x3C00, cache.v_meta[p, :, :, :, s:].shape).astype(np.uint16)
                 cache.k_ch0[p, :, s:] = rng.integers(0, 0x4000, cache.k_ch0[p, :, s:].shape).astype(np.uint16)
-                cache.k_codes[p, :, :, (s + 3) // 4:] = rng.integers(0, 256, cache.k_codes[p, :, :, (s + 3) // 4:].shape,
-                                                                     dtype=np.uint8)
+                cache.k_rows(p)[:, :, (s + 3) // 4:] = rng.integers(0, 256, cache.k_rows(p)[:, :, (s + 3) // 4:].shape,
+                                                                    dtype=np.uint8)
         return cache
 
     _, _, _, _, ref, _, out, _ = _decode_case(shape, 5)

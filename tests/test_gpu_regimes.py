@@ -211,5 +211,5 @@ def test_constant_groups(hq, hkv):
 
     cache, *_ = _check(prob, label="const", kprime_fn=const_page)
     p = int(prob.page_table[0, 1])
-    assert (cache.k_meta[p, :, 1:, 0] == 0).all()          # every key channel of the page has scale 0
+    assert (cache.k_meta_page(p)[:, 1:, 0] == 0).all()          # every key channel of the page has scale 0
     assert (cache.v_meta[int(prob.page_table[0, 0]), :, 0, 0, 0] == 0).all()

@@ -65,8 +65,9 @@ def test_decode_tiny_brute_force(orc, L, hq, n_keep):
                 if j == 0:
                     kv = float(cf.bf16(cache.k_ch0[p, 0, s]))
                 else:
-                    code = (int(cache.k_codes[p, 0, j, s // 4]) >> (2 * (s % 4))) & 3
-                    kv = float(np.float32(code) * cf.f16(cache.k_meta[p, 0, j, 0]) + cf.f16(cache.k_meta[p, 0, j, 1]))
+                    code = (int(cache.k_rows(p)[0, j, s // 4]) >> (2 * (s % 4))) & 3
+                    km = cache.k_meta_page(p)[0, j]
+                    kv = float(np.float32(code) * cf.f16(km[0]) + cf.f16(km[1]))
                 acc += float(qp[0, h, j]) * kv
             logits.append(acc / math.sqrt(128))
         m = max(logits)
@@ -93,8 +94,12 @@ def test_decode_invariant_to_page_permutation_and_slot_garbage(orc):
     out1, lse1 = orc.decode_attn(cache, qp, sel, prob.page_table, prob.seq_lens, prob.sm_scale)
     perm = np.random.default_rng(1).permutation(prob.num_pages)
     c2 = orc.Cache(prob.num_pages, shape.hkv)
-    for a_src, a_dst in zip(cache.arrays(), c2.arrays()):
+    moved = []
+    for a_src in cache.page_major():
+        a_dst = np.empty_like(a_src)
         a_dst[perm] = a_src
+        moved.append(a_dst)
+    c2.set_page_major(*moved)
     pt2 = np.where(prob.page_table >= 0, perm[np.maximum(prob.page_table, 0)], -1).astype(np.int32)
     # garbage in every slot past each sequence's end
     rng = np.random.default_rng(2)
@@ -105,8 +110,8 @@ def test_decode_invariant_to_page_permutation_and_slot_garbage(orc):
         if s:
             c2.v_codes[p, :, s:] = rng.integers(0, 256, c2.v_codes[p, :, s:].shape, dtype=np.uint8)
             c2.k_ch0[p, :, s:] = rng.integers(0, 0x3F00, c2.k_ch0[p, :, s:].shape).astype(np.uint16)
-            rows = c2.k_codes[p, :, :, s // 4 + 1:]
-            c2.k_codes[p, :, :, s // 4 + 1:] = rng.integers(0, 256, rows.shape, dtype=np.uint8)
+            rows = c2.k_rows(p)[:, :, s // 4 + 1:]
+            c2.k_rows(p)[:, :, s // 4 + 1:] = rng.integers(0, 256, rows.shape, dtype=np.uint8)
     out2, lse2 = orc.decode_attn(c2, qp, sel, pt2, prob.seq_lens, prob.sm_scale)
     np.testing.assert_array_equal(out1, out2)
     np.testing.assert_array_equal(lse1, lse2)

@@ -33,11 +33,13 @@ def test_golden_page_bytes(orc):
     assert not cache.k_ch0[0, 0, n:].any()
     for ch, row in e["k_rows"].items():
         j = int(ch)
-        assert list(cache.k_codes[0, 0, j, :2]) == row["bytes01"], ch
-        assert not cache.k_codes[0, 0, j, 2:].any()
-        assert cache.k_meta[0, 0, j, 0] == row["scale_bits"], ch
-        assert cache.k_meta[0, 0, j, 1] == row["zero_bits"], ch
-    assert not cache.k_codes[0, 0, 0].any() and not cache.k_meta[0, 0, 0].any()
+        assert list(cache.k_rows(0)[0, j, :2]) == row["bytes01"], ch
+        assert not cache.k_rows(0)[0, j, 2:].any()
+        assert cache.k_meta_page(0)[0, j, 0] == row["scale_bits"], ch
+        assert cache.k_meta_page(0)[0, j, 1] == row["zero_bits"], ch
+    assert not cache.k_rows(0)[0, 0].any() and not cache.k_meta_page(0)[0, 0].any()
+    # the other three slots of the page's block are untouched
+    assert not cache.k_codes[0, 0, :, 1:].any() and not cache.k_meta[0, 0, :, 1:].any()
     for t in range(n):
         assert list(cache.v_codes[0, 0, t]) == e["v_token_bytes"]
         assert list(cache.v_meta[0, 0, 0, :, t]) == e["v_scale_bits"]
@@ -162,7 +164,7 @@ def test_pack_layout_reads_back(orc):
             for pi in range((L + 127) // 128):
                 p = int(prob.page_table[b, pi])
                 sl = slice(pi * 128, min(L, pi * 128 + 128))
-                s = cf.f16(cache.k_meta[p, g, 1:, 0])
+                s = cf.f16(cache.k_meta_page(p)[g, 1:, 0])
                 err = np.abs(kh[sl, 1:] - kref[sl, 1:])
                 assert (err <= s / 2 + 4 * ulp32(np.abs(kref[sl, 1:]) + 3 * s)).all()
                 nval = sl.stop - sl.start
@@ -182,5 +184,5 @@ def test_pack_is_page_permutation_equivariant(orc):
     perm = np.random.default_rng(0).permutation(prob.num_pages).astype(np.int32)
     pt2 = np.where(prob.page_table >= 0, perm[np.maximum(prob.page_table, 0)], -1).astype(np.int32)
     c2 = orc.pack_cache(kp, prob.v, prob.cu_tokens, pt2, prob.num_pages)
-    for a1, a2 in zip(c1.arrays(), c2.arrays()):
+    for a1, a2 in zip(c1.page_major(), c2.page_major()):
         np.testing.assert_array_equal(a1, a2[perm])
