@@ -59,16 +59,16 @@ enum {
 
 /*
  * The paged INT2 cache (§3.3).  Plain struct filled by the caller (host
- * memory); the five buffers are device memory.  num_pages is a multiple of 4:
- * the pool is made of aligned blocks of four pages, and the key rows and key
- * metadata of a channel sit side by side for the block's four pages (page p is
- * slot p & 3 of block p >> 2), so a selected channel of a whole block is one
- * contiguous 128-byte run.  All little-endian:
- *   k_codes u8   [num_pages/4][Hkv][128 ch][4 slot][32]
+ * memory); the five buffers are device memory.  num_pages is a multiple of 8:
+ * the pool is made of aligned blocks of eight pages, and the key rows and key
+ * metadata of a channel sit side by side for the block's eight pages (page p
+ * is slot p & 7 of block p >> 3), so a selected channel of a whole block is
+ * one contiguous 256-byte run.  All little-endian:
+ *   k_codes u8   [num_pages/8][Hkv][128 ch][8 slot][32]
  *                                   channel j's 2-bit codes of one page's 128
  *                                   tokens; token t at byte t>>2, bits 2*(t&3).
  *                                   Rows of channel 0 are unused (zero).
- *   k_meta  f16  [num_pages/4][Hkv][128 ch][4 slot][2]
+ *   k_meta  f16  [num_pages/8][Hkv][128 ch][8 slot][2]
  *                                   (scale, zero) of channel j over the page's
  *                                   valid tokens; channel 0 entries unused (zero).
  * and per physical page p, KV head g:

@@ -144,16 +144,19 @@ def key_transform(k_bf16: np.ndarray, t_k_bf16: np.ndarray) -> np.ndarray:
 class Cache:
     """Host copy of the paged INT2 cache (see oracle.c for the layout).
 
-    Key rows and key metadata are stored in aligned blocks of four pages, so
-    the page pool holds a multiple of four pages (rounded up here);
+    Key rows and key metadata are stored in aligned blocks of eight pages, so
+    the page pool holds a multiple of eight pages (rounded up here);
     ``k_rows(p)`` and ``k_meta_page(p)`` are writable views of one page."""
 
+    BLOCK = 8
+
     def __init__(self, num_pages: int, hkv: int):
-        num_pages = -(-int(num_pages) // 4) * 4
+        K = self.BLOCK
+        num_pages = -(-int(num_pages) // K) * K
         self.num_pages, self.hkv = num_pages, hkv
-        nb = num_pages // 4
-        self.k_codes = np.zeros((nb, hkv, HEAD_DIM, 4, 32), dtype=np.uint8)
-        self.k_meta = np.zeros((nb, hkv, HEAD_DIM, 4, 2), dtype=np.uint16)
+        nb = num_pages // K
+        self.k_codes = np.zeros((nb, hkv, HEAD_DIM, K, 32), dtype=np.uint8)
+        self.k_meta = np.zeros((nb, hkv, HEAD_DIM, K, 2), dtype=np.uint16)
         self.k_ch0 = np.zeros((num_pages, hkv, PAGE), dtype=np.uint16)
         self.v_codes = np.zeros((num_pages, hkv, PAGE, 32), dtype=np.uint8)
         self.v_meta = np.zeros((num_pages, hkv, 2, 4, PAGE), dtype=np.uint16)
@@ -163,11 +166,11 @@ class Cache:
 
     def k_rows(self, p: int) -> np.ndarray:
         """[Hkv][128 ch][32] key rows of physical page p (a view)."""
-        return self.k_codes[p >> 2, :, :, p & 3]
+        return self.k_codes[p // self.BLOCK, :, :, p % self.BLOCK]
 
     def k_meta_page(self, p: int) -> np.ndarray:
         """[Hkv][128 ch][2] key (scale, zero) of physical page p (a view)."""
-        return self.k_meta[p >> 2, :, :, p & 3]
+        return self.k_meta[p // self.BLOCK, :, :, p % self.BLOCK]
 
     def page_major(self):
         """All five buffers indexed by physical page first:
@@ -178,9 +181,10 @@ class Cache:
         return kc, km, self.k_ch0, self.v_codes, self.v_meta
 
     def set_page_major(self, kc, km, k0, vc, vm):
-        nb = self.num_pages // 4
-        self.k_codes[...] = kc.reshape(nb, 4, self.hkv, HEAD_DIM, 32).transpose(0, 2, 3, 1, 4)
-        self.k_meta[...] = km.reshape(nb, 4, self.hkv, HEAD_DIM, 2).transpose(0, 2, 3, 1, 4)
+        K = self.BLOCK
+        nb = self.num_pages // K
+        self.k_codes[...] = kc.reshape(nb, K, self.hkv, HEAD_DIM, 32).transpose(0, 2, 3, 1, 4)
+        self.k_meta[...] = km.reshape(nb, K, self.hkv, HEAD_DIM, 2).transpose(0, 2, 3, 1, 4)
         self.k_ch0[...], self.v_codes[...], self.v_meta[...] = k0, vc, vm
 
 

@@ -17,13 +17,13 @@
  * tokens.  Query head h uses KV head h / (Hq/Hkv).
  *
  * Cache format (all little-endian).  Physical pages come in aligned blocks
- * of four (page p is slot p & 3 of block p >> 2); per block B, KV head g:
- *   k_codes u8   [P/4][Hkv][128 ch][4 slot][32]  channel-major rows (§3.3: one
+ * of eight (page p is slot p & 7 of block p >> 3); per block B, KV head g:
+ *   k_codes u8   [P/8][Hkv][128 ch][8 slot][32]  channel-major rows (§3.3: one
  *                                       channel of one page per contiguous
- *                                       32-byte row); the four pages' rows of
+ *                                       32-byte row); the eight pages' rows of
  *                                       a channel are adjacent.  Token t at
  *                                       byte t>>2, bits 2*(t&3).  Row 0 zero.
- *   k_meta  f16  [P/4][Hkv][128 ch][4 slot][2]  (scale, zero) per channel and
+ *   k_meta  f16  [P/8][Hkv][128 ch][8 slot][2]  (scale, zero) per channel and
  *                                       page; channel 0 entries zero.
  * and per physical page p:
  *   k_ch0   bf16 [P][Hkv][128 tok]     channel 0 of k' kept in bf16 (§3.3).
@@ -44,10 +44,10 @@
 #define VGROUP 32
 
 /* Index of the 32-byte key row (and of the 2-entry key metadata) of channel j
- * of physical page p, KV head g: block p >> 2, slot p & 3. */
+ * of physical page p, KV head g: block p >> 3, slot p & 7. */
 static size_t krow(int64_t p, int g, int hkv, int j)
 {
-    return ((((size_t)(p >> 2) * (size_t)hkv + (size_t)g) * HD + (size_t)j) * 4) + (size_t)(p & 3);
+    return ((((size_t)(p >> 3) * (size_t)hkv + (size_t)g) * HD + (size_t)j) * 8) + (size_t)(p & 7);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -88,14 +88,17 @@ def _check(rc: int, where: str):
 
 class Cache:
     """Device buffers of the paged INT2 cache (layout in include/dqk.h).  The
-    page pool is a whole number of aligned 4-page blocks (rounded up here)."""
+    page pool is a whole number of aligned 8-page blocks (rounded up here)."""
+
+    BLOCK = 8
 
     def __init__(self, num_pages: int, num_kv_heads: int, device="cuda"):
         import torch
-        self.num_pages, self.num_kv_heads = -(-int(num_pages) // 4) * 4, int(num_kv_heads)
+        K = self.BLOCK
+        self.num_pages, self.num_kv_heads = -(-int(num_pages) // K) * K, int(num_kv_heads)
         P, H = self.num_pages, self.num_kv_heads
-        self.k_codes = torch.zeros((P // 4, H, HEAD_DIM, 4, 32), dtype=torch.uint8, device=device)
-        self.k_meta = torch.zeros((P // 4, H, HEAD_DIM, 4, 2), dtype=torch.int16, device=device)
+        self.k_codes = torch.zeros((P // K, H, HEAD_DIM, K, 32), dtype=torch.uint8, device=device)
+        self.k_meta = torch.zeros((P // K, H, HEAD_DIM, K, 2), dtype=torch.int16, device=device)
         self.k_ch0 = torch.zeros((P, H, PAGE), dtype=torch.int16, device=device)
         self.v_codes = torch.zeros((P, H, PAGE, 32), dtype=torch.uint8, device=device)
         self.v_meta = torch.zeros((P, H, 2, 4, PAGE), dtype=torch.int16, device=device)

@@ -32,7 +32,7 @@ int check_cache(const dqk_cache *c) {
 // n_keep = 0: the largest count any n_keep can resolve to (workspace sizing)
 int resolve_splits(int batch, int hq, int hkv, int max_pages, int num_splits, int n_keep) {
     if (num_splits > 0) return num_splits;
-    if (dqk::use_mfma_decode(hq, hkv)) return dqk::decode_splits_mfma(batch, hkv, max_pages, n_keep);
+    if (dqk::use_mfma_decode(hq, hkv, n_keep)) return dqk::decode_splits_mfma(batch, hkv, max_pages, n_keep);
     return dqk::decode_splits_generic(batch, hkv, max_pages);
 }
 
@@ -109,7 +109,7 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
     if (batch < 1 || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM || max_pages < 1 ||
         num_splits < 0 || num_splits > max_pages)
         return DQK_ERR_SHAPE;
-    const bool mfma = dqk::use_mfma_decode(hq, hkv);
+    const bool mfma = dqk::use_mfma_decode(hq, hkv, n_keep);
     if (!mfma && hq / hkv > dqk::GENERIC_MAX_GROUP) return DQK_ERR_UNSUPPORTED;
     if ((int64_t)batch * hkv > 65535 || batch * hq > 2147483647 / 2) return DQK_ERR_UNSUPPORTED;
     if (!aligned16(q_prime) || !aligned16(sel_idx) || !aligned16(page_table) || !aligned16(seq_lens) ||

@@ -4,24 +4,27 @@
 // bf16 copy, channel-major INT2 key rows and token-major values with separate
 // metadata (§3.3); one softmax over the whole context (§3.4).
 //
-// Work decomposition.  A workgroup is 8 waves and owns one split (a run of
-// aligned 4-page blocks) of one (sequence, KV head).  The block is the unit of
-// staging: its selected key rows (one 128-byte run per channel: the four
-// pages' 32-byte rows side by side), key metadata, channel 0, value codes and
-// value metadata go through LDS by direct global->LDS loads, three blocks in
-// flight.  Wave (w, hf) handles tokens 64hf..64hf+63 of page w of every block
-// and keeps its own online softmax; the eight partials are combined in LDS at
-// the end of the split.  Step u scores block u and multiplies the values of
-// block u - 1 in one instruction stream; the keys of block u + 2 and the
-// values of block u + 1 load meanwhile.
+// Work decomposition.  A workgroup (8 waves, one per CU) owns one split (a run
+// of 8-page blocks) of one (sequence, KV head) and walks it in steps of four
+// pages.  Loads go straight from HBM to LDS: the selected key rows of a whole
+// 8-page block (one 256-byte run per channel), its key metadata and channel 0
+// into one of two key stages, the value codes and value metadata of each
+// 4-page half into one of three value stages, two steps ahead, every wave
+// issuing a fixed share.  Waves 0-3 score: at step u wave w takes page w of
+// half u (all 128 tokens, four heads), keeps the online softmax of that page
+// stream and leaves the fp16 probabilities and the per-head rescale factor in
+// LDS.  Waves 4-7 multiply: wave 4 + w takes the values of page w of half
+// u - 1.  Each SIMD thus runs one VALU-heavy and one MFMA-heavy wave.  The
+// four page streams are combined in LDS at the end of the split.
 //
 // Scores (v_mfma_f32_16x16x32_f16).  The 32-deep k dimension is (token group
-// tg, 16 selected channels): A row i holds token 32tg + 8(i >> 2) + 4m + (i & 3)
-// of tile m, so a lane reads one 16-bit word (8 tokens) of each of its eight
-// channel rows and one AND per dword gives two codes as binary16 subnormals
-// code * 2^(2(i & 3) - 24).  The 16 columns are (tg, head, limb), block
-// diagonal in tg; the limbs are the fp16 hi and lo parts of
-// q~ = log2(e)/sqrt(d) * q' * scale, computed once per page into LDS.
+// tg, 16 selected channels): A row i of tile m holds token 64 tg + 4 i + m,
+// so a lane reads one byte (four tokens) of each of its eight channel rows
+// and one AND per dword and tile yields two codes as binary16 subnormals
+// code * 2^(2m - 24).  The 16 columns are (tg, head, limb), block diagonal in
+// tg; the limbs are the fp16 hi and lo parts of q~ = log2(e)/sqrt(d) * q' *
+// scale, computed once per page into LDS.  The zero points enter through an
+// fp32 bias per head and page.
 //
 // Values.  O[(group q, head h)][channel] += (P * scale')[.][token] x
 // code[token][channel] on the same MFMA, with P * scale' in fp16 where
@@ -43,38 +46,57 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int GRP = 4;          // query heads per KV head handled here
-constexpr int NW = 8;           // waves per workgroup
+constexpr int NW = 8;           // waves per workgroup: 4 scoring, 4 multiplying
 constexpr int NTHR = 64 * NW;
-constexpr int NSTAGE = 3;
+constexpr int NVST = 3;         // value stages
 constexpr int PBOOST = 14;      // probabilities are kept as 2^(x - m + 14)
 constexpr int EMIN = -15, EMAX = 15;  // clamp of the value-scale exponent
+constexpr int TABN = 64;        // blocks of a split whose alignment is tabulated up front
+constexpr int MAX_KS = 7;       // 16-channel k-steps: up to 112 selected INT2 channels
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+static_assert(KBLK == 8, "the kernel walks 8-page blocks in halves of four pages");
 
 // ---------------------------------------------------------------- LDS layout
 template <int KS>
 struct Lay {
-    static constexpr int NR = 16 * KS;         // key row slots (selected INT2 channels, padded)
-    static constexpr int KC = 0;               // [NR][128 B]; 16-byte chunk c of row r at c ^ ((r >> 3) & 1)
-    static constexpr int KM = KC + NR * 128;   // [NR][4 pages] (scale | zero << 16)
-    static constexpr int K0 = KM + NR * 16;    // [4 pages][128] bf16 channel 0
-    static constexpr int VC = K0 + 1024;       // [4 pages][128 tokens][32 B]
-    static constexpr int VM = VC + 16384;      // [4 pages][2 planes][4 groups][128] fp16; chunk c of (., q) at c ^ q
-    static constexpr int STAGE = VM + 8192;
-    static constexpr int PBW = 4 * 144;        // per wave: P [4 heads][64 tokens] fp16, rows padded to 144 B
-    static constexpr int PB = NSTAGE * STAGE;
-    static constexpr int QT = PB + NW * PBW;   // per wave: q~ B fragments [KS][256 B]
-    static constexpr int ZERO = QT + NW * KS * 256;  // KS * 256 B of zeros
-    static constexpr int ONES = ZERO + KS * 256;     // 16 B of fp16 ones, then 16 B of zeros
-    static constexpr int TOTAL = ONES + 32;
-    // global -> LDS loads of one block: key rows (2 KS x 1 KB), key metadata
-    // (KS x 64 dwords), channel 0 (1 KB); value codes (16 x 1 KB), value metadata (8 x 1 KB)
-    static constexpr int NKI = 3 * KS + 1;
-    static constexpr int KN = (NKI + NW - 1) / NW;   // key instructions per wave per block
-    static constexpr int VN = 3;                     // value instructions per wave per block
+    static constexpr int NR = 16 * KS;              // key row slots (selected INT2 channels, padded)
+    static constexpr int NMR = (NR + 31) / 32 * 32;  // key metadata rows (whole load instructions)
+    // key stage: rows [NR][256 B] (16-byte chunk c of row r at c ^ (2 ((r >> 3) & 1))),
+    // metadata [NMR][8 pages] (scale | zero << 16), channel 0 [8 pages][128] bf16
+    static constexpr int KC = 0;
+    static constexpr int KM = KC + NR * 256;
+    static constexpr int K0 = KM + NMR * 32;
+    static constexpr int KST = K0 + 2048;
+    // value stage: codes [4 pages][128 tokens][32 B], metadata [4 pages][2 planes][4 groups][128]
+    // fp16 (16-byte chunk c of (page, plane, q) at c ^ q)
+    static constexpr int VS = 2 * KST;
+    static constexpr int VC = 0;
+    static constexpr int VM = 16384;
+    static constexpr int VST = 24576;
+    static constexpr int PBROW = 272;               // P of one head: 128 fp16 + 16 B of padding
+    static constexpr int PBPAGE = 4 * PBROW;
+    static constexpr int PBBUF = 4 * PBPAGE;
+    static constexpr int PB = VS + NVST * VST;      // [2 buffers][4 pages][4 heads][PBROW]
+    static constexpr int AL = PB + 2 * PBBUF;       // [2 buffers][4 pages][4 heads] float rescale factors
+    static constexpr int QT = AL + 2 * 16 * 4;      // [4 scoring waves][KS][256 B] q~ B fragments
+    static constexpr int ZERO = QT + 4 * KS * 256;  // KS * 256 bytes of zeros
+    static constexpr int ONES = ZERO + KS * 256;    // 256 bytes of fp16 1.0
+    static constexpr int TOTAL = ONES + 256;
+    // global -> LDS loads: a key block is NRI row, NMI metadata and 2 channel-0
+    // instructions; a value half is 16 code and 8 metadata instructions
+    static constexpr int NRI = NR / 4;
+    static constexpr int NMI = NMR / 32;
+    static constexpr int NKI = NRI + NMI + 2;
+    static constexpr int KN = (NKI + NW - 1) / NW;  // key instructions per wave per block
+    static constexpr int VN = 3;                    // value instructions per wave per half
     static_assert(TOTAL <= 160 * 1024, "LDS");
-    static_assert(STAGE % 16 == 0 && KM % 16 == 0 && K0 % 16 == 0 && VC % 16 == 0 && VM % 16 == 0, "align");
-    static_assert(2 * (KN + VN) <= 63, "vmcnt range");
+    static_assert(KST % 16 == 0 && KM % 16 == 0 && K0 % 16 == 0 && VS % 16 == 0 && PB % 16 == 0 &&
+                      QT % 16 == 0 && ZERO % 16 == 0 && ONES % 16 == 0,
+                  "align");
+    static_assert(KN + VN <= 63, "vmcnt range");
+    static_assert(4 * GRP * PART_FLOATS * 4 <= PB, "exchange area");
+    static_assert(GRP * D * 4 + D * 4 <= VST, "prologue scratch");
 };
 
 // ---------------------------------------------------------------- small helpers
@@ -93,10 +115,6 @@ template <typename T>
 __device__ __forceinline__ void lds_st(uint32_t a, T v) {
     *reinterpret_cast<__attribute__((address_space(3))) T *>((uintptr_t)a) = v;
 }
-// Two 16-bit LDS words -> one dword (lo, hi).
-__device__ __forceinline__ uint32_t lds_pair(uint32_t a_lo, uint32_t a_hi) {
-    return __builtin_amdgcn_perm(lds_ld<uint16_t>(a_hi), lds_ld<uint16_t>(a_lo), 0x05040100u);
-}
 
 // Direct global -> LDS loads: 16 or 4 bytes per lane written at M0 + lane * size.
 // Issued from asm so that the compiler's wait-for-all before LDS reads does
@@ -109,32 +127,15 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t a) {
 }
 __device__ __forceinline__ void dma16_s(uint64_t sbase, uint32_t voff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %0" ::"s"((const void *)(uintptr_t)sbase),
-                 "v"(voff), "s"(lds)
+                 "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory", "m0");
 }
-__device__ __forceinline__ void dma4_s(uint64_t sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, %0" ::"s"((const void *)(uintptr_t)sbase),
-                 "v"(voff), "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma16_v(uint64_t addr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"((const void *)(uintptr_t)addr),
-                 "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma4_v(uint64_t addr, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"((const void *)(uintptr_t)addr), "s"(lds)
-                 : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Own loads down to N outstanding, then the workgroup barrier, as one
-// statement so that no LDS access can be scheduled between the two.
+// Own global->LDS loads down to N outstanding and own LDS accesses done,
+// then the workgroup barrier, as one statement so that no LDS access can be
+// scheduled between the wait and the barrier.
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
@@ -189,139 +190,250 @@ __device__ __forceinline__ uint32_t pow2_h(int e) {
     return e >= -14 ? (uint32_t)(e + 15) << 10 : 0x0200u;
 }
 
-// ---------------------------------------------------------------- block addressing
-// Base addresses of one 4-page block of one KV head in the five buffers, for
-// the aligned case (the block's pages are physical pages 4k .. 4k+3).
-struct BlockBase {
-    uint64_t kc, km, k0, vc, vm;
-};
 
-__device__ __forceinline__ BlockBase block_base(const dqk_cache &c, int64_t k, int g, int hkv) {
-    BlockBase bb;
-    const uint64_t kb = (uint64_t)k * hkv + g;         // key block index
-    const uint64_t pg = (uint64_t)(4 * k) * hkv + g;   // first page of the block
-    bb.kc = uniform64((uint64_t)(uintptr_t)c.k_codes + kb * (D * KBLK * ROW_BYTES));
-    bb.km = uniform64((uint64_t)(uintptr_t)c.k_meta + kb * (D * KBLK * 4));
-    bb.k0 = uniform64((uint64_t)(uintptr_t)c.k_ch0 + pg * (PG * 2));
-    bb.vc = uniform64((uint64_t)(uintptr_t)c.v_codes + pg * (PG * ROW_BYTES));
-    bb.vm = uniform64((uint64_t)(uintptr_t)c.v_meta + pg * (2 * VGROUPS * PG * 2));
-    return bb;
-}
-
-// Physical pages of block `blk` of a sequence: pages[j] for its valid slots,
-// slot 0's page repeated for the others; aligned iff page 4k + j sits in slot j.
-struct BlockPages {
-    int64_t p[4];
-    bool aligned;
-    int nvalid;  // valid pages in the block
-};
-
-__device__ __forceinline__ BlockPages block_pages(const int32_t *__restrict__ ptab, int blk, int npages) {
-    BlockPages bp;
-    const int lp = 4 * blk;
-    bp.nvalid = min(4, npages - lp);
-    bp.p[0] = ptab[lp];
-    bool al = (bp.p[0] & 3) == 0;
-#pragma unroll
-    for (int j = 1; j < 4; ++j) {
-        bp.p[j] = j < bp.nvalid ? (int64_t)ptab[lp + j] : bp.p[0];
-        al = al && (j >= bp.nvalid || bp.p[j] == bp.p[0] + j);
-    }
-    bp.aligned = al;
-    return bp;
-}
-
-// Global -> LDS load instructions of one block, numbered 0 .. NKI-1 (keys) and
-// 0 .. 23 (values).  Key instruction idx: 0 .. 2KS-1 key rows 8 idx .. 8 idx + 7
-// (8 lanes per row: 16-byte chunk cd of the row's 128-byte run at LDS chunk
-// cd ^ (idx & 1)); 2KS .. 3KS-1 key metadata rows 16 j .. 16 j + 15 (a dword per
-// page); 3KS channel 0 of the four pages.  Value instruction idx: 0 .. 15 value
-// codes of page idx >> 2, token rows 32 (idx & 3) .. + 31; 16 .. 23 value
-// metadata of page (idx - 16) >> 1, plane (idx - 16) & 1 (chunk cd of group q
-// at LDS chunk cd ^ q).
-//
-// Per lane, the page slot of its chunk and its byte offset within that page's
-// data (key rows / metadata: within the channel's run, the slot excluded).
-struct LanePart {
-    uint32_t slot, off;
-};
-
-template <int KS>
-__device__ __forceinline__ int key_row(int idx, int lane) {
-    return idx < 2 * KS ? 8 * idx + (lane >> 3) : idx < 3 * KS ? 16 * (idx - 2 * KS) + (lane >> 2) : 0;
-}
-
-template <int KS>
-__device__ __forceinline__ LanePart key_part(int idx, int lane, int chan_r) {
-    if (idx < 2 * KS) {
-        const int cs = (lane & 7) ^ (idx & 1);
-        return {(uint32_t)(cs >> 1), (uint32_t)(chan_r * (KBLK * ROW_BYTES) + (cs & 1) * 16)};
-    }
-    if (idx < 3 * KS) return {(uint32_t)(lane & 3), (uint32_t)(chan_r * (KBLK * 4))};
-    return {(uint32_t)(lane >> 4), (uint32_t)((lane & 15) * 16)};
-}
-
-__device__ __forceinline__ LanePart val_part(int idx, int lane) {
-    if (idx < 16) return {(uint32_t)(idx >> 2), (uint32_t)((idx & 3) * 1024 + lane * 16)};
-    const int j = idx - 16, q = lane >> 4, cd = lane & 15;
-    return {(uint32_t)(j >> 1), (uint32_t)((j & 1) * 1024 + q * 256 + ((cd ^ q) * 16))};
-}
-
+// ---------------------------------------------------------------- load plan
+// Key instruction idx of an 8-page block: 0 .. NRI-1 rows 4 idx .. 4 idx + 3
+// (16 lanes a row; LDS chunk c of row r receives the row's global chunk
+// c ^ (2 ((r >> 3) & 1)), i.e. page slot (chunk >> 1), half (chunk & 1));
+// NRI .. NRI+NMI-1 metadata rows 32 j .. 32 j + 31 (two lanes a row, pages
+// 4 h .. 4 h + 3 each); NRI + NMI + {0, 1} channel 0 of pages 4 i .. 4 i + 3.
+// Value instruction idx of a 4-page half: 0 .. 15 codes of page idx >> 2,
+// token rows 32 (idx & 3) .. + 31; 16 .. 23 metadata of page (idx - 16) >> 1,
+// plane (idx - 16) & 1 (LDS chunk c of group q receives chunk c ^ q).
+// Regions: 0 key rows, 1 key metadata, 2 channel 0, 3 value codes, 4 value metadata.
 template <int KS>
 __device__ __forceinline__ int key_region(int idx) {
-    return idx < 2 * KS ? 0 : idx < 3 * KS ? 1 : 2;
+    using Ly = Lay<KS>;
+    return idx < Ly::NRI ? 0 : idx < Ly::NRI + Ly::NMI ? 1 : 2;
 }
-__device__ __forceinline__ int val_region(int idx) { return idx < 16 ? 3 : 4; }
-
 template <int KS>
 __device__ __forceinline__ uint32_t key_lds(int idx) {
     using Ly = Lay<KS>;
-    return idx < 2 * KS ? Ly::KC + idx * 1024 : idx < 3 * KS ? Ly::KM + (idx - 2 * KS) * 256 : Ly::K0;
+    return idx < Ly::NRI ? Ly::KC + idx * 1024 : idx < Ly::NRI + Ly::NMI ? Ly::KM + (idx - Ly::NRI) * 1024
+                                                                        : Ly::K0 + (idx - Ly::NRI - Ly::NMI) * 1024;
 }
+template <int KS>
+__device__ __forceinline__ int key_row(int idx, int lane) {
+    using Ly = Lay<KS>;
+    return idx < Ly::NRI ? 4 * idx + (lane >> 4) : idx < Ly::NRI + Ly::NMI ? 32 * (idx - Ly::NRI) + (lane >> 1) : 0;
+}
+// Per-lane byte offset of key instruction idx from the base of an aligned block.
+template <int KS>
+__device__ __forceinline__ uint32_t key_aoff(int idx, int lane, int chan, int hkv) {
+    using Ly = Lay<KS>;
+    if (idx < Ly::NRI) {
+        const int r = 4 * idx + (lane >> 4);
+        const int cd = (lane & 15) ^ (2 * ((r >> 3) & 1));
+        return (uint32_t)(chan * (KBLK * ROW_BYTES) + cd * 16);
+    }
+    if (idx < Ly::NRI + Ly::NMI) return (uint32_t)(chan * (KBLK * 4) + (lane & 1) * 16);
+    const int i = idx - Ly::NRI - Ly::NMI;
+    return (uint32_t)(4 * i + (lane >> 4)) * (uint32_t)(hkv * PG * 2) + (uint32_t)((lane & 15) * 16);
+}
+__device__ __forceinline__ int val_region(int idx) { return idx < 16 ? 3 : 4; }
 template <int KS>
 __device__ __forceinline__ uint32_t val_lds(int idx) {
     using Ly = Lay<KS>;
     return idx < 16 ? Ly::VC + idx * 1024 : Ly::VM + (idx - 16) * 1024;
 }
-
-// Offset of a lane's chunk from the aligned block's base in its region.
-__device__ __forceinline__ uint32_t aligned_off(int region, LanePart lp, int hkv) {
-    switch (region) {
-        case 0: return lp.off + lp.slot * ROW_BYTES;
-        case 1: return lp.off + lp.slot * 4;
-        case 2: return lp.off + lp.slot * (uint32_t)(hkv * PG * 2);
-        case 3: return lp.off + lp.slot * (uint32_t)(hkv * PG * ROW_BYTES);
-        default: return lp.off + lp.slot * (uint32_t)(hkv * 2 * VGROUPS * PG * 2);
-    }
+// Per-lane byte offset of value instruction idx from the base of an aligned half.
+__device__ __forceinline__ uint32_t val_aoff(int idx, int lane, int hkv) {
+    if (idx < 16) return (uint32_t)(idx >> 2) * (uint32_t)(hkv * PG * ROW_BYTES) + (uint32_t)((idx & 3) * 1024 + lane * 16);
+    const int j = idx - 16, q = lane >> 4;
+    return (uint32_t)(j >> 1) * (uint32_t)(hkv * 2 * VGROUPS * PG * 2) +
+           (uint32_t)((j & 1) * 1024 + q * 256 + (((lane & 15) ^ q) * 16));
 }
 
-// Issue one planned load of a block into stage `st` (LDS byte address):
-// region and lds are wave-uniform; aoff is the lane's aligned offset and lp its
-// (slot, offset) for a block whose pages are not an aligned group.
-__device__ __forceinline__ void issue(int region, uint32_t lds_rel, uint32_t aoff, LanePart lp, const BlockPages &bp,
-                                      const BlockBase &bb, const dqk_cache &c, int g, int hkv, uint32_t st) {
-    const uint32_t lds = st + lds_rel;
-    if (bp.aligned) {  // wave-uniform
-        switch (region) {
-            case 0: dma16_s(bb.kc, aoff, lds); break;
-            case 1: dma4_s(bb.km, aoff, lds); break;
-            case 2: dma16_s(bb.k0, aoff, lds); break;
-            case 3: dma16_s(bb.vc, aoff, lds); break;
-            default: dma16_s(bb.vm, aoff, lds); break;
+// Base of KV head g's data in region r for aligned block (half) 0, and the
+// stride from one aligned block (key regions) or half (value regions) to the next.
+// (selects, not a switch: the region is wave-uniform and no indexed access
+// to the cache descriptor is wanted)
+__device__ __forceinline__ uint64_t region_base(const dqk_cache &c, int r, int g) {
+    const uint64_t kc = (uint64_t)(uintptr_t)c.k_codes + (uint64_t)g * (D * KBLK * ROW_BYTES);
+    const uint64_t km = (uint64_t)(uintptr_t)c.k_meta + (uint64_t)g * (D * KBLK * 4);
+    const uint64_t k0 = (uint64_t)(uintptr_t)c.k_ch0 + (uint64_t)g * (PG * 2);
+    const uint64_t vc = (uint64_t)(uintptr_t)c.v_codes + (uint64_t)g * (PG * ROW_BYTES);
+    const uint64_t vm = (uint64_t)(uintptr_t)c.v_meta + (uint64_t)g * (2 * VGROUPS * PG * 2);
+    return r == 0 ? kc : r == 1 ? km : r == 2 ? k0 : r == 3 ? vc : vm;
+}
+__device__ __forceinline__ uint64_t region_stride(int r, int hkv) {
+    const uint32_t e = r == 0 ? D * KBLK * ROW_BYTES
+                     : r == 1 ? D * KBLK * 4
+                     : r == 2 ? KBLK * PG * 2
+                     : r == 3 ? 4 * PG * ROW_BYTES
+                              : 4 * 2 * VGROUPS * PG * 2;
+    return (uint64_t)hkv * e;
+}
+
+// Aligned-block index of block bi of a sequence (its valid pages are physical
+// pages 8k .. 8k + nvalid - 1 in slot order), or -1.
+__device__ __forceinline__ int block_aligned(const int32_t *__restrict__ ptab, int bi, int npages) {
+    const int lp = KBLK * bi, nv = min(KBLK, npages - lp);
+    const int p0 = ptab[lp];
+    bool al = (p0 & (KBLK - 1)) == 0;
+#pragma unroll
+    for (int j = 1; j < KBLK; ++j)
+        if (j < nv) al = al && ptab[lp + j] == p0 + j;
+    return al ? p0 / KBLK : -1;
+}
+
+// Physical page of slot s of block bi (slot 0's page for slots past the end).
+struct BlockPages {
+    const int32_t *pt;  // the block's page-table entries
+    int nv;             // valid slots
+    __device__ __forceinline__ int operator()(int s) const { return pt[s < nv ? s : 0]; }
+};
+__device__ __forceinline__ BlockPages block_pages(const int32_t *__restrict__ ptab, int bi, int npages) {
+    return BlockPages{ptab + KBLK * bi, min(KBLK, npages - KBLK * bi)};
+}
+
+// Loads of a block whose pages are not an aligned group: each lane fetches
+// its 16 bytes from its own page through registers and stores them where the
+// direct load would have put them.
+template <int KS>
+__device__ __forceinline__ void slow_key(int idx, int lane, int chan, const BlockPages &p, const dqk_cache &c, int g,
+                                         int hkv, uint32_t lds) {
+    using Ly = Lay<KS>;
+    u32x4 v;
+    if (idx < Ly::NRI) {
+        const int r = 4 * idx + (lane >> 4);
+        const int cd = (lane & 15) ^ (2 * ((r >> 3) & 1));
+        const int pp = p(cd >> 1);
+        v = *reinterpret_cast<const u32x4 *>(c.k_codes + krow(pp, g, hkv, chan) * ROW_BYTES + (cd & 1) * 16);
+    } else if (idx < Ly::NRI + Ly::NMI) {
+        const int h = lane & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = *reinterpret_cast<const uint32_t *>(c.k_meta + krow(p(4 * h + i), g, hkv, chan) * 2);
+    } else {
+        const int i = idx - Ly::NRI - Ly::NMI;
+        const int pp = p(4 * i + (lane >> 4));
+        v = *reinterpret_cast<const u32x4 *>(c.k_ch0 + ((size_t)pp * hkv + g) * PG + (lane & 15) * 8);
+    }
+    lds_st<u32x4>(lds + lane * 16, v);
+}
+
+__device__ __forceinline__ void slow_val(int idx, int lane, const BlockPages &p, int hb, const dqk_cache &c, int g,
+                                         int hkv, uint32_t lds) {
+    u32x4 v;
+    if (idx < 16) {
+        const int pp = p(4 * hb + (idx >> 2));
+        v = *reinterpret_cast<const u32x4 *>(c.v_codes + ((size_t)pp * hkv + g) * (PG * ROW_BYTES) + (idx & 3) * 1024 +
+                                             lane * 16);
+    } else {
+        const int j = idx - 16, q = lane >> 4;
+        const int pp = p(4 * hb + (j >> 1));
+        v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(c.v_meta) +
+                                             ((size_t)pp * hkv + g) * (2 * VGROUPS * PG * 2) + (j & 1) * 1024 +
+                                             q * 256 + (((lane & 15) ^ q) * 16));
+    }
+    lds_st<u32x4>(lds + lane * 16, v);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    half2v h;
+    h[0] = (_Float16)a;
+    h[1] = (_Float16)b;
+    return as_u32(h);
+}
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// The loads of one split: which instructions this wave issues for every block
+// (the same plan each time), the alignment table, and the pipeline's wait.
+template <int KS>
+struct Feeder {
+    using Ly = Lay<KS>;
+    uint32_t S;
+    const dqk_cache *c;
+    const int32_t *ptab;
+    int g, hkv, lane, wv, npages, B0, nb, nst;
+    int tab;   // lane j: aligned index of block B0 + j (j < TABN), or -1
+    int pend;  // loads of this wave issued at the previous step (the ones allowed in flight)
+    int kidx[Ly::KN], kchan[Ly::KN];
+    uint32_t kaoff[Ly::KN], vaoff[Ly::VN];
+    uint64_t kbase[Ly::KN], kstr[Ly::KN], vbase[Ly::VN], vstr[Ly::VN];
+
+    __device__ __forceinline__ uint32_t kstage(int j) const { return S + (uint32_t)(j & 1) * Ly::KST; }
+    __device__ __forceinline__ uint32_t vstage(int u) const { return S + Ly::VS + (uint32_t)(u % NVST) * Ly::VST; }
+    __device__ __forceinline__ int blk_of(int j) const {
+        return j < TABN ? __builtin_amdgcn_readlane(tab, j)
+                        : __builtin_amdgcn_readfirstlane(block_aligned(ptab, B0 + j, npages));
+    }
+    // Plans from the selected channels (chan_of: key row slot -> channel).
+    template <typename ChanOf>
+    __device__ __forceinline__ void plan(ChanOf chan_of) {
+#pragma unroll
+        for (int k = 0; k < Ly::KN; ++k) {
+            kidx[k] = __builtin_amdgcn_readfirstlane((wv + NW * k) % Ly::NKI);
+            kchan[k] = chan_of(key_row<KS>(kidx[k], lane));
+            kaoff[k] = key_aoff<KS>(kidx[k], lane, kchan[k], hkv);
+            kbase[k] = uniform64(region_base(*c, key_region<KS>(kidx[k]), g));
+            kstr[k] = uniform64(region_stride(key_region<KS>(kidx[k]), hkv));
         }
-        return;
+#pragma unroll
+        for (int k = 0; k < Ly::VN; ++k) {
+            const int idx = wv + NW * k;
+            vaoff[k] = val_aoff(idx, lane, hkv);
+            vbase[k] = uniform64(region_base(*c, val_region(idx), g));
+            vstr[k] = uniform64(region_stride(val_region(idx), hkv));
+        }
+        tab = -1;
+        if (lane < min(nb, TABN)) tab = block_aligned(ptab, B0 + lane, npages);
+        pend = 0;
     }
-    const int64_t p = lp.slot == 0 ? bp.p[0] : lp.slot == 1 ? bp.p[1] : lp.slot == 2 ? bp.p[2] : bp.p[3];
-    const uint64_t pg = (uint64_t)p * hkv + g;
-    const uint64_t kr = (uint64_t)((p >> 2) * hkv + g) * (D * KBLK) + (uint64_t)(p & 3);  // key row index, channel 0
-    switch (region) {
-        case 0: dma16_v((uint64_t)(uintptr_t)c.k_codes + kr * ROW_BYTES + lp.off, lds); break;
-        case 1: dma4_v((uint64_t)(uintptr_t)c.k_meta + kr * 4 + lp.off, lds); break;
-        case 2: dma16_v((uint64_t)(uintptr_t)c.k_ch0 + pg * (PG * 2) + lp.off, lds); break;
-        case 3: dma16_v((uint64_t)(uintptr_t)c.v_codes + pg * (PG * ROW_BYTES) + lp.off, lds); break;
-        default: dma16_v((uint64_t)(uintptr_t)c.v_meta + pg * (2 * VGROUPS * PG * 2) + lp.off, lds); break;
+    // Loads of block j's keys / half u's values; true when the block took the
+    // register path (which leaves no load of this wave in flight).
+    __device__ __forceinline__ bool issue_keys(int j) const {
+        const uint32_t st = kstage(j);
+        const int k = blk_of(j);
+        if (k >= 0) {
+#pragma unroll
+            for (int i = 0; i < Ly::KN; ++i)
+                dma16_s(uniform64(kbase[i] + (uint64_t)(uint32_t)k * kstr[i]), kaoff[i], st + key_lds<KS>(kidx[i]));
+            return false;
+        }
+        const BlockPages p = block_pages(ptab, B0 + j, npages);
+#pragma unroll
+        for (int i = 0; i < Ly::KN; ++i) slow_key<KS>(kidx[i], lane, kchan[i], p, *c, g, hkv, st + key_lds<KS>(kidx[i]));
+        return true;
     }
-}
+    __device__ __forceinline__ bool issue_vals(int u) const {
+        const uint32_t st = vstage(u);
+        const int j = u >> 1, hb = u & 1;
+        const int k = blk_of(j);
+        if (k >= 0) {
+            const uint32_t hx = 2 * (uint32_t)k + (uint32_t)hb;
+#pragma unroll
+            for (int i = 0; i < Ly::VN; ++i)
+                dma16_s(uniform64(vbase[i] + (uint64_t)hx * vstr[i]), vaoff[i], st + val_lds<KS>(wv + NW * i));
+            return false;
+        }
+        const BlockPages p = block_pages(ptab, B0 + j, npages);
+#pragma unroll
+        for (int i = 0; i < Ly::VN; ++i) slow_val(wv + NW * i, lane, p, hb, *c, g, hkv, st + val_lds<KS>(wv + NW * i));
+        return true;
+    }
+    // Start of step u: this wave's loads older than the previous step are done,
+    // then the workgroup barrier; then the loads of half u + 1's values and (at
+    // even steps) block u/2 + 1's keys.  halfpages(u): whether half u holds a page.
+    template <typename HalfPages>
+    __device__ __forceinline__ void top(int u, HalfPages halfpages) {
+        if (u > 0 && pend == Ly::KN + Ly::VN)
+            wait_vm_barrier<Ly::KN + Ly::VN>();
+        else if (u > 0 && pend == Ly::KN)
+            wait_vm_barrier<Ly::KN>();
+        else if (u > 0 && pend == Ly::VN)
+            wait_vm_barrier<Ly::VN>();
+        else
+            wait_vm_barrier<0>();
+        int np = 0;
+        if (u + 1 < nst && halfpages(u + 1)) np = issue_vals(u + 1) ? 0 : np + Ly::VN;
+        if (!(u & 1) && (u >> 1) + 1 < nb) np = issue_keys((u >> 1) + 1) ? 0 : np + Ly::KN;
+        pend = np;
+    }
+};
 
 // ---------------------------------------------------------------- the kernel
 template <int KS>
@@ -338,20 +450,19 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const int hkv = c.num_kv_heads;
     const int b = bg / hkv, g = bg - b * hkv;
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int w = wv & 3, hf = wv >> 2;  // page slot and token half of this wave
-    const int G = lane >> 4, n = lane & 15;
+    const int w = wv & 3;  // page of the half this wave scores (waves 0-3) or multiplies (waves 4-7)
     const int L = seq_lens[b];
     const int npages = (L + PG - 1) / PG;
-    const int nblk = (npages + 3) >> 2;
+    const int nblk = (npages + KBLK - 1) / KBLK;
     const int per = (nblk + nsplit - 1) / nsplit;
     const int B0 = min(nblk, split * per), B1 = min(nblk, B0 + per);
-    const int nst = B1 - B0;
+    const int nb = B1 - B0;   // 8-page blocks of this split
+    const int nst = 2 * nb;   // 4-page halves
     const int32_t *ptab = page_table + (size_t)b * max_pages;
-    auto stage = [&](int u) { return S + (uint32_t)(u % NSTAGE) * Ly::STAGE; };
     float *part_base = partials + (((size_t)b * hq + (size_t)g * GRP) * nsplit + split) * PART_FLOATS;
     const size_t hstride = (size_t)nsplit * PART_FLOATS;
 
-    if (nst <= 0) {  // nothing of this sequence falls in this split: an empty partial
+    if (nb <= 0) {  // nothing of this sequence falls in this split: an empty partial
         const int h = tid >> 7, ch = tid & (D - 1);
         part_base[h * hstride + ch] = 0.0f;
         if (ch == 0) {
@@ -361,220 +472,273 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
         }
         return;
     }
+    // valid tokens of page slot ps of block j (relative to B0)
+    auto page_valid = [&](int j, int ps) { return min(PG, max(0, L - PG * (KBLK * (B0 + j) + ps))); };
 
-    // ---- q' of the four heads and the selected channels into LDS (stage 2, free until step 0)
-    const uint32_t scr = stage(2);
+    // ---- q' of the four heads and the selected channels into LDS (value stage 2, first loaded at step 1)
+    const uint32_t scr = S + Ly::VS + 2 * Ly::VST;
     {
         const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q_prime + ((size_t)b * hq + (size_t)g * GRP) * D);
         const int32_t *ssrc = sel_idx + ((size_t)b * hkv + g) * n_keep;
         if (tid < 128) lds_st<u32x4>(scr + tid * 16, qsrc[tid]);
         if (tid < 128) lds_st<int32_t>(scr + GRP * D * 4 + tid * 4, tid < n_keep ? ssrc[tid] : 0);
-        // constant areas: zeros for the off-diagonal q~ fragments, fp16 ones / zeros
         for (int i = tid; i < KS * 64; i += NTHR) lds_st<uint32_t>(S + Ly::ZERO + i * 4, 0u);
-        if (tid < 8) lds_st<uint32_t>(S + Ly::ONES + tid * 4, tid < 4 ? 0x3C003C00u : 0u);
+        if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
     }
     __syncthreads();
     auto qv = [&](int h, int j) { return lds_ld<float>(scr + (h * D + j) * 4); };
     const int has0 = lds_ld<int32_t>(scr + GRP * D * 4) == 0;  // the list is ascending
     const int R = n_keep - has0;                                 // selected INT2 channels
-    // channel of key row slot r (rows past R read row 0, which is zero)
+    // channel of key row slot r (slots past R read channel 0's all-zero row)
     auto chan_of = [&](int r) { return r < R ? lds_ld<int32_t>(scr + GRP * D * 4 + (r + has0) * 4) : 0; };
 
-    // ---- load plans (the same for every block): this wave issues key
-    //      instructions wv + 8k (a wave past the end repeats a real load: same
-    //      bytes, same place) and value instructions wv + 8k
-    uint32_t kaoff[Ly::KN], kchan[Ly::KN], vaoff[Ly::VN];
-#pragma unroll
-    for (int k = 0; k < Ly::KN; ++k) {
-        const int idx = (wv + NW * k) % Ly::NKI;
-        kchan[k] = (uint32_t)chan_of(key_row<KS>(idx, lane));
-        kaoff[k] = aligned_off(key_region<KS>(idx), key_part<KS>(idx, lane, (int)kchan[k]), hkv);
-    }
-#pragma unroll
-    for (int k = 0; k < Ly::VN; ++k) {
-        const int idx = wv + NW * k;
-        vaoff[k] = aligned_off(val_region(idx), val_part(idx, lane), hkv);
-    }
-    auto issue_keys = [&](const BlockPages &bp, const BlockBase &bb, uint32_t st) {
-#pragma unroll
-        for (int k = 0; k < Ly::KN; ++k) {
-            const int idx = (wv + NW * k) % Ly::NKI;
-            issue(key_region<KS>(idx), key_lds<KS>(idx), kaoff[k], bp.aligned ? LanePart{0, 0} : key_part<KS>(idx, lane, (int)kchan[k]),
-                  bp, bb, c, g, hkv, st);
-        }
-    };
-    auto issue_vals = [&](const BlockPages &bp, const BlockBase &bb, uint32_t st) {
-#pragma unroll
-        for (int k = 0; k < Ly::VN; ++k) {
-            const int idx = wv + NW * k;
-            issue(val_region(idx), val_lds<KS>(idx), vaoff[k], bp.aligned ? LanePart{0, 0} : val_part(idx, lane), bp,
-                  bb, c, g, hkv, st);
-        }
-    };
+    // ---- load plans, the same for every block: key instructions wv + 8k (a
+    //      wave past the end repeats a real load: same bytes, same place) and
+    //      value instructions wv + 8k
+    Feeder<KS> fd;
+    fd.S = S;
+    fd.c = &c;
+    fd.ptab = ptab;
+    fd.g = g;
+    fd.hkv = hkv;
+    fd.lane = lane;
+    fd.wv = wv;
+    fd.npages = npages;
+    fd.B0 = B0;
+    fd.nb = nb;
+    fd.nst = nst;
+    fd.plan(chan_of);
+    auto halfpages = [&](int u) { return page_valid(u >> 1, 4 * (u & 1)) > 0; };
 
-    // ---- per-lane constants of the q~ precompute: lane l owns dword l of every
-    //      k-step: channel slots 16 ks + 8 G1 + 2 ep + {0, 1}, head hq_, limb ll_q
+    // ---- per-lane constants of both roles (q' products from the scratch)
     const float C = sm_scale * LOG2E;
-    const int G1 = lane >> 5, hq_ = (lane >> 3) & 3, llq = (lane >> 2) & 1, ep = lane & 3;
-    uint32_t QH[KS], QL[KS];
+    const int ar = lane & 15, Gk = lane >> 4;
+    constexpr int NPI = (KS + 1) / 2;  // channel pairs per lane in the q~ precompute
+    float QC[NPI][2];
+    const int hp = lane >> 4, j16 = lane & 15;  // q~ precompute: head, pair index
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        half2v h, l;
+    for (int i = 0; i < NPI; ++i)
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int r = 16 * ks + 8 * G1 + 2 * ep + u;
-            const float v = r < R ? qv(hq_, chan_of(r)) * C : 0.0f;
-            const _Float16 vh = (_Float16)v;
-            const _Float16 vl = (_Float16)(v - (float)vh);
-            h[u] = llq ? vh : (_Float16)0.0f;
-            l[u] = llq ? vl : vh;
+        for (int e = 0; e < 2; ++e) {
+            const int slot = 2 * (j16 + 16 * i) + e;
+            QC[i][e] = (slot < 16 * KS && slot < R) ? qv(hp, chan_of(slot)) * C : 0.0f;
         }
-        QH[ks] = as_u32(h);
-        QL[ks] = as_u32(l);
-    }
-    // score lanes: column n = (tg, head hh, limb ll); rows 4G + r
-    const int tg = n >> 3, hh = (n >> 1) & 3, ll = n & 1;
+    const int hh = (ar >> 1) & 3;  // score column head
     const float q0c = has0 ? qv(hh, 0) * C : 0.0f;
-    __syncthreads();  // every wave is done with the scratch in stage 2
+    __syncthreads();  // scratch read by every wave
 
-    // score A reads: word 4 tg_a + (n >> 2) of the wave's 16 bytes of each row
-    const int tga = G >> 1;
-    const uint32_t ka_base = Ly::KC + (8 * (G & 1)) * 128 + (((2 * w + hf) ^ (G & 1)) * 16) +
-                             2 * (4 * tga + (n >> 2));
-    const uint32_t amask = 0x00030003u << (2 * (n & 3));
-    // score B reads: the q~ fragment (or zeros off the token-group diagonal)
-    const uint32_t qt_w = S + Ly::QT + wv * (KS * 256);
-    const uint32_t qb_lane = (tga == tg ? qt_w : S + Ly::ZERO) + ((G & 1) * 8 + (n & 7)) * 16;
-    // ch0 / P write: tokens 32 tg + 8 G + 4 ll + r of the wave's 64
-    const int tok4 = 32 * tg + 8 * G + 4 * ll;
-    const uint32_t pb_w = S + Ly::PB + wv * Ly::PBW;
-    // value lanes: row (q, h) = (n >> 2, n & 3); k = tokens 32 ps + 8 G + e of the wave's 64
-    const int qv_ = n >> 2, hv = n & 3;
-    const uint32_t pr_lane = pb_w + hv * 144 + 16 * G;                               // + 64 ps
-    const uint32_t sp_lane = Ly::VM + w * 2048 + qv_ * 256 + (((8 * hf + G) ^ qv_) * 16);  // + 64 ps
-    const int cz = n & 3;
-    const uint32_t bz_lane = cz == 0 ? sp_lane + 1024 : cz == 2 ? sp_lane : 0u;       // stage-relative (0: constant)
-    const uint32_t bz_const = S + Ly::ONES + (cz == 1 ? 0u : 16u);
-    const uint32_t vc_lane = Ly::VC + w * 4096 + (64 * hf + 8 * G) * 32 + 2 * n;      // + 1024 ps + 32 e
-    half8 M15;
-    {
-        const _Float16 m = (_Float16)(cz == 3 ? -1.5f : 0.0f);
-        M15 = half8{m, m, m, m, m, m, m, m};
-    }
+    // ---- prologue loads: keys of block 0, values of half 0
+    fd.issue_keys(0);
+    fd.issue_vals(0);
 
-    // ---- state
-    float m_run = -__builtin_huge_valf();  // integer running maximum (log2 units) of head hh
-    float l32 = 0.0f;                      // fp32 sum of 2^(x - m) over this lane's tokens of head hh
-    int e_run = EMIN;                      // running exponent of the value scales
-    f32x4 O[8];
+    const uint32_t xw = S + (uint32_t)w * (GRP * PART_FLOATS * 4);  // this page stream's exchange slot
+    if (wv < 4) {
+        // ================= scoring waves: page w of every half
+        const int tga = Gk >> 1, cs8 = Gk & 1;        // A: token group and channel half of the k-chunk
+        const int tgc = ar >> 3, ll = ar & 1;         // B / output column (tg, head hh, limb)
+        const uint32_t qt_w = S + Ly::QT + (uint32_t)w * (KS * 256);
+        const uint32_t qb_lane = (tga == tgc ? qt_w : S + Ly::ZERO) + cs8 * 128 + hh * 32 + ll * 16;
+        const int tok0 = 64 * tgc + 16 * Gk + 2 * ll;       // this lane's tokens: tok0 + 4 r + mm
+        float m_run = -__builtin_huge_valf();  // integer running maximum (log2 units) of head hh
+        float l32 = 0.0f;                      // fp32 sum of 2^(x - m) over this lane's tokens
+
+        for (int u = 0; u <= nst; ++u) {
+            fd.top(u, halfpages);
+            if (u >= nst) continue;
+            const int ps = 4 * (u & 1) + w;
+            const int nv = page_valid(u >> 1, ps);
+            if (nv <= 0) continue;
+            const uint32_t kst = fd.kstage(u >> 1);
+
+            // ---- q~ limbs of the page into this wave's fragments, bias sum_j z_j C q'_j in fp32.
+            //      q~ is scaled by 2^kq (largest |q~| of the page near 2^14) so that its
+            //      products with the codes stay far above the binary16 subnormal range.
+            float bacc = 0.0f, vmax = 0.0f;
+            float vq[NPI][2];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 Oz = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < NPI; ++i) {
+                const int c0 = 2 * (j16 + 16 * i);
+                vq[i][0] = vq[i][1] = 0.0f;
+                if (c0 < 16 * KS) {
+                    const uint32_t d0 = lds_ld<uint32_t>(kst + Ly::KM + c0 * 32 + ps * 4);
+                    const uint32_t d1 = lds_ld<uint32_t>(kst + Ly::KM + (c0 + 1) * 32 + ps * 4);
+                    vq[i][0] = QC[i][0] * h2f(d0 & 0xFFFFu);
+                    vq[i][1] = QC[i][1] * h2f(d1 & 0xFFFFu);
+                    vmax = fmaxf(vmax, fmaxf(__builtin_fabsf(vq[i][0]), __builtin_fabsf(vq[i][1])));
+                    bacc = __builtin_fmaf(QC[i][0], h2f(d0 >> 16), bacc);
+                    bacc = __builtin_fmaf(QC[i][1], h2f(d1 >> 16), bacc);
+                }
+            }
+            vmax = fmaxf(vmax, dpp<DPP_XOR1>(vmax));
+            vmax = fmaxf(vmax, dpp<DPP_XOR2>(vmax));
+            vmax = fmaxf(vmax, dpp<DPP_ROR4>(vmax));
+            vmax = fmaxf(vmax, dpp<DPP_ROR8>(vmax));
+            vmax = max_x32(max_x16(vmax));
+            const int ev = (int)((__float_as_uint(vmax) >> 23) & 255u) - 127;  // floor(log2 vmax)
+            const int kq = vmax > 0.0f ? min(100, max(-100, 14 - ev)) : 0;
+            const float sq = __uint_as_float((uint32_t)(127 + kq) << 23);
+#pragma unroll
+            for (int i = 0; i < NPI; ++i) {
+                const int c0 = 2 * (j16 + 16 * i);
+                if (c0 < 16 * KS) {
+                    const float v0 = vq[i][0] * sq, v1 = vq[i][1] * sq;
+                    const _Float16 hi0 = (_Float16)v0, hi1 = (_Float16)v1;
+                    const uint32_t off = (c0 >> 4) * 256 + ((c0 >> 3) & 1) * 128 + hp * 32 + (c0 & 7) * 2;
+                    half2v hi;
+                    hi[0] = hi0;
+                    hi[1] = hi1;
+                    lds_st<uint32_t>(qt_w + off, as_u32(hi));
+                    lds_st<uint32_t>(qt_w + off + 16, pack_h2(v0 - (float)hi0, v1 - (float)hi1));
+                }
+            }
+            // code units: tiles 0, 2 at 2^-20, tiles 1, 3 at 2^-18; undo them and 2^kq
+            const float comp0 = __uint_as_float((uint32_t)(127 + 20 - kq) << 23);
+            const float comp1 = __uint_as_float((uint32_t)(127 + 18 - kq) << 23);
+            bacc += dpp<DPP_XOR1>(bacc);
+            bacc += dpp<DPP_XOR2>(bacc);
+            bacc += dpp<DPP_ROR4>(bacc);
+            bacc += dpp<DPP_ROR8>(bacc);  // every lane of row h holds head h's bias
+            const float b0 = bcast_lane(bacc, 0), b1 = bcast_lane(bacc, 16), b2 = bcast_lane(bacc, 32),
+                        b3 = bcast_lane(bacc, 48);
+            const float bias = hh == 0 ? b0 : hh == 1 ? b1 : hh == 2 ? b2 : b3;
 
-    // ---- prologue loads: keys of block 0, values of block 0, keys of block 1
-    auto blk_info = [&](int u, BlockPages &bp, BlockBase &bb) {
-        bp = block_pages(ptab, B0 + u, npages);
-        bb = block_base(c, bp.p[0] >> 2, g, hkv);
-    };
-    {
-        BlockPages bp;
-        BlockBase bb;
-        blk_info(0, bp, bb);
-        issue_keys(bp, bb, stage(0));
-        issue_vals(bp, bb, stage(0));
-        if (nst > 1) {
-            blk_info(1, bp, bb);
-            issue_keys(bp, bb, stage(1));
-        }
-    }
-
-    const float comp[4] = {16777216.0f, 4194304.0f, 1048576.0f, 262144.0f};  // 2^(24 - 2r)
-
-    for (int u = 0; u <= nst; ++u) {
-        // loads issued at the previous step may stay in flight
-        const int pend = (u + 1 < nst ? Ly::KN : 0) + (u < nst ? Ly::VN : 0);
-        if (pend == Ly::KN + Ly::VN)
-            wait_vm_barrier<Ly::KN + Ly::VN>();
-        else if (pend == Ly::VN)
-            wait_vm_barrier<Ly::VN>();
-        else
-            wait_vm_barrier<0>();
-        // keys of block u + 2, values of block u + 1
-        if (u + 2 < nst) {
-            BlockPages bp;
-            BlockBase bb;
-            blk_info(u + 2, bp, bb);
-            issue_keys(bp, bb, stage(u + 2));
-        }
-        if (u + 1 < nst) {
-            BlockPages bp;
-            BlockBase bb;
-            blk_info(u + 1, bp, bb);
-            issue_vals(bp, bb, stage(u + 1));
-        }
-
-        const uint32_t sk = stage(u), sv = stage(u + NSTAGE - 1);  // keys of block u, values of block u - 1
-        // valid tokens of this wave in the scored block and in the multiplied block
-        const int nv_s = u < nst ? min(64, max(0, L - PG * (4 * (B0 + u) + w) - 64 * hf)) : 0;
-        const int nv_v = u >= 1 ? min(64, max(0, L - PG * (4 * (B0 + u - 1) + w) - 64 * hf)) : 0;
-
-        // ---- q~ of the scored page into this wave's LDS area, and the bias sum_j z_j C q'_j
-        float bias = 0.0f;
-        if (nv_s > 0) {
-            float zsum = 0.0f;
+            // ---- scores: four token tiles
+            f32x4 Sc[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Sc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint32_t ab = kst + Ly::KC + cs8 * (8 * 256) + ((((2 * ps + tga) ^ (2 * cs8))) * 16) + ar;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                const int r0 = 16 * ks + 8 * G1 + 2 * ep;
-                const uint32_t d0 = lds_ld<uint32_t>(sk + Ly::KM + r0 * 16 + w * 4);
-                const uint32_t d1 = lds_ld<uint32_t>(sk + Ly::KM + (r0 + 1) * 16 + w * 4);
-                const half2v s2 = as_half2(__builtin_amdgcn_perm(d1, d0, 0x05040100u));
-                const half2v qh = as_half2(QH[ks]), ql = as_half2(QL[ks]);
-                const half2v t1 = qh * s2;
-                const half2v t2 = __builtin_elementwise_fma(qh, s2, -t1);
-                lds_st<uint32_t>(qt_w + ks * 256 + lane * 4, as_u32(__builtin_elementwise_fma(ql, s2, t2)));
-                // z . (hi + lo) of the two channels, exact products, fp32 sums
-                const half2v z2 = as_half2(__builtin_amdgcn_perm(d1, d0, 0x07060302u));
-                zsum = __builtin_amdgcn_fdot2(z2, ql, __builtin_amdgcn_fdot2(z2, qh, zsum, false), false);
+                u32x4 X;
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const uint32_t lo = lds_ld<uint8_t>(ab + (16 * ks + 2 * e2) * 256);
+                    const uint32_t hi = lds_ld<uint8_t>(ab + (16 * ks + 2 * e2 + 1) * 256);
+                    X[e2] = lo | (hi << 16);
+                }
+                const u32x4 Bq = lds_ld<u32x4>(qb_lane + ks * 256);
+                // codes at bits 4..7 of each half (tiles 0, 1 shifted up): units 2^-20, 2^-18
+                const u32x4 XS = X << 4;
+                Sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(XS & 0x00300030u), as_half8(Bq), Sc[0], 0, 0, 0);
+                Sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(XS & 0x00C000C0u), as_half8(Bq), Sc[1], 0, 0, 0);
+                Sc[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(X & 0x00300030u), as_half8(Bq), Sc[2], 0, 0, 0);
+                Sc[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(X & 0x00C000C0u), as_half8(Bq), Sc[3], 0, 0, 0);
             }
-            if (!llq) zsum = 0.0f;  // limb-0 lanes hold (0, hi) only
-            // sum over the lanes of head hq_: bits 0, 1 (ep), 2 (limb), 5 (G1)
-            zsum += dpp<DPP_XOR1>(zsum);
-            zsum += dpp<DPP_XOR2>(zsum);      // every lane of a quad holds the quad's sum
-            zsum += dpp<DPP_HMIRROR>(zsum);   // plus the other quad of its 8
-            zsum = sum_x32(zsum);
-            // lane 8h holds head h's bias
-            const float b0 = bcast_lane(zsum, 0), b1 = bcast_lane(zsum, 8), b2 = bcast_lane(zsum, 16),
-                        b3 = bcast_lane(zsum, 24);
-            bias = hh == 0 ? b0 : hh == 1 ? b1 : hh == 2 ? b2 : b3;
-        }
-        wait_lgkm0();  // q~ written (and the previous step's P stores done)
 
-        // ---- value-scale exponent of the multiplied page; rescale O when it grows
-        u32x4 spv[2], keep[2];
-        if (nv_v > 0) {
+            // ---- logits (log2 units) of this lane's 8 tokens: tiles 2 ll, 2 ll + 1 joined with the other limb
+            float x[4][2];
+            const uint32_t k0a = kst + Ly::K0 + ps * 256 + tok0 * 2;
 #pragma unroll
-            for (int ps = 0; ps < 2; ++ps) {
-                spv[ps] = lds_ld<u32x4>(sv + sp_lane + 64 * ps);
-                keep[ps] = u32x4{~0u, ~0u, ~0u, ~0u};
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t kw = lds_ld<uint32_t>(k0a + r * 8);
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const float mine = ll ? Sc[2 + mm][r] : Sc[mm][r];
+                    const float give = ll ? Sc[mm][r] : Sc[2 + mm][r];
+                    float v = __builtin_fmaf(mine + dpp<DPP_XOR1>(give), mm ? comp1 : comp0, bias);
+                    v = __builtin_fmaf(q0c, __uint_as_float(mm ? (kw & 0xFFFF0000u) : (kw << 16)), v);
+                    x[r][mm] = v;
+                }
             }
-            if (nv_v < 64) {  // metadata past the sequence end is unspecified: keep it out of everything
+            if (nv < PG) {  // tokens past the sequence end (their bytes are unspecified) get no weight
 #pragma unroll
-                for (int ps = 0; ps < 2; ++ps)
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int mm = 0; mm < 2; ++mm)
+                        if (tok0 + 4 * r + mm >= nv) x[r][mm] = -__builtin_huge_valf();
+            }
+            // ---- integer running maximum of head hh, rescale factor for the multiplying wave
+            float bm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[1][0], x[1][1])),
+                             fmaxf(fmaxf(x[2][0], x[2][1]), fmaxf(x[3][0], x[3][1])));
+            bm = fmaxf(bm, dpp<DPP_XOR1>(bm));
+            bm = fmaxf(bm, dpp<DPP_ROR8>(bm));
+            bm = max_x32(max_x16(bm));
+            const float m_new = fmaxf(m_run, ceilf(bm));
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf, 1 when unchanged
+            m_run = m_new;
+            l32 *= alpha;
+            // ---- probabilities 2^(x - m + 14) -> fp16 -> the P buffer of this half
+            const uint32_t pbw = S + Ly::PB + (uint32_t)(u & 1) * Ly::PBBUF + (uint32_t)w * Ly::PBPAGE + hh * Ly::PBROW +
+                                 tok0 * 2;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p0 = __builtin_amdgcn_exp2f(x[r][0] - m_new + (float)PBOOST);
+                const float p1 = __builtin_amdgcn_exp2f(x[r][1] - m_new + (float)PBOOST);
+                l32 += p0 + p1;
+                lds_st<uint32_t>(pbw + r * 8, pack_h2(p0, p1));
+            }
+            if (lane < 8 && ll == 0)  // lane 2h: column (0, h, 0)
+                lds_st<float>(S + Ly::AL + (uint32_t)(((u & 1) * 16 + w * 4 + hh) * 4), alpha);
+        }
+        // ---- this stream's m and l32 per head
+        float l32h = l32 + dpp<DPP_XOR1>(l32);
+        l32h += dpp<DPP_ROR8>(l32h);
+        l32h = sum_x32(sum_x16(l32h));
+        __syncthreads();  // every wave is done with the stages: the exchange reuses them
+        if (lane < 8 && ll == 0) {
+            lds_st<float>(xw + (hh * PART_FLOATS + D) * 4, m_run);
+            lds_st<float>(xw + (hh * PART_FLOATS + D + 2) * 4, l32h);
+        }
+    } else {
+        // ================= multiplying waves: page w of every half, one step behind
+        const int q = ar >> 2, hv = ar & 3, cz = ar & 3;  // A row (group q, head hv); Oz column (q, cz)
+        const uint32_t pr_lane = S + Ly::PB + (uint32_t)w * Ly::PBPAGE + hv * Ly::PBROW + 16 * Gk;  // + buffer, + 64 ps
+        const uint32_t sp_lane = Ly::VM + (uint32_t)w * 2048 + q * 256 + ((Gk ^ q) * 16);         // + 64 ps
+        const uint32_t bz_rel = cz == 0 ? sp_lane + 1024 : sp_lane;  // zero points / scales
+        const uint32_t bz_const = S + (cz == 1 ? Ly::ONES : Ly::ZERO);
+        const bool bz_var = (cz & 1) == 0;
+        const uint32_t vc_lane = Ly::VC + (uint32_t)w * 4096 + (8 * Gk) * 32 + 2 * ar;  // + 1024 ps + 32 e
+        half8 M15;
+        {
+            const _Float16 m = (_Float16)(cz == 3 ? -1.5f : 0.0f);
+            M15 = half8{m, m, m, m, m, m, m, m};
+        }
+        int e_run = EMIN;  // running exponent of the value scales
+        f32x4 O[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 Oz = {0.f, 0.f, 0.f, 0.f};
+
+        for (int u = 0; u <= nst; ++u) {
+            fd.top(u, halfpages);
+            if (u < 1) continue;
+            const int uu = u - 1;
+            const int nv = page_valid(uu >> 1, 4 * (uu & 1) + w);
+            if (nv <= 0) continue;
+            const uint32_t vst = fd.vstage(uu);
+            const int buf = uu & 1;
+            // ---- softmax rescale of what this stream holds
+            const f32x4 al = lds_ld<f32x4>(S + Ly::AL + (uint32_t)((buf * 16 + w * 4) * 4));
+            if (al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) {  // wave-uniform
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) O[t][r] *= al[r];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Oz[r] *= al[r];
+            }
+            // ---- value-scale exponent of the page; rescale O when it grows
+            u32x4 spv[4], keep[4];
+#pragma unroll
+            for (int ps = 0; ps < 4; ++ps) spv[ps] = lds_ld<u32x4>(vst + sp_lane + 64 * ps);
+            if (nv < PG) {  // metadata past the sequence end is unspecified: keep it out of everything
+#pragma unroll
+                for (int ps = 0; ps < 4; ++ps) {
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
-                        const int t = 32 * ps + 8 * G + 2 * e2;
-                        keep[ps][e2] = (t < nv_v ? 0x0000FFFFu : 0u) | (t + 1 < nv_v ? 0xFFFF0000u : 0u);
+                        const int t = 32 * ps + 8 * Gk + 2 * e2;
+                        keep[ps][e2] = (t < nv ? 0x0000FFFFu : 0u) | (t + 1 < nv ? 0xFFFF0000u : 0u);
                     }
-#pragma unroll
-                for (int ps = 0; ps < 2; ++ps) spv[ps] &= keep[ps];
+                    spv[ps] &= keep[ps];
+                }
             }
             uint32_t mx = 0;
 #pragma unroll
-            for (int ps = 0; ps < 2; ++ps)
+            for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t x = spv[ps][e];
-                    mx = max(mx, max(x & 0xFFFFu, x >> 16));
+                    const uint32_t xx = spv[ps][e];
+                    mx = max(mx, max(xx & 0xFFFFu, xx >> 16));
                 }
             mx = max(mx, dpp_u<DPP_ROR4>(mx));
             mx = max(mx, dpp_u<DPP_ROR8>(mx));
@@ -588,152 +752,80 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                 if (cz == 3) Oz *= f;
                 e_run = e_pg;
             }
-        }
-        const uint32_t sc_h = pow2_h(-e_run);
-        const half2v sc2 = as_half2(sc_h | (sc_h << 16));
-
-        // ---- scores of the scored page and value products of the multiplied page
-        f32x4 Sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        if (nv_s > 0) {
+            const uint32_t sc_h = pow2_h(-e_run);
+            const half2v sc2 = as_half2(sc_h | (sc_h << 16));
+            // ---- value products, 32 tokens per step
+            const uint32_t prb = pr_lane + (uint32_t)buf * Ly::PBBUF;
 #pragma unroll
-            for (int i = 0; i < KS; ++i) {
-                const uint32_t ka = sk + ka_base + (16 * i) * 128;
-                u32x4 X;
-#pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) X[e2] = lds_pair(ka + (2 * e2) * 128, ka + (2 * e2 + 1) * 128);
-                const u32x4 Bq = lds_ld<u32x4>(qb_lane + i * 256);
-                const u32x4 A0 = X & amask, A1 = (X >> 8) & amask;
-                Sc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(A0), as_half8(Bq), Sc[0], 0, 0, 0);
-                Sc[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(A1), as_half8(Bq), Sc[1], 0, 0, 0);
-            }
-        }
-        if (nv_v > 0) {
-#pragma unroll
-            for (int ps = 0; ps < 2; ++ps) {
-                const u32x4 Pp = lds_ld<u32x4>(pr_lane + 64 * ps);
-                const u32x4 sp = spv[ps];
-                u32x4 Bz = lds_ld<u32x4>(bz_lane ? sv + bz_lane + 64 * ps : bz_const);
-                if (nv_v < 64) Bz &= keep[ps];
+            for (int ps = 0; ps < 4; ++ps) {
+                const u32x4 Pp = lds_ld<u32x4>(prb + 64 * ps);
+                u32x4 Bz = lds_ld<u32x4>(bz_var ? vst + bz_rel + 64 * ps : bz_const + 64 * ps);
+                if (nv < PG) Bz &= keep[ps];
                 u32x4 A;
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) A[e2] = as_u32(as_half2(Pp[e2]) * (as_half2(sp[e2]) * sc2));
-                const uint32_t vb = sv + vc_lane + 1024 * ps;
+                for (int e2 = 0; e2 < 4; ++e2) A[e2] = as_u32(as_half2(Pp[e2]) * (as_half2(spv[ps][e2]) * sc2));
+                const uint32_t vb = vst + vc_lane + 1024 * ps;
                 u32x4 X;
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) X[e2] = lds_pair(vb + (2 * e2) * 32, vb + (2 * e2 + 1) * 32);
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const uint32_t lo = lds_ld<uint16_t>(vb + (2 * e2) * 32);
+                    const uint32_t hi = lds_ld<uint16_t>(vb + (2 * e2 + 1) * 32);
+                    X[e2] = lo | (hi << 16);
+                }
                 const half8 Ah = as_half8(A);
                 Oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(Pp), as_half8(Bz), Oz, 0, 0, 0);
                 Oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, M15, Oz, 0, 0, 0);
-                const u32x4 XR = X >> 6;
-                O[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(X & 0x00030003u), O[0], 0, 0, 0);
-                O[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(X & 0x000C000Cu), O[1], 0, 0, 0);
-                O[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(X & 0x00300030u), O[2], 0, 0, 0);
-                O[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(X & 0x00C000C0u), O[3], 0, 0, 0);
-                O[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(X & 0x03000300u), O[4], 0, 0, 0);
-                O[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XR & 0x00300030u), O[5], 0, 0, 0);
-                O[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XR & 0x00C000C0u), O[6], 0, 0, 0);
-                O[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XR & 0x03000300u), O[7], 0, 0, 0);
+                // channel t of each 16-bit word moved to bit 4, 6 or 8 (units 2^-20, 2^-18, 2^-16):
+                // the lowest subnormal positions lose product bits in the MFMA
+                const u32x4 XL = X << 4, XM = X >> 2, XH = X >> 8;
+                O[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XL & 0x00300030u), O[0], 0, 0, 0);
+                O[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XL & 0x00C000C0u), O[1], 0, 0, 0);
+                O[2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XL & 0x03000300u), O[2], 0, 0, 0);
+                O[3] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XM & 0x00300030u), O[3], 0, 0, 0);
+                O[4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XM & 0x00C000C0u), O[4], 0, 0, 0);
+                O[5] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XM & 0x03000300u), O[5], 0, 0, 0);
+                O[6] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XH & 0x00300030u), O[6], 0, 0, 0);
+                O[7] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, as_half8(XH & 0x00C000C0u), O[7], 0, 0, 0);
             }
         }
-        if (nv_s <= 0) continue;
-
-        // ---- logits (log2 units) of 4 tokens: tile ll of this lane, joined with the other limb
-        float x[4];
-        {
-            const u32x2 k0 = lds_ld<u32x2>(sk + Ly::K0 + w * 256 + (64 * hf + tok4) * 2);
+        // ---- this stream's o and l: lanes with ar >> 2 == Gk hold channels 8 ar + t of
+        //      group Gk for heads r = 0..3; columns 4 Gk + c of Oz hold the group's sums
+        float col[4][4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float mine = ll ? Sc[1][r] : Sc[0][r];
-                const float give = ll ? Sc[0][r] : Sc[1][r];
-                float v = __builtin_fmaf(mine + dpp<DPP_XOR1>(give), comp[r], bias);
-                const uint32_t kw = k0[r >> 1];
-                v = __builtin_fmaf(q0c, __uint_as_float((r & 1) ? (kw & 0xFFFF0000u) : (kw << 16)), v);
-                x[r] = (tok4 + r < nv_s) ? v : -__builtin_huge_valf();
-            }
+        for (int r = 0; r < 4; ++r) {
+            col[0][r] = dpp<DPP_QB<0>>(Oz[r]);
+            col[1][r] = dpp<DPP_QB<1>>(Oz[r]);
+            col[2][r] = dpp<DPP_QB<2>>(Oz[r]);
+            col[3][r] = dpp<DPP_QB<3>>(Oz[r]);
         }
-        // ---- integer running maximum of head hh
-        float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        bm = fmaxf(bm, dpp<DPP_XOR1>(bm));
-        bm = fmaxf(bm, dpp<DPP_ROR8>(bm));
-        bm = max_x32(max_x16(bm));
-        const float m_new = fmaxf(m_run, ceilf(bm));
-        if (__builtin_amdgcn_ballot_w64(m_new != m_run)) {  // O holds pages up to u - 1
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // head hh; 0 when m_run = -inf
-            float a[GRP];
-#pragma unroll
-            for (int h = 0; h < GRP; ++h) a[h] = bcast_lane(alpha, 2 * h);  // lane 2h: column (0, h, 0)
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) O[t][r] *= a[r];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Oz[r] *= a[r];
-            l32 *= alpha;
-        }
-        m_run = m_new;
-        // ---- probabilities 2^(x - m + 14) -> fp16 -> this wave's P buffer
-        {
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m_new + (float)PBOOST);
-            l32 += (p[0] + p[1]) + (p[2] + p[3]);
-            half2v h01, h23;
-            h01[0] = (_Float16)p[0];
-            h01[1] = (_Float16)p[1];
-            h23[0] = (_Float16)p[2];
-            h23[1] = (_Float16)p[3];
-            lds_st<u32x2>(pb_w + hh * 144 + tok4 * 2, u32x2{as_u32(h01), as_u32(h23)});
-        }
-    }
-
-    // ---- this wave's partials: lanes with n >> 2 == G hold channels 8n + t of group G
-    //      for heads r = 0..3; columns 4G + c of Oz hold the group's sums
-    float col[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        col[0][r] = dpp<DPP_QB<0>>(Oz[r]);
-        col[1][r] = dpp<DPP_QB<1>>(Oz[r]);
-        col[2][r] = dpp<DPP_QB<2>>(Oz[r]);
-        col[3][r] = dpp<DPP_QB<3>>(Oz[r]);
-    }
-    // l32 of head hh: sum over its 16 lanes (G, tg, ll)
-    float l32h = l32 + dpp<DPP_XOR1>(l32);
-    l32h += dpp<DPP_ROR8>(l32h);
-    l32h = sum_x32(sum_x16(l32h));
-    const float escale = __uint_as_float((uint32_t)(127 + e_run) << 23);
-    __syncthreads();  // every wave is done with the stages: reuse stage 0 for the exchange
-    // exchange: [wave][head][o[128], m, l, l32, pad] floats
-    const uint32_t xw = S + (uint32_t)wv * (GRP * PART_FLOATS * 4);
-    if ((n >> 2) == G) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float o = __builtin_fmaf(escale, __builtin_fmaf(O[t][r], t < 5 ? (16777216.0f / (float)(1u << (2 * t))) : (16777216.0f / (float)(1u << (2 * t - 6))), col[3][r]),
-                                               __builtin_fmaf(1.5f, col[2][r], col[0][r]));
-                lds_st<float>(xw + (r * PART_FLOATS + 8 * n + t) * 4, o);
-            }
-        if (n == 4 * G) {  // one lane per row block: l = sum P (column 1)
+        const float escale = __uint_as_float((uint32_t)(127 + e_run) << 23);
+        __syncthreads();  // every wave is done with the stages: the exchange reuses them
+        if ((ar >> 2) == Gk) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (r == G) lds_st<float>(xw + (r * PART_FLOATS + D + 1) * 4, col[1][r]);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float comp = t % 3 == 0 ? 1048576.0f : t % 3 == 1 ? 262144.0f : 65536.0f;  // 2^20, 2^18, 2^16
+                    const float o = __builtin_fmaf(escale, __builtin_fmaf(O[t][r], comp, col[3][r]),
+                                                   __builtin_fmaf(1.5f, col[2][r], col[0][r]));
+                    lds_st<float>(xw + (r * PART_FLOATS + 8 * ar + t) * 4, o);
+                }
+            if (ar == 4 * Gk) {  // l of head Gk: column (Gk, 1), row (Gk, Gk)
+                const float lg = Gk == 0 ? col[1][0] : Gk == 1 ? col[1][1] : Gk == 2 ? col[1][2] : col[1][3];
+                lds_st<float>(xw + (Gk * PART_FLOATS + D + 1) * 4, lg);
+            }
         }
     }
-    if (lane < 8 && (lane & 1) == 0) {  // lane 2h: column (0, h, 0): m and l32 of head h
-        const int h = lane >> 1;
-        lds_st<float>(xw + (h * PART_FLOATS + D) * 4, m_run);
-        lds_st<float>(xw + (h * PART_FLOATS + D + 2) * 4, l32h);
-    }
     __syncthreads();
-    // combine the eight waves: thread (h, ch)
+    // ---- combine the four page streams: thread (h, ch)
     {
         const int h = tid >> 7, ch = tid & (D - 1);
         float M = -__builtin_huge_valf();
 #pragma unroll
-        for (int v = 0; v < NW; ++v) M = fmaxf(M, lds_ld<float>(S + ((v * GRP + h) * PART_FLOATS + D) * 4));
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, lds_ld<float>(S + ((v * GRP + h) * PART_FLOATS + D) * 4));
         float o = 0.0f, l = 0.0f, l3 = 0.0f;
 #pragma unroll
-        for (int v = 0; v < NW; ++v) {
+        for (int v = 0; v < 4; ++v) {
             const uint32_t base = S + (uint32_t)((v * GRP + h) * PART_FLOATS) * 4;
             const float mv = lds_ld<float>(base + D * 4);
             const float f = mv == -__builtin_huge_valf() ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
@@ -756,24 +848,26 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
 
 }  // namespace
 
-bool use_mfma_decode(int hq, int hkv) { return hkv > 0 && hq == GRP * hkv; }
+bool use_mfma_decode(int hq, int hkv, int n_keep) {
+    return hkv > 0 && hq == GRP * hkv && n_keep <= 16 * MAX_KS;
+}
 
 static int ks_of(int n_keep) {
     const int k = (n_keep + 15) / 16;
-    return k < 1 ? 1 : k > 8 ? 8 : k;
+    return k < 1 ? 1 : k > MAX_KS ? MAX_KS : k;
 }
 
 int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep) {
     (void)n_keep;
     // one 8-wave workgroup per CU (LDS-bound): enough splits to give each of the
-    // 256 CUs one, at least 8 blocks per split; long contexts split so that no
-    // split exceeds 32 blocks (ragged batches stay balanced)
+    // 256 CUs one, at least 4 blocks (32 pages) per split; long contexts split so
+    // that no split exceeds 16 blocks (ragged batches stay balanced)
     const int units = batch * hkv;
-    const int nblk = (max_pages + 3) / 4;
+    const int nblk = (max_pages + KBLK - 1) / KBLK;
     int s = (256 + units - 1) / units;
-    const int cap = (nblk + 7) / 8;
+    const int cap = (nblk + 3) / 4;
     if (s > cap) s = cap;
-    const int need = (nblk + 31) / 32;
+    const int need = (nblk + 15) / 16;
     if (s < need) s = need;
     if (s > nblk) s = nblk;
     return s < 1 ? 1 : s;
@@ -796,8 +890,7 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
         case 4: return launch_ks<4>(a, s);
         case 5: return launch_ks<5>(a, s);
         case 6: return launch_ks<6>(a, s);
-        case 7: return launch_ks<7>(a, s);
-        default: return launch_ks<8>(a, s);
+        default: return launch_ks<7>(a, s);
     }
 }
 

@@ -13,14 +13,14 @@ constexpr int PG = DQK_PAGE;
 constexpr int ROW_BYTES = 32;     // 128 two-bit codes
 constexpr int VGROUPS = 4;        // value groups of 32 channels
 
-// Physical pages come in aligned blocks of four: key rows and key metadata of
-// a channel sit side by side for the block's four pages.
-constexpr int KBLK = 4;
+// Physical pages come in aligned blocks of eight: key rows and key metadata of
+// a channel sit side by side for the block's eight pages.
+constexpr int KBLK = 8;
 
 // Index of the 32-byte key row (and of the (scale, zero) pair) of channel j of
 // physical page p, KV head g.
 __host__ __device__ __forceinline__ size_t krow(int64_t p, int g, int hkv, int j) {
-    return ((((size_t)(p >> 2) * (size_t)hkv + (size_t)g) * D + (size_t)j) * KBLK) + (size_t)(p & 3);
+    return ((((size_t)(p / KBLK) * (size_t)hkv + (size_t)g) * D + (size_t)j) * KBLK) + (size_t)(p % KBLK);
 }
 
 // Partial of one (b, h, split): o[128] (unnormalised, relative to m), m (natural
@@ -142,7 +142,7 @@ int decode_splits_generic(int batch, int hkv, int max_pages);
 hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 
 // MFMA path (group size 4, the GQA 32/8 shape).
-bool use_mfma_decode(int hq, int hkv);
+bool use_mfma_decode(int hq, int hkv, int n_keep);  // n_keep 0: any count it serves
 int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep);  // n_keep 0: the largest
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 

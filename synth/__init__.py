@@ -161,12 +161,13 @@ def make_kv_seq(shape: Shape, seed: int, b: int, outl: Optional[np.ndarray] = No
 def make_page_table(shape: Shape, seed: int):
     """int32 [batch][max_pages] page table (unused slots = -1) and pool size.
 
-    The pool is handed out in aligned blocks of four pages (the cache keeps
-    the key rows of a block's four pages side by side): sequence b gets
-    ceil(pages_b / 4) blocks and its logical page i sits in slot i % 4 of its
-    block i // 4.  ``shuffle_pages`` permutes the blocks of the pool."""
+    The pool is handed out in aligned blocks of eight pages (the cache keeps
+    the key rows of a block's eight pages side by side): sequence b gets
+    ceil(pages_b / 8) blocks and its logical page i sits in slot i % 8 of its
+    block i // 8.  ``shuffle_pages`` permutes the blocks of the pool."""
+    K = 8
     pps = shape.pages_per_seq
-    nblk = [(n + 3) // 4 for n in pps]
+    nblk = [(n + K - 1) // K for n in pps]
     total_blocks = int(sum(nblk))
     blocks = np.arange(total_blocks, dtype=np.int32)
     if shape.shuffle_pages:
@@ -176,9 +177,9 @@ def make_page_table(shape: Shape, seed: int):
     for b, n in enumerate(pps):
         mine = blocks[off:off + nblk[b]]
         i = np.arange(n)
-        pt[b, :n] = 4 * mine[i // 4] + i % 4
+        pt[b, :n] = K * mine[i // K] + i % K
         off += nblk[b]
-    return pt, 4 * total_blocks
+    return pt, K * total_blocks
 
 
 @dataclasses.dataclass

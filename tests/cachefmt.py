@@ -1,9 +1,9 @@
 """Independent numpy reader of the paged INT2 cache format (test helper).
 
-Layout (key rows and key metadata in aligned blocks of four pages; page p is
-slot p & 3 of block p >> 2):
-  k_codes u8 [P/4][Hkv][128 ch][4][32]  token t at byte t>>2, bits 2*(t&3)
-  k_meta f16 [P/4][Hkv][128 ch][4][2]   (scale, zero)
+Layout (key rows and key metadata in aligned blocks of eight pages; page p
+is slot p & 7 of block p >> 3):
+  k_codes u8 [P/8][Hkv][128 ch][8][32]  token t at byte t>>2, bits 2*(t&3)
+  k_meta f16 [P/8][Hkv][128 ch][8][2]   (scale, zero)
   k_ch0 bf16 [P][Hkv][128 tok]
   v_codes u8 [P][Hkv][128 tok][32]  channel c at byte c>>2, bits 2*(c&3)
   v_meta f16 [P][Hkv][2][4][128]    [0]=scale, [1]=zero per (group, token)
@@ -30,7 +30,7 @@ def unpack_rows(rows: np.ndarray) -> np.ndarray:
 
 def k_codes(cache, p, g):
     """codes [128 ch][128 tok]"""
-    return unpack_rows(cache.k_codes[p >> 2, g, :, p & 3])
+    return unpack_rows(cache.k_codes[p >> 3, g, :, p & 7])
 
 
 def v_codes(cache, p, g):
@@ -41,8 +41,8 @@ def v_codes(cache, p, g):
 def decode_k(cache, p, g):
     """Dequantized k' of a page: [128 tok][128 ch] fp32 (channel 0 from bf16)."""
     c = k_codes(cache, p, g).astype(np.float32)            # [ch][tok]
-    s = f16(cache.k_meta[p >> 2, g, :, p & 3, 0])[:, None]
-    z = f16(cache.k_meta[p >> 2, g, :, p & 3, 1])[:, None]
+    s = f16(cache.k_meta[p >> 3, g, :, p & 7, 0])[:, None]
+    z = f16(cache.k_meta[p >> 3, g, :, p & 7, 1])[:, None]
     k = (c * s + z).T.copy()
     k[:, 0] = bf16(cache.k_ch0[p, g])
     return k
