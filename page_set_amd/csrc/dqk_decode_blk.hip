@@ -44,6 +44,7 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int GRP = 4;          // query heads per KV head handled here
 constexpr int NW = 8;           // waves per workgroup: 4 scoring, 4 multiplying
@@ -68,13 +69,15 @@ struct Lay {
     static constexpr int KM = KC + NR * 256;
     static constexpr int K0 = KM + NMR * 32;
     static constexpr int KST = K0 + 2048;
-    // value stage: codes [4 pages][128 tokens][32 B], metadata [4 pages][2 planes][4 groups][128]
-    // fp16 (16-byte chunk c of (page, plane, q) at c ^ q)
+    // value stage: codes [token group G 4][32-token step 4][4 pages][8 tokens][32 B], each
+    // group followed by 64 bytes of padding (the four groups read together fall in
+    // different banks); metadata [4 pages][2 planes][4 groups q][128] fp16 with
+    // 16-byte chunk c of (page, plane, q) at c ^ 4q
     static constexpr int VS = 2 * KST;
     static constexpr int VC = 0;
-    static constexpr int VM = 16384;
-    static constexpr int VST = 24576;
-    static constexpr int PBROW = 272;               // P of one head: 128 fp16 + 16 B of padding
+    static constexpr int VM = 16384 + 3 * 64;
+    static constexpr int VST = VM + 8192;
+    static constexpr int PBROW = 320;               // P of one head: 128 fp16 + 64 B of padding
     static constexpr int PBPAGE = 4 * PBROW;
     static constexpr int PBBUF = 4 * PBPAGE;
     static constexpr int PB = VS + NVST * VST;      // [2 buffers][4 pages][4 heads][PBROW]
@@ -103,6 +106,7 @@ struct Lay {
 __device__ __forceinline__ half8 as_half8(u32x4 v) { return __builtin_bit_cast(half8, v); }
 __device__ __forceinline__ half2v as_half2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
 __device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
@@ -231,17 +235,26 @@ __device__ __forceinline__ uint32_t key_aoff(int idx, int lane, int chan, int hk
     return (uint32_t)(4 * i + (lane >> 4)) * (uint32_t)(hkv * PG * 2) + (uint32_t)((lane & 15) * 16);
 }
 __device__ __forceinline__ int val_region(int idx) { return idx < 16 ? 3 : 4; }
+// Value code instruction idx = 4 G + s: tokens 32 s + 8 G .. + 7 of the half's
+// four pages (16 lanes a page); metadata instruction 16 + j: page j >> 1,
+// plane j & 1.
 template <int KS>
 __device__ __forceinline__ uint32_t val_lds(int idx) {
     using Ly = Lay<KS>;
-    return idx < 16 ? Ly::VC + idx * 1024 : Ly::VM + (idx - 16) * 1024;
+    return idx < 16 ? Ly::VC + idx * 1024 + 64 * (idx >> 2) : Ly::VM + (idx - 16) * 1024;
+}
+__device__ __forceinline__ uint32_t vcode_off(int idx, int lane) {  // within the page
+    return (uint32_t)((32 * (idx & 3) + 8 * (idx >> 2)) * ROW_BYTES + (lane & 15) * 16);
+}
+__device__ __forceinline__ uint32_t vmeta_off(int j, int lane) {  // within the page
+    const int q = lane >> 4;
+    return (uint32_t)((j & 1) * 1024 + q * 256 + (((lane & 15) ^ (4 * q)) * 16));
 }
 // Per-lane byte offset of value instruction idx from the base of an aligned half.
 __device__ __forceinline__ uint32_t val_aoff(int idx, int lane, int hkv) {
-    if (idx < 16) return (uint32_t)(idx >> 2) * (uint32_t)(hkv * PG * ROW_BYTES) + (uint32_t)((idx & 3) * 1024 + lane * 16);
-    const int j = idx - 16, q = lane >> 4;
-    return (uint32_t)(j >> 1) * (uint32_t)(hkv * 2 * VGROUPS * PG * 2) +
-           (uint32_t)((j & 1) * 1024 + q * 256 + (((lane & 15) ^ q) * 16));
+    if (idx < 16) return (uint32_t)(lane >> 4) * (uint32_t)(hkv * PG * ROW_BYTES) + vcode_off(idx, lane);
+    const int j = idx - 16;
+    return (uint32_t)(j >> 1) * (uint32_t)(hkv * 2 * VGROUPS * PG * 2) + vmeta_off(j, lane);
 }
 
 // Base of KV head g's data in region r for aligned block (half) 0, and the
@@ -317,15 +330,13 @@ __device__ __forceinline__ void slow_val(int idx, int lane, const BlockPages &p,
                                          int hkv, uint32_t lds) {
     u32x4 v;
     if (idx < 16) {
-        const int pp = p(4 * hb + (idx >> 2));
-        v = *reinterpret_cast<const u32x4 *>(c.v_codes + ((size_t)pp * hkv + g) * (PG * ROW_BYTES) + (idx & 3) * 1024 +
-                                             lane * 16);
+        const int pp = p(4 * hb + (lane >> 4));
+        v = *reinterpret_cast<const u32x4 *>(c.v_codes + ((size_t)pp * hkv + g) * (PG * ROW_BYTES) + vcode_off(idx, lane));
     } else {
-        const int j = idx - 16, q = lane >> 4;
+        const int j = idx - 16;
         const int pp = p(4 * hb + (j >> 1));
         v = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(c.v_meta) +
-                                             ((size_t)pp * hkv + g) * (2 * VGROUPS * PG * 2) + (j & 1) * 1024 +
-                                             q * 256 + (((lane & 15) ^ q) * 16));
+                                             ((size_t)pp * hkv + g) * (2 * VGROUPS * PG * 2) + vmeta_off(j, lane));
     }
     lds_st<u32x4>(lds + lane * 16, v);
 }
@@ -614,7 +625,7 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const uint32_t lo = lds_ld<uint8_t>(ab + (16 * ks + 2 * e2) * 256);
                     const uint32_t hi = lds_ld<uint8_t>(ab + (16 * ks + 2 * e2 + 1) * 256);
-                    X[e2] = lo | (hi << 16);
+                    X[e2] = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u);  // lo byte -> byte 0, hi byte -> byte 2
                 }
                 const u32x4 Bq = lds_ld<u32x4>(qb_lane + ks * 256);
                 // codes at bits 4..7 of each half (tiles 0, 1 shifted up): units 2^-20, 2^-18
@@ -683,11 +694,14 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
         // ================= multiplying waves: page w of every half, one step behind
         const int q = ar >> 2, hv = ar & 3, cz = ar & 3;  // A row (group q, head hv); Oz column (q, cz)
         const uint32_t pr_lane = S + Ly::PB + (uint32_t)w * Ly::PBPAGE + hv * Ly::PBROW + 16 * Gk;  // + buffer, + 64 ps
-        const uint32_t sp_lane = Ly::VM + (uint32_t)w * 2048 + q * 256 + ((Gk ^ q) * 16);         // + 64 ps
-        const uint32_t bz_rel = cz == 0 ? sp_lane + 1024 : sp_lane;  // zero points / scales
+        // scales of group q, tokens 32 ps + 8 Gk .. + 7: chunk 4 ps + Gk stored at (4 ps + Gk) ^ 4 q
+        uint32_t sp_lane[4];
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps) sp_lane[ps] = Ly::VM + (uint32_t)w * 2048 + q * 256 + 16 * (4 * (ps ^ q) + Gk);
+        const uint32_t bz_plane = cz == 0 ? 1024u : 0u;  // zero points / scales
         const uint32_t bz_const = S + (cz == 1 ? Ly::ONES : Ly::ZERO);
         const bool bz_var = (cz & 1) == 0;
-        const uint32_t vc_lane = Ly::VC + (uint32_t)w * 4096 + (8 * Gk) * 32 + 2 * ar;  // + 1024 ps + 32 e
+        const uint32_t vc_lane = Ly::VC + 4160u * Gk + 256u * w + 2 * ar;  // + 1024 ps + 32 e
         half8 M15;
         {
             const _Float16 m = (_Float16)(cz == 3 ? -1.5f : 0.0f);
@@ -720,7 +734,7 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
             // ---- value-scale exponent of the page; rescale O when it grows
             u32x4 spv[4], keep[4];
 #pragma unroll
-            for (int ps = 0; ps < 4; ++ps) spv[ps] = lds_ld<u32x4>(vst + sp_lane + 64 * ps);
+            for (int ps = 0; ps < 4; ++ps) spv[ps] = lds_ld<u32x4>(vst + sp_lane[ps]);
             if (nv < PG) {  // metadata past the sequence end is unspecified: keep it out of everything
 #pragma unroll
                 for (int ps = 0; ps < 4; ++ps) {
@@ -732,14 +746,15 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                     spv[ps] &= keep[ps];
                 }
             }
-            uint32_t mx = 0;
+            // largest scale of the page: packed 16-bit maxima (scales are >= 0, so their
+            // bit patterns order like their values)
+            u16x2 m2 = as_u16x2(spv[0][0]);
 #pragma unroll
             for (int ps = 0; ps < 4; ++ps)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t xx = spv[ps][e];
-                    mx = max(mx, max(xx & 0xFFFFu, xx >> 16));
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (ps | e) m2 = __builtin_elementwise_max(m2, as_u16x2(spv[ps][e]));
+            uint32_t mx = max((uint32_t)m2[0], (uint32_t)m2[1]);
             mx = max(mx, dpp_u<DPP_ROR4>(mx));
             mx = max(mx, dpp_u<DPP_ROR8>(mx));
             mx = umax_x32(umax_x16(mx));
@@ -752,25 +767,32 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                 if (cz == 3) Oz *= f;
                 e_run = e_pg;
             }
-            const uint32_t sc_h = pow2_h(-e_run);
-            const half2v sc2 = as_half2(sc_h | (sc_h << 16));
+            // scale' = scale * 2^-E (skipped when E = 0)
+            if (e_run != 0) {  // wave-uniform
+                const uint32_t sc_h = pow2_h(-e_run);
+                const half2v sc2 = as_half2(sc_h | (sc_h << 16));
+#pragma unroll
+                for (int ps = 0; ps < 4; ++ps)
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) spv[ps][e2] = as_u32(as_half2(spv[ps][e2]) * sc2);
+            }
             // ---- value products, 32 tokens per step
             const uint32_t prb = pr_lane + (uint32_t)buf * Ly::PBBUF;
 #pragma unroll
             for (int ps = 0; ps < 4; ++ps) {
                 const u32x4 Pp = lds_ld<u32x4>(prb + 64 * ps);
-                u32x4 Bz = lds_ld<u32x4>(bz_var ? vst + bz_rel + 64 * ps : bz_const + 64 * ps);
+                u32x4 Bz = lds_ld<u32x4>(bz_var ? vst + sp_lane[ps] + bz_plane : bz_const + 64 * ps);
                 if (nv < PG) Bz &= keep[ps];
                 u32x4 A;
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) A[e2] = as_u32(as_half2(Pp[e2]) * (as_half2(spv[ps][e2]) * sc2));
+                for (int e2 = 0; e2 < 4; ++e2) A[e2] = as_u32(as_half2(Pp[e2]) * as_half2(spv[ps][e2]));
                 const uint32_t vb = vst + vc_lane + 1024 * ps;
                 u32x4 X;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
                     const uint32_t lo = lds_ld<uint16_t>(vb + (2 * e2) * 32);
                     const uint32_t hi = lds_ld<uint16_t>(vb + (2 * e2 + 1) * 32);
-                    X[e2] = lo | (hi << 16);
+                    X[e2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                 }
                 const half8 Ah = as_half8(A);
                 Oz = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(Pp), as_half8(Bz), Oz, 0, 0, 0);
