@@ -159,6 +159,30 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
                     hipStream_t stream);
 
 /*
+ * dqk_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Allocates nothing (no hipMalloc, no
+ * allocating library call): the split partials live in a 16 MiB device array
+ * inside the library, one per GPU, held until the process ends.  Its address
+ * is looked up on the calling thread's current device (hipGetDevice), which
+ * must be the device of the stream and of every buffer.
+ *   Limit: batch * hq * splits * 528 bytes <= dqk_decode_noalloc_max_bytes()
+ *   (16 MiB), splits as dqk_decode_attn resolves num_splits; larger requests
+ *   return DQK_ERR_WORKSPACE before anything is enqueued.
+ *   Calls that overlap on one GPU (different streams, or different host
+ *   threads) share that array and race; serialize them.  Every call rewrites
+ *   all the partials it reads, so nothing has to be cleared between calls.
+ * Arguments, results and other errors as dqk_decode_attn.
+ */
+int dqk_decode_attn_noalloc(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
+                            int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                            const int32_t *seq_lens, float sm_scale, int32_t num_splits, float *out, float *lse,
+                            hipStream_t stream);
+
+/* Size of the partials array dqk_decode_attn_noalloc uses (bytes). */
+size_t dqk_decode_noalloc_max_bytes(void);
+
+/*
  * Unpruned BF16 decode attention, the baseline the paper's throughput is
  * measured against (§4.4): softmax(q k^T * sm_scale) v in original
  * coordinates, no transform.

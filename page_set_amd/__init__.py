@@ -61,6 +61,11 @@ def lib():
         L.dqk_decode_attn.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, P, i32, P, ctypes.c_float, i32,
                                       P, sz, P, P, P]
         L.dqk_decode_attn.restype = ctypes.c_int
+        L.dqk_decode_attn_noalloc.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, P, i32, P,
+                                              ctypes.c_float, i32, P, P, P]
+        L.dqk_decode_attn_noalloc.restype = ctypes.c_int
+        L.dqk_decode_noalloc_max_bytes.argtypes = []
+        L.dqk_decode_noalloc_max_bytes.restype = sz
         L.dqk_decode_attn_bf16.argtypes = [P, P, i32, i32, P, i32, i32, P, i32, P, ctypes.c_float, i32, P, sz, P, P,
                                            P]
         L.dqk_decode_attn_bf16.restype = ctypes.c_int
@@ -171,6 +176,28 @@ def dqk_decode_attn(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_sca
                                max_pages, _ptr(seq_lens), float(sm_scale), int(num_splits), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream))
     _check(rc, "dqk_decode_attn")
+    return out, lse
+
+
+def dqk_decode_attn_noalloc(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_scale: float,
+                            num_splits: int = 0, out=None, lse=None, want_lse: bool = True, stream=None):
+    """dqk_decode_attn through the entry point that allocates nothing on the
+    device (its partials live in the library's own scratch array); out / lse
+    are allocated here only when not given."""
+    import torch
+    B, hq = int(q_prime.shape[0]), int(q_prime.shape[1])
+    n_keep = int(sel_idx.shape[2])
+    max_pages = int(page_table.shape[1])
+    dev = q_prime.device
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    s = cache.struct()
+    rc = lib().dqk_decode_attn_noalloc(ctypes.byref(s), _ptr(q_prime), _ptr(sel_idx), n_keep, B, hq, _ptr(page_table),
+                                       max_pages, _ptr(seq_lens), float(sm_scale), int(num_splits), _ptr(out),
+                                       _ptr(lse), _stream(stream))
+    _check(rc, "dqk_decode_attn_noalloc")
     return out, lse
 
 

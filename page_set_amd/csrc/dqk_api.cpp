@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dqk_internal.h"
 
 namespace {
@@ -34,6 +36,34 @@ int resolve_splits(int batch, int hq, int hkv, int max_pages, int num_splits, in
     if (num_splits > 0) return num_splits;
     if (dqk::use_mfma_decode(hq, hkv, n_keep)) return dqk::decode_splits_mfma(batch, hkv, max_pages, n_keep);
     return dqk::decode_splits_generic(batch, hkv, max_pages);
+}
+
+// ---- scratch of the entry point that allocates nothing: split partials in a
+//      file-scope device array (each GPU the library runs on holds its own copy
+//      until the process ends); host code uses only the address
+//      hipGetSymbolAddress returns for the current device, never the name.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+__device__ __align__(256) float scratch[NOALLOC_SCRATCH_BYTES / sizeof(float)];
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[NOALLOC_MAX_DEVICES];
+
+// Device address of `scratch` on the current device, looked up once per device.
+int scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return DQK_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e);
+        if (!p) return DQK_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DQK_OK;
 }
 
 }  // namespace
@@ -123,6 +153,29 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
     if (e != hipSuccess) return hip_status(e);
     return hip_status(dqk::launch_merge(a.partials, batch, hq, splits, out, lse, stream));
 }
+
+int dqk_decode_attn_noalloc(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
+                            int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                            const int32_t *seq_lens, float sm_scale, int32_t num_splits, float *out, float *lse,
+                            hipStream_t stream) {
+    // the checks dqk_decode_attn repeats, here so that the partials' size is
+    // known (and rejected when too large) before any HIP call
+    int st = check_cache(c);
+    if (st) return st;
+    const int hkv = c->num_kv_heads;
+    if (batch < 1 || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM || max_pages < 1 ||
+        num_splits < 0 || num_splits > max_pages)
+        return DQK_ERR_SHAPE;
+    const int splits = resolve_splits(batch, hq, hkv, max_pages, num_splits, n_keep);
+    if ((size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float) > NOALLOC_SCRATCH_BYTES) return DQK_ERR_WORKSPACE;
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st) return st;
+    return dqk_decode_attn(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale,
+                           num_splits, ws, NOALLOC_SCRATCH_BYTES, out, lse, stream);
+}
+
+size_t dqk_decode_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
 
 int dqk_decode_attn_bf16(const void *k_pages, const void *v_pages, int32_t hkv, int32_t num_pages,
                          const void *q_bf16, int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,

@@ -77,7 +77,7 @@ def test_decode_validation():
     assert _dec(nk=0) == pa.DQK_ERR_SHAPE
     assert _dec(ns=17) == pa.DQK_ERR_SHAPE
     assert _dec(c=_cache(num_kv_heads=0)) == pa.DQK_ERR_SHAPE
-    assert _dec(c=_cache(num_pages=62)) == pa.DQK_ERR_SHAPE        # the pool is whole 4-page blocks
+    assert _dec(c=_cache(num_pages=60)) == pa.DQK_ERR_SHAPE        # the pool is whole 8-page blocks
     assert _dec(hq=8 * 32) == pa.DQK_ERR_UNSUPPORTED          # group of 32 query heads
     assert _dec(c=_cache(v_meta=4096 + 2)) == pa.DQK_ERR_ALIGN
     assert _dec(lse=MIS) == pa.DQK_ERR_ALIGN
@@ -137,3 +137,22 @@ def test_stream_read_validation():
     assert L.dqk_stream_read(A, 0, A, None) == pa.DQK_ERR_SHAPE
     assert L.dqk_stream_read(A, 16384 + 16, A, None) == pa.DQK_ERR_SHAPE
     assert L.dqk_stream_read(MIS, 16384, A, None) == pa.DQK_ERR_ALIGN
+
+
+def _noalloc(c=None, **kw):
+    c = c or _cache()
+    a = dict(qp=A, sel=A, nk=77, B=4, hq=32, pt=A, mp=16, sl=A, sm=0.088, ns=0, out=A, lse=None)
+    a.update(kw)
+    return pa.lib().dqk_decode_attn_noalloc(ctypes.byref(c), a["qp"], a["sel"], a["nk"], a["B"], a["hq"], a["pt"],
+                                            a["mp"], a["sl"], a["sm"], a["ns"], a["out"], a["lse"], None)
+
+
+def test_noalloc_validation_before_any_device_call():
+    """Shape errors and partials beyond the library's 16 MiB array are
+    reported on the host, before the array's address is looked up."""
+    assert pa.lib().dqk_decode_noalloc_max_bytes() == 16 << 20
+    assert _noalloc(c=_cache(k_codes=None)) == pa.DQK_ERR_NULL
+    assert _noalloc(hq=30) == pa.DQK_ERR_SHAPE
+    assert _noalloc(ns=17) == pa.DQK_ERR_SHAPE
+    # 64 sequences x 64 heads x 16 splits x 528 bytes = 33 MiB of partials
+    assert _noalloc(c=pa.dqk_cache(16, 64, 4096, 4096, 4096, 4096, 4096), B=64, hq=64, ns=16) == pa.DQK_ERR_WORKSPACE
