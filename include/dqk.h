@@ -159,6 +159,21 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
                     hipStream_t stream);
 
 /*
+ * dqk_select_channels followed by dqk_decode_attn, as one call: for the
+ * group-4 MFMA decode (Hq = 4 Hkv, 17 <= n_keep <= 112) the selection runs in
+ * the decode kernel's prologue, one launch instead of two; otherwise the two
+ * calls are made in sequence.  Results are identical to the two calls
+ * (q_prime and sel_idx bit for bit, then the same decode).
+ *   q_bf16, t_q          as dqk_select_channels.
+ *   q_prime, sel_idx     outputs as dqk_select_channels (required).
+ * Other arguments, workspace size and errors as dqk_decode_attn.
+ */
+int dqk_select_decode_attn(const dqk_cache *c, const void *q_bf16, const float *t_q, int32_t n_keep, int32_t batch,
+                           int32_t hq, const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                           float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
+                           float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream);
+
+/*
  * dqk_decode_attn without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation.  Allocates nothing (no hipMalloc, no

@@ -154,6 +154,41 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
     return hip_status(dqk::launch_merge(a.partials, batch, hq, splits, out, lse, stream));
 }
 
+int dqk_select_decode_attn(const dqk_cache *c, const void *q_bf16, const float *t_q, int32_t n_keep, int32_t batch,
+                           int32_t hq, const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                           float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
+                           float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!q_bf16 || !t_q || !page_table || !seq_lens || !workspace || !out || !q_prime || !sel_idx) return DQK_ERR_NULL;
+    const int hkv = c->num_kv_heads;
+    if (batch < 1 || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM || max_pages < 1 ||
+        num_splits < 0 || num_splits > max_pages)
+        return DQK_ERR_SHAPE;
+    if (!dqk::fused_select_ok(hq, hkv, n_keep)) {  // two launches: selection, then decode
+        st = dqk_select_channels(q_bf16, t_q, batch, hq, hkv, n_keep, q_prime, sel_idx, stream);
+        if (st) return st;
+        return dqk_decode_attn(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale,
+                               num_splits, workspace, ws_bytes, out, lse, stream);
+    }
+    if ((int64_t)batch * hkv > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(q_bf16) || !aligned16(t_q) || !aligned16(q_prime) || !aligned16(sel_idx) ||
+        !aligned16(page_table) || !aligned16(seq_lens) || !aligned16(workspace) || !aligned16(out) ||
+        (lse && !aligned16(lse)))
+        return DQK_ERR_ALIGN;
+    const int splits = resolve_splits(batch, hq, hkv, max_pages, num_splits, n_keep);
+    if (ws_bytes < (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float)) return DQK_ERR_WORKSPACE;
+    dqk::DecodeArgs a{c,         nullptr,  nullptr, n_keep, batch,  hq, hkv, page_table, max_pages, seq_lens,
+                      sm_scale, splits, static_cast<float *>(workspace), out, lse};
+    a.q_bf16 = static_cast<const uint16_t *>(q_bf16);
+    a.t_q = t_q;
+    a.qp_out = q_prime;
+    a.sel_out = sel_idx;
+    hipError_t e = dqk::launch_decode_mfma(a, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(dqk::launch_merge(a.partials, batch, hq, splits, out, lse, stream));
+}
+
 int dqk_decode_attn_noalloc(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
                             int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
                             const int32_t *seq_lens, float sm_scale, int32_t num_splits, float *out, float *lse,

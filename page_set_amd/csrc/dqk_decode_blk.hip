@@ -47,7 +47,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int GRP = 4;          // query heads per KV head handled here
-constexpr int NW = 8;           // waves per workgroup: 4 scoring, 4 multiplying
+constexpr int NW = 12;          // waves per workgroup: 4 scoring, 8 multiplying (two per page)
 constexpr int NTHR = 64 * NW;
 constexpr int NVST = 3;         // value stages
 constexpr int PBOOST = 14;      // probabilities are kept as 2^(x - m + 14)
@@ -86,19 +86,32 @@ struct Lay {
     static constexpr int ZERO = QT + 4 * KS * 256;  // KS * 256 bytes of zeros
     static constexpr int ONES = ZERO + KS * 256;    // 256 bytes of fp16 1.0
     static constexpr int TOTAL = ONES + 256;
+    // the selection run inside the decode (prologue only): T_Q of the KV head
+    // [128][128] fp32 at 0, the four heads' q in fp32, the pooled energies and
+    // a ballot word after it; q' and the selected channels go to the usual
+    // scratch in value stage 2, which lies past all of them
+    static constexpr int SCR = VS + 2 * VST;
+    static constexpr int FT = 0;
+    static constexpr int FQ = D * D * 4;
+    static constexpr int FS = FQ + GRP * D * 4;
+    static constexpr int FM = FS + D * 4;
+    static constexpr bool FUSABLE = FM + 16 <= SCR && FM + 16 <= TOTAL;
+    // the values of the first half can load during the selection (their stage lies past it)
+    static constexpr bool EARLY_V = FM + 16 <= VS + VST;
     // global -> LDS loads: a key block is NRI row, NMI metadata and 2 channel-0
     // instructions; a value half is 16 code and 8 metadata instructions
     static constexpr int NRI = NR / 4;
     static constexpr int NMI = NMR / 32;
     static constexpr int NKI = NRI + NMI + 2;
     static constexpr int KN = (NKI + NW - 1) / NW;  // key instructions per wave per block
-    static constexpr int VN = 3;                    // value instructions per wave per half
+    static constexpr int VN = 24 / NW;              // value instructions per wave per half
+    static_assert(24 % NW == 0, "value loads split evenly");
     static_assert(TOTAL <= 160 * 1024, "LDS");
     static_assert(KST % 16 == 0 && KM % 16 == 0 && K0 % 16 == 0 && VS % 16 == 0 && PB % 16 == 0 &&
                       QT % 16 == 0 && ZERO % 16 == 0 && ONES % 16 == 0,
                   "align");
     static_assert(KN + VN <= 63, "vmcnt range");
-    static_assert(4 * GRP * PART_FLOATS * 4 <= PB, "exchange area");
+    static_assert(8 * GRP * PART_FLOATS * 4 <= PB, "exchange area");
     static_assert(GRP * D * 4 + D * 4 <= VST, "prologue scratch");
 };
 
@@ -367,22 +380,14 @@ struct Feeder {
     uint64_t kbase[Ly::KN], kstr[Ly::KN], vbase[Ly::VN], vstr[Ly::VN];
 
     __device__ __forceinline__ uint32_t kstage(int j) const { return S + (uint32_t)(j & 1) * Ly::KST; }
-    __device__ __forceinline__ uint32_t vstage(int u) const { return S + Ly::VS + (uint32_t)(u % NVST) * Ly::VST; }
+    // half u -> value stage (u + 1) % 3: half 0 in stage 1, clear of the prologue's scratch areas
+    __device__ __forceinline__ uint32_t vstage(int u) const { return S + Ly::VS + (uint32_t)((u + 1) % NVST) * Ly::VST; }
     __device__ __forceinline__ int blk_of(int j) const {
         return j < TABN ? __builtin_amdgcn_readlane(tab, j)
                         : __builtin_amdgcn_readfirstlane(block_aligned(ptab, B0 + j, npages));
     }
-    // Plans from the selected channels (chan_of: key row slot -> channel).
-    template <typename ChanOf>
-    __device__ __forceinline__ void plan(ChanOf chan_of) {
-#pragma unroll
-        for (int k = 0; k < Ly::KN; ++k) {
-            kidx[k] = __builtin_amdgcn_readfirstlane((wv + NW * k) % Ly::NKI);
-            kchan[k] = chan_of(key_row<KS>(kidx[k], lane));
-            kaoff[k] = key_aoff<KS>(kidx[k], lane, kchan[k], hkv);
-            kbase[k] = uniform64(region_base(*c, key_region<KS>(kidx[k]), g));
-            kstr[k] = uniform64(region_stride(key_region<KS>(kidx[k]), hkv));
-        }
+    // Value plans and the alignment table (independent of the selected channels).
+    __device__ __forceinline__ void plan_vals() {
 #pragma unroll
         for (int k = 0; k < Ly::VN; ++k) {
             const int idx = wv + NW * k;
@@ -393,6 +398,18 @@ struct Feeder {
         tab = -1;
         if (lane < min(nb, TABN)) tab = block_aligned(ptab, B0 + lane, npages);
         pend = 0;
+    }
+    // Key plans from the selected channels (chan_of: key row slot -> channel).
+    template <typename ChanOf>
+    __device__ __forceinline__ void plan_keys(ChanOf chan_of) {
+#pragma unroll
+        for (int k = 0; k < Ly::KN; ++k) {
+            kidx[k] = __builtin_amdgcn_readfirstlane((wv + NW * k) % Ly::NKI);
+            kchan[k] = chan_of(key_row<KS>(kidx[k], lane));
+            kaoff[k] = key_aoff<KS>(kidx[k], lane, kchan[k], hkv);
+            kbase[k] = uniform64(region_base(*c, key_region<KS>(kidx[k]), g));
+            kstr[k] = uniform64(region_stride(key_region<KS>(kidx[k]), hkv));
+        }
     }
     // Loads of block j's keys / half u's values; true when the block took the
     // register path (which leaves no load of this wave in flight).
@@ -447,12 +464,96 @@ struct Feeder {
 };
 
 // ---------------------------------------------------------------- the kernel
+// The channel selection of one (sequence, KV head), as dqk_select_channels
+// computes it (the same fp32 fma chains in the same order, the same rank
+// rule), into the LDS scratch the decode prologue reads: q' [4][128] at scr,
+// the ascending channel list after it.  qp_out / sel_out (may be null)
+// receive the same values in global memory.
 template <int KS>
+__device__ __forceinline__ void select_into_lds(uint32_t S, uint32_t scr, const uint16_t *__restrict__ q_bf16,
+                                                const float *__restrict__ t_q, int b, int g, int hq, int hkv,
+                                                int n_keep, float *__restrict__ qp_out, int32_t *__restrict__ sel_out) {
+    using Ly = Lay<KS>;
+    const int tid = threadIdx.x;
+    // every load of the transform is issued before any is stored
+    const u32x4 *tsrc = reinterpret_cast<const u32x4 *>(t_q + (size_t)g * D * D);
+    constexpr int NT = (D * D / 4 + NTHR - 1) / NTHR;
+    u32x4 tv[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const int i = tid + k * NTHR;
+        if (i < D * D / 4) tv[k] = tsrc[i];
+    }
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const int i = tid + k * NTHR;
+        if (i < D * D / 4) lds_st<u32x4>(S + Ly::FT + i * 16, tv[k]);
+    }
+    const uint16_t *qg = q_bf16 + ((size_t)b * hq + (size_t)g * GRP) * D;
+    for (int i = tid; i < GRP * D; i += NTHR) lds_st<float>(S + Ly::FQ + i * 4, bf2f(qg[i]));
+    if (tid < D) lds_st<int32_t>(scr + GRP * D * 4 + tid * 4, 0);
+    __syncthreads();
+    // q'_{h,j}: fma chain over ascending input channel i
+    if (tid < GRP * D) {
+        const int h = tid >> 7, j = tid & (D - 1);
+        float acc = 0.0f;
+#pragma unroll 4
+        for (int i = 0; i < D; i += 4) {
+            const f32x4 qv4 = lds_ld<f32x4>(S + Ly::FQ + (h * D + i) * 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc = __builtin_fmaf(qv4[k], lds_ld<float>(S + Ly::FT + ((i + k) * D + j) * 4), acc);
+        }
+        lds_st<float>(scr + (h * D + j) * 4, acc);
+        if (qp_out) qp_out[((size_t)b * hq + (size_t)g * GRP + h) * D + j] = acc;
+    }
+    __syncthreads();
+    // pooled energy S_j: fma chain over ascending head
+    if (tid < D) {
+        float e = 0.0f;
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) {
+            const float v = lds_ld<float>(scr + (h * D + tid) * 4);
+            e = __builtin_fmaf(v, v, e);
+        }
+        lds_st<float>(S + Ly::FS + tid * 4, e);
+    }
+    __syncthreads();
+    // channel j is kept iff fewer than n_keep channels beat it (larger S, or equal S at a lower index)
+    bool keep = false;
+    if (tid < D) {
+        const float e = lds_ld<float>(S + Ly::FS + tid * 4);
+        int rank = 0;
+#pragma unroll
+        for (int jj = 0; jj < D; jj += 4) {
+            const f32x4 o = lds_ld<f32x4>(S + Ly::FS + jj * 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rank += (o[k] > e) | ((o[k] == e) & (jj + k < tid));
+        }
+        keep = rank < n_keep;
+    }
+    const unsigned long long m = __ballot(keep);  // waves 0, 1: channels 0..63, 64..127
+    if (tid == 0) lds_st<unsigned long long>(S + Ly::FM, m);
+    __syncthreads();
+    if (tid < D && keep) {
+        const int ln = tid & 63;
+        const unsigned long long below = ln ? (m & ((1ull << ln) - 1ull)) : 0ull;
+        const int pos = __popcll(below) + (tid >= 64 ? __popcll(lds_ld<unsigned long long>(S + Ly::FM)) : 0);
+        if (pos < n_keep) {
+            lds_st<int32_t>(scr + GRP * D * 4 + pos * 4, tid);
+            if (sel_out) sel_out[((size_t)b * hkv + g) * n_keep + pos] = tid;
+        }
+    }
+}
+
+template <int KS, bool FUSED>
 __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const float *__restrict__ q_prime,
                                                           const int32_t *__restrict__ sel_idx, int n_keep, int hq,
                                                           const int32_t *__restrict__ page_table, int max_pages,
                                                           const int32_t *__restrict__ seq_lens, float sm_scale,
-                                                          int nsplit, float *__restrict__ partials) {
+                                                          int nsplit, float *__restrict__ partials,
+                                                          const uint16_t *__restrict__ q_bf16,
+                                                          const float *__restrict__ t_q, float *__restrict__ qp_out,
+                                                          int32_t *__restrict__ sel_out) {
     using Ly = Lay<KS>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[Ly::TOTAL];
     const uint32_t S = lds_addr(smem);
@@ -461,7 +562,9 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const int hkv = c.num_kv_heads;
     const int b = bg / hkv, g = bg - b * hkv;
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int w = wv & 3;  // page of the half this wave scores (waves 0-3) or multiplies (waves 4-7)
+    // page of the half this wave scores (waves 0-3) or multiplies (waves 4-11, token half th)
+    const int w = wv < 4 ? wv : (wv - 4) & 3;
+    const int th = wv < 4 ? 0 : (wv - 4) >> 2;
     const int L = seq_lens[b];
     const int npages = (L + PG - 1) / PG;
     const int nblk = (npages + KBLK - 1) / KBLK;
@@ -473,7 +576,11 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     float *part_base = partials + (((size_t)b * hq + (size_t)g * GRP) * nsplit + split) * PART_FLOATS;
     const size_t hstride = (size_t)nsplit * PART_FLOATS;
 
+    if (FUSED && nb <= 0 && split == 0) {  // still deliver the selection of this (sequence, KV head)
+        select_into_lds<KS>(S, S + Ly::SCR, q_bf16, t_q, b, g, hq, hkv, n_keep, qp_out, sel_out);
+    }
     if (nb <= 0) {  // nothing of this sequence falls in this split: an empty partial
+        if (tid >= GRP * D) return;
         const int h = tid >> 7, ch = tid & (D - 1);
         part_base[h * hstride + ch] = 0.0f;
         if (ch == 0) {
@@ -486,9 +593,32 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     // valid tokens of page slot ps of block j (relative to B0)
     auto page_valid = [&](int j, int ps) { return min(PG, max(0, L - PG * (KBLK * (B0 + j) + ps))); };
 
-    // ---- q' of the four heads and the selected channels into LDS (value stage 2, first loaded at step 1)
-    const uint32_t scr = S + Ly::VS + 2 * Ly::VST;
-    {
+    // ---- the loader: value plans first (they do not depend on the selection)
+    Feeder<KS> fd;
+    fd.S = S;
+    fd.c = &c;
+    fd.ptab = ptab;
+    fd.g = g;
+    fd.hkv = hkv;
+    fd.lane = lane;
+    fd.wv = wv;
+    fd.npages = npages;
+    fd.B0 = B0;
+    fd.nb = nb;
+    fd.nst = nst;
+    fd.plan_vals();
+    constexpr bool early_v = FUSED && Ly::EARLY_V;
+    if constexpr (early_v) fd.issue_vals(0);  // in flight while the selection runs
+
+    // ---- q' of the four heads and the selected channels into LDS (value stage 2)
+    const uint32_t scr = S + Ly::SCR;
+    if constexpr (FUSED) {
+        static_assert(Ly::FUSABLE, "selection scratch");
+        select_into_lds<KS>(S, scr, q_bf16, t_q, b, g, hq, hkv, n_keep, split == 0 ? qp_out : nullptr,
+                            split == 0 ? sel_out : nullptr);
+        for (int i = tid; i < KS * 64; i += NTHR) lds_st<uint32_t>(S + Ly::ZERO + i * 4, 0u);
+        if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
+    } else {
         const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q_prime + ((size_t)b * hq + (size_t)g * GRP) * D);
         const int32_t *ssrc = sel_idx + ((size_t)b * hkv + g) * n_keep;
         if (tid < 128) lds_st<u32x4>(scr + tid * 16, qsrc[tid]);
@@ -502,23 +632,9 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const int R = n_keep - has0;                                 // selected INT2 channels
     // channel of key row slot r (slots past R read channel 0's all-zero row)
     auto chan_of = [&](int r) { return r < R ? lds_ld<int32_t>(scr + GRP * D * 4 + (r + has0) * 4) : 0; };
-
-    // ---- load plans, the same for every block: key instructions wv + 8k (a
-    //      wave past the end repeats a real load: same bytes, same place) and
-    //      value instructions wv + 8k
-    Feeder<KS> fd;
-    fd.S = S;
-    fd.c = &c;
-    fd.ptab = ptab;
-    fd.g = g;
-    fd.hkv = hkv;
-    fd.lane = lane;
-    fd.wv = wv;
-    fd.npages = npages;
-    fd.B0 = B0;
-    fd.nb = nb;
-    fd.nst = nst;
-    fd.plan(chan_of);
+    // key load plans, the same for every block: key instructions wv + 12k (a
+    // wave past the end repeats a real load: same bytes, same place)
+    fd.plan_keys(chan_of);
     auto halfpages = [&](int u) { return page_valid(u >> 1, 4 * (u & 1)) > 0; };
 
     // ---- per-lane constants of both roles (q' products from the scratch)
@@ -540,9 +656,10 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
 
     // ---- prologue loads: keys of block 0, values of half 0
     fd.issue_keys(0);
-    fd.issue_vals(0);
+    if constexpr (!early_v) fd.issue_vals(0);
 
-    const uint32_t xw = S + (uint32_t)w * (GRP * PART_FLOATS * 4);  // this page stream's exchange slot
+    // exchange slots [4 page streams][2 token halves][4 heads][PART_FLOATS]
+    const uint32_t xw = S + (uint32_t)(2 * w + th) * (GRP * PART_FLOATS * 4);
     if (wv < 4) {
         // ================= scoring waves: page w of every half
         const int tga = Gk >> 1, cs8 = Gk & 1;        // A: token group and channel half of the k-chunk
@@ -691,17 +808,19 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
             lds_st<float>(xw + (hh * PART_FLOATS + D + 2) * 4, l32h);
         }
     } else {
-        // ================= multiplying waves: page w of every half, one step behind
+        // ================= multiplying waves: tokens 64 th .. 64 th + 63 of page w of every
+        //                   half, one step behind (32-token steps ps = 2 th, 2 th + 1)
         const int q = ar >> 2, hv = ar & 3, cz = ar & 3;  // A row (group q, head hv); Oz column (q, cz)
-        const uint32_t pr_lane = S + Ly::PB + (uint32_t)w * Ly::PBPAGE + hv * Ly::PBROW + 16 * Gk;  // + buffer, + 64 ps
+        const uint32_t pr_lane = S + Ly::PB + (uint32_t)w * Ly::PBPAGE + hv * Ly::PBROW + 16 * Gk + 128 * th;
         // scales of group q, tokens 32 ps + 8 Gk .. + 7: chunk 4 ps + Gk stored at (4 ps + Gk) ^ 4 q
-        uint32_t sp_lane[4];
+        uint32_t sp_lane[2];
 #pragma unroll
-        for (int ps = 0; ps < 4; ++ps) sp_lane[ps] = Ly::VM + (uint32_t)w * 2048 + q * 256 + 16 * (4 * (ps ^ q) + Gk);
+        for (int j = 0; j < 2; ++j)
+            sp_lane[j] = Ly::VM + (uint32_t)w * 2048 + q * 256 + 16 * (4 * ((2 * th + j) ^ q) + Gk);
         const uint32_t bz_plane = cz == 0 ? 1024u : 0u;  // zero points / scales
         const uint32_t bz_const = S + (cz == 1 ? Ly::ONES : Ly::ZERO);
         const bool bz_var = (cz & 1) == 0;
-        const uint32_t vc_lane = Ly::VC + 4160u * Gk + 256u * w + 2 * ar;  // + 1024 ps + 32 e
+        const uint32_t vc_lane = Ly::VC + 4160u * Gk + 256u * w + 2 * ar + 2048u * th;  // + 1024 j + 32 e
         half8 M15;
         {
             const _Float16 m = (_Float16)(cz == 3 ? -1.5f : 0.0f);
@@ -717,11 +836,11 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
             fd.top(u, halfpages);
             if (u < 1) continue;
             const int uu = u - 1;
-            const int nv = page_valid(uu >> 1, 4 * (uu & 1) + w);
-            if (nv <= 0) continue;
-            const uint32_t vst = fd.vstage(uu);
+            const int nvp = page_valid(uu >> 1, 4 * (uu & 1) + w);  // valid tokens of the page
+            if (nvp <= 0) continue;                                    // not scored either
             const int buf = uu & 1;
-            // ---- softmax rescale of what this stream holds
+            // ---- softmax rescale of what this stream holds (also when this half holds
+            //      no token of the page: the scoring wave may have raised the maximum)
             const f32x4 al = lds_ld<f32x4>(S + Ly::AL + (uint32_t)((buf * 16 + w * 4) * 4));
             if (al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) {  // wave-uniform
 #pragma unroll
@@ -731,34 +850,37 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Oz[r] *= al[r];
             }
-            // ---- value-scale exponent of the page; rescale O when it grows
-            u32x4 spv[4], keep[4];
+            const int nv = nvp - 64 * th;  // valid tokens of this half
+            if (nv <= 0) continue;
+            const uint32_t vst = fd.vstage(uu);
+            // ---- value-scale exponent of these tokens; rescale O when it grows
+            u32x4 spv[2], keep[2];
 #pragma unroll
-            for (int ps = 0; ps < 4; ++ps) spv[ps] = lds_ld<u32x4>(vst + sp_lane[ps]);
-            if (nv < PG) {  // metadata past the sequence end is unspecified: keep it out of everything
+            for (int j = 0; j < 2; ++j) spv[j] = lds_ld<u32x4>(vst + sp_lane[j]);
+            if (nv < 64) {  // metadata past the sequence end is unspecified: keep it out of everything
 #pragma unroll
-                for (int ps = 0; ps < 4; ++ps) {
+                for (int j = 0; j < 2; ++j) {
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2) {
-                        const int t = 32 * ps + 8 * Gk + 2 * e2;
-                        keep[ps][e2] = (t < nv ? 0x0000FFFFu : 0u) | (t + 1 < nv ? 0xFFFF0000u : 0u);
+                        const int t = 32 * j + 8 * Gk + 2 * e2;
+                        keep[j][e2] = (t < nv ? 0x0000FFFFu : 0u) | (t + 1 < nv ? 0xFFFF0000u : 0u);
                     }
-                    spv[ps] &= keep[ps];
+                    spv[j] &= keep[j];
                 }
             }
-            // largest scale of the page: packed 16-bit maxima (scales are >= 0, so their
-            // bit patterns order like their values)
-            u16x2 m2 = as_u16x2(spv[0][0]);
+            // largest scale: packed 16-bit maxima (scales are >= 0, so their bit
+            // patterns order like their values), as a tree
+            u16x2 m2[4];
 #pragma unroll
-            for (int ps = 0; ps < 4; ++ps)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (ps | e) m2 = __builtin_elementwise_max(m2, as_u16x2(spv[ps][e]));
-            uint32_t mx = max((uint32_t)m2[0], (uint32_t)m2[1]);
+            for (int e = 0; e < 4; ++e) m2[e] = __builtin_elementwise_max(as_u16x2(spv[0][e]), as_u16x2(spv[1][e]));
+            m2[0] = __builtin_elementwise_max(m2[0], m2[1]);
+            m2[2] = __builtin_elementwise_max(m2[2], m2[3]);
+            m2[0] = __builtin_elementwise_max(m2[0], m2[2]);
+            uint32_t mx = max((uint32_t)m2[0][0], (uint32_t)m2[0][1]);
             mx = max(mx, dpp_u<DPP_ROR4>(mx));
             mx = max(mx, dpp_u<DPP_ROR8>(mx));
             mx = umax_x32(umax_x16(mx));
-            const int ex = (int)((mx >> 10) & 31u);
+            const int ex = __builtin_amdgcn_readfirstlane((int)((mx >> 10) & 31u));
             const int e_pg = min(EMAX, max(EMIN, ex == 0 ? EMIN : ex - 15));
             if (e_pg > e_run) {  // wave-uniform
                 const float f = __uint_as_float((uint32_t)(127 + e_run - e_pg) << 23);
@@ -772,21 +894,21 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                 const uint32_t sc_h = pow2_h(-e_run);
                 const half2v sc2 = as_half2(sc_h | (sc_h << 16));
 #pragma unroll
-                for (int ps = 0; ps < 4; ++ps)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) spv[ps][e2] = as_u32(as_half2(spv[ps][e2]) * sc2);
+                    for (int e2 = 0; e2 < 4; ++e2) spv[j][e2] = as_u32(as_half2(spv[j][e2]) * sc2);
             }
             // ---- value products, 32 tokens per step
             const uint32_t prb = pr_lane + (uint32_t)buf * Ly::PBBUF;
 #pragma unroll
-            for (int ps = 0; ps < 4; ++ps) {
-                const u32x4 Pp = lds_ld<u32x4>(prb + 64 * ps);
-                u32x4 Bz = lds_ld<u32x4>(bz_var ? vst + sp_lane[ps] + bz_plane : bz_const + 64 * ps);
-                if (nv < PG) Bz &= keep[ps];
+            for (int j = 0; j < 2; ++j) {
+                const u32x4 Pp = lds_ld<u32x4>(prb + 64 * j);
+                u32x4 Bz = lds_ld<u32x4>(bz_var ? vst + sp_lane[j] + bz_plane : bz_const + 64 * j);
+                if (nv < 64) Bz &= keep[j];
                 u32x4 A;
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) A[e2] = as_u32(as_half2(Pp[e2]) * as_half2(spv[ps][e2]));
-                const uint32_t vb = vst + vc_lane + 1024 * ps;
+                for (int e2 = 0; e2 < 4; ++e2) A[e2] = as_u32(as_half2(Pp[e2]) * as_half2(spv[j][e2]));
+                const uint32_t vb = vst + vc_lane + 1024 * j;
                 u32x4 X;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {
@@ -839,22 +961,23 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
         }
     }
     __syncthreads();
-    // ---- combine the four page streams: thread (h, ch)
-    {
+    // ---- combine the four page streams (two token halves each): thread (h, ch)
+    if (tid < GRP * D) {
         const int h = tid >> 7, ch = tid & (D - 1);
+        auto slot = [&](int v, int half) { return S + (uint32_t)(((2 * v + half) * GRP + h) * PART_FLOATS) * 4; };
         float M = -__builtin_huge_valf();
 #pragma unroll
-        for (int v = 0; v < 4; ++v) M = fmaxf(M, lds_ld<float>(S + ((v * GRP + h) * PART_FLOATS + D) * 4));
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, lds_ld<float>(slot(v, 0) + D * 4));
         float o = 0.0f, l = 0.0f, l3 = 0.0f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const uint32_t base = S + (uint32_t)((v * GRP + h) * PART_FLOATS) * 4;
-            const float mv = lds_ld<float>(base + D * 4);
+            const float mv = lds_ld<float>(slot(v, 0) + D * 4);
             const float f = mv == -__builtin_huge_valf() ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
-            o = __builtin_fmaf(lds_ld<float>(base + ch * 4), f, o);
+            o = __builtin_fmaf(lds_ld<float>(slot(v, 0) + ch * 4) + lds_ld<float>(slot(v, 1) + ch * 4), f, o);
             if (ch == 0) {
-                l = __builtin_fmaf(lds_ld<float>(base + (D + 1) * 4), f, l);
-                l3 = __builtin_fmaf(lds_ld<float>(base + (D + 2) * 4), f, l3);
+                l = __builtin_fmaf(lds_ld<float>(slot(v, 0) + (D + 1) * 4) + lds_ld<float>(slot(v, 1) + (D + 1) * 4), f,
+                                   l);
+                l3 = __builtin_fmaf(lds_ld<float>(slot(v, 0) + (D + 2) * 4), f, l3);
             }
         }
         float *dst = part_base + (size_t)h * hstride;
@@ -895,12 +1018,36 @@ int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep) {
     return s < 1 ? 1 : s;
 }
 
+bool fused_select_ok(int hq, int hkv, int n_keep) {
+    if (!use_mfma_decode(hq, hkv, n_keep)) return false;
+    switch (ks_of(n_keep)) {
+        case 1: return Lay<1>::FUSABLE;
+        case 2: return Lay<2>::FUSABLE;
+        case 3: return Lay<3>::FUSABLE;
+        case 4: return Lay<4>::FUSABLE;
+        case 5: return Lay<5>::FUSABLE;
+        case 6: return Lay<6>::FUSABLE;
+        default: return Lay<7>::FUSABLE;
+    }
+}
+
+template <int KS, bool FUSED>
+static hipError_t launch_ks2(const DecodeArgs &a, hipStream_t s) {
+    dim3 grid(a.num_splits, a.batch * a.hkv);
+    hipLaunchKernelGGL((decode_blk_kernel<KS, FUSED>), grid, dim3(NTHR), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep,
+                       a.hq, a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials, a.q_bf16,
+                       a.t_q, a.qp_out, a.sel_out);
+    return hipGetLastError();
+}
+
 template <int KS>
 static hipError_t launch_ks(const DecodeArgs &a, hipStream_t s) {
-    dim3 grid(a.num_splits, a.batch * a.hkv);
-    hipLaunchKernelGGL(decode_blk_kernel<KS>, grid, dim3(NTHR), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep, a.hq,
-                       a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials);
-    return hipGetLastError();
+    if constexpr (Lay<KS>::FUSABLE) {
+        if (a.q_bf16) return launch_ks2<KS, true>(a, s);
+    } else {
+        if (a.q_bf16) return hipErrorInvalidValue;
+    }
+    return launch_ks2<KS, false>(a, s);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {

@@ -134,6 +134,13 @@ struct DecodeArgs {
     int num_splits;
     float *partials;
     float *out, *lse;
+    // selection fused into the MFMA decode (dqk_select_decode_attn): q bf16
+    // [batch][hq][128] and T_Q fp32 [hkv][128][128] replace q_prime / sel_idx
+    // as inputs, which then receive the selection's results
+    const uint16_t *q_bf16 = nullptr;
+    const float *t_q = nullptr;
+    float *qp_out = nullptr;
+    int32_t *sel_out = nullptr;
 };
 
 // Generic path: any group size up to 16.
@@ -145,6 +152,8 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 bool use_mfma_decode(int hq, int hkv, int n_keep);  // n_keep 0: any count it serves
 int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep);  // n_keep 0: the largest
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
+// Whether the MFMA decode can run the selection itself for this n_keep.
+bool fused_select_ok(int hq, int hkv, int n_keep);
 
 struct DecodeBf16Args {
     const uint16_t *k_pages, *v_pages;
@@ -158,6 +167,13 @@ struct DecodeBf16Args {
     int num_splits;
     float *partials;
     float *out, *lse;
+    // selection fused into the MFMA decode (dqk_select_decode_attn): q bf16
+    // [batch][hq][128] and T_Q fp32 [hkv][128][128] replace q_prime / sel_idx
+    // as inputs, which then receive the selection's results
+    const uint16_t *q_bf16 = nullptr;
+    const float *t_q = nullptr;
+    float *qp_out = nullptr;
+    int32_t *sel_out = nullptr;
 };
 
 hipError_t launch_decode_bf16(const DecodeBf16Args &a, hipStream_t s);

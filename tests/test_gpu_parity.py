@@ -202,3 +202,37 @@ def test_decode_bf16_parity(shape):
     torch.cuda.synchronize()
     assert (gu.row_rel_err(gu.host(out), ref) <= gu.TOL).all()
     np.testing.assert_allclose(gu.host(lse), ref_lse, rtol=1e-5, atol=1e-5)
+
+
+FUSED_CASES = [
+    ("nk77-ragged", synth.Shape(3, 32, 8, [5000, 131, 2800], 77, shuffle_pages=True), 0),
+    ("nk52-splits7", synth.Shape(2, 32, 8, [4000, 129], 52), 7),
+    ("nk103", synth.Shape(1, 32, 8, [3000], 103), 0),
+    ("nk20", synth.Shape(1, 32, 8, [1700], 20), 3),
+    ("nk10-two-calls", synth.Shape(1, 32, 8, [1700], 10), 0),
+    ("nk128-two-calls", synth.Shape(1, 32, 8, [900], 128), 0),
+    ("g2-two-calls", synth.Shape(2, 16, 8, [900, 300], 77), 0),
+]
+
+
+@pytest.mark.parametrize("name,shape,ns", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_select_decode_one_call_equals_two_calls(name, shape, ns):
+    """dqk_select_decode_attn (selection inside the decode kernel where it
+    can, two launches otherwise) returns exactly what dqk_select_channels then
+    dqk_decode_attn return, and its selection matches the oracle."""
+    _say("select+decode", name)
+    prob = synth.make_problem(shape, seed=31)
+    cache, _ = oracle.quantize_append(prob.k, prob.v, prob.t_k, prob.cu_tokens, prob.page_table, prob.num_pages)
+    gc = gu.cache_to_device(cache)
+    d = gu.upload(prob)
+    qp1, sel1 = pa.dqk_select_channels(d["q"], d["t_q"], shape.hkv, shape.n_keep)
+    out1, lse1 = pa.dqk_decode_attn(gc, qp1, sel1, d["page_table"], d["seq_lens"], prob.sm_scale, num_splits=ns)
+    out2, lse2, qp2, sel2 = pa.dqk_select_decode_attn(gc, d["q"], d["t_q"], shape.n_keep, d["page_table"],
+                                                      d["seq_lens"], prob.sm_scale, num_splits=ns)
+    torch.cuda.synchronize()
+    qp_ref, sel_ref = oracle.select_channels(prob.q, prob.t_q, shape.hkv, shape.n_keep)
+    np.testing.assert_array_equal(gu.host(sel2), sel_ref)
+    np.testing.assert_array_equal(gu.host(qp2).view(np.uint32), qp_ref.view(np.uint32))
+    np.testing.assert_array_equal(gu.host(sel2), gu.host(sel1))
+    np.testing.assert_array_equal(gu.host(out2), gu.host(out1))
+    np.testing.assert_array_equal(gu.host(lse2), gu.host(lse1))

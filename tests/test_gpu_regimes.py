@@ -163,6 +163,17 @@ def test_late_sharp_token():
     _check(prob, label="late")
 
 
+def test_sharp_token_in_a_short_last_page():
+    """The largest logit sits in a last page holding fewer than 65 tokens, so
+    the running maximum rises on a page whose second token half is empty:
+    everything accumulated for that half so far must still be rescaled."""
+    _say("sharp token in a short last page")
+    shape = synth.Shape(1, 8, 2, [32768 + 40], 77)
+    prob = synth.make_problem(shape, seed=209)
+    _sink(prob, [32768 + 30], 10.0)
+    _check(prob, label="short-last-page")
+
+
 @pytest.mark.parametrize("qscale", [8.0])
 def test_sharp_softmax_scaled_queries(qscale):
     _say("q x", qscale)
