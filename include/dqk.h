@@ -160,7 +160,7 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
 
 /*
  * dqk_select_channels followed by dqk_decode_attn, as one call: for the
- * group-4 MFMA decode (Hq = 4 Hkv, 17 <= n_keep <= 112) the selection runs in
+ * group-4 MFMA decode (Hq = 4 Hkv, 17 <= n_keep <= 128) the selection runs in
  * the decode kernel's prologue, one launch instead of two; otherwise the two
  * calls are made in sequence.  Results are identical to the two calls
  * (q_prime and sel_idx bit for bit, then the same decode).

@@ -49,11 +49,10 @@ typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 constexpr int GRP = 4;          // query heads per KV head handled here
 constexpr int NW = 12;          // waves per workgroup: 4 scoring, 8 multiplying (two per page)
 constexpr int NTHR = 64 * NW;
-constexpr int NVST = 3;         // value stages
 constexpr int PBOOST = 14;      // probabilities are kept as 2^(x - m + 14)
 constexpr int EMIN = -15, EMAX = 15;  // clamp of the value-scale exponent
 constexpr int TABN = 64;        // blocks of a split whose alignment is tabulated up front
-constexpr int MAX_KS = 7;       // 16-channel k-steps: up to 112 selected INT2 channels
+constexpr int MAX_KS = 8;       // 16-channel k-steps: up to 128 selected channels
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 static_assert(KBLK == 8, "the kernel walks 8-page blocks in halves of four pages");
@@ -80,7 +79,10 @@ struct Lay {
     static constexpr int PBROW = 320;               // P of one head: 128 fp16 + 64 B of padding
     static constexpr int PBPAGE = 4 * PBROW;
     static constexpr int PBBUF = 4 * PBPAGE;
-    static constexpr int PB = VS + NVST * VST;      // [2 buffers][4 pages][4 heads][PBROW]
+    // three value stages (values two steps ahead); two when the key stages leave no room
+    // for a third (values then one step ahead)
+    static constexpr int NV = KS <= 7 ? 3 : 2;
+    static constexpr int PB = VS + NV * VST;        // [2 buffers][4 pages][4 heads][PBROW]
     static constexpr int AL = PB + 2 * PBBUF;       // [2 buffers][4 pages][4 heads] float rescale factors
     static constexpr int QT = AL + 2 * 16 * 4;      // [4 scoring waves][KS][256 B] q~ B fragments
     static constexpr int ZERO = QT + 4 * KS * 256;  // KS * 256 bytes of zeros
@@ -89,15 +91,15 @@ struct Lay {
     // the selection run inside the decode (prologue only): T_Q of the KV head
     // [128][128] fp32 at 0, the four heads' q in fp32, the pooled energies and
     // a ballot word after it; q' and the selected channels go to the usual
-    // scratch in value stage 2, which lies past all of them
-    static constexpr int SCR = VS + 2 * VST;
+    // scratch in the last value stage, which lies past all of them
+    static constexpr int SCR = VS + (NV - 1) * VST;
     static constexpr int FT = 0;
     static constexpr int FQ = D * D * 4;
     static constexpr int FS = FQ + GRP * D * 4;
     static constexpr int FM = FS + D * 4;
     static constexpr bool FUSABLE = FM + 16 <= SCR && FM + 16 <= TOTAL;
     // the values of the first half can load during the selection (their stage lies past it)
-    static constexpr bool EARLY_V = FM + 16 <= VS + VST;
+    static constexpr bool EARLY_V = NV == 3 && FM + 16 <= VS + VST;
     // global -> LDS loads: a key block is NRI row, NMI metadata and 2 channel-0
     // instructions; a value half is 16 code and 8 metadata instructions
     static constexpr int NRI = NR / 4;
@@ -380,8 +382,11 @@ struct Feeder {
     uint64_t kbase[Ly::KN], kstr[Ly::KN], vbase[Ly::VN], vstr[Ly::VN];
 
     __device__ __forceinline__ uint32_t kstage(int j) const { return S + (uint32_t)(j & 1) * Ly::KST; }
-    // half u -> value stage (u + 1) % 3: half 0 in stage 1, clear of the prologue's scratch areas
-    __device__ __forceinline__ uint32_t vstage(int u) const { return S + Ly::VS + (uint32_t)((u + 1) % NVST) * Ly::VST; }
+    // half u -> value stage (u + 1) % 3 (half 0 in stage 1, clear of the prologue's scratch
+    // areas), or u % 2 with two stages
+    __device__ __forceinline__ uint32_t vstage(int u) const {
+        return S + Ly::VS + (uint32_t)((u + (Ly::NV == 3 ? 1 : 0)) % Ly::NV) * Ly::VST;
+    }
     __device__ __forceinline__ int blk_of(int j) const {
         return j < TABN ? __builtin_amdgcn_readlane(tab, j)
                         : __builtin_amdgcn_readfirstlane(block_aligned(ptab, B0 + j, npages));
@@ -443,9 +448,10 @@ struct Feeder {
         for (int i = 0; i < Ly::VN; ++i) slow_val(wv + NW * i, lane, p, hb, *c, g, hkv, st + val_lds<KS>(wv + NW * i));
         return true;
     }
-    // Start of step u: this wave's loads older than the previous step are done,
-    // then the workgroup barrier; then the loads of half u + 1's values and (at
-    // even steps) block u/2 + 1's keys.  halfpages(u): whether half u holds a page.
+    // Start of step u: this wave's loads older than the previous step (with two
+    // value stages: all but the previous step's key loads) are done, then the
+    // workgroup barrier; then the loads of half u + 1's values (half u's) and,
+    // at even steps, block u/2 + 1's keys.  halfpages(u): whether half u holds a page.
     template <typename HalfPages>
     __device__ __forceinline__ void top(int u, HalfPages halfpages) {
         if (u > 0 && pend == Ly::KN + Ly::VN)
@@ -457,7 +463,11 @@ struct Feeder {
         else
             wait_vm_barrier<0>();
         int np = 0;
-        if (u + 1 < nst && halfpages(u + 1)) np = issue_vals(u + 1) ? 0 : np + Ly::VN;
+        if constexpr (Ly::NV == 3) {  // values of half u + 1: needed two steps later
+            if (u + 1 < nst && halfpages(u + 1)) np = issue_vals(u + 1) ? 0 : np + Ly::VN;
+        } else {  // values of half u: needed at the next step, so never left in flight
+            if (u < nst && halfpages(u)) issue_vals(u);
+        }
         if (!(u & 1) && (u >> 1) + 1 < nb) np = issue_keys((u >> 1) + 1) ? 0 : np + Ly::KN;
         pend = np;
     }
@@ -607,8 +617,9 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     fd.nb = nb;
     fd.nst = nst;
     fd.plan_vals();
-    constexpr bool early_v = FUSED && Ly::EARLY_V;
-    if constexpr (early_v) fd.issue_vals(0);  // in flight while the selection runs
+    // in flight while the selection runs (or q' and the channel list are staged)
+    constexpr bool early_v = Ly::NV == 3 && (!FUSED || Ly::EARLY_V);
+    if constexpr (early_v) fd.issue_vals(0);
 
     // ---- q' of the four heads and the selected channels into LDS (value stage 2)
     const uint32_t scr = S + Ly::SCR;
@@ -654,9 +665,9 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const float q0c = has0 ? qv(hh, 0) * C : 0.0f;
     __syncthreads();  // scratch read by every wave
 
-    // ---- prologue loads: keys of block 0, values of half 0
+    // ---- prologue loads: keys of block 0, values of half 0 (with two value stages, at step 0)
     fd.issue_keys(0);
-    if constexpr (!early_v) fd.issue_vals(0);
+    if constexpr (!early_v && Ly::NV == 3) fd.issue_vals(0);
 
     // exchange slots [4 page streams][2 token halves][4 heads][PART_FLOATS]
     const uint32_t xw = S + (uint32_t)(2 * w + th) * (GRP * PART_FLOATS * 4);
@@ -1027,7 +1038,8 @@ bool fused_select_ok(int hq, int hkv, int n_keep) {
         case 4: return Lay<4>::FUSABLE;
         case 5: return Lay<5>::FUSABLE;
         case 6: return Lay<6>::FUSABLE;
-        default: return Lay<7>::FUSABLE;
+        case 7: return Lay<7>::FUSABLE;
+        default: return Lay<8>::FUSABLE;
     }
 }
 
@@ -1059,7 +1071,8 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s) {
         case 4: return launch_ks<4>(a, s);
         case 5: return launch_ks<5>(a, s);
         case 6: return launch_ks<6>(a, s);
-        default: return launch_ks<7>(a, s);
+        case 7: return launch_ks<7>(a, s);
+        default: return launch_ks<8>(a, s);
     }
 }
 

@@ -210,7 +210,8 @@ FUSED_CASES = [
     ("nk103", synth.Shape(1, 32, 8, [3000], 103), 0),
     ("nk20", synth.Shape(1, 32, 8, [1700], 20), 3),
     ("nk10-two-calls", synth.Shape(1, 32, 8, [1700], 10), 0),
-    ("nk128-two-calls", synth.Shape(1, 32, 8, [900], 128), 0),
+    ("nk128", synth.Shape(1, 32, 8, [900], 128), 0),
+    ("nk113-ragged", synth.Shape(2, 32, 8, [2100, 77], 113, shuffle_pages=True), 5),
     ("g2-two-calls", synth.Shape(2, 16, 8, [900, 300], 77), 0),
 ]
 
