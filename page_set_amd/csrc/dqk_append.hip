@@ -3,17 +3,25 @@
 // stored, §3.4; channel-major 32-byte key rows with channel 0 in bf16 outside
 // the INT2 range and token-major values with separate metadata, §3.3).
 //
-// One workgroup (4 waves) per (logical page, sequence, KV head).
-//   1. The page's 128x128 bf16 key tile and T_K (transposed, so that the
-//      contraction index is contiguous) are staged in LDS with padded rows.
-//   2. Wave w computes k' for output channels 32w..32w+31 and all 128 tokens
+// One workgroup (4 waves) per (run of NPW logical pages, sequence, KV head).
+//   1. T_K is staged once in LDS, transposed so that the contraction index is
+//      contiguous (pairs of rows per 4-byte store), and each wave keeps the B
+//      fragments of its 32 output channels in VGPRs for all pages of the run.
+//      The LDS buffer then holds one page's key tile.
+//   2. Per page: the key tile goes global -> LDS by direct loads (16-byte
+//      chunks XOR-swizzled within each 256-byte row so that the MFMA operand
+//      reads are conflict-free), and the values, which do not need the tile,
+//      are packed while it is in flight.
+//   3. Wave w computes k' for output channels 32w..32w+31 and all 128 tokens
 //      with v_mfma_f32_16x16x32_bf16 (8 token tiles x 2 channel tiles x 4
 //      k-steps).  Token tile mt, row i holds token 32*(i/4) + 4*mt + i%4, so
 //      every lane ends up with 32 consecutive tokens of two channels: the
 //      8-byte slice of each channel row it packs and stores directly.
-//   3. Per channel: min/max over valid tokens (in-lane, then across the four
+//   4. Per channel: min/max over valid tokens (in-lane, then across the four
 //      16-lane rows), the binary16 grid, codes, one 8-byte store per lane.
-//   4. Values: 512 (token, 32-channel group) units, two per lane.
+//   5. Values: 512 (token, 32-channel group) units per page, two per lane,
+//      consecutive lanes on consecutive tokens of one group.
+// Full pages take a path without per-token checks.
 // Built with -ffp-contract=off: the grid arithmetic must round as written.
 #include "dqk_internal.h"
 
@@ -25,7 +33,44 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int LDS_ROW = D + 8;  // bf16 elements per padded LDS row (272 bytes)
+constexpr int NPW = 4;                     // logical pages per workgroup
+constexpr int KLD = PG * (D / 8) / 256;     // 16-byte key-tile chunks per thread
+constexpr int VLD = PG * VGROUPS / 256;     // value units per thread
+
+// 16-byte chunk c of LDS row r sits at slot c ^ swz(r), rows of 256 bytes.
+// Key tile (rows = tokens): the 16 rows an operand read touches,
+// 32 (i / 4) + 4 mt + i % 4, get distinct slots.  T_K^T (rows = output
+// channels): 16 consecutive rows get distinct slots.
+__device__ __forceinline__ uint32_t swz_k(int r) { return (uint32_t)((r & 3) | ((r >> 3) & 12)); }
+__device__ __forceinline__ uint32_t swz_t(int r) { return (uint32_t)(r & 15); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
+}
+template <typename T>
+__device__ __forceinline__ T lds_ld(uint32_t a) {
+    return *(__attribute__((address_space(3))) const T *)(uintptr_t)a;
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(uint32_t a, T v) {
+    *(__attribute__((address_space(3))) T *)(uintptr_t)a = v;
+}
+// 16 bytes per lane global -> LDS at M0 + 16 lane (the LDS base must be uniform)
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, %0" ::"s"(sbase), "v"(voff),
+                 "s"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory", "m0");
+}
+// The thread index as a value the compiler cannot see through: per-page
+// address arithmetic derived from it is redone in each page iteration instead
+// of being hoisted out of the loop into registers held across all of it.
+__device__ __forceinline__ int fresh_tid() {
+    int t = (int)threadIdx.x;
+    __asm__ volatile("" : "+v"(t));
+    return t;
+}
+// every load of this wave done, own LDS accesses done, then the barrier
+__device__ __forceinline__ void wait_all_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float wave_row_min(float x) {
     x = fminf(x, __shfl_xor(x, 16));
@@ -36,160 +81,211 @@ __device__ __forceinline__ float wave_row_max(float x) {
     return fmaxf(x, __shfl_xor(x, 32));
 }
 
-__global__ __launch_bounds__(256) void append_kernel(dqk_cache c, const uint16_t *__restrict__ kin,
+// Values of one (token, group) unit from its 64 loaded bytes: 32 channels ->
+// codes (2 bits each, channel e at bits 2e), scale and zero point.
+__device__ __forceinline__ void pack_value_unit(const u32x4 (&raw)[4], uint64_t &bits, uint16_t &sb, uint16_t &zb) {
+    float x[32];
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[w4 * 8 + 2 * e] = __uint_as_float(raw[w4][e] << 16);
+            x[w4 * 8 + 2 * e + 1] = __uint_as_float(raw[w4][e] & 0xFFFF0000u);
+        }
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) {
+        mn = fminf(mn, x[e]);
+        mx = fmaxf(mx, x[e]);
+    }
+    const Grid gr = make_grid(mn, mx);
+    const Thresholds th = thresholds(gr);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        lo |= code2(x[e], th) << (2 * e);
+        hi |= code2(x[16 + e], th) << (2 * e);
+    }
+    bits = (uint64_t)lo | ((uint64_t)hi << 32);
+    sb = gr.sb;
+    zb = gr.zb;
+}
+
+// k' of the tile in LDS for 16 output channels (channel tile nt of this
+// wave's 32), then the packed key rows, metadata and channel 0.  FULL: all 128
+// tokens valid; DBG: k' also goes to kprime_dbg.
+template <bool FULL, bool DBG>
+__device__ __forceinline__ void keys_of_page(const dqk_cache &c, uint32_t ks, const bf16x8 (&bop)[4], int nt,
+                                             int64_t p, int g, int hkv, int nvalid, int64_t t0,
+                                             float *__restrict__ kprime_dbg) {
+    const int tid = fresh_tid(), lane = tid & 63, w = tid >> 6;
+    const int G = lane >> 4, n = lane & 15;
+    f32x4 acc[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = {0.f, 0.f, 0.f, 0.f};
+    // A row n of token tile mt is token 32 (n / 4) + 4 mt + n % 4, whose swizzle
+    // swz_k is n for every mt: one address per k-step, mt in the offset field
+    const uint32_t arow = ks + (uint32_t)(32 * (n >> 2) + (n & 3)) * 256;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t ak = arow + ((uint32_t)((4 * kk + G) ^ n) << 4);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const bf16x8 aop = lds_ld<bf16x8>(ak + mt * 1024);
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[kk], acc[mt], 0, 0, 0);
+        }
+    }
+    const size_t pg = (size_t)p * hkv + g;
+    // lane holds tokens 32G .. 32G+31 of channel 32w + 16nt + n
+    const int ch = 32 * w + 16 * nt + n;
+    if (DBG) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = 32 * G + 4 * mt + r;
+                if (FULL || tok < nvalid) kprime_dbg[((size_t)(t0 + tok) * hkv + g) * D + ch] = acc[mt][r];
+            }
+    }
+    uint8_t *row = c.k_codes + krow(p, g, hkv, ch) * ROW_BYTES + 8 * G;
+    if (ch == 0) {
+        uint16_t *k0 = c.k_ch0 + pg * PG + 32 * G;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = 32 * G + 4 * mt + r;
+                k0[4 * mt + r] = (FULL || tok < nvalid) ? f2bf_rne(acc[mt][r]) : (uint16_t)0;
+            }
+        *reinterpret_cast<uint64_t *>(row) = 0;
+        if (G == 0) *reinterpret_cast<uint32_t *>(c.k_meta + krow(p, g, hkv, ch) * 2) = 0u;
+        return;
+    }
+    float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = 32 * G + 4 * mt + r;
+            if (FULL || tok < nvalid) {
+                mn = fminf(mn, acc[mt][r]);
+                mx = fmaxf(mx, acc[mt][r]);
+            }
+        }
+    mn = wave_row_min(mn);
+    mx = wave_row_max(mx);
+    const Grid gr = make_grid(mn, mx);
+    const Thresholds th = thresholds(gr);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = 32 * G + 4 * mt + r;
+            const uint32_t cd = (FULL || tok < nvalid) ? code2(acc[mt][r], th) : 0u;
+            if (mt < 4)
+                lo |= cd << (8 * mt + 2 * r);
+            else
+                hi |= cd << (8 * (mt - 4) + 2 * r);
+        }
+    *reinterpret_cast<uint64_t *>(row) = (uint64_t)lo | ((uint64_t)hi << 32);
+    if (G == 0)
+        *reinterpret_cast<uint32_t *>(c.k_meta + krow(p, g, hkv, ch) * 2) = (uint32_t)gr.sb | ((uint32_t)gr.zb << 16);
+}
+
+template <bool DBG>
+__global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, const uint16_t *__restrict__ kin,
                                                      const uint16_t *__restrict__ vin,
                                                      const uint16_t *__restrict__ t_k,
                                                      const int32_t *__restrict__ cu_tokens,
                                                      const int32_t *__restrict__ page_table, int max_pages,
                                                      float *__restrict__ kprime_dbg) {
-    __shared__ __attribute__((aligned(16))) uint16_t ks[PG * LDS_ROW];  // [token][in ch]
-    __shared__ __attribute__((aligned(16))) uint16_t tt[D * LDS_ROW];   // [out ch][in ch]
+    // T_K^T [out ch][in ch] first, then each page's key tile [token][in ch]; rows of 256 bytes
+    __shared__ __attribute__((aligned(16))) uint16_t lds_tile[PG * D];
+    const uint32_t ks = lds_addr(lds_tile);
 
-    const int pi = blockIdx.x, sq = blockIdx.y, g = blockIdx.z;
+    const int sq = blockIdx.y, g = blockIdx.z;
     const int hkv = c.num_kv_heads;
     const int64_t tok0 = cu_tokens[sq];
     const int64_t L = (int64_t)cu_tokens[sq + 1] - tok0;
-    if ((int64_t)pi * PG >= L) return;
-    const int nvalid = (int)min<int64_t>(PG, L - (int64_t)pi * PG);
-    const int64_t p = page_table[(size_t)sq * max_pages + pi];
-    const int64_t t0 = tok0 + (int64_t)pi * PG;
-    const int tid = threadIdx.x;
-
-    // ---- stage keys and T_K^T in LDS
-    for (int ch = tid; ch < PG * (D / 8); ch += 256) {
-        const int t = ch >> 4, part = ch & 15;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (t < nvalid)
-            val = *reinterpret_cast<const u32x4 *>(kin + ((size_t)(t0 + t) * hkv + g) * D + part * 8);
-        *reinterpret_cast<u32x4 *>(&ks[t * LDS_ROW + part * 8]) = val;
-    }
+    const int pi0 = blockIdx.x * NPW;
+    if ((int64_t)pi0 * PG >= L) return;
+    const int pi_end = (int)min<int64_t>(min(pi0 + NPW, max_pages), (L + PG - 1) / PG);
+    // ---- T_K^T: thread (row pair rp, column octet oc) stores the two rows'
+    //      elements of each column as one 4-byte word
     const uint16_t *T = t_k + (size_t)g * D * D;
-    for (int ch = tid; ch < D * (D / 8); ch += 256) {
-        const int i = ch >> 4, j0 = (ch & 15) * 8;
-        u32x4 val = *reinterpret_cast<const u32x4 *>(T + (size_t)i * D + j0);
+    for (int it = threadIdx.x; it < (D / 2) * (D / 8); it += 256) {
+        const int rp = it & (D / 2 - 1), oc = it / (D / 2);
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(T + (size_t)(2 * rp) * D + oc * 8);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(T + (size_t)(2 * rp + 1) * D + oc * 8);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            tt[(j0 + 2 * e) * LDS_ROW + i] = (uint16_t)(val[e] & 0xFFFFu);
-            tt[(j0 + 2 * e + 1) * LDS_ROW + i] = (uint16_t)(val[e] >> 16);
+        for (int e = 0; e < 8; ++e) {
+            const int row = oc * 8 + e;
+            const uint32_t word = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+            lds_st<uint32_t>(ks + row * 256 + ((((uint32_t)rp >> 2) ^ swz_t(row)) << 4) + (rp & 3) * 4, word);
         }
-    }
-
-    // ---- values (independent of the key tile): two (token, group) units per lane
-    const size_t pg = (size_t)p * hkv + g;
-    for (int u = tid; u < PG * VGROUPS; u += 256) {
-        const int t = u >> 2, q = u & 3;
-        uint64_t bits = 0;
-        uint16_t sb = 0, zb = 0;
-        if (t < nvalid) {
-            const uint16_t *src = vin + ((size_t)(t0 + t) * hkv + g) * D + q * 32;
-            float x[32];
-#pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) {
-                u32x4 raw = *reinterpret_cast<const u32x4 *>(src + w4 * 8);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[w4 * 8 + 2 * e] = __uint_as_float(raw[e] << 16);
-                    x[w4 * 8 + 2 * e + 1] = __uint_as_float(raw[e] & 0xFFFF0000u);
-                }
-            }
-            float mn = x[0], mx = x[0];
-#pragma unroll
-            for (int e = 1; e < 32; ++e) {
-                mn = fminf(mn, x[e]);
-                mx = fmaxf(mx, x[e]);
-            }
-            const Grid gr = make_grid(mn, mx);
-            const Thresholds th = thresholds(gr);
-#pragma unroll
-            for (int e = 0; e < 32; ++e) bits |= (uint64_t)code2(x[e], th) << (2 * e);
-            sb = gr.sb;
-            zb = gr.zb;
-        }
-        *reinterpret_cast<uint64_t *>(c.v_codes + (pg * PG + t) * ROW_BYTES + q * 8) = bits;
-        c.v_meta[(pg * 2 + 0) * VGROUPS * PG + q * PG + t] = sb;
-        c.v_meta[(pg * 2 + 1) * VGROUPS * PG + q * PG + t] = zb;
     }
     __syncthreads();
-
-    // ---- k' = k T_K on MFMA
-    const int lane = tid & 63, w = tid >> 6;
+    bf16x8 bop[2][4];  // [channel tile][k-step]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int G = lane >> 4, n = lane & 15;
-    f32x4 acc[8][2];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 bop[2];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-            bop[nt] = *reinterpret_cast<const bf16x8 *>(&tt[(32 * w + 16 * nt + n) * LDS_ROW + 32 * kk + 8 * G]);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const int i = n;  // A row held by this lane
-            const int tok = 32 * (i >> 2) + 4 * mt + (i & 3);
-            const bf16x8 aop = *reinterpret_cast<const bf16x8 *>(&ks[tok * LDS_ROW + 32 * kk + 8 * G]);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[nt], acc[mt][nt], 0, 0, 0);
+        for (int nt = 0; nt < 2; ++nt) {
+            const int row = 32 * w + 16 * nt + n;
+            bop[nt][kk] = lds_ld<bf16x8>(ks + row * 256 + (((4 * kk + G) ^ swz_t(row)) << 4));
         }
-    }
 
-    // ---- epilogue: lane holds tokens 32G .. 32G+31 of channels 32w + 16nt + n
+    for (int pi = pi0; pi < pi_end; ++pi) {
+        const int nvalid = (int)min<int64_t>(PG, L - (int64_t)pi * PG);
+        const int64_t p = page_table[(size_t)sq * max_pages + pi];
+        const int64_t t0 = tok0 + (int64_t)pi * PG;
+        const size_t pg = (size_t)p * hkv + g;
+
+        __syncthreads();  // the previous tile (or T_K^T) has been read by every wave
+        const int tid = fresh_tid(), lane = tid & 63, w = tid >> 6;
+        // ---- key tile: chunk slot s of row r <- input chunk s ^ swz_k(r) (rows past
+        //      the sequence end re-read token 0: their k' is never used)
+        const uint16_t *kbase = kin + ((size_t)t0 * hkv + g) * D;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        const int ch = 32 * w + 16 * nt + n;
-        if (kprime_dbg) {
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = 32 * G + 4 * mt + r;
-                    if (tok < nvalid) kprime_dbg[((size_t)(t0 + tok) * hkv + g) * D + ch] = acc[mt][nt][r];
-                }
+        for (int i = 0; i < KLD; ++i) {
+            const int row = 4 * (KLD * w + i) + (lane >> 4);
+            const uint32_t ch = (uint32_t)(lane & 15) ^ swz_k(row);
+            const int src = row < nvalid ? row : 0;
+            dma16(kbase, (uint32_t)((src * hkv * D + ch * 8) * 2), ks + (KLD * w + i) * 1024);
         }
-        uint8_t *row = c.k_codes + krow(p, g, hkv, ch) * ROW_BYTES + 8 * G;
-        if (ch == 0) {
-            uint16_t *k0 = c.k_ch0 + pg * PG + 32 * G;
+
+        // ---- values: unit (token t, group q), consecutive lanes on consecutive tokens
+        u32x4 raw[VLD][4];
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+        for (int k = 0; k < VLD; ++k) {
+            const int u = tid + 256 * k, t = u & (PG - 1), q = u / PG;
+            const uint16_t *src = vin + ((size_t)(t0 + (t < nvalid ? t : 0)) * hkv + g) * D + q * 32;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = 32 * G + 4 * mt + r;
-                    k0[4 * mt + r] = tok < nvalid ? f2bf_rne(acc[mt][nt][r]) : (uint16_t)0;
-                }
-            *reinterpret_cast<uint64_t *>(row) = 0;
-            if (G == 0) *reinterpret_cast<uint32_t *>(c.k_meta + krow(p, g, hkv, ch) * 2) = 0u;
-            continue;
+            for (int w4 = 0; w4 < 4; ++w4) raw[k][w4] = *reinterpret_cast<const u32x4 *>(src + w4 * 8);
         }
-        float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
+        for (int k = 0; k < VLD; ++k) {
+            __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
+            const int u = tid + 256 * k, t = u & (PG - 1), q = u / PG;
+            uint64_t bits = 0;
+            uint16_t sb = 0, zb = 0;
+            if (t < nvalid) pack_value_unit(raw[k], bits, sb, zb);
+            *reinterpret_cast<uint64_t *>(c.v_codes + (pg * PG + t) * ROW_BYTES + q * 8) = bits;
+            c.v_meta[(pg * 2 + 0) * VGROUPS * PG + q * PG + t] = sb;
+            c.v_meta[(pg * 2 + 1) * VGROUPS * PG + q * PG + t] = zb;
+        }
+
+        wait_all_barrier();  // the tile has landed
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = 32 * G + 4 * mt + r;
-                if (tok < nvalid) {
-                    mn = fminf(mn, acc[mt][nt][r]);
-                    mx = fmaxf(mx, acc[mt][nt][r]);
-                }
-            }
-        mn = wave_row_min(mn);
-        mx = wave_row_max(mx);
-        const Grid gr = make_grid(mn, mx);
-        const Thresholds th = thresholds(gr);
-        uint64_t bits = 0;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = 32 * G + 4 * mt + r;
-                const uint64_t cd = tok < nvalid ? code2(acc[mt][nt][r], th) : 0u;
-                bits |= cd << (8 * mt + 2 * r);
-            }
-        *reinterpret_cast<uint64_t *>(row) = bits;
-        if (G == 0)
-            *reinterpret_cast<uint32_t *>(c.k_meta + krow(p, g, hkv, ch) * 2) = (uint32_t)gr.sb | ((uint32_t)gr.zb << 16);
+        for (int nt = 0; nt < 2; ++nt) {
+            if (nvalid == PG)
+                keys_of_page<true, DBG>(c, ks, bop[nt], nt, p, g, hkv, nvalid, t0, kprime_dbg);
+            else
+                keys_of_page<false, DBG>(c, ks, bop[nt], nt, p, g, hkv, nvalid, t0, kprime_dbg);
+            __builtin_amdgcn_sched_barrier(0);  // one channel tile's accumulators live at a time
+        }
     }
 }
 
@@ -198,9 +294,13 @@ __global__ __launch_bounds__(256) void append_kernel(dqk_cache c, const uint16_t
 hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k, int n_seqs,
                          const int32_t *cu_tokens, const int32_t *page_table, int max_pages, float *kprime_dbg,
                          hipStream_t s) {
-    dim3 grid(max_pages, n_seqs, c.num_kv_heads);
-    hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, s, c, k, v, t_k, cu_tokens, page_table, max_pages,
-                       kprime_dbg);
+    dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
+    if (kprime_dbg)
+        hipLaunchKernelGGL(append_kernel<true>, grid, dim3(256), 0, s, c, k, v, t_k, cu_tokens, page_table, max_pages,
+                           kprime_dbg);
+    else
+        hipLaunchKernelGGL(append_kernel<false>, grid, dim3(256), 0, s, c, k, v, t_k, cu_tokens, page_table,
+                           max_pages, kprime_dbg);
     return hipGetLastError();
 }
 

@@ -123,6 +123,13 @@ __device__ __forceinline__ half2v as_half2(uint32_t v) { return __builtin_bit_ca
 __device__ __forceinline__ uint32_t as_u32(half2v v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
 
+// An LDS address computed once per step: the empty asm keeps the compiler from
+// re-associating (step base + per-lane constant) + immediate, so that every
+// access below folds the immediate into the instruction's offset field.
+__device__ __forceinline__ uint32_t pinned(uint32_t a) {
+    __asm__ volatile("" : "+v"(a));
+    return a;
+}
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
 }
@@ -919,7 +926,7 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                 u32x4 A;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) A[e2] = as_u32(as_half2(Pp[e2]) * as_half2(spv[j][e2]));
-                const uint32_t vb = vst + vc_lane + 1024 * j;
+                const uint32_t vb = pinned(vst + vc_lane + 1024 * j);
                 u32x4 X;
 #pragma unroll
                 for (int e2 = 0; e2 < 4; ++e2) {

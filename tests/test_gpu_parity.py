@@ -82,6 +82,25 @@ def test_append_stagewise(name, shape):
     assert n_diff <= max(4, 1e-4 * cg.size)
 
 
+@pytest.mark.parametrize("shape", [synth.Shape(3, 8, 2, [1153, 128, 77], 77, shuffle_pages=True),
+                                   synth.Shape(1, 32, 8, [4100], 77)], ids=["ragged-runs", "gqa-4100"])
+def test_append_without_readback_writes_the_same_cache(shape):
+    """The k' readback is a build option of the append kernel: without it the
+    cache bytes are identical (that build is the one used in production)."""
+    _say("append without readback", shape.seq_lens)
+    prob = synth.make_problem(shape, seed=9)
+    d = gu.upload(prob)
+    c1 = pa.Cache(prob.num_pages, shape.hkv)
+    c2 = pa.Cache(prob.num_pages, shape.hkv)
+    kdbg = torch.empty((prob.k.shape[0], shape.hkv, 128), dtype=torch.float32, device="cuda")
+    pa.dqk_quantize_append(c1, d["k"], d["v"], d["t_k"], d["cu"], d["page_table"], kprime_dbg=kdbg)
+    pa.dqk_quantize_append(c2, d["k"], d["v"], d["t_k"], d["cu"], d["page_table"])
+    torch.cuda.synchronize()
+    for nm, a, b in zip(["k_codes", "k_meta", "k_ch0", "v_codes", "v_meta"], gu.cache_to_host(c1).arrays(),
+                        gu.cache_to_host(c2).arrays()):
+        np.testing.assert_array_equal(a, b, err_msg=nm)
+
+
 # ----------------------------------------------------------------- decode
 def _decode_case(shape, seed, num_splits=0, cache_fn=None):
     prob = synth.make_problem(shape, seed=seed)
