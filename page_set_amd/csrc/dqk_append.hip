@@ -111,6 +111,32 @@ __device__ __forceinline__ void pack_value_unit(const u32x4 (&raw)[4], uint64_t 
     zb = gr.zb;
 }
 
+// The values of one page: thread tid packs units (token t, group q0 + 2 k),
+// t = tid % 128, q0 = tid / 128.  FULL: all 128 tokens valid.
+template <bool FULL>
+__device__ __forceinline__ void values_of_page(const dqk_cache &c, const uint16_t *__restrict__ vin, int tid,
+                                               size_t pg, int g, int hkv, int nvalid, int64_t t0) {
+    const int t = tid & (PG - 1), q0 = tid / PG;
+    const bool valid = FULL || t < nvalid;
+    const uint16_t *vsrc = vin + ((size_t)(t0 + (valid ? t : 0)) * hkv + g) * D + q0 * 32;
+    u32x4 raw[VLD][4];
+#pragma unroll
+    for (int k = 0; k < VLD; ++k)
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) raw[k][w4] = *reinterpret_cast<const u32x4 *>(vsrc + 64 * k + w4 * 8);
+#pragma unroll
+    for (int k = 0; k < VLD; ++k) {
+        __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
+        const int q = q0 + 2 * k;
+        uint64_t bits = 0;
+        uint16_t sb = 0, zb = 0;
+        if (valid) pack_value_unit(raw[k], bits, sb, zb);
+        *reinterpret_cast<uint64_t *>(c.v_codes + (pg * PG + t) * ROW_BYTES + q * 8) = bits;
+        c.v_meta[(pg * 2 + 0) * VGROUPS * PG + q * PG + t] = sb;
+        c.v_meta[(pg * 2 + 1) * VGROUPS * PG + q * PG + t] = zb;
+    }
+}
+
 // k' of the tile in LDS for 16 output channels (channel tile nt of this
 // wave's 32), then the packed key rows, metadata and channel 0.  FULL: all 128
 // tokens valid; DBG: k' also goes to kprime_dbg.
@@ -129,11 +155,13 @@ __device__ __forceinline__ void keys_of_page(const dqk_cache &c, uint32_t ks, co
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const uint32_t ak = arow + ((uint32_t)((4 * kk + G) ^ n) << 4);
+        bf16x8 aop[8];  // the k-step's eight A fragments in flight together
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const bf16x8 aop = lds_ld<bf16x8>(ak + mt * 1024);
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[kk], acc[mt], 0, 0, 0);
-        }
+        for (int mt = 0; mt < 8; ++mt) aop[mt] = lds_ld<bf16x8>(ak + mt * 1024);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mt], bop[kk], acc[mt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
     const size_t pg = (size_t)p * hkv + g;
     // lane holds tokens 32G .. 32G+31 of channel 32w + 16nt + n
@@ -244,38 +272,35 @@ __global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, const uint1
         const size_t pg = (size_t)p * hkv + g;
 
         __syncthreads();  // the previous tile (or T_K^T) has been read by every wave
-        const int tid = fresh_tid(), lane = tid & 63, w = tid >> 6;
-        // ---- key tile: chunk slot s of row r <- input chunk s ^ swz_k(r) (rows past
-        //      the sequence end re-read token 0: their k' is never used)
-        const uint16_t *kbase = kin + ((size_t)t0 * hkv + g) * D;
+        const int tid = fresh_tid(), lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        // ---- key tile: chunk slot s of row r <- input chunk s ^ swz_k(r).  Load i
+        //      of wave w covers rows 32 w + 4 i + G, whose swizzle is G | 4 w for
+        //      every i: full pages step a scalar base and keep one lane offset;
+        //      rows past the sequence end re-read token 0 (their k' is never used).
+        const int row0 = 4 * KLD * w + G;
+        const uint32_t slot_off = ((uint32_t)(lane & 15) ^ (uint32_t)(G | 4 * w)) * 16;
+        const uint32_t tile_w = ks + (uint32_t)(KLD * w) * 1024;
+        if (nvalid == PG) {
+            const uint32_t voff = (uint32_t)(G * hkv * D) * 2 + slot_off;
 #pragma unroll
-        for (int i = 0; i < KLD; ++i) {
-            const int row = 4 * (KLD * w + i) + (lane >> 4);
-            const uint32_t ch = (uint32_t)(lane & 15) ^ swz_k(row);
-            const int src = row < nvalid ? row : 0;
-            dma16(kbase, (uint32_t)((src * hkv * D + ch * 8) * 2), ks + (KLD * w + i) * 1024);
+            for (int i = 0; i < KLD; ++i)
+                dma16(kin + ((size_t)(t0 + 4 * KLD * w + 4 * i) * hkv + g) * D, voff, tile_w + i * 1024);
+        } else {
+            const uint16_t *kbase = kin + ((size_t)t0 * hkv + g) * D;
+#pragma unroll
+            for (int i = 0; i < KLD; ++i) {
+                const int row = row0 + 4 * i;
+                const int src = row < nvalid ? row : 0;
+                dma16(kbase, (uint32_t)(src * hkv * D) * 2 + slot_off, tile_w + i * 1024);
+            }
         }
 
-        // ---- values: unit (token t, group q), consecutive lanes on consecutive tokens
-        u32x4 raw[VLD][4];
-#pragma unroll
-        for (int k = 0; k < VLD; ++k) {
-            const int u = tid + 256 * k, t = u & (PG - 1), q = u / PG;
-            const uint16_t *src = vin + ((size_t)(t0 + (t < nvalid ? t : 0)) * hkv + g) * D + q * 32;
-#pragma unroll
-            for (int w4 = 0; w4 < 4; ++w4) raw[k][w4] = *reinterpret_cast<const u32x4 *>(src + w4 * 8);
-        }
-#pragma unroll
-        for (int k = 0; k < VLD; ++k) {
-            __builtin_amdgcn_sched_barrier(0);  // one unit's values live at a time
-            const int u = tid + 256 * k, t = u & (PG - 1), q = u / PG;
-            uint64_t bits = 0;
-            uint16_t sb = 0, zb = 0;
-            if (t < nvalid) pack_value_unit(raw[k], bits, sb, zb);
-            *reinterpret_cast<uint64_t *>(c.v_codes + (pg * PG + t) * ROW_BYTES + q * 8) = bits;
-            c.v_meta[(pg * 2 + 0) * VGROUPS * PG + q * PG + t] = sb;
-            c.v_meta[(pg * 2 + 1) * VGROUPS * PG + q * PG + t] = zb;
-        }
+        // ---- values: unit k is (token t, group q0 + 2 k), consecutive lanes on
+        //      consecutive tokens; both units of a lane share the token
+        if (nvalid == PG)
+            values_of_page<true>(c, vin, tid, pg, g, hkv, nvalid, t0);
+        else
+            values_of_page<false>(c, vin, tid, pg, g, hkv, nvalid, t0);
 
         wait_all_barrier();  // the tile has landed
 #pragma unroll
