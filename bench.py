@@ -87,8 +87,8 @@ def write_traffic(fetch_csv, write_csv, out_json):
     rec = {"kernel_hash": source_hash(), "fetch_scale": round(ff, 4), "write_scale": round(fw, 4),
            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w, "kernels": {}}
     total = 0.0
-    for k in fetch:
-        if "decode_blk_kernel" in k or "merge_kernel" in k:
+    for k in fetch:  # the one-call entry's kernels: the decode with the selection inside, then the merge
+        if ("decode_blk_kernel" in k and "true>" in k) or "merge_kernel" in k:
             b = fetch[k] * 1024 * ff + write.get(k, 0.0) * 1024 * fw
             rec["kernels"][k[:60]] = {"fetch_kib": fetch[k], "write_kib": write.get(k, 0.0), "hbm_bytes": b}
             total += b
@@ -366,12 +366,13 @@ def _summary(name, w, r, n_keep):
     rec = {"workload": name, "batch": B, "context": (max(w.shape.seq_lens) if len(set(w.shape.seq_lens)) == 1
                                                      else "ragged"),
            "n_keep": n_keep, "t_step_us": round(r["t_step_us"], 2), "tokens_per_s": round(B / (r["t_step_us"] * 1e-6), 1),
-           "select_us": round(r["select_us"], 2), "decode_call_us": round(r["decode_us"], 2),
+           "entry": "dqk_select_decode_attn", "call_us": round(r["decode_us"], 2),
            "algorithmic_bytes_per_step": int(r["step_bytes"]),
            "bytes_per_token_head": round(r["bytes_per_token_head"], 3),
            "achieved_step_gbs": round(r["step_bytes"] / (r["t_step_us"] * 1e-6) / 1e9, 1),
            "frac_step": round(r["step_bytes"] / (r["t_step_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-           "achieved_decode_gbs": round(r["decode_bytes"] / (r["decode_us"] * 1e-6) / 1e9, 1),
+           "achieved_call_gbs": round(r["step_bytes"] / (r["decode_us"] * 1e-6) / 1e9, 1),
+           "frac_call": round(r["step_bytes"] / (r["decode_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
            "cache_copies": len(w.caches)}
     return rec
 
@@ -379,8 +380,8 @@ def _summary(name, w, r, n_keep):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--sparsity", type=float, default=0.4)
     ap.add_argument("--seed", type=int, default=0)
@@ -413,33 +414,37 @@ def main():
     w = Int2Workload(shape, args.seed, pa, torch)
     log(f"[bench] cache built on GPU in {time.time() - t0:.1f}s ({w.caches[0].nbytes() / 1e6:.1f} MB, "
         f"{len(w.caches)} copies)")
-    # the step: dqk_select_channels then dqk_decode_attn (split decode + merge)
-    r = w.time_steps(n_keep, args.steps, args.warmup, args.num_splits, fused=False)
-    # for context: the same step as one call with the selection inside the decode launch
-    r1 = w.time_steps(n_keep, max(10, args.steps // 2), args.warmup, args.num_splits, fused=True)
+    # the step: dqk_select_decode_attn, one call (the selection in the decode
+    # kernel's prologue, split decode, merge)
+    r = w.time_steps(n_keep, args.steps, args.warmup, args.num_splits, fused=True)
+    # for context: the same step as two calls, dqk_select_channels then dqk_decode_attn
+    r2 = w.time_steps(n_keep, max(10, args.steps // 2), args.warmup, args.num_splits, fused=False)
     B = shape.batch
     ms_per_step = r["t_step_us"] * 1e-3
-    log(f"[bench] {r['t_step_us']:.1f} us/step; select {r['select_us']:.1f} us; decode call {r['decode_us']:.1f} us "
-        f"(p10 {r['decode_p10_us']:.1f}, p90 {r['decode_p90_us']:.1f}); as one call: {r1['t_step_us']:.1f} us/step "
-        f"(call {r1['decode_us']:.1f} us)")
+    log(f"[bench] {r['t_step_us']:.1f} us/step (one call, {r['decode_us']:.1f} us on the stream, p10 "
+        f"{r['decode_p10_us']:.1f}, p90 {r['decode_p90_us']:.1f}); as two calls: {r2['t_step_us']:.1f} us/step "
+        f"(select {r2['select_us']:.1f} us, decode call {r2['decode_us']:.1f} us)")
 
-    achieved = r["decode_bytes"] / (r["decode_us"] * 1e-6) / 1e9
+    achieved = r["step_bytes"] / (r["decode_us"] * 1e-6) / 1e9
     achieved_step = r["step_bytes"] / (r["t_step_us"] * 1e-6) / 1e9
     khash = source_hash()
     tr = committed_traffic(khash)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": (tr["hbm_bytes_per_launch"] if tr else None),
-            "kernel": "dqk_decode_attn (split decode + merge), HIP events on its stream",
-            "algorithmic_bytes_per_launch": int(r["decode_bytes"]),
+            "kernel": "dqk_select_decode_attn (decode kernel with the selection in its prologue, then merge), "
+                      "HIP events on its stream",
+            "algorithmic_bytes_per_launch": int(r["step_bytes"]),
             "bytes_per_token_head": round(r["bytes_per_token_head"], 3),
             "avg_launch_us": round(r["decode_us"], 2),
-            "step_definition": "dqk_select_channels + dqk_decode_attn (decode + merge), wall clock per step",
+            "step_definition": "dqk_select_decode_attn (selection + split decode + merge), wall clock per step",
             "algorithmic_bytes_per_step": int(r["step_bytes"]),
             "achieved_step": round(achieved_step, 1), "frac_step": round(achieved_step / PEAK_HBM_GBS, 4),
-            "select_us": round(r["select_us"], 2),
-            "one_call_step": {"entry": "dqk_select_decode_attn", "t_step_us": round(r1["t_step_us"], 2),
-                              "call_us": round(r1["decode_us"], 2)},
+            "two_call_step": {"entries": "dqk_select_channels + dqk_decode_attn",
+                              "t_step_us": round(r2["t_step_us"], 2), "select_us": round(r2["select_us"], 2),
+                              "decode_call_us": round(r2["decode_us"], 2),
+                              "frac_step": round(r2["step_bytes"] / (r2["t_step_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                                 4)},
             "kernel_source_hash": khash}
     roof["stream_read_gbs"] = round(stream_read_gbs(torch, pa, int(r["decode_bytes"])), 1)
     roof["frac_of_stream_read"] = round(achieved / roof["stream_read_gbs"], 4)
@@ -468,7 +473,7 @@ def main():
         sub = args.sub_steps
         sweep = {}
         for nk in (128, 103, 77, 52):
-            rs = w.time_steps(nk, sub, 5)
+            rs = w.time_steps(nk, sub, 100, fused=True)
             sweep[str(nk)] = _summary(shape.name, w, rs, nk)
             log(f"[bench] sweep n_keep {nk}: {rs['t_step_us']:.1f} us/step")
         configs["3_sparsity_sweep"] = sweep
@@ -476,13 +481,13 @@ def main():
         torch.cuda.empty_cache()
         s1 = synth.config_shape(1, args.seed)
         w1 = Int2Workload(s1, args.seed, pa, torch)
-        configs["1"] = _summary(s1.name, w1, w1.time_steps(s1.n_keep, sub, 5), s1.n_keep)
+        configs["1"] = _summary(s1.name, w1, w1.time_steps(s1.n_keep, sub, 100, fused=True), s1.n_keep)
         log(f"[bench] config 1: {configs['1']['t_step_us']} us/step")
         del w1
         s2 = synth.config_shape(2, args.seed)
         w2 = Int2Workload(s2, args.seed, pa, torch)
-        c2 = {"int2_40": _summary(s2.name, w2, w2.time_steps(77, sub, 5), 77),
-              "int2_0": _summary(s2.name, w2, w2.time_steps(128, sub, 5), 128)}
+        c2 = {"int2_40": _summary(s2.name, w2, w2.time_steps(77, sub, 100, fused=True), 77),
+              "int2_0": _summary(s2.name, w2, w2.time_steps(128, sub, 100, fused=True), 128)}
         prob2 = w2.prob
         del w2
         torch.cuda.empty_cache()
@@ -517,7 +522,7 @@ def main():
         torch.cuda.empty_cache()
         s4 = synth.config_shape(4, args.seed)
         w4 = Int2Workload(s4, args.seed, pa, torch, one_call=True)
-        c4 = _summary(s4.name, w4, w4.time_steps(s4.n_keep, sub, 5), s4.n_keep)
+        c4 = _summary(s4.name, w4, w4.time_steps(s4.n_keep, sub, 100, fused=True), s4.n_keep)
         c4["total_tokens"] = int(np.sum(s4.seq_lens))
         c4["append"] = append_roofline(w4.append_s, w4.append_tokens, w4.prob.num_pages, s4.hkv)
         c4["append"]["workload"] = f"one call over the ragged batch ({c4['total_tokens']} tokens, shuffled pages)"

@@ -77,7 +77,9 @@ enum {
  *                                              byte c>>2, bits 2*(c&3).
  *   v_meta  f16  [num_pages][Hkv][2][4][128]    [0][q][t] scale, [1][q][t] zero
  *                                              of token t, channels 32q..32q+31.
- * Dequantized value = fma(code, scale, zero) in fp32.  Grid of a group with
+ * The value a code stands for is fma(code, scale, zero) in fp32 (the
+ * definition the decode approximates; its arithmetic is stated at
+ * dqk_decode_attn).  Grid of a group with
  * minimum mn and maximum mx: zero = mn rounded down to binary16, scale =
  * fp32((mx - zero) / 3) rounded up to binary16; code = number of thresholds
  * fma(c + 0.5, scale, zero), c = 0, 1, 2, that the value reaches.
@@ -152,6 +154,25 @@ size_t dqk_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t
  *   workspace   device scratch of at least dqk_decode_workspace_size() bytes.
  *   out         fp32 [batch][hq][128].
  *   lse         fp32 [batch][hq] or NULL: log-sum-exp of the logits.
+ * Arithmetic of the group-4 MFMA decode (hq = 4 hkv, n_keep <= 128; other
+ * groups run a VALU decode with fp32 dequantisation, fma(code, scale, zero)):
+ *   - logits: fp32 sums; the query-side operand C q'_j s_j (C = sm_scale
+ *     log2 e, s_j the key scale) enters as two binary16 limbs (>= 21
+ *     significant bits) scaled per page by a power of two that brings the
+ *     page's largest |C q' s| near 2^14; codes enter exactly; the zero-point
+ *     term sum_j C q'_j z_j is an fp32 sum.  Requires |C q'_j s_j| and the
+ *     logits finite in fp32.
+ *   - probabilities P = 2^(x - m + 14), m the split's integer running
+ *     maximum (log2 units), are rounded to binary16: relative error <= 2^-11;
+ *     weights below 2^-28 of the split's largest are binary16 subnormals
+ *     (absolute error 2^-39 of it) and below 2^-38 of it they are 0.
+ *   - values: P s' is rounded to binary16 (<= 2^-11 relative), s' = s 2^-E
+ *     with E in [-15, 15] the split's running exponent of the value scales;
+ *     the zero points enter as sum_t P_t z_t (binary16 z, fp32 sums).  Value
+ *     scales and zero points are binary16 by format (|value| <= 65504).
+ *   Results therefore depend on the split count through these roundings
+ *   (each split rounds relative to its own maxima), within about
+ *   2^-10 sum_t p_t (|z_t + 1.5 s_t| + 2 |s_t (c_t - 1.5)|) per element.
  */
 int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep, int32_t batch,
                     int32_t hq, const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,

@@ -64,3 +64,16 @@ def gather_seq(cache, page_table, b, L, g):
         ks.append(decode_k(cache, p, g))
         vs.append(decode_v(cache, p, g))
     return np.concatenate(ks)[:L], np.concatenate(vs)[:L]
+
+
+def gather_vparts(cache, page_table, b, L, g):
+    """Value codes [L][128], scales and zero points [L][128] (each channel's
+    group metadata) of sequence b, KV head g."""
+    cs, ss, zs = [], [], []
+    grp = np.arange(128) // 32
+    for pi in range((L + 127) // 128):
+        p = int(page_table[b, pi])
+        cs.append(v_codes(cache, p, g))
+        ss.append(f16(cache.v_meta[p, g, 0])[grp].T)
+        zs.append(f16(cache.v_meta[p, g, 1])[grp].T)
+    return np.concatenate(cs)[:L], np.concatenate(ss)[:L], np.concatenate(zs)[:L]

@@ -84,3 +84,45 @@ def lse_bound(cache, qp, sel, page_table, seq_lens, sm_scale, lse_ref):
 def assert_lse(lse, lse_ref, bound):
     err = np.abs(np.asarray(lse, np.float64) - lse_ref)
     assert (err <= bound).all(), f"lse error {err.max():.3e} above the derived bound (worst ratio {(err / bound).max():.2f})"
+
+
+def split_bound(cache, qp, sel, page_table, seq_lens, sm_scale):
+    """Allowed |o(one split count) - o(another)| per (b, h, channel) for the
+    group-4 MFMA decode.
+
+    Each split rounds the probabilities P_t = 2^(x_t - m + 14), m its own
+    integer running maximum, to binary16, and the products A_t = P_t s'_t
+    (s' = s 2^-E, E the split's running scale exponent) to binary16 again;
+    u = 2^-11 is the unit roundoff of each.  With p_t the exact softmax
+    weights, one split's output differs from the exact sum by at most
+      sum_t p_t (u |z_t + 1.5 s_t| + 2u |s_t| |c_t - 1.5|)   centred value terms
+      + u |o_c|                                              the sum of P (normalisation)
+      + 2^-15 sum_t p_t |v_t|                                fp32 accumulation
+      + 2^-24 max_t s_t                                      subnormal P s'
+      + L 2^-38 max_t |v_t|                                  subnormal P,
+    two splits by twice that."""
+    from tests import cachefmt as cf
+    u = 2.0 ** -11
+    B, hq = qp.shape[0], qp.shape[1]
+    hkv = sel.shape[1]
+    grp = hq // hkv
+    bound = np.zeros((B, hq, 128))
+    for b in range(B):
+        L = int(seq_lens[b])
+        for g in range(hkv):
+            kh, vh = cf.gather_seq(cache, page_table, b, L, g)
+            codes, sc, zp = cf.gather_vparts(cache, page_table, b, L, g)
+            mask = np.zeros(128)
+            mask[sel[b, g]] = 1.0
+            q = qp[b, g * grp:(g + 1) * grp].astype(np.float64) * mask
+            x = (kh.astype(np.float64) @ q.T) * sm_scale            # [L][grp]
+            p = np.exp(x - x.max(0))
+            p /= p.sum(0)
+            v = vh.astype(np.float64)
+            s64, z64 = sc.astype(np.float64), zp.astype(np.float64)
+            centred = u * np.abs(z64 + 1.5 * s64) + 2 * u * np.abs(s64) * np.abs(codes - 1.5)
+            o = p.T @ v                                              # [grp][128]
+            one = (p.T @ centred + u * np.abs(o) + 2.0 ** -15 * (p.T @ np.abs(v))
+                   + 2.0 ** -24 * np.abs(s64).max() + L * 2.0 ** -38 * np.abs(v).max(0))
+            bound[b, g * grp:(g + 1) * grp] = 2 * one
+    return bound

@@ -151,13 +151,13 @@ def test_decode_config1_full():
     assert (rel <= gu.TOL).all()
 
 
-@pytest.mark.parametrize("hq,hkv,tol", [(32, 8, 1e-3), (16, 8, 1e-5)], ids=["mfma-g4", "generic-g2"])
-def test_decode_split_invariance_and_permutation(hq, hkv, tol):
-    """Split count changes only rounding: the group-4 MFMA path rounds the
-    probabilities and P * scale to fp16 relative to each split's running
-    maximum (two roundings of at most 2^-12 relative each, so the outputs of
-    two split counts may differ by about 2^-10 of a row's scale), the generic
-    path keeps fp32 throughout."""
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 8)], ids=["mfma-g4", "generic-g2"])
+def test_decode_split_invariance_and_permutation(hq, hkv):
+    """Split count changes only rounding.  The group-4 MFMA path rounds the
+    probabilities and P * scale to binary16 relative to each split's running
+    maximum: two split counts agree within the bound derived from those
+    roundings (gpu_util.split_bound), element by element.  The generic path
+    keeps fp32 throughout (1e-5 of the row)."""
     _say("decode splits/permutation", hq, hkv)
     shape = synth.Shape(2, hq, hkv, [4000, 2500], 77)
     outs = []
@@ -165,8 +165,15 @@ def test_decode_split_invariance_and_permutation(hq, hkv, tol):
         prob, cache, qp, sel, ref, ref_lse, out, lse = _decode_case(shape, 9, num_splits=ns)
         outs.append(out)
         assert (gu.row_rel_err(out, ref) <= gu.TOL).all()
-    for o in outs[1:]:
-        assert (gu.row_rel_err(o, outs[0]) <= tol).all()
+    if hq == 4 * hkv:
+        bound = gu.split_bound(cache, qp, sel, prob.page_table, prob.seq_lens, prob.sm_scale)
+        for o in outs[1:]:
+            diff = np.abs(o.astype(np.float64) - outs[0])
+            _say(f"  split difference / derived bound: max {(diff / bound).max():.3f}")
+            assert (diff <= bound).all()
+    else:
+        for o in outs[1:]:
+            assert (gu.row_rel_err(o, outs[0]) <= 1e-5).all()
 
     def permute(cache, prob):
         perm = np.random.default_rng(4).permutation(prob.num_pages)
