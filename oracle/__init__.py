@@ -31,6 +31,15 @@ decode_bf16            attention computed from the raw unpaged bf16 keys and
                        tail-garbage invariance (tests/test_oracle_bf16.py)
 paged_bf16             token t of sequence b lands at [page_table[b][t//128]][g]
                        [t%128], checked element by element
+prefill_tiered         tier membership counted token by token; INT2 pages equal
+                       pack_cache of the shifted token range; tier bytes equal
+                       bf16(k') and v slot by slot (tests/test_oracle_tiers.py)
+append_token           token-by-token appends from any length reproduce the
+                       prefill of the final length byte for byte
+decode_tiered          textbook attention (numpy, fp64) over the three token
+                       sources decoded independently; all-BF16 sequences reduce
+                       to attention on bf16 k', v; with every tier token moved
+                       into pages it equals decode_attn on the same tokens
 =====================  ==========================================================
 
 Parity unpinned: the accuracy tables of the paper (need models and datasets).
@@ -83,6 +92,13 @@ def _load():
         _lib.orc_decode_attn.restype = i32
         _lib.orc_decode_bf16.argtypes = [P, P, i32, P, i32, i32, P, i32, P, f64, P, P]
         _lib.orc_decode_bf16.restype = i32
+        _lib.orc_bf16_round_array.argtypes = [P, i64, P]
+        _lib.orc_bf16_round_array.restype = None
+        _lib.orc_tier_pages.argtypes = [i64]
+        _lib.orc_tier_pages.restype = i64
+        _lib.orc_decode_tiered.argtypes = [P, P, P, P, P, i32, P, P, P, P, P, P, i32, i32, i32, P, i32, P, f64, P,
+                                           P]
+        _lib.orc_decode_tiered.restype = i32
     return _lib
 
 
@@ -268,3 +284,123 @@ def paged_bf16(k_bf16, v_bf16, cu_tokens, page_table, num_pages: int):
             kb[p, :, : t1 - t0, :] = np.transpose(k_bf16[t0:t1], (1, 0, 2))
             vb[p, :, : t1 - t0, :] = np.transpose(v_bf16[t0:t1], (1, 0, 2))
     return kb, vb
+
+
+# ---------------------------------------------------------------- BF16 tiers
+# The first 64 and the most recent 256 tokens of a sequence stay in BF16 for
+# keys and values (Dual-QK §3.3), scored under the same channel mask and in
+# one softmax with the INT2 pages (§3.4).  Reading: tokens [0, 64) are the
+# sink (slot t); INT2 page i holds tokens [64 + 128 i, 64 + 128 i + 128) and
+# there are P = floor((L - 320) / 128) of them (0 below 320), so a page is
+# packed once all its tokens are older than the 256 most recent; tokens
+# [64 + 128 P, L) are the tail (256..383 of them once L >= 320), in slot
+# (t - 64) mod 384.  Tier keys are the fp32 k' of key_transform rounded to
+# bf16 (round to nearest even); tier values are the bf16 inputs; the tail
+# also keeps the raw bf16 keys, from which its oldest page is packed.
+SINK, RECENT, TAIL_SLOTS = 64, 256, 384
+
+
+def tier_pages(L: int) -> int:
+    """INT2 pages of a sequence of L tokens."""
+    return int(_load().orc_tier_pages(int(L)))
+
+
+class Tiers:
+    """BF16 tiers of a batch: sink_k, sink_v [B][Hkv][64][128]; tail_k,
+    tail_v, tail_kraw [B][Hkv][384][128]; all bf16 bits (uint16)."""
+
+    def __init__(self, batch: int, hkv: int):
+        self.batch, self.hkv = batch, hkv
+        self.sink_k = np.zeros((batch, hkv, SINK, HEAD_DIM), np.uint16)
+        self.sink_v = np.zeros_like(self.sink_k)
+        self.tail_k = np.zeros((batch, hkv, TAIL_SLOTS, HEAD_DIM), np.uint16)
+        self.tail_v = np.zeros_like(self.tail_k)
+        self.tail_kraw = np.zeros_like(self.tail_k)
+
+    def arrays(self):
+        return self.sink_k, self.sink_v, self.tail_k, self.tail_v, self.tail_kraw
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bits, round to nearest even (the oracle's scalar rule)."""
+    flat = np.ascontiguousarray(x, np.float32).ravel()
+    out = np.empty(flat.size, np.uint16)
+    _load().orc_bf16_round_array(_p(flat), flat.size, _p(out))
+    return out.reshape(np.shape(x))
+
+
+def _put_tier_token(tiers: Tiers, b: int, t: int, kprime_t, k_t, v_t):
+    """Token t of sequence b (k' fp32 [Hkv][128], raw k and v bf16 bits) into its tier slot."""
+    kb = _bf16_bits(kprime_t)
+    if t < SINK:
+        tiers.sink_k[b, :, t] = kb
+        tiers.sink_v[b, :, t] = v_t
+    else:
+        slot = (t - SINK) % TAIL_SLOTS
+        tiers.tail_k[b, :, slot] = kb
+        tiers.tail_v[b, :, slot] = v_t
+        tiers.tail_kraw[b, :, slot] = k_t
+
+
+def prefill_tiered(k_bf16, v_bf16, t_k_bf16, cu_tokens, page_table, num_pages: int):
+    """Whole sequences into the tiered layout; returns (cache, tiers)."""
+    k = _c(k_bf16, np.uint16)
+    v = _c(v_bf16, np.uint16)
+    cu = _c(cu_tokens, np.int32)
+    pt = _c(page_table, np.int32)
+    B, hkv = len(cu) - 1, k.shape[1]
+    kp = key_transform(k, t_k_bf16)
+    cache = Cache(num_pages, hkv)
+    tiers = Tiers(B, hkv)
+    ks, vs, cu2, rows = [], [], [0], []
+    for b in range(B):
+        t0, L = int(cu[b]), int(cu[b + 1] - cu[b])
+        P = tier_pages(L)
+        for t in list(range(min(L, SINK))) + list(range(SINK + PAGE * P, L)):
+            _put_tier_token(tiers, b, t, kp[t0 + t], k[t0 + t], v[t0 + t])
+        ks.append(kp[t0 + SINK:t0 + SINK + PAGE * P])
+        vs.append(v[t0 + SINK:t0 + SINK + PAGE * P])
+        cu2.append(cu2[-1] + PAGE * P)
+        rows.append(pt[b])
+    if cu2[-1] > 0:
+        pack_cache(np.concatenate(ks), np.concatenate(vs), np.array(cu2, np.int32), np.stack(rows), num_pages,
+                   cache)
+    return cache, tiers
+
+
+def append_token(cache: Cache, tiers: Tiers, k_new, v_new, t_k_bf16, seq_lens_before, page_table):
+    """One new token per sequence (k_new, v_new bf16 [B][Hkv][128]) at position
+    seq_lens_before[b]; when the new length completes a page's age, that page
+    is packed from the tail's raw keys and values into page_table[b][i]."""
+    k = _c(k_new, np.uint16)
+    v = _c(v_new, np.uint16)
+    pt = _c(page_table, np.int32)
+    kp = key_transform(k, t_k_bf16)
+    for b in range(k.shape[0]):
+        t = int(seq_lens_before[b])
+        _put_tier_token(tiers, b, t, kp[b], k[b], v[b])
+        P0, P1 = tier_pages(t), tier_pages(t + 1)
+        if P1 > P0:
+            slots = [(PAGE * P0 + i) % TAIL_SLOTS for i in range(PAGE)]
+            kr = np.ascontiguousarray(tiers.tail_kraw[b][:, slots].transpose(1, 0, 2))
+            vr = np.ascontiguousarray(tiers.tail_v[b][:, slots].transpose(1, 0, 2))
+            quantize_append(kr, vr, t_k_bf16, np.array([0, PAGE], np.int32), pt[b:b + 1, P0:P0 + 1],
+                            cache.num_pages, cache)
+
+
+def decode_tiered(cache: Cache, tiers: Tiers, q_prime, sel_idx, page_table, seq_lens, sm_scale: float):
+    qp = _c(q_prime, np.float32)
+    sel = _c(sel_idx, np.int32)
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    B, hq = qp.shape[0], qp.shape[1]
+    n_keep = sel.shape[2]
+    out = np.empty((B, hq, HEAD_DIM), dtype=np.float64)
+    lse = np.empty((B, hq), dtype=np.float64)
+    ta = [_c(a, np.uint16) for a in (tiers.sink_k, tiers.sink_v, tiers.tail_k, tiers.tail_v)]
+    rc = _load().orc_decode_tiered(*[_p(a) for a in cache.arrays()], cache.hkv, *[_p(a) for a in ta], _p(qp),
+                                   _p(sel), n_keep, B, hq, _p(pt), pt.shape[1], _p(sl), float(sm_scale), _p(out),
+                                   _p(lse))
+    if rc:
+        raise ValueError(f"decode_tiered failed (rc={rc})")
+    return out, lse

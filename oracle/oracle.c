@@ -481,3 +481,122 @@ int orc_decode_bf16(const uint16_t *kb, const uint16_t *vb, int hkv, const uint1
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Protected BF16 tiers (§3.3: the first 64 and the most recent 256 tokens of
+ * a sequence stay in BF16 for keys and values, under the same channel mask;
+ * §3.4: one softmax over every token).  Reading: a sequence of length L keeps
+ *   tokens [0, min(L, 64))            in the sink (slot t),
+ *   tokens [64, 64 + 128 P)           in P INT2 pages, P = floor((L - 320)/128)
+ *                                     for L >= 320, else 0 (a page is packed
+ *                                     once all its tokens are older than the
+ *                                     256 most recent),
+ *   tokens [64 + 128 P, L)            in the tail (slot (t - 64) mod 384);
+ * tier keys are k' = k T_K rounded to bf16, tier values the bf16 inputs.
+ *   sink_k, sink_v  bf16 [batch][Hkv][64][128]
+ *   tail_k, tail_v  bf16 [batch][Hkv][384][128]                              */
+#define SINK 64
+#define RECENT 256
+#define TAIL_SLOTS 384
+
+int64_t orc_tier_pages(int64_t L)
+{
+    return L >= SINK + RECENT ? (L - SINK - RECENT) / PG : 0;
+}
+
+int orc_decode_tiered(const uint8_t *k_codes, const uint16_t *k_meta, const uint16_t *k_ch0, const uint8_t *v_codes,
+                      const uint16_t *v_meta, int hkv, const uint16_t *sink_k, const uint16_t *sink_v,
+                      const uint16_t *tail_k, const uint16_t *tail_v, const float *q_prime, const int32_t *sel_idx,
+                      int n_keep, int batch, int hq, const int32_t *page_table, int max_pages,
+                      const int32_t *seq_lens, double sm_scale, double *out, double *lse)
+{
+    if (hkv <= 0 || hq % hkv || n_keep < 1 || n_keep > HD)
+        return -2;
+    int grp = hq / hkv;
+    for (int b = 0; b < batch; ++b) {
+        int64_t L = seq_lens[b];
+        int64_t n_int2 = (int64_t)PG * orc_tier_pages(L);
+        double *logit = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        if (!logit)
+            return -7;
+        for (int h = 0; h < hq; ++h) {
+            int g = h / grp;
+            const float *qp = q_prime + ((size_t)b * hq + h) * HD;
+            const int32_t *M = sel_idx + ((size_t)b * hkv + g) * n_keep;
+            double mx = -INFINITY;
+            for (int64_t t = 0; t < L; ++t) {
+                double acc = 0.0;
+                if (t < SINK || t >= SINK + n_int2) {
+                    /* a BF16 tier token: k' rounded to bf16 */
+                    const uint16_t *kr = t < SINK
+                                             ? sink_k + (((size_t)b * hkv + g) * SINK + (size_t)t) * HD
+                                             : tail_k + (((size_t)b * hkv + g) * TAIL_SLOTS +
+                                                         (size_t)((t - SINK) % TAIL_SLOTS)) * HD;
+                    for (int m = 0; m < n_keep; ++m)
+                        acc += (double)qp[M[m]] * (double)orc_bf16_value(kr[M[m]]);
+                } else {
+                    int64_t i = t - SINK; /* INT2 token index */
+                    int64_t p = page_table[(size_t)b * max_pages + (i >> 7)];
+                    int s = (int)(i & (PG - 1));
+                    size_t pg = (size_t)p * hkv + g;
+                    for (int m = 0; m < n_keep; ++m) {
+                        int j = M[m];
+                        float kv;
+                        if (j == 0) {
+                            kv = orc_bf16_value(k_ch0[pg * PG + s]);
+                        } else {
+                            size_t r = krow(p, g, hkv, j);
+                            int c = (k_codes[r * 32 + (s >> 2)] >> (2 * (s & 3))) & 3;
+                            kv = orc_dequant(c, k_meta[r * 2], k_meta[r * 2 + 1]);
+                        }
+                        acc += (double)qp[j] * (double)kv;
+                    }
+                }
+                logit[t] = acc * sm_scale;
+                if (logit[t] > mx)
+                    mx = logit[t];
+            }
+            double l = 0.0, o[HD];
+            for (int c = 0; c < HD; ++c)
+                o[c] = 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                double pw = exp(logit[t] - mx);
+                l += pw;
+                if (t < SINK || t >= SINK + n_int2) {
+                    const uint16_t *vr = t < SINK
+                                             ? sink_v + (((size_t)b * hkv + g) * SINK + (size_t)t) * HD
+                                             : tail_v + (((size_t)b * hkv + g) * TAIL_SLOTS +
+                                                         (size_t)((t - SINK) % TAIL_SLOTS)) * HD;
+                    for (int c = 0; c < HD; ++c)
+                        o[c] += pw * (double)orc_bf16_value(vr[c]);
+                } else {
+                    int64_t i = t - SINK;
+                    int64_t p = page_table[(size_t)b * max_pages + (i >> 7)];
+                    int s = (int)(i & (PG - 1));
+                    size_t pg = (size_t)p * hkv + g;
+                    const uint8_t *vr = v_codes + (pg * PG + s) * 32;
+                    const uint16_t *vm = v_meta + pg * 2 * 4 * PG;
+                    for (int c = 0; c < HD; ++c) {
+                        int q = c / VGROUP;
+                        int code = (vr[c >> 2] >> (2 * (c & 3))) & 3;
+                        o[c] += pw * (double)orc_dequant(code, vm[(0 * 4 + q) * PG + s], vm[(1 * 4 + q) * PG + s]);
+                    }
+                }
+            }
+            for (int c = 0; c < HD; ++c)
+                out[((size_t)b * hq + h) * HD + c] = o[c] / l;
+            if (lse)
+                lse[(size_t)b * hq + h] = mx + log(l);
+        }
+        free(logit);
+    }
+    return 0;
+}
+
+/* bf16 bits of n fp32 values, round to nearest even (orc_bf16_round_nearest
+ * element by element). */
+void orc_bf16_round_array(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_bf16_round_nearest(x[i]);
+}
