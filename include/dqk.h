@@ -232,6 +232,78 @@ int dqk_decode_attn_bf16(const void *k_pages, const void *v_pages, int32_t hkv, 
                          size_t ws_bytes, float *out, float *lse, hipStream_t stream);
 
 /*
+ * Protected BF16 tiers (§3.3: the first 64 and the most recent 256 tokens of
+ * a sequence stay in BF16 for keys and values and use the same channel mask;
+ * §3.4: one softmax over every token).  In the tiered layout a sequence of
+ * length L keeps
+ *   tokens [0, min(L, 64))        in the sink, slot t;
+ *   tokens [64, 64 + 128 P)       in P INT2 pages, P = floor((L - 320) / 128)
+ *                                 for L >= 320, else 0: logical INT2 page i
+ *                                 (page_table[b][i]) holds tokens
+ *                                 64 + 128 i .. 64 + 128 i + 127, all older
+ *                                 than the 256 most recent tokens;
+ *   tokens [64 + 128 P, L)        in the tail (256..383 tokens once L >= 320),
+ *                                 slot (t - 64) mod 384.
+ * Tier keys are k' = k T_K (fp32) rounded to bf16 (nearest even); tier values
+ * are the bf16 inputs; the tail also keeps the raw bf16 keys, from which its
+ * oldest page is packed when the sequence grows past it.
+ */
+#define DQK_TIER_SINK 64
+#define DQK_TIER_RECENT 256
+#define DQK_TIER_TAIL_SLOTS 384
+
+typedef struct dqk_tiers {
+    int32_t batch;        /* sequences                                   */
+    int32_t num_kv_heads; /* must equal the cache's                      */
+    uint16_t *sink_k;     /* bf16 [batch][Hkv][64][128]  k' of the sink   */
+    uint16_t *sink_v;     /* bf16 [batch][Hkv][64][128]                   */
+    uint16_t *tail_k;     /* bf16 [batch][Hkv][384][128] k' of the tail   */
+    uint16_t *tail_v;     /* bf16 [batch][Hkv][384][128]                  */
+    uint16_t *tail_kraw;  /* bf16 [batch][Hkv][384][128] raw k of the tail */
+} dqk_tiers;
+
+/*
+ * Prefill into the tiered layout: sequence b (tokens cu_tokens[b] ..
+ * cu_tokens[b+1]-1 of k_bf16 / v_bf16, as dqk_quantize_append) fills its
+ * sink and tail slots and its INT2 pages page_table[b][0 .. P-1].
+ * Requires n_seqs <= tiers->batch; other arguments and errors as
+ * dqk_quantize_append.
+ */
+int dqk_prefill_tiered(const dqk_cache *c, const dqk_tiers *tiers, const void *k_bf16, const void *v_bf16,
+                       const void *t_k_bf16, int32_t n_seqs, const int32_t *cu_tokens, int64_t total_tokens,
+                       const int32_t *page_table, int32_t max_pages, hipStream_t stream);
+
+/*
+ * Per-token append (a decode step): sequence b gains one token at position
+ * lens_before[b] (device int32 [batch], its length before the call), keys
+ * k_bf16 and values v_bf16 bf16 [batch][Hkv][128].  The token goes to its
+ * sink or tail slot; if the new length lets a page leave the recent window,
+ * that page is packed from the tail into page_table[b][P] (P = INT2 pages
+ * before the call) exactly as the prefill would pack it.  The caller then
+ * counts the token in its lengths.  Two kernels, stream-ordered.
+ */
+int dqk_append_token(const dqk_cache *c, const dqk_tiers *tiers, const void *k_bf16, const void *v_bf16,
+                     const void *t_k_bf16, int32_t batch, const int32_t *lens_before, const int32_t *page_table,
+                     int32_t max_pages, hipStream_t stream);
+
+/* Bytes of workspace dqk_decode_attn_tiered needs. */
+size_t dqk_decode_tiered_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t max_pages,
+                                        int32_t num_splits);
+
+/*
+ * Decode attention over the tiered layout: the INT2 pages of each sequence
+ * (as dqk_decode_attn, over its P pages) and its BF16 sink and tail tokens
+ * (logit = sm_scale * sum_{j in M} q'_j k'_j with the bf16 k', value the
+ * bf16 v) under one softmax, merged by log-sum-exp.  seq_lens[b] is the
+ * sequence's full length L (>= 1).  Other arguments, the workspace (of
+ * dqk_decode_tiered_workspace_size bytes) and errors as dqk_decode_attn.
+ */
+int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const float *q_prime, const int32_t *sel_idx,
+                           int32_t n_keep, int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                           const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
+                           size_t ws_bytes, float *out, float *lse, hipStream_t stream);
+
+/*
  * dqk_stream_read -- measurement helper, not part of the attention path: a
  * plain streaming read of `bytes` bytes (a multiple of 16 KiB) at `src`,
  * 16 bytes per lane through LDS, as the reference point for the decode

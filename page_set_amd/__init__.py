@@ -40,6 +40,15 @@ class dqk_cache(ctypes.Structure):
                 ("v_codes", ctypes.c_void_p), ("v_meta", ctypes.c_void_p)]
 
 
+class dqk_tiers(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("sink_k", ctypes.c_void_p), ("sink_v", ctypes.c_void_p), ("tail_k", ctypes.c_void_p),
+                ("tail_v", ctypes.c_void_p), ("tail_kraw", ctypes.c_void_p)]
+
+
+TIER_SINK, TIER_RECENT, TIER_TAIL_SLOTS = 64, 256, 384
+
+
 def lib():
     """The loaded libdqk (raises if it has not been built)."""
     global _lib
@@ -72,6 +81,16 @@ def lib():
         L.dqk_decode_attn_bf16.argtypes = [P, P, i32, i32, P, i32, i32, P, i32, P, ctypes.c_float, i32, P, sz, P, P,
                                            P]
         L.dqk_decode_attn_bf16.restype = ctypes.c_int
+        T = ctypes.POINTER(dqk_tiers)
+        L.dqk_prefill_tiered.argtypes = [ctypes.POINTER(dqk_cache), T, P, P, P, i32, P, i64, P, i32, P]
+        L.dqk_prefill_tiered.restype = ctypes.c_int
+        L.dqk_append_token.argtypes = [ctypes.POINTER(dqk_cache), T, P, P, P, i32, P, P, i32, P]
+        L.dqk_append_token.restype = ctypes.c_int
+        L.dqk_decode_tiered_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.dqk_decode_tiered_workspace_size.restype = sz
+        L.dqk_decode_attn_tiered.argtypes = [ctypes.POINTER(dqk_cache), T, P, P, i32, i32, i32, P, i32, P,
+                                             ctypes.c_float, i32, P, sz, P, P, P]
+        L.dqk_decode_attn_tiered.restype = ctypes.c_int
         L.dqk_stream_read.argtypes = [P, sz, P, P]
         L.dqk_stream_read.restype = ctypes.c_int
         _lib = L
@@ -127,6 +146,72 @@ class Cache:
         kc = self.k_codes.permute(0, 3, 1, 2, 4).reshape(P, H, HEAD_DIM, 32)
         km = self.k_meta.permute(0, 3, 1, 2, 4).reshape(P, H, HEAD_DIM, 2)
         return kc, km, self.k_ch0, self.v_codes, self.v_meta
+
+
+class Tiers:
+    """Device buffers of the BF16 tiers (layout in include/dqk.h):
+    sink_k, sink_v [B][Hkv][64][128]; tail_k, tail_v, tail_kraw [B][Hkv][384][128]; bf16 bits."""
+
+    def __init__(self, batch: int, num_kv_heads: int, device="cuda"):
+        import torch
+        self.batch, self.num_kv_heads = int(batch), int(num_kv_heads)
+        B, H = self.batch, self.num_kv_heads
+        self.sink_k = torch.zeros((B, H, TIER_SINK, HEAD_DIM), dtype=torch.int16, device=device)
+        self.sink_v = torch.zeros_like(self.sink_k)
+        self.tail_k = torch.zeros((B, H, TIER_TAIL_SLOTS, HEAD_DIM), dtype=torch.int16, device=device)
+        self.tail_v = torch.zeros_like(self.tail_k)
+        self.tail_kraw = torch.zeros_like(self.tail_k)
+
+    def arrays(self):
+        return self.sink_k, self.sink_v, self.tail_k, self.tail_v, self.tail_kraw
+
+    def struct(self) -> dqk_tiers:
+        return dqk_tiers(self.batch, self.num_kv_heads, *[a.data_ptr() for a in self.arrays()])
+
+
+def dqk_prefill_tiered(cache: Cache, tiers: Tiers, k, v, t_k, cu_tokens, page_table, stream=None):
+    n_seqs = cu_tokens.numel() - 1
+    s, t = cache.struct(), tiers.struct()
+    rc = lib().dqk_prefill_tiered(ctypes.byref(s), ctypes.byref(t), _ptr(k), _ptr(v), _ptr(t_k), n_seqs,
+                                  _ptr(cu_tokens), int(k.shape[0]), _ptr(page_table), int(page_table.shape[1]),
+                                  _stream(stream))
+    _check(rc, "dqk_prefill_tiered")
+
+
+def dqk_append_token(cache: Cache, tiers: Tiers, k_new, v_new, t_k, lens_before, page_table, stream=None):
+    s, t = cache.struct(), tiers.struct()
+    rc = lib().dqk_append_token(ctypes.byref(s), ctypes.byref(t), _ptr(k_new), _ptr(v_new), _ptr(t_k),
+                                int(k_new.shape[0]), _ptr(lens_before), _ptr(page_table), int(page_table.shape[1]),
+                                _stream(stream))
+    _check(rc, "dqk_append_token")
+
+
+def dqk_decode_tiered_workspace_size(batch: int, hq: int, hkv: int, max_pages: int, num_splits: int = 0) -> int:
+    return int(lib().dqk_decode_tiered_workspace_size(batch, hq, hkv, max_pages, num_splits))
+
+
+def dqk_decode_attn_tiered(cache: Cache, tiers: Tiers, q_prime, sel_idx, page_table, seq_lens, sm_scale: float,
+                           num_splits: int = 0, workspace=None, out=None, lse=None, want_lse: bool = True,
+                           stream=None):
+    import torch
+    B, hq = int(q_prime.shape[0]), int(q_prime.shape[1])
+    n_keep = int(sel_idx.shape[2])
+    max_pages = int(page_table.shape[1])
+    dev = q_prime.device
+    if workspace is None:
+        n = dqk_decode_tiered_workspace_size(B, hq, cache.num_kv_heads, max_pages, num_splits)
+        workspace = torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    s, t = cache.struct(), tiers.struct()
+    rc = lib().dqk_decode_attn_tiered(ctypes.byref(s), ctypes.byref(t), _ptr(q_prime), _ptr(sel_idx), n_keep, B, hq,
+                                      _ptr(page_table), max_pages, _ptr(seq_lens), float(sm_scale), int(num_splits),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+                                      _ptr(lse), _stream(stream))
+    _check(rc, "dqk_decode_attn_tiered")
+    return out, lse
 
 
 def dqk_quantize_append(cache: Cache, k, v, t_k, cu_tokens, page_table, kprime_dbg=None, stream=None):

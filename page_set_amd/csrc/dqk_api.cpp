@@ -31,6 +31,15 @@ int check_cache(const dqk_cache *c) {
     return DQK_OK;
 }
 
+int check_tiers(const dqk_tiers *t, const dqk_cache *c) {
+    if (!t || !t->sink_k || !t->sink_v || !t->tail_k || !t->tail_v || !t->tail_kraw) return DQK_ERR_NULL;
+    if (t->batch < 1 || t->num_kv_heads != c->num_kv_heads) return DQK_ERR_SHAPE;
+    if (!aligned16(t->sink_k) || !aligned16(t->sink_v) || !aligned16(t->tail_k) || !aligned16(t->tail_v) ||
+        !aligned16(t->tail_kraw))
+        return DQK_ERR_ALIGN;
+    return DQK_OK;
+}
+
 // n_keep = 0: the largest count any n_keep can resolve to (workspace sizing)
 int resolve_splits(int batch, int hq, int hkv, int max_pages, int num_splits, int n_keep) {
     if (num_splits > 0) return num_splits;
@@ -211,6 +220,101 @@ int dqk_decode_attn_noalloc(const dqk_cache *c, const float *q_prime, const int3
 }
 
 size_t dqk_decode_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+int dqk_prefill_tiered(const dqk_cache *c, const dqk_tiers *tiers, const void *k_bf16, const void *v_bf16,
+                       const void *t_k_bf16, int32_t n_seqs, const int32_t *cu_tokens, int64_t total_tokens,
+                       const int32_t *page_table, int32_t max_pages, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    st = check_tiers(tiers, c);
+    if (st) return st;
+    if (!k_bf16 || !v_bf16 || !t_k_bf16 || !cu_tokens || !page_table) return DQK_ERR_NULL;
+    if (n_seqs < 1 || n_seqs > tiers->batch || max_pages < 1 || total_tokens < 1) return DQK_ERR_SHAPE;
+    if (n_seqs > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(t_k_bf16) || !aligned16(cu_tokens) ||
+        !aligned16(page_table))
+        return DQK_ERR_ALIGN;
+    const uint16_t *k = static_cast<const uint16_t *>(k_bf16), *v = static_cast<const uint16_t *>(v_bf16);
+    const uint16_t *tk = static_cast<const uint16_t *>(t_k_bf16);
+    hipError_t e = dqk::launch_tier_fill(*tiers, k, v, tk, n_seqs, cu_tokens, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(dqk::launch_append_tiered(*c, k, v, tk, n_seqs, cu_tokens, page_table, max_pages, stream));
+}
+
+int dqk_append_token(const dqk_cache *c, const dqk_tiers *tiers, const void *k_bf16, const void *v_bf16,
+                     const void *t_k_bf16, int32_t batch, const int32_t *lens_before, const int32_t *page_table,
+                     int32_t max_pages, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    st = check_tiers(tiers, c);
+    if (st) return st;
+    if (!k_bf16 || !v_bf16 || !t_k_bf16 || !lens_before || !page_table) return DQK_ERR_NULL;
+    if (batch < 1 || batch > tiers->batch || max_pages < 1) return DQK_ERR_SHAPE;
+    if (batch > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(t_k_bf16) || !aligned16(lens_before) ||
+        !aligned16(page_table))
+        return DQK_ERR_ALIGN;
+    const uint16_t *k = static_cast<const uint16_t *>(k_bf16), *v = static_cast<const uint16_t *>(v_bf16);
+    const uint16_t *tk = static_cast<const uint16_t *>(t_k_bf16);
+    hipError_t e = dqk::launch_tier_token(*tiers, k, v, tk, batch, lens_before, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(dqk::launch_pack_tail(*c, *tiers, tk, batch, lens_before, page_table, max_pages, stream));
+}
+
+namespace {
+// workspace of the tiered decode: INT2 split partials, one partial per row
+// for the BF16 tokens, the INT2 lengths
+size_t tiered_ws_bytes(int batch, int hq, int splits) {
+    const size_t main = (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float);
+    const size_t tier = (size_t)batch * hq * dqk::PART_FLOATS * sizeof(float);
+    const size_t lens = ((size_t)batch * sizeof(int32_t) + 15) / 16 * 16;
+    return main + tier + lens;
+}
+}  // namespace
+
+size_t dqk_decode_tiered_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t max_pages,
+                                        int32_t num_splits) {
+    if (batch < 1 || hq < 1 || hkv < 1 || max_pages < 1 || num_splits < 0) return 0;
+    int s = resolve_splits(batch, hq, hkv, max_pages, num_splits, 0);
+    const int s_gen = num_splits > 0 ? num_splits : dqk::decode_splits_generic(batch, hkv, max_pages);
+    if (s_gen > s) s = s_gen;
+    return tiered_ws_bytes(batch, hq, s);
+}
+
+int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const float *q_prime, const int32_t *sel_idx,
+                           int32_t n_keep, int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                           const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
+                           size_t ws_bytes, float *out, float *lse, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    st = check_tiers(tiers, c);
+    if (st) return st;
+    if (!q_prime || !sel_idx || !page_table || !seq_lens || !workspace || !out) return DQK_ERR_NULL;
+    const int hkv = c->num_kv_heads;
+    if (batch < 1 || batch > tiers->batch || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM ||
+        max_pages < 1 || num_splits < 0 || num_splits > max_pages)
+        return DQK_ERR_SHAPE;
+    const bool mfma = dqk::use_mfma_decode(hq, hkv, n_keep);
+    if (hq / hkv > dqk::GENERIC_MAX_GROUP) return DQK_ERR_UNSUPPORTED;
+    if ((int64_t)batch * hkv > 65535 || batch * hq > 2147483647 / 2) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(q_prime) || !aligned16(sel_idx) || !aligned16(page_table) || !aligned16(seq_lens) ||
+        !aligned16(workspace) || !aligned16(out) || (lse && !aligned16(lse)))
+        return DQK_ERR_ALIGN;
+    const int splits = resolve_splits(batch, hq, hkv, max_pages, num_splits, n_keep);
+    if (ws_bytes < tiered_ws_bytes(batch, hq, splits)) return DQK_ERR_WORKSPACE;
+    float *parts = static_cast<float *>(workspace);
+    float *tier_parts = parts + (size_t)batch * hq * splits * dqk::PART_FLOATS;
+    int32_t *int2_lens = reinterpret_cast<int32_t *>(tier_parts + (size_t)batch * hq * dqk::PART_FLOATS);
+    hipError_t e = dqk::launch_tier_lens(seq_lens, batch, int2_lens, stream);
+    if (e != hipSuccess) return hip_status(e);
+    dqk::DecodeArgs a{c,         q_prime,  sel_idx, n_keep, batch, hq, hkv, page_table, max_pages, int2_lens,
+                      sm_scale, splits, parts,   out,    lse};
+    e = mfma ? dqk::launch_decode_mfma(a, stream) : dqk::launch_decode_generic(a, stream);
+    if (e != hipSuccess) return hip_status(e);
+    e = dqk::launch_tier_decode(*tiers, q_prime, sel_idx, n_keep, batch, hq, seq_lens, sm_scale, tier_parts, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(dqk::launch_merge_extra(parts, batch, hq, splits, tier_parts, out, lse, stream));
+}
 
 int dqk_decode_attn_bf16(const void *k_pages, const void *v_pages, int32_t hkv, int32_t num_pages,
                          const void *q_bf16, int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,

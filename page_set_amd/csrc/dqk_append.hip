@@ -111,14 +111,15 @@ __device__ __forceinline__ void pack_value_unit(const u32x4 (&raw)[4], uint64_t 
     zb = gr.zb;
 }
 
-// The values of one page: thread tid packs units (token t, group q0 + 2 k),
-// t = tid % 128, q0 = tid / 128.  FULL: all 128 tokens valid.
+// The values of one page (token t's 128 values at vpage + t vstride): thread
+// tid packs units (token t, group q0 + 2 k), t = tid % 128, q0 = tid / 128.
+// FULL: all 128 tokens valid.
 template <bool FULL>
-__device__ __forceinline__ void values_of_page(const dqk_cache &c, const uint16_t *__restrict__ vin, int tid,
-                                               size_t pg, int g, int hkv, int nvalid, int64_t t0) {
+__device__ __forceinline__ void values_of_page(const dqk_cache &c, const uint16_t *__restrict__ vpage,
+                                               size_t vstride, int tid, size_t pg, int nvalid) {
     const int t = tid & (PG - 1), q0 = tid / PG;
     const bool valid = FULL || t < nvalid;
-    const uint16_t *vsrc = vin + ((size_t)(t0 + (valid ? t : 0)) * hkv + g) * D + q0 * 32;
+    const uint16_t *vsrc = vpage + (size_t)(valid ? t : 0) * vstride + q0 * 32;
     u32x4 raw[VLD][4];
 #pragma unroll
     for (int k = 0; k < VLD; ++k)
@@ -221,11 +222,31 @@ __device__ __forceinline__ void keys_of_page(const dqk_cache &c, uint32_t ks, co
         *reinterpret_cast<uint32_t *>(c.k_meta + krow(p, g, hkv, ch) * 2) = (uint32_t)gr.sb | ((uint32_t)gr.zb << 16);
 }
 
-template <bool DBG>
-__global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, const uint16_t *__restrict__ kin,
-                                                     const uint16_t *__restrict__ vin,
-                                                     const uint16_t *__restrict__ t_k,
-                                                     const int32_t *__restrict__ cu_tokens,
+// Where the pages of a launch come from.
+//   APPEND_PLAIN   sequence sq = blockIdx.y, tokens cu_tokens[sq] ..; logical
+//                  page i holds tokens 128 i .. (the last one may be partial).
+//   APPEND_TIERED  the same inputs, but page i holds tokens 64 + 128 i .. and
+//                  only the tier_pages(L) whole pages older than the 256 most
+//                  recent tokens are written (the rest stays in the BF16 tiers).
+//   APPEND_TAIL    sequence b = blockIdx.y gains token lens_before[b]; if the
+//                  new length completes a page's age, that page (tier_pages of
+//                  the old length) is packed from the tail's raw keys and
+//                  values (slots (128 i .. 128 i + 127) mod 384).
+enum { APPEND_PLAIN = 0, APPEND_TIERED = 1, APPEND_TAIL = 2 };
+
+struct AppendSrc {
+    const uint16_t *kin, *vin;
+    const int32_t *cu_tokens;
+    const int32_t *lens_before;
+    const uint16_t *tail_kraw, *tail_v;
+};
+
+__device__ __forceinline__ int64_t tier_pages_of(int64_t L) {
+    return L >= TIER_SINK + TIER_RECENT ? (L - TIER_SINK - TIER_RECENT) / PG : 0;
+}
+
+template <bool DBG, int MODE>
+__global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, AppendSrc src, const uint16_t *__restrict__ t_k,
                                                      const int32_t *__restrict__ page_table, int max_pages,
                                                      float *__restrict__ kprime_dbg) {
     // T_K^T [out ch][in ch] first, then each page's key tile [token][in ch]; rows of 256 bytes
@@ -234,11 +255,24 @@ __global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, const uint1
 
     const int sq = blockIdx.y, g = blockIdx.z;
     const int hkv = c.num_kv_heads;
-    const int64_t tok0 = cu_tokens[sq];
-    const int64_t L = (int64_t)cu_tokens[sq + 1] - tok0;
-    const int pi0 = blockIdx.x * NPW;
-    if ((int64_t)pi0 * PG >= L) return;
-    const int pi_end = (int)min<int64_t>(min(pi0 + NPW, max_pages), (L + PG - 1) / PG);
+    int64_t tok0 = 0, first0 = 0;  // input token of the sequence's start and of page 0
+    int pi0, pi_end;
+    if constexpr (MODE == APPEND_TAIL) {
+        const int64_t Lb = src.lens_before[sq];
+        const int64_t P0 = tier_pages_of(Lb);
+        if (tier_pages_of(Lb + 1) == P0 || P0 >= max_pages) return;
+        pi0 = (int)P0;
+        pi_end = pi0 + 1;
+    } else {
+        tok0 = src.cu_tokens[sq];
+        const int64_t L = (int64_t)src.cu_tokens[sq + 1] - tok0;
+        const int64_t npg = MODE == APPEND_TIERED ? tier_pages_of(L) : (L + PG - 1) / PG;
+        first0 = tok0 + (MODE == APPEND_TIERED ? TIER_SINK : 0);
+        pi0 = blockIdx.x * NPW;
+        if (pi0 >= npg) return;
+        pi_end = (int)min<int64_t>(min(pi0 + NPW, max_pages), npg);
+    }
+    const int64_t L_plain = MODE == APPEND_PLAIN ? (int64_t)src.cu_tokens[sq + 1] - tok0 : 0;
     // ---- T_K^T: thread (row pair rp, column octet oc) stores the two rows'
     //      elements of each column as one 4-byte word
     const uint16_t *T = t_k + (size_t)g * D * D;
@@ -266,10 +300,23 @@ __global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, const uint1
         }
 
     for (int pi = pi0; pi < pi_end; ++pi) {
-        const int nvalid = (int)min<int64_t>(PG, L - (int64_t)pi * PG);
+        const int nvalid = MODE == APPEND_PLAIN ? (int)min<int64_t>(PG, L_plain - (int64_t)pi * PG) : PG;
         const int64_t p = page_table[(size_t)sq * max_pages + pi];
-        const int64_t t0 = tok0 + (int64_t)pi * PG;
+        const int64_t t0 = first0 + (int64_t)pi * PG;  // input token of the page's slot 0 (not APPEND_TAIL)
         const size_t pg = (size_t)p * hkv + g;
+        // the page's token rows: row t at kpage + t kstride (and the same for values)
+        const uint16_t *kpage, *vpage;
+        size_t kstride;
+        if constexpr (MODE == APPEND_TAIL) {
+            const size_t slot0 = ((size_t)sq * hkv + g) * TIER_TAIL_SLOTS + (size_t)((PG * pi) % TIER_TAIL_SLOTS);
+            kpage = src.tail_kraw + slot0 * D;
+            vpage = src.tail_v + slot0 * D;
+            kstride = D;
+        } else {
+            kpage = src.kin + ((size_t)t0 * hkv + g) * D;
+            vpage = src.vin + ((size_t)t0 * hkv + g) * D;
+            kstride = (size_t)hkv * D;
+        }
 
         __syncthreads();  // the previous tile (or T_K^T) has been read by every wave
         const int tid = fresh_tid(), lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -281,26 +328,25 @@ __global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, const uint1
         const uint32_t slot_off = ((uint32_t)(lane & 15) ^ (uint32_t)(G | 4 * w)) * 16;
         const uint32_t tile_w = ks + (uint32_t)(KLD * w) * 1024;
         if (nvalid == PG) {
-            const uint32_t voff = (uint32_t)(G * hkv * D) * 2 + slot_off;
+            const uint32_t voff = (uint32_t)(G * kstride) * 2 + slot_off;
 #pragma unroll
             for (int i = 0; i < KLD; ++i)
-                dma16(kin + ((size_t)(t0 + 4 * KLD * w + 4 * i) * hkv + g) * D, voff, tile_w + i * 1024);
+                dma16(kpage + (size_t)(4 * KLD * w + 4 * i) * kstride, voff, tile_w + i * 1024);
         } else {
-            const uint16_t *kbase = kin + ((size_t)t0 * hkv + g) * D;
 #pragma unroll
             for (int i = 0; i < KLD; ++i) {
                 const int row = row0 + 4 * i;
-                const int src = row < nvalid ? row : 0;
-                dma16(kbase, (uint32_t)(src * hkv * D) * 2 + slot_off, tile_w + i * 1024);
+                const int srow = row < nvalid ? row : 0;
+                dma16(kpage, (uint32_t)(srow * kstride) * 2 + slot_off, tile_w + i * 1024);
             }
         }
 
         // ---- values: unit k is (token t, group q0 + 2 k), consecutive lanes on
         //      consecutive tokens; both units of a lane share the token
         if (nvalid == PG)
-            values_of_page<true>(c, vin, tid, pg, g, hkv, nvalid, t0);
+            values_of_page<true>(c, vpage, kstride, tid, pg, nvalid);
         else
-            values_of_page<false>(c, vin, tid, pg, g, hkv, nvalid, t0);
+            values_of_page<false>(c, vpage, kstride, tid, pg, nvalid);
 
         wait_all_barrier();  // the tile has landed
 #pragma unroll
@@ -320,12 +366,32 @@ hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *
                          const int32_t *cu_tokens, const int32_t *page_table, int max_pages, float *kprime_dbg,
                          hipStream_t s) {
     dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
+    const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr};
     if (kprime_dbg)
-        hipLaunchKernelGGL(append_kernel<true>, grid, dim3(256), 0, s, c, k, v, t_k, cu_tokens, page_table, max_pages,
-                           kprime_dbg);
-    else
-        hipLaunchKernelGGL(append_kernel<false>, grid, dim3(256), 0, s, c, k, v, t_k, cu_tokens, page_table,
+        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                            max_pages, kprime_dbg);
+    else
+        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+                           max_pages, kprime_dbg);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_tiered(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                                int n_seqs, const int32_t *cu_tokens, const int32_t *page_table, int max_pages,
+                                hipStream_t s) {
+    dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
+    const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr};
+    hipLaunchKernelGGL((append_kernel<false, APPEND_TIERED>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+                       max_pages, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_tail(const dqk_cache &c, const dqk_tiers &t, const uint16_t *t_k, int batch,
+                            const int32_t *lens_before, const int32_t *page_table, int max_pages, hipStream_t s) {
+    dim3 grid(1, batch, c.num_kv_heads);
+    const AppendSrc src{nullptr, nullptr, nullptr, lens_before, t.tail_kraw, t.tail_v};
+    hipLaunchKernelGGL((append_kernel<false, APPEND_TAIL>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+                       max_pages, nullptr);
     return hipGetLastError();
 }
 

@@ -307,27 +307,32 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const uint16_t *__rest
 // (sequence, query head), lane = channel.
 constexpr int MERGE_FAST = 32;  // splits whose partials one lane keeps in registers
 
-__global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ partials, int nsplit,
-                                                  float *__restrict__ out, float *__restrict__ lse) {
+__global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ partials, int nsplit_main,
+                                                  const float *__restrict__ extra, float *__restrict__ out,
+                                                  float *__restrict__ lse) {
     // one block of 128 lanes per (sequence, query head); lane c owns output channel c
     __shared__ float w_lds[D];
     __shared__ float red[3][D / 64];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const float *P = partials + (size_t)bh * nsplit * PART_FLOATS;
+    const float *P = partials + (size_t)bh * nsplit_main * PART_FLOATS;
+    // partial s: split s of the decode, or (s = nsplit_main) the extra one of this row
+    const int nsplit = nsplit_main + (extra ? 1 : 0);
+    const float *X = extra ? extra + (size_t)bh * PART_FLOATS : nullptr;
+    auto part = [&](int s) { return s < nsplit_main ? P + (size_t)s * PART_FLOATS : X; };
     // every load that does not depend on the maximum is issued up front
     float xf[MERGE_FAST];
     if (nsplit <= MERGE_FAST) {
 #pragma unroll
-        for (int s = 0; s < MERGE_FAST; ++s) xf[s] = s < nsplit ? P[(size_t)s * PART_FLOATS + tid] : 0.0f;
+        for (int s = 0; s < MERGE_FAST; ++s) xf[s] = s < nsplit ? part(s)[tid] : 0.0f;
     }
     float M = -__builtin_huge_valf(), m_own = -__builtin_huge_valf(), l_own = 0.0f, l32_own = 0.0f;
     if (tid < nsplit) {
-        m_own = P[(size_t)tid * PART_FLOATS + D];
-        l_own = P[(size_t)tid * PART_FLOATS + D + 1];
-        l32_own = P[(size_t)tid * PART_FLOATS + D + 2];
+        m_own = part(tid)[D];
+        l_own = part(tid)[D + 1];
+        l32_own = part(tid)[D + 2];
     }
     M = m_own;
-    for (int s = tid + D; s < nsplit; s += D) M = fmaxf(M, P[(size_t)s * PART_FLOATS + D]);
+    for (int s = tid + D; s < nsplit; s += D) M = fmaxf(M, part(s)[D]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     if (lane == 0) red[0][wv] = M;
@@ -340,9 +345,9 @@ __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part
         if (tid < n) {
             float m = m_own, l = l_own, l32 = l32_own;
             if (s0 > 0) {
-                m = P[(size_t)(s0 + tid) * PART_FLOATS + D];
-                l = P[(size_t)(s0 + tid) * PART_FLOATS + D + 1];
-                l32 = P[(size_t)(s0 + tid) * PART_FLOATS + D + 2];
+                m = part(s0 + tid)[D];
+                l = part(s0 + tid)[D + 1];
+                l32 = part(s0 + tid)[D + 2];
             }
             const float w = l > 0.0f ? __expf(m - M) : 0.0f;
             w_lds[tid] = w;
@@ -355,16 +360,15 @@ __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part
             for (int s = 0; s < MERGE_FAST; ++s)
                 if (s < n) acc = __builtin_fmaf(xf[s], w_lds[s], acc);
         } else {
-            const float *Pc = P + (size_t)s0 * PART_FLOATS + tid;
             int s = 0;
             for (; s + 8 <= n; s += 8) {  // eight independent loads in flight, sums kept in split order
                 float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = Pc[(size_t)(s + e) * PART_FLOATS];
+                for (int e = 0; e < 8; ++e) x[e] = part(s0 + s + e)[tid];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], w_lds[s + e], acc);
             }
-            for (; s < n; ++s) acc = __builtin_fmaf(Pc[(size_t)s * PART_FLOATS], w_lds[s], acc);
+            for (; s < n; ++s) acc = __builtin_fmaf(part(s0 + s)[tid], w_lds[s], acc);
         }
     }
 #pragma unroll
@@ -453,7 +457,13 @@ hipError_t launch_decode_bf16(const DecodeBf16Args &a, hipStream_t s) {
 
 hipError_t launch_merge(const float *partials, int batch, int hq, int num_splits, float *out, float *lse,
                         hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3(D), 0, s, partials, num_splits, out, lse);
+    hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3(D), 0, s, partials, num_splits, nullptr, out, lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_extra(const float *partials, int batch, int hq, int num_splits, const float *extra,
+                              float *out, float *lse, hipStream_t s) {
+    hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3(D), 0, s, partials, num_splits, extra, out, lse);
     return hipGetLastError();
 }
 

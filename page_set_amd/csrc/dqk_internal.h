@@ -13,6 +13,11 @@ constexpr int PG = DQK_PAGE;
 constexpr int ROW_BYTES = 32;     // 128 two-bit codes
 constexpr int VGROUPS = 4;        // value groups of 32 channels
 
+// BF16 tiers: sink tokens, the recent window, tail ring slots.
+constexpr int TIER_SINK = DQK_TIER_SINK;
+constexpr int TIER_RECENT = DQK_TIER_RECENT;
+constexpr int TIER_TAIL_SLOTS = DQK_TIER_TAIL_SLOTS;
+
 // Physical pages come in aligned blocks of eight: key rows and key metadata of
 // a channel sit side by side for the block's eight pages.
 constexpr int KBLK = 8;
@@ -121,6 +126,19 @@ hipError_t launch_select(const uint16_t *q, const float *t_q, int batch, int hq,
 hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k, int n_seqs,
                          const int32_t *cu_tokens, const int32_t *page_table, int max_pages, float *kprime_dbg,
                          hipStream_t s);
+hipError_t launch_append_tiered(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                                int n_seqs, const int32_t *cu_tokens, const int32_t *page_table, int max_pages,
+                                hipStream_t s);
+hipError_t launch_pack_tail(const dqk_cache &c, const dqk_tiers &t, const uint16_t *t_k, int batch,
+                            const int32_t *lens_before, const int32_t *page_table, int max_pages, hipStream_t s);
+// BF16 tiers (dqk_tiers.hip)
+hipError_t launch_tier_fill(const dqk_tiers &t, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                            int n_seqs, const int32_t *cu_tokens, hipStream_t s);
+hipError_t launch_tier_token(const dqk_tiers &t, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                             int batch, const int32_t *lens_before, hipStream_t s);
+hipError_t launch_tier_lens(const int32_t *seq_lens, int batch, int32_t *int2_lens, hipStream_t s);
+hipError_t launch_tier_decode(const dqk_tiers &t, const float *q_prime, const int32_t *sel_idx, int n_keep, int batch,
+                              int hq, const int32_t *seq_lens, float sm_scale, float *tier_partials, hipStream_t s);
 
 struct DecodeArgs {
     const dqk_cache *c;
@@ -182,5 +200,8 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hip
 
 hipError_t launch_merge(const float *partials, int batch, int hq, int num_splits, float *out, float *lse,
                         hipStream_t s);
+// The merge with one more partial per (sequence, query head) row at extra + row * PART_FLOATS.
+hipError_t launch_merge_extra(const float *partials, int batch, int hq, int num_splits, const float *extra,
+                              float *out, float *lse, hipStream_t s);
 
 }  // namespace dqk

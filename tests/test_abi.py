@@ -156,3 +156,55 @@ def test_noalloc_validation_before_any_device_call():
     assert _noalloc(ns=17) == pa.DQK_ERR_SHAPE
     # 64 sequences x 64 heads x 16 splits x 528 bytes = 33 MiB of partials
     assert _noalloc(c=pa.dqk_cache(16, 64, 4096, 4096, 4096, 4096, 4096), B=64, hq=64, ns=16) == pa.DQK_ERR_WORKSPACE
+
+
+def _tiers(**kw):
+    t = pa.dqk_tiers(4, 8, 4096, 4096, 4096, 4096, 4096)
+    for k, v in kw.items():
+        setattr(t, k, v)
+    return t
+
+
+def test_tiered_validation():
+    """Every tier entry point rejects bad arguments on the host (nothing is
+    enqueued, so no device is touched)."""
+    L = pa.lib()
+    c = _cache()
+
+    def pre(t=None, **kw):
+        a = dict(k=A, v=A, tk=A, n=2, cu=A, tot=300, pt=A, mp=4)
+        a.update(kw)
+        return L.dqk_prefill_tiered(ctypes.byref(c), ctypes.byref(t or _tiers()), a["k"], a["v"], a["tk"], a["n"],
+                                    a["cu"], a["tot"], a["pt"], a["mp"], None)
+
+    assert pre(t=_tiers(tail_kraw=None)) == pa.DQK_ERR_NULL
+    assert pre(k=None) == pa.DQK_ERR_NULL
+    assert pre(n=5) == pa.DQK_ERR_SHAPE                     # more sequences than the tiers hold
+    assert pre(t=_tiers(num_kv_heads=4)) == pa.DQK_ERR_SHAPE  # head count differs from the cache's
+    assert pre(t=_tiers(sink_v=4096 + 2)) == pa.DQK_ERR_ALIGN
+
+    def app(t=None, **kw):
+        a = dict(k=A, v=A, tk=A, B=4, lb=A, pt=A, mp=4)
+        a.update(kw)
+        return L.dqk_append_token(ctypes.byref(c), ctypes.byref(t or _tiers()), a["k"], a["v"], a["tk"], a["B"],
+                                  a["lb"], a["pt"], a["mp"], None)
+
+    assert app(lb=None) == pa.DQK_ERR_NULL
+    assert app(B=0) == pa.DQK_ERR_SHAPE
+    assert app(B=5) == pa.DQK_ERR_SHAPE
+    assert app(pt=MIS) == pa.DQK_ERR_ALIGN
+
+    def dec(t=None, **kw):
+        a = dict(qp=A, sel=A, nk=77, B=4, hq=32, pt=A, mp=16, sl=A, ns=0, ws=A, wsb=1 << 30, out=A)
+        a.update(kw)
+        return L.dqk_decode_attn_tiered(ctypes.byref(c), ctypes.byref(t or _tiers()), a["qp"], a["sel"], a["nk"],
+                                        a["B"], a["hq"], a["pt"], a["mp"], a["sl"], 0.088, a["ns"], a["ws"], a["wsb"],
+                                        a["out"], None, None)
+
+    assert dec(t=_tiers(sink_k=None)) == pa.DQK_ERR_NULL
+    assert dec(hq=30) == pa.DQK_ERR_SHAPE
+    assert dec(B=5) == pa.DQK_ERR_SHAPE
+    need = pa.dqk_decode_tiered_workspace_size(4, 32, 8, 16, 4)
+    assert need == 4 * 32 * 4 * 132 * 4 + 4 * 32 * 132 * 4 + 16
+    assert dec(ns=4, wsb=need - 4) == pa.DQK_ERR_WORKSPACE
+    assert dec(out=MIS) == pa.DQK_ERR_ALIGN
