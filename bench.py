@@ -361,6 +361,92 @@ class Int2Workload:
                 "bytes_per_token_head": cache_bytes / (hkv * float(np.sum(self.prob.seq_lens)))}
 
 
+def tiered_record(shape, seed, pa, torch, steps):
+    """The headline workload in the protected-tier layout: one prefill call
+    into the BF16 sink/tail tiers and the INT2 pages, then per step the
+    selection, the tiered decode and one appended token per sequence, each
+    timed with HIP events on the stream (one cache; the step's bytes exceed
+    the Infinity Cache)."""
+    from page_set_amd import traffic
+    prob = synth.make_problem(shape, seed, materialize_kv=False)
+    B, hq, hkv, n_keep = shape.batch, shape.hq, shape.hkv, shape.n_keep
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    q, t_q, t_k = dev(prob.q.view(np.int16)), dev(prob.t_q), dev(prob.t_k.view(np.int16))
+    pt, cu = dev(prob.page_table), dev(prob.cu_tokens)
+    kv = [synth.make_kv_seq(shape, seed, b, prob.outliers) for b in range(B)]
+    k_d = dev(np.concatenate([x[0] for x in kv]).view(np.int16))
+    v_d = dev(np.concatenate([x[1] for x in kv]).view(np.int16))
+    extra = [kv[b][0][-1:].copy() for b in range(B)]  # the token appended each step (its position grows)
+    del kv
+    cache = pa.Cache(prob.num_pages, hkv)
+    tiers = pa.Tiers(B, hkv)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pa.dqk_prefill_tiered(cache, tiers, k_d, v_d, t_k, cu, pt)  # warm
+    torch.cuda.synchronize()
+    e0.record(stream)
+    pa.dqk_prefill_tiered(cache, tiers, k_d, v_d, t_k, cu, pt)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prefill_us = e0.elapsed_time(e1) * 1e3
+    del k_d, v_d
+    lens = dev(prob.seq_lens)
+    qp = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, hkv, n_keep), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    mp = int(prob.page_table.shape[1])
+    ws_n = pa.dqk_decode_tiered_workspace_size(B, hq, hkv, mp, 0)
+    ws = torch.empty(ws_n // 4 + 4, dtype=torch.float32, device="cuda")
+    kn = dev(np.concatenate(extra).reshape(B, hkv, 128).view(np.int16))
+    vn = torch.zeros_like(kn)
+    sel_call = pa.prepared("dqk_select_channels", q, t_q, B, hq, hkv, n_keep, qp, sel, stream)
+    dec_call = pa.prepared("dqk_decode_attn_tiered", cache, tiers, qp, sel, n_keep, B, hq, pt, mp, lens,
+                           float(prob.sm_scale), 0, ws, ws.numel() * 4, out, None, stream)
+    for _ in range(100):
+        sel_call()
+        dec_call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sel_call()
+        dec_call()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        dec_call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    dec_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    # appends: one token per sequence per call, 128 calls, so that each sequence
+    # packs one page from its tail on the way (the page table has room for it)
+    n_app = 128
+    assert int(max(traffic.tier_pages(int(L) + n_app) for L in prob.seq_lens)) < mp
+    app_evs = []
+    for _ in range(n_app):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        pa.dqk_append_token(cache, tiers, kn, vn, t_k, lens, pt, stream=stream)
+        b.record(stream)
+        app_evs.append((a, b))
+        lens += 1
+    torch.cuda.synchronize()
+    app_us = [a.elapsed_time(b) * 1e3 for a, b in app_evs]
+    sel_h = sel.cpu().numpy()
+    cache_bytes = traffic.decode_tiered_bytes(prob.seq_lens, sel_h)
+    fixed = traffic.decode_fixed_bytes(B, hq, hkv, n_keep, mp)
+    step_bytes = cache_bytes + fixed["decode"] + fixed["select"]
+    return {"workload": shape.name + "-tiered", "entries": "dqk_select_channels + dqk_decode_attn_tiered",
+            "t_step_us": round(t_step * 1e6, 2), "tokens_per_s": round(B / t_step, 1),
+            "decode_call_us": round(dec_us, 2), "algorithmic_bytes_per_step": int(step_bytes),
+            "frac_step": round(step_bytes / t_step / 1e9 / PEAK_HBM_GBS, 4),
+            "prefill_us": round(prefill_us, 1), "append_token_us": round(float(np.median(app_us)), 2),
+            "append_token_max_us": round(float(np.max(app_us)), 2),
+            "append_note": "median and max over 128 calls, one token per sequence each; the max includes "
+                           "packing a page from the tail"}
+
+
 def _summary(name, w, r, n_keep):
     B = w.shape.batch
     rec = {"workload": name, "batch": B, "context": (max(w.shape.seq_lens) if len(set(w.shape.seq_lens)) == 1
@@ -529,6 +615,10 @@ def main():
         configs["4"] = c4
         log(f"[bench] config 4: {c4['t_step_us']} us/step")
         del w4
+        torch.cuda.empty_cache()
+        configs["3_tiered"] = tiered_record(shape, args.seed, pa, torch, sub)
+        log(f"[bench] config 3 tiered: {configs['3_tiered']['t_step_us']} us/step, append token "
+            f"{configs['3_tiered']['append_token_us']} us")
         rec["configs"] = configs
 
     if not args.no_cpu_baseline:

@@ -298,7 +298,7 @@ def dqk_select_decode_attn(cache: Cache, q, t_q, n_keep: int, page_table, seq_le
 def prepared(name: str, *args):
     """A zero-argument callable that invokes C entry point `name` with the
     given arguments, marshalled once (torch tensors become their device
-    addresses, a Cache its struct, None NULL, streams their handles), and
+    addresses, a Cache or Tiers its struct, None NULL, streams their handles), and
     raises on a non-zero status.  For tight launch loops; the tensors must
     outlive the callable."""
     import torch
@@ -306,7 +306,7 @@ def prepared(name: str, *args):
     fn = getattr(L, name)
     conv, keep = [], []
     for a in args:
-        if isinstance(a, Cache):
+        if isinstance(a, (Cache, Tiers)):
             st = a.struct()
             keep.append(st)
             conv.append(ctypes.byref(st))

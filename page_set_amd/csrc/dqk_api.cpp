@@ -266,7 +266,7 @@ namespace {
 // for the BF16 tokens, the INT2 lengths
 size_t tiered_ws_bytes(int batch, int hq, int splits) {
     const size_t main = (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float);
-    const size_t tier = (size_t)batch * hq * dqk::PART_FLOATS * sizeof(float);
+    const size_t tier = (size_t)batch * hq * dqk::TIER_PARTIALS * dqk::PART_FLOATS * sizeof(float);
     const size_t lens = ((size_t)batch * sizeof(int32_t) + 15) / 16 * 16;
     return main + tier + lens;
 }
@@ -304,16 +304,18 @@ int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const flo
     if (ws_bytes < tiered_ws_bytes(batch, hq, splits)) return DQK_ERR_WORKSPACE;
     float *parts = static_cast<float *>(workspace);
     float *tier_parts = parts + (size_t)batch * hq * splits * dqk::PART_FLOATS;
-    int32_t *int2_lens = reinterpret_cast<int32_t *>(tier_parts + (size_t)batch * hq * dqk::PART_FLOATS);
-    hipError_t e = dqk::launch_tier_lens(seq_lens, batch, int2_lens, stream);
+    int32_t *int2_lens =
+        reinterpret_cast<int32_t *>(tier_parts + (size_t)batch * hq * dqk::TIER_PARTIALS * dqk::PART_FLOATS);
+    // the BF16 tokens first: that kernel also writes the INT2 lengths the decode reads
+    hipError_t e = dqk::launch_tier_decode(*tiers, q_prime, sel_idx, n_keep, batch, hq, seq_lens, sm_scale, tier_parts,
+                                           int2_lens, stream);
     if (e != hipSuccess) return hip_status(e);
     dqk::DecodeArgs a{c,         q_prime,  sel_idx, n_keep, batch, hq, hkv, page_table, max_pages, int2_lens,
                       sm_scale, splits, parts,   out,    lse};
     e = mfma ? dqk::launch_decode_mfma(a, stream) : dqk::launch_decode_generic(a, stream);
     if (e != hipSuccess) return hip_status(e);
-    e = dqk::launch_tier_decode(*tiers, q_prime, sel_idx, n_keep, batch, hq, seq_lens, sm_scale, tier_parts, stream);
-    if (e != hipSuccess) return hip_status(e);
-    return hip_status(dqk::launch_merge_extra(parts, batch, hq, splits, tier_parts, out, lse, stream));
+    return hip_status(
+        dqk::launch_merge_extra(parts, batch, hq, splits, tier_parts, dqk::TIER_PARTIALS, out, lse, stream));
 }
 
 int dqk_decode_attn_bf16(const void *k_pages, const void *v_pages, int32_t hkv, int32_t num_pages,

@@ -308,17 +308,19 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const uint16_t *__rest
 constexpr int MERGE_FAST = 32;  // splits whose partials one lane keeps in registers
 
 __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ partials, int nsplit_main,
-                                                  const float *__restrict__ extra, float *__restrict__ out,
-                                                  float *__restrict__ lse) {
+                                                  const float *__restrict__ extra, int n_extra,
+                                                  float *__restrict__ out, float *__restrict__ lse) {
     // one block of 128 lanes per (sequence, query head); lane c owns output channel c
     __shared__ float w_lds[D];
     __shared__ float red[3][D / 64];
     const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const float *P = partials + (size_t)bh * nsplit_main * PART_FLOATS;
-    // partial s: split s of the decode, or (s = nsplit_main) the extra one of this row
-    const int nsplit = nsplit_main + (extra ? 1 : 0);
-    const float *X = extra ? extra + (size_t)bh * PART_FLOATS : nullptr;
-    auto part = [&](int s) { return s < nsplit_main ? P + (size_t)s * PART_FLOATS : X; };
+    // partial s: split s of the decode, or (s >= nsplit_main) extra partial s - nsplit_main of this row
+    const int nsplit = nsplit_main + (extra ? n_extra : 0);
+    const float *X = extra ? extra + (size_t)bh * n_extra * PART_FLOATS : nullptr;
+    auto part = [&](int s) {
+        return s < nsplit_main ? P + (size_t)s * PART_FLOATS : X + (size_t)(s - nsplit_main) * PART_FLOATS;
+    };
     // every load that does not depend on the maximum is issued up front
     float xf[MERGE_FAST];
     if (nsplit <= MERGE_FAST) {
@@ -457,13 +459,14 @@ hipError_t launch_decode_bf16(const DecodeBf16Args &a, hipStream_t s) {
 
 hipError_t launch_merge(const float *partials, int batch, int hq, int num_splits, float *out, float *lse,
                         hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3(D), 0, s, partials, num_splits, nullptr, out, lse);
+    hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3(D), 0, s, partials, num_splits, nullptr, 0, out, lse);
     return hipGetLastError();
 }
 
 hipError_t launch_merge_extra(const float *partials, int batch, int hq, int num_splits, const float *extra,
-                              float *out, float *lse, hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3(D), 0, s, partials, num_splits, extra, out, lse);
+                              int n_extra, float *out, float *lse, hipStream_t s) {
+    hipLaunchKernelGGL(merge_kernel, dim3(batch * hq), dim3(D), 0, s, partials, num_splits, extra, n_extra, out,
+                       lse);
     return hipGetLastError();
 }
 

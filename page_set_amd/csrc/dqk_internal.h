@@ -17,6 +17,8 @@ constexpr int VGROUPS = 4;        // value groups of 32 channels
 constexpr int TIER_SINK = DQK_TIER_SINK;
 constexpr int TIER_RECENT = DQK_TIER_RECENT;
 constexpr int TIER_TAIL_SLOTS = DQK_TIER_TAIL_SLOTS;
+// partials of the BF16 tokens per (sequence, query head): 64 tokens each
+constexpr int TIER_PARTIALS = (TIER_SINK + TIER_RECENT + 128 - 1 + 63) / 64;
 
 // Physical pages come in aligned blocks of eight: key rows and key metadata of
 // a channel sit side by side for the block's eight pages.
@@ -136,9 +138,9 @@ hipError_t launch_tier_fill(const dqk_tiers &t, const uint16_t *k, const uint16_
                             int n_seqs, const int32_t *cu_tokens, hipStream_t s);
 hipError_t launch_tier_token(const dqk_tiers &t, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
                              int batch, const int32_t *lens_before, hipStream_t s);
-hipError_t launch_tier_lens(const int32_t *seq_lens, int batch, int32_t *int2_lens, hipStream_t s);
 hipError_t launch_tier_decode(const dqk_tiers &t, const float *q_prime, const int32_t *sel_idx, int n_keep, int batch,
-                              int hq, const int32_t *seq_lens, float sm_scale, float *tier_partials, hipStream_t s);
+                              int hq, const int32_t *seq_lens, float sm_scale, float *tier_partials,
+                              int32_t *int2_lens, hipStream_t s);
 
 struct DecodeArgs {
     const dqk_cache *c;
@@ -200,8 +202,9 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hip
 
 hipError_t launch_merge(const float *partials, int batch, int hq, int num_splits, float *out, float *lse,
                         hipStream_t s);
-// The merge with one more partial per (sequence, query head) row at extra + row * PART_FLOATS.
+// The merge with n_extra more partials per (sequence, query head) row at
+// extra + (row * n_extra + i) * PART_FLOATS.
 hipError_t launch_merge_extra(const float *partials, int batch, int hq, int num_splits, const float *extra,
-                              float *out, float *lse, hipStream_t s);
+                              int n_extra, float *out, float *lse, hipStream_t s);
 
 }  // namespace dqk

@@ -9,10 +9,11 @@
 //                       input channel, rounded to bf16) of the sink and tail
 //                       tokens, their values, and the tail's raw keys.
 //   tier_token_kernel   one new token per sequence into its tier slot.
-//   tier_lens_kernel    128 x (INT2 pages) per sequence, the length the INT2
-//                       decode sees.
-//   tier_decode_kernel  the BF16 tokens' partial (o, m, l) per query head,
-//                       merged with the INT2 splits by the log-sum-exp merge.
+//   tier_decode_kernel  partials (o, m, l) per query head of the BF16 tokens,
+//                       64 tokens per workgroup (TIER_PARTIALS per head),
+//                       merged with the INT2 splits by the log-sum-exp merge;
+//                       it also writes 128 x (INT2 pages) per sequence, the
+//                       length the INT2 decode that follows it sees.
 #include "dqk_internal.h"
 
 namespace dqk {
@@ -114,32 +115,84 @@ __global__ __launch_bounds__(D) void tier_token_kernel(dqk_tiers t, const uint16
     if (!in_sink) t.tail_kraw[row * D + j] = kin[src + j];
 }
 
-__global__ void tier_lens_kernel(const int32_t *__restrict__ seq_lens, int batch, int32_t *__restrict__ int2_lens) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b < batch) int2_lens[b] = (int32_t)(PG * tier_pages(seq_lens[b]));
-}
-
 constexpr int MAX_TIER = TIER_SINK + TIER_RECENT + PG - 1;  // 447 tier tokens at most
-constexpr int TD_MAXG = 16;                                  // query heads per KV head
+constexpr int TD_MAXG = 16;                                  // query heads per KV head, at most
+static_assert(TD_MAXG == GENERIC_MAX_GROUP, "the tiered decode takes the generic decode's groups");
+constexpr int TCH = 64;                                      // tier tokens per workgroup
+constexpr int N_TCH = (MAX_TIER + TCH - 1) / TCH;           // 7 partials per (sequence, query head)
 
-// grid (batch * hkv), 256 lanes.  Logits of the tier tokens for the group's
-// query heads (masked q' in LDS, one token per lane, fp32 fma over ascending
-// channel), per-head maximum and exp-sum, then o[h][c] with lane c.
+// grid (N_TCH, batch * hkv), 256 lanes: tier tokens 64 c .. 64 c + 63 of one
+// (sequence, KV head).  Logits per (token, head) pair (masked q' in LDS, the
+// bf16 k' row from memory, fp32 fma over ascending channel); one wave per
+// head reduces the chunk's 64 logits to (m, l); lane c then sums p v over
+// the chunk.  Writes one partial per query head (empty chunks: m = -inf,
+// l = 0).
+template <int GRP>
 __global__ __launch_bounds__(256) void tier_decode_kernel(dqk_tiers t, const float *__restrict__ q_prime,
                                                           const int32_t *__restrict__ sel_idx, int n_keep, int hq,
                                                           const int32_t *__restrict__ seq_lens, float sm_scale,
-                                                          float *__restrict__ part) {
-    __shared__ float qm[TD_MAXG][D];
-    __shared__ float x[TD_MAXG][MAX_TIER];
-    __shared__ float red[4];
-    __shared__ float m_s[TD_MAXG], l_s[TD_MAXG];
-    const int hkv = t.num_kv_heads, grp = hq / hkv;
-    const int b = blockIdx.x / hkv, g = blockIdx.x % hkv;
+                                                          float *__restrict__ part, int32_t *__restrict__ int2_lens) {
+    __shared__ float qm[GRP][D];
+    __shared__ float x[GRP][TCH];
+    __shared__ float m_s[GRP], l_s[GRP];
+    constexpr int grp = GRP;
+    const int hkv = t.num_kv_heads;
+    const int chunk = blockIdx.x;
+    const int b = blockIdx.y / hkv, g = blockIdx.y % hkv;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t L = seq_lens[b];
     int n_sink, n_tier;
     int64_t tail0;
     tier_extent(L, n_sink, tail0, n_tier);
+    const int i0 = chunk * TCH;
+    const int n = max(0, min(TCH, n_tier - i0));
+    if (chunk == 0 && g == 0 && threadIdx.x == 0) int2_lens[b] = (int32_t)(PG * tier_pages(L));
+
+    if (n == 0) {  // a chunk past the tier tokens: empty partials
+        for (int e = tid; e < grp * D; e += 256) {
+            float *dst = part + (((size_t)b * hq + (size_t)g * grp + e / D) * N_TCH + chunk) * PART_FLOATS;
+            dst[e % D] = 0.0f;
+            if (e % D == 0) {
+                dst[D] = -__builtin_huge_valf();
+                dst[D + 1] = 0.0f;
+                dst[D + 2] = 0.0f;
+            }
+        }
+        return;
+    }
+    // row of chunk token r (r clamped to the chunk, so every load is unconditional):
+    // sink slot, or tail slot (t - 64) mod 384 in 32-bit arithmetic
+    const size_t sink0 = ((size_t)b * hkv + g) * TIER_SINK, tail_base = ((size_t)b * hkv + g) * TIER_TAIL_SLOTS;
+    auto row_of = [&](int r, bool &in_sink) {
+        const int i = i0 + min(r, n - 1);
+        in_sink = i < n_sink;
+        return in_sink ? sink0 + (size_t)i
+                       : tail_base + (size_t)((uint32_t)(tail0 - TIER_SINK + (i - n_sink)) % (uint32_t)TIER_TAIL_SLOTS);
+    };
+    auto krow_of = [&](int r) {
+        bool s0;
+        const size_t row = row_of(r, s0);
+        return (s0 ? t.sink_k : t.tail_k) + row * D;
+    };
+    // ---- every load that does not depend on q' first: this lane's key row
+    //      (token tid / grp, for the logit of head tid % grp) and its channel's
+    //      values over the chunk
+    const int c = tid & (D - 1), half = tid >> 7;
+    const int r_own = tid / grp, h_own = tid % grp;
+    const bool has_pair = grp <= 4 && r_own < n;  // one (token, head) pair per lane when they fit
+    u32x4 w[16];
+    {
+        const uint16_t *kr = krow_of(grp <= 4 ? r_own : 0);
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) w[cc] = *reinterpret_cast<const u32x4 *>(kr + 8 * cc);
+    }
+    uint16_t vraw[TCH];
+#pragma unroll
+    for (int r = 0; r < TCH; ++r) {
+        bool s0;
+        const size_t row = row_of(r, s0);
+        vraw[r] = (s0 ? t.sink_v : t.tail_v)[row * D + c];
+    }
 
     for (int e = tid; e < grp * D; e += 256) qm[e / D][e % D] = 0.0f;
     __syncthreads();
@@ -149,73 +202,65 @@ __global__ __launch_bounds__(256) void tier_decode_kernel(dqk_tiers t, const flo
         qm[h][jj] = q_prime[((size_t)b * hq + (size_t)g * grp + h) * D + jj];
     }
     __syncthreads();
-    // ---- logits
-    for (int i = tid; i < n_tier; i += 256) {
-        const int64_t tok = tier_token(i, n_sink, tail0);
-        const uint16_t *kr = (tok < TIER_SINK ? t.sink_k + sink_row(b, g, hkv, tok) * D
-                                              : t.tail_k + tail_row(b, g, hkv, tok) * D);
-        float acc[TD_MAXG];
+    // ---- logits of (token r, head h) pairs
+    auto logit = [&](const u32x4 (&kw)[16], int h) {
+        float acc = 0.0f;
 #pragma unroll
-        for (int h = 0; h < TD_MAXG; ++h) acc[h] = 0.0f;
-        for (int c8 = 0; c8 < D; c8 += 8) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(kr + c8);
+        for (int cc = 0; cc < 16; ++cc)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float kv = __uint_as_float(e & 1 ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
-#pragma unroll
-                for (int h = 0; h < TD_MAXG; ++h)
-                    if (h < grp) acc[h] = __builtin_fmaf(qm[h][c8 + e], kv, acc[h]);
+            for (int e2 = 0; e2 < 8; ++e2) {
+                const float kv = __uint_as_float(e2 & 1 ? (kw[cc][e2 >> 1] & 0xFFFF0000u) : (kw[cc][e2 >> 1] << 16));
+                acc = __builtin_fmaf(qm[h][8 * cc + e2], kv, acc);
             }
-        }
+        return acc * sm_scale;
+    };
+    if (grp <= 4) {
+        if (has_pair) x[h_own][r_own] = logit(w, h_own);
+    } else {
+        for (int e = tid; e < n * grp; e += 256) {
+            const int r = e / grp, h = e % grp;
+            const uint16_t *kr = krow_of(r);
+            u32x4 kw[16];
 #pragma unroll
-        for (int h = 0; h < TD_MAXG; ++h)
-            if (h < grp) x[h][i] = acc[h] * sm_scale;
+            for (int cc = 0; cc < 16; ++cc) kw[cc] = *reinterpret_cast<const u32x4 *>(kr + 8 * cc);
+            x[h][r] = logit(kw, h);
+        }
     }
     __syncthreads();
-    // ---- per head: maximum, weights exp(x - m), their sum
-    for (int h = 0; h < grp; ++h) {
-        float m = -__builtin_huge_valf();
-        for (int i = tid; i < n_tier; i += 256) m = fmaxf(m, x[h][i]);
+    // ---- per head (one wave each, lane = token): maximum, weights, their sum
+    for (int h = wv; h < grp; h += 4) {
+        const float xv = lane < n ? x[h][lane] : -__builtin_huge_valf();
+        float m = xv;
         for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-        if (lane == 0) red[wv] = m;
-        __syncthreads();
-        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        __syncthreads();
-        float l = 0.0f;
-        for (int i = tid; i < n_tier; i += 256) {
-            const float p = __expf(x[h][i] - m);
-            x[h][i] = p;
-            l += p;
-        }
+        const float p = lane < n ? __expf(xv - m) : 0.0f;
+        float l = p;
         for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-        if (lane == 0) red[wv] = l;
-        __syncthreads();
-        if (tid == 0) {
-            m_s[h] = m;
-            l_s[h] = red[0] + red[1] + red[2] + red[3];
+        x[h][lane] = p;
+        if (lane == 0) {
+            m_s[h] = n > 0 ? m : -__builtin_huge_valf();
+            l_s[h] = l;
         }
-        __syncthreads();
     }
-    // ---- o[h][c] = sum_i p[h][i] v[i][c]: lane c, heads h = half, half + 2, ...
-    const int c = tid & (D - 1), half = tid >> 7;
-    float o[TD_MAXG / 2];
+    __syncthreads();
+    // ---- o[h][c] = sum_r p[h][r] v[r][c] (p = 0 past the chunk's tokens): lane c,
+    //      heads h = half, half + 2, ...
+    constexpr int HH = (GRP + 1) / 2;  // heads per lane half
+    float o[HH];
 #pragma unroll
-    for (int k = 0; k < TD_MAXG / 2; ++k) o[k] = 0.0f;
-    for (int i = 0; i < n_tier; ++i) {
-        const int64_t tok = tier_token(i, n_sink, tail0);
-        const float vv = bf(tok < TIER_SINK ? t.sink_v[sink_row(b, g, hkv, tok) * D + c]
-                                            : t.tail_v[tail_row(b, g, hkv, tok) * D + c]);
+    for (int k = 0; k < HH; ++k) o[k] = 0.0f;
+    if (GRP % 2 == 0 || half == 0) {
 #pragma unroll
-        for (int k = 0; k < TD_MAXG / 2; ++k) {
-            const int h = half + 2 * k;
-            if (h < grp) o[k] = __builtin_fmaf(x[h][i], vv, o[k]);
+        for (int r = 0; r < TCH; ++r) {
+            const float vv = bf(vraw[r]);
+#pragma unroll
+            for (int k = 0; k < HH; ++k) o[k] = __builtin_fmaf(x[half + 2 * k][r], vv, o[k]);
         }
     }
 #pragma unroll
-    for (int k = 0; k < TD_MAXG / 2; ++k) {
+    for (int k = 0; k < HH; ++k) {
         const int h = half + 2 * k;
         if (h < grp) {
-            float *dst = part + ((size_t)b * hq + (size_t)g * grp + h) * PART_FLOATS;
+            float *dst = part + (((size_t)b * hq + (size_t)g * grp + h) * N_TCH + chunk) * PART_FLOATS;
             dst[c] = o[k];
             if (c == 0) {
                 dst[D] = m_s[h];
@@ -227,6 +272,8 @@ __global__ __launch_bounds__(256) void tier_decode_kernel(dqk_tiers t, const flo
 }
 
 }  // namespace
+
+static_assert(N_TCH == TIER_PARTIALS, "tier partials per (sequence, query head)");
 
 hipError_t launch_tier_fill(const dqk_tiers &t, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
                             int n_seqs, const int32_t *cu_tokens, hipStream_t s) {
@@ -241,16 +288,33 @@ hipError_t launch_tier_token(const dqk_tiers &t, const uint16_t *k, const uint16
     return hipGetLastError();
 }
 
-hipError_t launch_tier_lens(const int32_t *seq_lens, int batch, int32_t *int2_lens, hipStream_t s) {
-    hipLaunchKernelGGL(tier_lens_kernel, dim3((batch + 255) / 256), dim3(256), 0, s, seq_lens, batch, int2_lens);
-    return hipGetLastError();
-}
-
 hipError_t launch_tier_decode(const dqk_tiers &t, const float *q_prime, const int32_t *sel_idx, int n_keep, int batch,
-                              int hq, const int32_t *seq_lens, float sm_scale, float *tier_partials, hipStream_t s) {
-    hipLaunchKernelGGL(tier_decode_kernel, dim3(batch * t.num_kv_heads), dim3(256), 0, s, t, q_prime, sel_idx, n_keep,
-                       hq, seq_lens, sm_scale, tier_partials);
-    return hipGetLastError();
+                              int hq, const int32_t *seq_lens, float sm_scale, float *tier_partials,
+                              int32_t *int2_lens, hipStream_t s) {
+    const dim3 grid(N_TCH, batch * t.num_kv_heads);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, t, q_prime, sel_idx, n_keep, hq, seq_lens, sm_scale,
+                           tier_partials, int2_lens);
+        return hipGetLastError();
+    };
+    switch (hq / t.num_kv_heads) {  // 1 .. TD_MAXG (checked by the caller)
+        case 1: return go(tier_decode_kernel<1>);
+        case 2: return go(tier_decode_kernel<2>);
+        case 3: return go(tier_decode_kernel<3>);
+        case 4: return go(tier_decode_kernel<4>);
+        case 5: return go(tier_decode_kernel<5>);
+        case 6: return go(tier_decode_kernel<6>);
+        case 7: return go(tier_decode_kernel<7>);
+        case 8: return go(tier_decode_kernel<8>);
+        case 9: return go(tier_decode_kernel<9>);
+        case 10: return go(tier_decode_kernel<10>);
+        case 11: return go(tier_decode_kernel<11>);
+        case 12: return go(tier_decode_kernel<12>);
+        case 13: return go(tier_decode_kernel<13>);
+        case 14: return go(tier_decode_kernel<14>);
+        case 15: return go(tier_decode_kernel<15>);
+        default: return go(tier_decode_kernel<16>);
+    }
 }
 
 }  // namespace dqk

@@ -102,6 +102,25 @@ def decode_cache_bytes(seq_lens, sel_idx) -> int:
     return total
 
 
+TIER_SINK, TIER_RECENT = 64, 256
+
+
+def tier_pages(L: int) -> int:
+    """INT2 pages of a sequence of L tokens in the tiered layout: pages of
+    tokens 64 + 128 i .., all older than the 256 most recent tokens."""
+    return (L - TIER_SINK - TIER_RECENT) // PAGE if L >= TIER_SINK + TIER_RECENT else 0
+
+
+def decode_tiered_bytes(seq_lens, sel_idx) -> int:
+    """Cache bytes a tiered decode step reads: the INT2 pages as
+    decode_cache_bytes, and per BF16 token (sink and tail) the selected
+    channels of its bf16 k' plus its 128 bf16 values."""
+    B, hkv, n_keep = sel_idx.shape
+    int2 = decode_cache_bytes([PAGE * tier_pages(int(L)) for L in seq_lens], sel_idx)
+    tier_tokens = sum(int(L) - PAGE * tier_pages(int(L)) for L in seq_lens)
+    return int2 + tier_tokens * hkv * (n_keep * 2 + D * 2)
+
+
 def decode_fixed_bytes(batch: int, hq: int, hkv: int, n_keep: int, max_pages: int) -> Dict[str, int]:
     """Per-step bytes outside the cache: the select step reads q (bf16) and
     T_Q (fp32) and writes q' and the selected indices; decode reads q', the

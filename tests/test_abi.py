@@ -205,6 +205,6 @@ def test_tiered_validation():
     assert dec(hq=30) == pa.DQK_ERR_SHAPE
     assert dec(B=5) == pa.DQK_ERR_SHAPE
     need = pa.dqk_decode_tiered_workspace_size(4, 32, 8, 16, 4)
-    assert need == 4 * 32 * 4 * 132 * 4 + 4 * 32 * 132 * 4 + 16
+    assert need == 4 * 32 * 4 * 132 * 4 + 4 * 32 * 7 * 132 * 4 + 16   # 7 partials of 64 BF16 tokens
     assert dec(ns=4, wsb=need - 4) == pa.DQK_ERR_WORKSPACE
     assert dec(out=MIS) == pa.DQK_ERR_ALIGN

@@ -41,3 +41,29 @@ def test_decode_cache_bytes_counts_the_actual_mask():
     got = traffic.decode_cache_bytes(lens, sel)
     want = (2 * 76 * 36 + 256 * 50) + (2 * 77 * 36 + 256 * 48) + 2 * (2 * 76 * 36 + 130 * 50)
     assert got == want
+
+
+def test_tiered_bytes_by_enumeration():
+    """decode_tiered_bytes against a token-by-token count: every token is in
+    the sink, an INT2 page or the tail, and reads what its tier stores."""
+    from page_set_amd import traffic as tr
+    rng = np.random.default_rng(3)
+    for L in (1, 64, 65, 319, 320, 447, 448, 5000, 131072):
+        sel = np.sort(rng.choice(128, size=(1, 2, 77), replace=True), axis=-1).astype(np.int32)
+        sel[0, 0, 0] = 0  # head 0 keeps channel 0, head 1 may not
+        want = 0
+        for g in range(2):
+            s = sel[0, g]
+            has0 = bool((s == 0).any())
+            r = len(s) - (1 if has0 else 0)
+            P = tr.tier_pages(L)
+            n_int2 = 0
+            for t in range(L):
+                if t < 64 or t >= 64 + 128 * P:
+                    want += 77 * 2 + 128 * 2
+                else:
+                    n_int2 += 1
+                    want += (2 if has0 else 0) + 48
+            assert n_int2 == 128 * P
+            want += P * r * 36
+        assert tr.decode_tiered_bytes([L], sel) == want
