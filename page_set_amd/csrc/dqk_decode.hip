@@ -210,6 +210,12 @@ __global__ __launch_bounds__(256) void decode_int2_kernel(dqk_cache c, const flo
 }
 
 // Unpruned BF16 baseline on a paged bf16 cache [P][Hkv][128 tok][128 ch].
+// Lane (token or channel t, half): heads half + 2 k, k < HP (HP = ceil(group
+// / 2); the query rows of heads past the group are zero, so their unused
+// results cost no branches).  Each page: the lane's whole key row in flight,
+// scores, the online softmax of §3.4 per head, then the values 32 tokens at a
+// time.
+template <int HP>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(const uint16_t *__restrict__ kp,
                                                           const uint16_t *__restrict__ vp, int hkv,
                                                           const uint16_t *__restrict__ q, int hq,
@@ -227,44 +233,47 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const uint16_t *__rest
     const int npages = (L + PG - 1) / PG;
     int p0, p1;
     split_range(npages, nsplit, split, p0, p1);
-    for (int i = tid; i < grp * D; i += 256) q_lds[i / D][i % D] = bf2f(q[((size_t)b * hq + (size_t)g * grp) * D + i]);
+    for (int i = tid; i < MAXG * D; i += 256)
+        q_lds[i / D][i % D] = i / D < grp ? bf2f(q[((size_t)b * hq + (size_t)g * grp) * D + i]) : 0.0f;
     if (tid < MAXG) {
         m_lds[tid] = -__builtin_huge_valf();
         l_lds[tid] = 0.0f;
     }
     __syncthreads();
     const int t = tid & (PG - 1), half = tid >> 7;
-    float o[HPER];
+    float o[HP];
 #pragma unroll
-    for (int k = 0; k < HPER; ++k) o[k] = 0.0f;
+    for (int k = 0; k < HP; ++k) o[k] = 0.0f;
     for (int pi = p0; pi < p1; ++pi) {
         const int64_t p = page_table[(size_t)b * max_pages + pi];
         const size_t pg = (size_t)p * hkv + g;
         const int nvalid = min(PG, L - pi * PG);
         {
-            float acc[HPER];
+            float acc[HP];
 #pragma unroll
-            for (int k = 0; k < HPER; ++k) acc[k] = 0.0f;
-            const uint4 *kr = reinterpret_cast<const uint4 *>(kp + (pg * PG + t) * D);
+            for (int k = 0; k < HP; ++k) acc[k] = 0.0f;
+            // the whole key row in flight at once (tokens past the end re-read row 0)
+            const uint4 *kr = reinterpret_cast<const uint4 *>(kp + (pg * PG + (t < nvalid ? t : 0)) * D);
+            uint4 krow[D / 8];
+#pragma unroll
+            for (int c8 = 0; c8 < D / 8; ++c8) krow[c8] = kr[c8];
+#pragma unroll
             for (int c8 = 0; c8 < D / 8; ++c8) {
-                const uint4 raw = kr[c8];
+                const uint4 raw = krow[c8];
                 const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float k_lo = __uint_as_float(wds[e] << 16), k_hi = __uint_as_float(wds[e] & 0xFFFF0000u);
                     const int cc = c8 * 8 + 2 * e;
 #pragma unroll
-                    for (int k = 0; k < HPER; ++k) {
+                    for (int k = 0; k < HP; ++k) {
                         const int h = half + 2 * k;
-                        if (h < grp) acc[k] = __builtin_fmaf(q_lds[h][cc + 1], k_hi, __builtin_fmaf(q_lds[h][cc], k_lo, acc[k]));
+                        acc[k] = __builtin_fmaf(q_lds[h][cc + 1], k_hi, __builtin_fmaf(q_lds[h][cc], k_lo, acc[k]));
                     }
                 }
             }
 #pragma unroll
-            for (int k = 0; k < HPER; ++k) {
-                const int h = half + 2 * k;
-                if (h < grp) lg[h][t] = acc[k] * sm_scale;
-            }
+            for (int k = 0; k < HP; ++k) lg[half + 2 * k][t] = acc[k] * sm_scale;
         }
         __syncthreads();
         for (int h = wv; h < grp; h += 4) softmax_page(lg[h], nvalid, &m_lds[h], &l_lds[h], &a_lds[h], lane);
@@ -272,24 +281,25 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const uint16_t *__rest
         {
             const int cch = t;
 #pragma unroll
-            for (int k = 0; k < HPER; ++k) {
-                const int h = half + 2 * k;
-                if (h < grp) o[k] *= a_lds[h];
-            }
+            for (int k = 0; k < HP; ++k) o[k] *= a_lds[half + 2 * k];
             const uint16_t *vc = vp + pg * PG * D + cch;
-            for (int tt = 0; tt < nvalid; ++tt) {
-                const float vv = bf2f(vc[(size_t)tt * D]);
+            // 32 tokens' values in flight per batch (weights past the end are 0)
+            for (int t0 = 0; t0 < nvalid; t0 += 32) {
+                uint16_t vraw[32];
 #pragma unroll
-                for (int k = 0; k < HPER; ++k) {
-                    const int h = half + 2 * k;
-                    if (h < grp) o[k] = __builtin_fmaf(lg[h][tt], vv, o[k]);
+                for (int e = 0; e < 32; ++e) vraw[e] = vc[(size_t)min(t0 + e, nvalid - 1) * D];
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    const float vv = bf2f(vraw[e]);
+#pragma unroll
+                    for (int k = 0; k < HP; ++k) o[k] = __builtin_fmaf(lg[half + 2 * k][t0 + e], vv, o[k]);
                 }
             }
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int k = 0; k < HPER; ++k) {
+    for (int k = 0; k < HP; ++k) {
         const int h = half + 2 * k;
         if (h < grp) {
             float *dst = partials + (((size_t)b * hq + (size_t)g * grp + h) * nsplit + split) * PART_FLOATS;
@@ -450,8 +460,19 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
 
 hipError_t launch_decode_bf16(const DecodeBf16Args &a, hipStream_t s) {
     dim3 grid(a.num_splits, a.batch * a.hkv);
-    hipLaunchKernelGGL(decode_bf16_kernel, grid, dim3(256), 0, s, a.k_pages, a.v_pages, a.hkv, a.q, a.hq,
-                       a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials);
+    const int grp = a.hq / a.hkv;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a.k_pages, a.v_pages, a.hkv, a.q, a.hq, a.page_table,
+                           a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials);
+    };
+    if (grp <= 2)
+        go(decode_bf16_kernel<1>);
+    else if (grp <= 4)
+        go(decode_bf16_kernel<2>);
+    else if (grp <= 8)
+        go(decode_bf16_kernel<4>);
+    else
+        go(decode_bf16_kernel<HPER>);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge(a.partials, a.batch, a.hq, a.num_splits, a.out, a.lse, s);
