@@ -314,16 +314,13 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(const uint16_t *__rest
 }
 
 // Log-sum-exp merge of the split partials: one workgroup (128 lanes) per
-// (sequence, query head), lane = channel.
-constexpr int MERGE_FAST = 32;  // splits whose partials one lane keeps in registers
-
+// (sequence, query head), lane = channel (merge_row in dqk_internal.h).
 __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ partials, int nsplit_main,
                                                   const float *__restrict__ extra, int n_extra,
                                                   float *__restrict__ out, float *__restrict__ lse) {
-    // one block of 128 lanes per (sequence, query head); lane c owns output channel c
     __shared__ float w_lds[D];
     __shared__ float red[3][D / 64];
-    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int bh = blockIdx.x;
     const float *P = partials + (size_t)bh * nsplit_main * PART_FLOATS;
     // partial s: split s of the decode, or (s >= nsplit_main) extra partial s - nsplit_main of this row
     const int nsplit = nsplit_main + (extra ? n_extra : 0);
@@ -331,71 +328,7 @@ __global__ __launch_bounds__(D) void merge_kernel(const float *__restrict__ part
     auto part = [&](int s) {
         return s < nsplit_main ? P + (size_t)s * PART_FLOATS : X + (size_t)(s - nsplit_main) * PART_FLOATS;
     };
-    // every load that does not depend on the maximum is issued up front
-    float xf[MERGE_FAST];
-    if (nsplit <= MERGE_FAST) {
-#pragma unroll
-        for (int s = 0; s < MERGE_FAST; ++s) xf[s] = s < nsplit ? part(s)[tid] : 0.0f;
-    }
-    float M = -__builtin_huge_valf(), m_own = -__builtin_huge_valf(), l_own = 0.0f, l32_own = 0.0f;
-    if (tid < nsplit) {
-        m_own = part(tid)[D];
-        l_own = part(tid)[D + 1];
-        l32_own = part(tid)[D + 2];
-    }
-    M = m_own;
-    for (int s = tid + D; s < nsplit; s += D) M = fmaxf(M, part(s)[D]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    if (lane == 0) red[0][wv] = M;
-    __syncthreads();
-    M = fmaxf(red[0][0], red[0][1]);
-    float lpart = 0.0f, l32part = 0.0f, acc = 0.0f;
-    for (int s0 = 0; s0 < nsplit; s0 += D) {
-        const int n = min(D, nsplit - s0);
-        if (s0 > 0) __syncthreads();  // previous chunk's weights are consumed
-        if (tid < n) {
-            float m = m_own, l = l_own, l32 = l32_own;
-            if (s0 > 0) {
-                m = part(s0 + tid)[D];
-                l = part(s0 + tid)[D + 1];
-                l32 = part(s0 + tid)[D + 2];
-            }
-            const float w = l > 0.0f ? __expf(m - M) : 0.0f;
-            w_lds[tid] = w;
-            lpart = __builtin_fmaf(l, w, lpart);
-            l32part = __builtin_fmaf(l32, w, l32part);
-        }
-        __syncthreads();
-        if (nsplit <= MERGE_FAST) {
-#pragma unroll
-            for (int s = 0; s < MERGE_FAST; ++s)
-                if (s < n) acc = __builtin_fmaf(xf[s], w_lds[s], acc);
-        } else {
-            int s = 0;
-            for (; s + 8 <= n; s += 8) {  // eight independent loads in flight, sums kept in split order
-                float x[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = part(s0 + s + e)[tid];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], w_lds[s + e], acc);
-            }
-            for (; s < n; ++s) acc = __builtin_fmaf(part(s0 + s)[tid], w_lds[s], acc);
-        }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        lpart += __shfl_xor(lpart, o);
-        l32part += __shfl_xor(l32part, o);
-    }
-    if (lane == 0) {
-        red[1][wv] = lpart;
-        red[2][wv] = l32part;
-    }
-    __syncthreads();
-    const float Lsum = red[1][0] + red[1][1];
-    out[(size_t)bh * D + tid] = acc / Lsum;
-    if (lse && tid == 0) lse[bh] = M + __logf(red[2][0] + red[2][1]);
+    merge_row(part, nsplit, (int)threadIdx.x, true, out + (size_t)bh * D, lse ? lse + bh : nullptr, w_lds, red);
 }
 
 // Plain streaming read (measurement reference): block i reads chunk i of

@@ -121,6 +121,90 @@ __device__ __forceinline__ uint32_t code2(float x, const Thresholds &t) {
     return (uint32_t)(x >= t.t0) + (uint32_t)(x >= t.t1) + (uint32_t)(x >= t.t2);
 }
 
+// ---------------------------------------------------------------- split merge
+// Log-sum-exp merge of one (sequence, query head) row: part(s) -> partial s
+// (o[128], m, l, l32), s < nsplit.  Executed by 128 lanes (tid 0..127, lane =
+// output channel) of a workgroup; every lane of the workgroup calls it (the
+// barriers are workgroup-wide), `active` false for lanes that only take part
+// in the barriers (a workgroup may merge several rows side by side).  w_lds: 128 floats, red: [3][2] floats of LDS owned by this
+// row.  Writes out[c] = sum_s w_s o_s[c] / sum_s w_s l_s and *lse = M +
+// log(sum_s w_s l32_s), w_s = exp(m_s - M) (0 for an empty partial).
+constexpr int MERGE_FAST = 32;  // splits whose partials one lane keeps in registers
+
+template <typename Part>
+__device__ __forceinline__ void merge_row(Part part, int nsplit, int tid, bool active, float *__restrict__ out,
+                                          float *__restrict__ lse, float *w_lds, float (*red)[D / 64]) {
+    const int lane = tid & 63, wv = tid >> 6;
+    // every load that does not depend on the maximum is issued up front
+    float xf[MERGE_FAST];
+    if (active && nsplit <= MERGE_FAST) {
+#pragma unroll
+        for (int s = 0; s < MERGE_FAST; ++s) xf[s] = s < nsplit ? part(s)[tid] : 0.0f;
+    }
+    float M = -__builtin_huge_valf(), m_own = -__builtin_huge_valf(), l_own = 0.0f, l32_own = 0.0f;
+    if (active && tid < nsplit) {
+        m_own = part(tid)[D];
+        l_own = part(tid)[D + 1];
+        l32_own = part(tid)[D + 2];
+    }
+    M = m_own;
+    if (active)
+        for (int s = tid + D; s < nsplit; s += D) M = fmaxf(M, part(s)[D]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    if (active && lane == 0) red[0][wv] = M;
+    __syncthreads();
+    if (active) M = fmaxf(red[0][0], red[0][1]);
+    float lpart = 0.0f, l32part = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += D) {
+        const int n = min(D, nsplit - s0);
+        if (s0 > 0) __syncthreads();  // previous chunk's weights are consumed
+        if (active && tid < n) {
+            float m = m_own, l = l_own, l32 = l32_own;
+            if (s0 > 0) {
+                m = part(s0 + tid)[D];
+                l = part(s0 + tid)[D + 1];
+                l32 = part(s0 + tid)[D + 2];
+            }
+            const float w = l > 0.0f ? __expf(m - M) : 0.0f;
+            w_lds[tid] = w;
+            lpart = __builtin_fmaf(l, w, lpart);
+            l32part = __builtin_fmaf(l32, w, l32part);
+        }
+        __syncthreads();
+        if (!active) continue;
+        if (nsplit <= MERGE_FAST) {
+#pragma unroll
+            for (int s = 0; s < MERGE_FAST; ++s)
+                if (s < n) acc = __builtin_fmaf(xf[s], w_lds[s], acc);
+        } else {
+            int s = 0;
+            for (; s + 8 <= n; s += 8) {  // eight independent loads in flight, sums kept in split order
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = part(s0 + s + e)[tid];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(x[e], w_lds[s + e], acc);
+            }
+            for (; s < n; ++s) acc = __builtin_fmaf(part(s0 + s)[tid], w_lds[s], acc);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lpart += __shfl_xor(lpart, o);
+        l32part += __shfl_xor(l32part, o);
+    }
+    if (active && lane == 0) {
+        red[1][wv] = lpart;
+        red[2][wv] = l32part;
+    }
+    __syncthreads();
+    if (!active) return;
+    const float Lsum = red[1][0] + red[1][1];
+    out[tid] = acc / Lsum;
+    if (lse && tid == 0) *lse = M + __logf(red[2][0] + red[2][1]);
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_select(const uint16_t *q, const float *t_q, int batch, int hq, int hkv, int n_keep, float *q_prime,
                          int32_t *sel_idx, hipStream_t s);
