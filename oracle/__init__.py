@@ -40,6 +40,19 @@ decode_tiered          textbook attention (numpy, fp64) over the three token
                        sources decoded independently; all-BF16 sequences reduce
                        to attention on bf16 k', v; with every tier token moved
                        into pages it equals decode_attn on the same tokens
+quantize_group_clip    clip 1 equals quantize_group; brute-force nearest level
+                       of the clipped grid inside it, saturation outside; the
+                       clipped range from the group extremes by hand
+select_channels_base   unit scales equal select_channels; equals plain
+                       selection with the base transform T_Q diag(sel_scale)
+                       formed explicitly (fp64), up to near-ties
+pack_cache_vrot        identity rotation and clip 1 equal pack_cache; a
+                       within-group channel permutation as R_V permutes the
+                       value codes of pack_cache exactly
+value_unrotate         permutation R_V: rotate, pack, decode and unrotate give
+                       decode_attn of the unrotated cache exactly; a Haar
+                       rotation and its inverse return the input (fp64 bound)
+                       (tests/test_oracle_vrot.py)
 =====================  ==========================================================
 
 Parity unpinned: the accuracy tables of the paper (need models and datasets).
@@ -94,6 +107,15 @@ def _load():
         _lib.orc_decode_bf16.restype = i32
         _lib.orc_bf16_round_array.argtypes = [P, i64, P]
         _lib.orc_bf16_round_array.restype = None
+        f32 = ctypes.c_float
+        _lib.orc_quantize_group_clip.argtypes = [P, i32, f32, P, P, P]
+        _lib.orc_quantize_group_clip.restype = None
+        _lib.orc_pack_cache_vrot.argtypes = [P, P, f32, i32, i32, P, P, i32, P, P, P, P, P]
+        _lib.orc_pack_cache_vrot.restype = None
+        _lib.orc_value_unrotate.argtypes = [P, P, i32, i32, i32, P]
+        _lib.orc_value_unrotate.restype = i32
+        _lib.orc_select_channels_base.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
+        _lib.orc_select_channels_base.restype = i32
         _lib.orc_tier_pages.argtypes = [i64]
         _lib.orc_tier_pages.restype = i64
         _lib.orc_decode_tiered.argtypes = [P, P, P, P, P, i32, P, P, P, P, P, P, i32, i32, i32, P, i32, P, f64, P,
@@ -138,6 +160,16 @@ def quantize_group(x: np.ndarray):
     s = ctypes.c_uint16()
     z = ctypes.c_uint16()
     _load().orc_quantize_group(_p(x), int(x.size), ctypes.byref(s), ctypes.byref(z), _p(codes))
+    return int(s.value), int(z.value), codes
+
+
+def quantize_group_clip(x: np.ndarray, clip: float):
+    """quantize_group on the clipped range [clip * min, clip * max] (fp32 products)."""
+    x = _c(x, np.float32)
+    codes = np.zeros(x.size, dtype=np.uint8)
+    s = ctypes.c_uint16()
+    z = ctypes.c_uint16()
+    _load().orc_quantize_group_clip(_p(x), int(x.size), float(clip), ctypes.byref(s), ctypes.byref(z), _p(codes))
     return int(s.value), int(z.value), codes
 
 
@@ -225,7 +257,61 @@ def quantize_append(k_bf16, v_bf16, t_k_bf16, cu_tokens, page_table, num_pages: 
     return pack_cache(kp, v_bf16, cu_tokens, page_table, num_pages, cache), kp
 
 
+def value_transform(v_bf16: np.ndarray, r_v_bf16: np.ndarray) -> np.ndarray:
+    """v' = v R_V per token and KV head (the same row-vector product as k T_K)."""
+    return key_transform(v_bf16, r_v_bf16)
+
+
+def pack_cache_vrot(kprime: np.ndarray, vprime: np.ndarray, clip: float, cu_tokens, page_table, num_pages: int,
+                    cache: Optional[Cache] = None) -> Cache:
+    """pack_cache with fp32 rotated values and clipped value grids."""
+    kp = _c(kprime, np.float32)
+    vp = _c(vprime, np.float32)
+    cu = _c(cu_tokens, np.int32)
+    pt = _c(page_table, np.int32)
+    hkv = kp.shape[1]
+    if cache is None:
+        cache = Cache(num_pages, hkv)
+    _load().orc_pack_cache_vrot(_p(kp), _p(vp), float(clip), hkv, len(cu) - 1, _p(cu), _p(pt), pt.shape[1],
+                                *[_p(a) for a in cache.arrays()])
+    return cache
+
+
+def quantize_append_vrot(k_bf16, v_bf16, t_k_bf16, r_v_bf16, clip: float, cu_tokens, page_table, num_pages: int,
+                         cache: Optional[Cache] = None):
+    """Keys as quantize_append; values rotated by R_V and clipped.  Returns (cache, k', v')."""
+    kp = key_transform(k_bf16, t_k_bf16)
+    vp = value_transform(v_bf16, r_v_bf16)
+    return pack_cache_vrot(kp, vp, clip, cu_tokens, page_table, num_pages, cache), kp, vp
+
+
+def value_unrotate(o, r_v_inv, hkv: int) -> np.ndarray:
+    """out = o R_V^{-1} per query head (fp64 in, fp64 out)."""
+    o = _c(o, np.float64)
+    r = _c(r_v_inv, np.float32)
+    B, hq = o.shape[0], o.shape[1]
+    out = np.empty_like(o)
+    rc = _load().orc_value_unrotate(_p(o), _p(r), B, hq, hkv, _p(out))
+    if rc:
+        raise ValueError(f"value_unrotate: bad shape (rc={rc})")
+    return out
+
+
 # ---------------------------------------------------------------- decode
+def select_channels_base(q_bf16, t_q, sel_scale, hkv: int, n_keep: int):
+    """select_channels ranking channels by the base-coordinate energy (q' * sel_scale)^2."""
+    q = _c(q_bf16, np.uint16)
+    tq = _c(t_q, np.float32)
+    sc = _c(sel_scale, np.float32)
+    B, hq = q.shape[0], q.shape[1]
+    qp = np.empty((B, hq, HEAD_DIM), dtype=np.float32)
+    sel = np.empty((B, hkv, n_keep), dtype=np.int32)
+    rc = _load().orc_select_channels_base(_p(q), _p(tq), _p(sc), B, hq, hkv, n_keep, _p(qp), _p(sel))
+    if rc:
+        raise ValueError(f"select_channels_base: bad shape (rc={rc})")
+    return qp, sel
+
+
 def select_channels(q_bf16, t_q, hkv: int, n_keep: int):
     q = _c(q_bf16, np.uint16)
     tq = _c(t_q, np.float32)

@@ -176,7 +176,10 @@ typedef struct {
     float s, z;
 } grid_t;
 
-static grid_t make_grid(const float *x, int n, int stride)
+/* clip scales both ends of the group range toward zero before the grid is
+ * fitted (1.0f leaves them as they are; values outside the clipped range take
+ * code 0 or 3 by the threshold rule). */
+static grid_t make_grid_clip(const float *x, int n, int stride, float clip)
 {
     float mn = x[0], mx = x[0];
     for (int i = 1; i < n; ++i) {
@@ -186,6 +189,8 @@ static grid_t make_grid(const float *x, int n, int stride)
         if (v > mx)
             mx = v;
     }
+    mn = clip * mn;
+    mx = clip * mx;
     if (mn == 0.0f)
         mn = 0.0f; /* canonical +0 */
     if (mx == 0.0f)
@@ -200,12 +205,23 @@ static grid_t make_grid(const float *x, int n, int stride)
     return g;
 }
 
+static grid_t make_grid(const float *x, int n, int stride) { return make_grid_clip(x, n, stride, 1.0f); }
+
 static int code_of(float x, const grid_t *g)
 {
     return (x >= fmaf(0.5f, g->s, g->z)) + (x >= fmaf(1.5f, g->s, g->z)) + (x >= fmaf(2.5f, g->s, g->z));
 }
 
 /* Exposed for tests: grid and codes of one group of n fp32 values. */
+void orc_quantize_group_clip(const float *x, int n, float clip, uint16_t *s_bits, uint16_t *z_bits, uint8_t *codes)
+{
+    grid_t g = make_grid_clip(x, n, 1, clip);
+    *s_bits = g.s_bits;
+    *z_bits = g.z_bits;
+    for (int i = 0; i < n; ++i)
+        codes[i] = (uint8_t)code_of(x[i], &g);
+}
+
 void orc_quantize_group(const float *x, int n, uint16_t *s_bits, uint16_t *z_bits, uint8_t *codes)
 {
     grid_t g = make_grid(x, n, 1);
@@ -249,9 +265,9 @@ void orc_key_transform(const uint16_t *k, const uint16_t *t_k, int64_t T, int hk
  * page past the sequence end get code 0, ch0 0 and metadata 0.
  *   kprime fp32 [T][Hkv][128], v bf16 [T][Hkv][128]
  *   cu_tokens [n_seqs+1], page_table [n_seqs][max_pages]                    */
-void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs, const int32_t *cu_tokens,
-                    const int32_t *page_table, int max_pages, uint8_t *k_codes, uint16_t *k_meta, uint16_t *k_ch0,
-                    uint8_t *v_codes, uint16_t *v_meta)
+static void pack_impl(const float *kprime, const uint16_t *v, const float *vf32, float vclip, int hkv, int n_seqs,
+                      const int32_t *cu_tokens, const int32_t *page_table, int max_pages, uint8_t *k_codes,
+                      uint16_t *k_meta, uint16_t *k_ch0, uint8_t *v_codes, uint16_t *v_meta)
 {
     for (int sq = 0; sq < n_seqs; ++sq) {
         int64_t t0 = cu_tokens[sq], L = (int64_t)cu_tokens[sq + 1] - t0;
@@ -288,12 +304,12 @@ void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs,
                     }
                 }
                 for (int s = 0; s < nvalid; ++s) {
-                    const uint16_t *vr = v + ((size_t)(base_tok + s) * hkv + g) * HD;
+                    size_t row = ((size_t)(base_tok + s) * hkv + g) * HD;
                     float vf[HD];
                     for (int c = 0; c < HD; ++c)
-                        vf[c] = orc_bf16_value(vr[c]);
+                        vf[c] = vf32 ? vf32[row + c] : orc_bf16_value(v[row + c]);
                     for (int q = 0; q < HD / VGROUP; ++q) {
-                        grid_t gr = make_grid(vf + q * VGROUP, VGROUP, 1);
+                        grid_t gr = make_grid_clip(vf + q * VGROUP, VGROUP, 1, vclip);
                         vm[(0 * 4 + q) * PG + s] = gr.s_bits;
                         vm[(1 * 4 + q) * PG + s] = gr.z_bits;
                         for (int c = q * VGROUP; c < (q + 1) * VGROUP; ++c)
@@ -305,6 +321,52 @@ void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs,
     }
 }
 
+void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs, const int32_t *cu_tokens,
+                    const int32_t *page_table, int max_pages, uint8_t *k_codes, uint16_t *k_meta, uint16_t *k_ch0,
+                    uint8_t *v_codes, uint16_t *v_meta)
+{
+    pack_impl(kprime, v, NULL, 1.0f, hkv, n_seqs, cu_tokens, page_table, max_pages, k_codes, k_meta, k_ch0, v_codes,
+              v_meta);
+}
+
+/* The same pack with rotated values (§3.3, values paragraph, and App. B.2,
+ * value quantization): the values arrive already rotated, v' = v R_V in fp32
+ * [T][Hkv][128] (the row-vector product of orc_key_transform with R_V in
+ * place of T_K), and each (token, KV head, 32-channel group) grid is fitted
+ * to the clipped range [clip * min, clip * max].  Keys are packed exactly as
+ * by orc_pack_cache (keys are not clipped).                                 */
+void orc_pack_cache_vrot(const float *kprime, const float *vprime, float clip, int hkv, int n_seqs,
+                         const int32_t *cu_tokens, const int32_t *page_table, int max_pages, uint8_t *k_codes,
+                         uint16_t *k_meta, uint16_t *k_ch0, uint8_t *v_codes, uint16_t *v_meta)
+{
+    pack_impl(kprime, NULL, vprime, clip, hkv, n_seqs, cu_tokens, page_table, max_pages, k_codes, k_meta, k_ch0,
+              v_codes, v_meta);
+}
+
+/* Inverse value rotation after aggregation (§3.4, last step): per query head
+ * h of KV head g = h / (hq / hkv), out_c = sum_j o_j R_inv[g][j][c] in fp64,
+ * ascending j.  o, out fp64 [B][Hq][128] (out may not alias o);
+ * r_inv fp32 [Hkv][128][128].                                               */
+int orc_value_unrotate(const double *o, const float *r_inv, int batch, int hq, int hkv, double *out)
+{
+    if (hkv <= 0 || hq % hkv)
+        return -2;
+    int grp = hq / hkv;
+    for (int b = 0; b < batch; ++b)
+        for (int h = 0; h < hq; ++h) {
+            const double *orow = o + ((size_t)b * hq + h) * HD;
+            const float *r = r_inv + (size_t)(h / grp) * HD * HD;
+            double *dst = out + ((size_t)b * hq + h) * HD;
+            for (int c = 0; c < HD; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < HD; ++j)
+                    acc += orow[j] * (double)r[(size_t)j * HD + c];
+                dst[c] = acc;
+            }
+        }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Query transform and dynamic channel selection (§3.2 Eq. 4, §3.3).
  * q'_{h,j} = sum_i q_{h,i} T_Q[g][i][j] as an fp32 fma chain over ascending i.
@@ -314,8 +376,8 @@ void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs,
  * are written in ascending channel order.
  *   q bf16 [B][Hq][128], t_q fp32 [Hkv][128][128]
  *   q_prime fp32 [B][Hq][128], sel_idx int32 [B][Hkv][n_keep]               */
-int orc_select_channels(const uint16_t *q, const float *t_q, int batch, int hq, int hkv, int n_keep, float *q_prime,
-                        int32_t *sel_idx)
+static int select_impl(const uint16_t *q, const float *t_q, const float *sel_scale, int batch, int hq, int hkv,
+                       int n_keep, float *q_prime, int32_t *sel_idx)
 {
     if (hkv <= 0 || hq % hkv || n_keep < 1 || n_keep > HD)
         return -2;
@@ -336,8 +398,10 @@ int orc_select_channels(const uint16_t *q, const float *t_q, int batch, int hq, 
                         acc = fmaf(orc_bf16_value(qr[i]), tq[(size_t)i * HD + j], acc);
                     qp[j] = acc;
                 }
-                for (int j = 0; j < HD; ++j)
-                    S[j] = fmaf(qp[j], qp[j], S[j]);
+                for (int j = 0; j < HD; ++j) {
+                    float e = sel_scale ? qp[j] * sel_scale[(size_t)g * HD + j] : qp[j];
+                    S[j] = fmaf(e, e, S[j]);
+                }
             }
             int32_t *out = sel_idx + ((size_t)b * hkv + g) * n_keep;
             int w = 0;
@@ -351,6 +415,23 @@ int orc_select_channels(const uint16_t *q, const float *t_q, int batch, int hq, 
             }
         }
     return 0;
+}
+
+int orc_select_channels(const uint16_t *q, const float *t_q, int batch, int hq, int hkv, int n_keep, float *q_prime,
+                        int32_t *sel_idx)
+{
+    return select_impl(q, t_q, NULL, batch, hq, hkv, n_keep, q_prime, sel_idx);
+}
+
+/* Selection in the base coordinates (§3.3, diagonal refinement, and App.
+ * C.2): with A = A_0 D folded into T_Q, the base query q A_0 is q' D^-1, so
+ * the energy of channel j sums (q'_{h,j} * sel_scale[g][j])^2 with sel_scale
+ * = 1 / delta_j (the product rounded to fp32, then the same fma chain); q'
+ * itself, which scores, is unchanged.  sel_scale fp32 [Hkv][128].          */
+int orc_select_channels_base(const uint16_t *q, const float *t_q, const float *sel_scale, int batch, int hq, int hkv,
+                             int n_keep, float *q_prime, int32_t *sel_idx)
+{
+    return select_impl(q, t_q, sel_scale, batch, hq, hkv, n_keep, q_prime, sel_idx);
 }
 
 /* ------------------------------------------------------------------------ */

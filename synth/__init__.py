@@ -35,6 +35,7 @@ PAGE = 128
 
 # stream identifiers for numpy SeedSequence spawning
 _ID_Q, _ID_K, _ID_V, _ID_T, _ID_OUTLIER, _ID_LEN, _ID_PERM = 1, 2, 3, 4, 5, 6, 7
+_ID_RV, _ID_D = 8, 9
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -126,6 +127,51 @@ def make_transforms(hkv: int, seed: int):
         tk64 = bf16_bits_to_f32(tk[g]).astype(np.float64)
         tq[g] = np.linalg.inv(tk64).T.astype(np.float32)
     return tk, tq
+
+
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order n (a power of two), entries +-1."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def make_value_rotation(hkv: int, seed: int):
+    """R_V (bf16 bits, [hkv][128][128]) and R_V^{-1} (fp32, [hkv][128][128]).
+
+    Stands in for the calibrated value rotation composed with a Hadamard
+    transform (§3.3 values paragraph, App. B.2): R_V = bf16(R H / sqrt(128))
+    with R Haar-orthogonal; the inverse is that of the stored bf16 matrix,
+    computed in fp64 and rounded to fp32 (the stored matrix is orthogonal
+    only up to bf16 rounding)."""
+    rng = _rng(seed, _ID_RV)
+    hn = hadamard(HEAD_DIM) / math.sqrt(HEAD_DIM)
+    rv = np.empty((hkv, HEAD_DIM, HEAD_DIM), dtype=np.uint16)
+    rinv = np.empty((hkv, HEAD_DIM, HEAD_DIM), dtype=np.float32)
+    for g in range(hkv):
+        a = rng.standard_normal((HEAD_DIM, HEAD_DIM))
+        qm, rm = np.linalg.qr(a)
+        qm = qm * np.sign(np.diag(rm))[None, :]
+        rv[g] = f32_to_bf16_bits((qm @ hn).astype(np.float32))
+        rinv[g] = np.linalg.inv(bf16_bits_to_f32(rv[g]).astype(np.float64)).astype(np.float32)
+    return rv, rinv
+
+
+def make_selection_scales(hkv: int, seed: int) -> np.ndarray:
+    """Per-channel selection weights 1/delta_j, fp32 [hkv][128].
+
+    Stands in for the diagonal refinement D of §3.3 (A = A_0 D): delta_0 = 1,
+    the other 127 entries log-uniform in [1/2, 2] and normalised to unit
+    geometric mean (App. B.2)."""
+    rng = _rng(seed, _ID_D)
+    out = np.empty((hkv, HEAD_DIM), dtype=np.float32)
+    for g in range(hkv):
+        u = rng.uniform(math.log(0.5), math.log(2.0), size=HEAD_DIM - 1)
+        u -= u.mean()
+        delta = np.concatenate([[1.0], np.exp(u)])
+        out[g] = (1.0 / delta).astype(np.float32)
+    return out
 
 
 def outlier_channels(hkv: int, n: int, seed: int) -> np.ndarray:
