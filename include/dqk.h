@@ -303,6 +303,60 @@ int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const flo
                            const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
                            size_t ws_bytes, float *out, float *lse, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Rotated values and selection in base coordinates (§3.3: the calibrated
+ * value rotation and clipping of App. B.2, and the diagonal refinement
+ * A = A_0 D with selection on the base queries q A_0, App. C.2; §3.4: the
+ * value rotation is undone after aggregation).  A cache written by
+ * dqk_quantize_append_vrot holds v' = v R_V in its value pages; any decode
+ * entry point aggregates v' unchanged and dqk_value_unrotate then maps each
+ * output row back, o = o' R_V^-1.
+ */
+
+/*
+ * dqk_quantize_append with rotated, clipped values.  Keys exactly as
+ * dqk_quantize_append (not clipped).  Values: v' = v R_V on MFMA (bf16 x bf16
+ * -> fp32 accumulator, no intermediate rounding), then per (token, KV head,
+ * 32-channel group) the binary16 grid of the clipped range
+ * [fp32(clip * min), fp32(clip * max)] of the group's v' (values beyond it
+ * take code 0 or 3).
+ *   r_v_bf16    bf16 [Hkv][128][128] value rotation R_V, [in ch][out ch].
+ *   clip        clipping ratio, 0 < clip <= 1 (the paper uses 0.92; 1 fits
+ *               the full range).
+ *   vprime_dbg  fp32 [total_tokens][Hkv][128] or NULL: receives v' = v R_V.
+ * Other arguments and errors as dqk_quantize_append; DQK_ERR_SHAPE for a clip
+ * outside (0, 1].
+ */
+int dqk_quantize_append_vrot(const dqk_cache *c, const void *k_bf16, const void *v_bf16, const void *t_k_bf16,
+                             const void *r_v_bf16, float clip, int32_t n_seqs, const int32_t *cu_tokens,
+                             int64_t total_tokens, const int32_t *page_table, int32_t max_pages, float *kprime_dbg,
+                             float *vprime_dbg, hipStream_t stream);
+
+/*
+ * dqk_select_channels with the channels ranked in base coordinates: with the
+ * refinement D folded into T_Q (q' = q A_0 D), the energy of channel j is
+ * S_j = sum over the KV head's query heads of e^2, e = fp32(q'_j *
+ * sel_scale[g][j]) (fp32 fma chain, ascending head), sel_scale = 1 / delta_j.
+ * q_prime is q T_Q as in dqk_select_channels (the scoring coordinates).
+ *   sel_scale  fp32 [hkv][128], finite.
+ * Other arguments and errors as dqk_select_channels.
+ */
+int dqk_select_channels_base(const void *q_bf16, const float *t_q, const float *sel_scale, int32_t batch,
+                             int32_t hq, int32_t hkv, int32_t n_keep, float *q_prime, int32_t *sel_idx,
+                             hipStream_t stream);
+
+/*
+ * Inverse value rotation of decode outputs, in place: for each sequence b and
+ * query head h (KV head g = h / (hq / hkv)), out[b][h][c] = sum_j
+ * out[b][h][j] r_v_inv[g][j][c], an fp32 fma chain over ascending j.
+ *   out       fp32 [batch][hq][128], the output of a decode entry point.
+ *   r_v_inv   fp32 [hkv][128][128] inverse of the stored R_V, [j][c].
+ * Requires hq % hkv == 0 and hq / hkv <= 64 (DQK_ERR_SHAPE /
+ * DQK_ERR_UNSUPPORTED).  One kernel, stream-ordered after the decode.
+ */
+int dqk_value_unrotate(float *out, const float *r_v_inv, int32_t batch, int32_t hq, int32_t hkv,
+                       hipStream_t stream);
+
 /*
  * dqk_stream_read -- measurement helper, not part of the attention path: a
  * plain streaming read of `bytes` bytes (a multiple of 16 KiB) at `src`,

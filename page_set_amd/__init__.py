@@ -91,6 +91,13 @@ def lib():
         L.dqk_decode_attn_tiered.argtypes = [ctypes.POINTER(dqk_cache), T, P, P, i32, i32, i32, P, i32, P,
                                              ctypes.c_float, i32, P, sz, P, P, P]
         L.dqk_decode_attn_tiered.restype = ctypes.c_int
+        L.dqk_quantize_append_vrot.argtypes = [ctypes.POINTER(dqk_cache), P, P, P, P, ctypes.c_float, i32, P, i64,
+                                               P, i32, P, P, P]
+        L.dqk_quantize_append_vrot.restype = ctypes.c_int
+        L.dqk_select_channels_base.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P]
+        L.dqk_select_channels_base.restype = ctypes.c_int
+        L.dqk_value_unrotate.argtypes = [P, P, i32, i32, i32, P]
+        L.dqk_value_unrotate.restype = ctypes.c_int
         L.dqk_stream_read.argtypes = [P, sz, P, P]
         L.dqk_stream_read.restype = ctypes.c_int
         _lib = L
@@ -234,6 +241,37 @@ def dqk_select_channels(q, t_q, hkv: int, n_keep: int, q_prime=None, sel_idx=Non
                                    _stream(stream))
     _check(rc, "dqk_select_channels")
     return q_prime, sel_idx
+
+
+def dqk_quantize_append_vrot(cache: Cache, k, v, t_k, r_v, clip: float, cu_tokens, page_table, kprime_dbg=None,
+                             vprime_dbg=None, stream=None):
+    n_seqs = cu_tokens.numel() - 1
+    s = cache.struct()
+    rc = lib().dqk_quantize_append_vrot(ctypes.byref(s), _ptr(k), _ptr(v), _ptr(t_k), _ptr(r_v), float(clip), n_seqs,
+                                        _ptr(cu_tokens), int(k.shape[0]), _ptr(page_table), int(page_table.shape[1]),
+                                        _ptr(kprime_dbg), _ptr(vprime_dbg), _stream(stream))
+    _check(rc, "dqk_quantize_append_vrot")
+
+
+def dqk_select_channels_base(q, t_q, sel_scale, hkv: int, n_keep: int, q_prime=None, sel_idx=None, stream=None):
+    import torch
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    if q_prime is None:
+        q_prime = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, hkv, n_keep), dtype=torch.int32, device=q.device)
+    rc = lib().dqk_select_channels_base(_ptr(q), _ptr(t_q), _ptr(sel_scale), B, hq, hkv, n_keep, _ptr(q_prime),
+                                        _ptr(sel_idx), _stream(stream))
+    _check(rc, "dqk_select_channels_base")
+    return q_prime, sel_idx
+
+
+def dqk_value_unrotate(out, r_v_inv, hkv: int, stream=None):
+    """out <- out R_V^-1 per query head, in place; returns out."""
+    B, hq = int(out.shape[0]), int(out.shape[1])
+    rc = lib().dqk_value_unrotate(_ptr(out), _ptr(r_v_inv), B, hq, hkv, _stream(stream))
+    _check(rc, "dqk_value_unrotate")
+    return out
 
 
 def dqk_decode_workspace_size(batch: int, hq: int, hkv: int, max_pages: int, num_splits: int = 0) -> int:

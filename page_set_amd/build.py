@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdqk.so")
 ARCH = os.environ.get("DQK_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["dqk_api.cpp", "dqk_select.hip", "dqk_append.hip", "dqk_decode.hip", "dqk_decode_blk.hip", "dqk_tiers.hip"]
+SOURCES = ["dqk_api.cpp", "dqk_select.hip", "dqk_append.hip", "dqk_decode.hip", "dqk_decode_blk.hip", "dqk_tiers.hip",
+           "dqk_vrot.hip"]
 # MFMA accumulators in ordinary VGPRs: the decode loop reads and rescales them
 # with VALU instructions, which would otherwise copy them out of AGPRs
 EXTRA = {"dqk_decode_blk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}

@@ -107,8 +107,8 @@ int dqk_select_channels(const void *q_bf16, const float *t_q, int32_t batch, int
     if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM) return DQK_ERR_SHAPE;
     if (hq / hkv > 64 || batch > 65535) return DQK_ERR_UNSUPPORTED;
     if (!aligned16(q_bf16) || !aligned16(t_q) || !aligned16(q_prime) || !aligned16(sel_idx)) return DQK_ERR_ALIGN;
-    return hip_status(dqk::launch_select(static_cast<const uint16_t *>(q_bf16), t_q, batch, hq, hkv, n_keep, q_prime,
-                                         sel_idx, stream));
+    return hip_status(dqk::launch_select(static_cast<const uint16_t *>(q_bf16), t_q, nullptr, batch, hq, hkv, n_keep,
+                                         q_prime, sel_idx, stream));
 }
 
 int dqk_quantize_append(const dqk_cache *c, const void *k_bf16, const void *v_bf16, const void *t_k_bf16,
@@ -126,6 +126,46 @@ int dqk_quantize_append(const dqk_cache *c, const void *k_bf16, const void *v_bf
                                          static_cast<const uint16_t *>(v_bf16),
                                          static_cast<const uint16_t *>(t_k_bf16), n_seqs, cu_tokens, page_table,
                                          max_pages, kprime_dbg, stream));
+}
+
+int dqk_quantize_append_vrot(const dqk_cache *c, const void *k_bf16, const void *v_bf16, const void *t_k_bf16,
+                             const void *r_v_bf16, float clip, int32_t n_seqs, const int32_t *cu_tokens,
+                             int64_t total_tokens, const int32_t *page_table, int32_t max_pages, float *kprime_dbg,
+                             float *vprime_dbg, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!k_bf16 || !v_bf16 || !t_k_bf16 || !r_v_bf16 || !cu_tokens || !page_table) return DQK_ERR_NULL;
+    if (n_seqs < 1 || max_pages < 1 || total_tokens < 1 || !(clip > 0.0f && clip <= 1.0f)) return DQK_ERR_SHAPE;
+    if (n_seqs > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(t_k_bf16) || !aligned16(r_v_bf16) ||
+        !aligned16(cu_tokens) || !aligned16(page_table) || (kprime_dbg && !aligned16(kprime_dbg)) ||
+        (vprime_dbg && !aligned16(vprime_dbg)))
+        return DQK_ERR_ALIGN;
+    return hip_status(dqk::launch_append_vrot(
+        *c, static_cast<const uint16_t *>(k_bf16), static_cast<const uint16_t *>(v_bf16),
+        static_cast<const uint16_t *>(t_k_bf16), static_cast<const uint16_t *>(r_v_bf16), clip, n_seqs, cu_tokens,
+        page_table, max_pages, kprime_dbg, vprime_dbg, stream));
+}
+
+int dqk_select_channels_base(const void *q_bf16, const float *t_q, const float *sel_scale, int32_t batch,
+                             int32_t hq, int32_t hkv, int32_t n_keep, float *q_prime, int32_t *sel_idx,
+                             hipStream_t stream) {
+    if (!q_bf16 || !t_q || !sel_scale || !q_prime || !sel_idx) return DQK_ERR_NULL;
+    if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM) return DQK_ERR_SHAPE;
+    if (hq / hkv > 64 || batch > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(q_bf16) || !aligned16(t_q) || !aligned16(sel_scale) || !aligned16(q_prime) || !aligned16(sel_idx))
+        return DQK_ERR_ALIGN;
+    return hip_status(dqk::launch_select(static_cast<const uint16_t *>(q_bf16), t_q, sel_scale, batch, hq, hkv,
+                                         n_keep, q_prime, sel_idx, stream));
+}
+
+int dqk_value_unrotate(float *out, const float *r_v_inv, int32_t batch, int32_t hq, int32_t hkv,
+                       hipStream_t stream) {
+    if (!out || !r_v_inv) return DQK_ERR_NULL;
+    if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return DQK_ERR_SHAPE;
+    if (hq / hkv > 64 || batch > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(out) || !aligned16(r_v_inv)) return DQK_ERR_ALIGN;
+    return hip_status(dqk::launch_value_unrotate(out, r_v_inv, batch, hq, hkv, stream));
 }
 
 size_t dqk_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t max_pages, int32_t num_splits) {

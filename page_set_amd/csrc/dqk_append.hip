@@ -22,6 +22,16 @@
 //   5. Values: 512 (token, 32-channel group) units per page, two per lane,
 //      consecutive lanes on consecutive tokens of one group.
 // Full pages take a path without per-token checks.
+//
+// Rotated values (§3.3 values paragraph, App. B.2 value quantization): the
+// values are multiplied by R_V on MFMA too, v' = v R_V, and each (token,
+// 32-channel group) grid is fitted to the clipped range [clip min, clip max].
+// R_V^T is staged like T_K^T and wave w keeps the A fragments of output
+// channels 32w..32w+31 (value group w) in VGPRs.  After a page's keys the
+// value tile replaces the key tile in LDS (rows = tokens, chunk c of row r at
+// slot c ^ (r & 15)); the 16 x 16 output tiles are (channel, token), so a lane
+// holds four consecutive channels of one token (one code byte) and the
+// group's other 24 channels sit in the lanes 16 and 32 apart.
 // Built with -ffp-contract=off: the grid arithmetic must round as written.
 #include "dqk_internal.h"
 
@@ -43,6 +53,8 @@ constexpr int VLD = PG * VGROUPS / 256;     // value units per thread
 // channels): 16 consecutive rows get distinct slots.
 __device__ __forceinline__ uint32_t swz_k(int r) { return (uint32_t)((r & 3) | ((r >> 3) & 12)); }
 __device__ __forceinline__ uint32_t swz_t(int r) { return (uint32_t)(r & 15); }
+// Value tile (rows = tokens): an operand read touches rows 16 tt + n, n = 0..15.
+__device__ __forceinline__ uint32_t swz_v(int r) { return (uint32_t)(r & 15); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)p;
@@ -79,6 +91,41 @@ __device__ __forceinline__ float wave_row_min(float x) {
 __device__ __forceinline__ float wave_row_max(float x) {
     x = fmaxf(x, __shfl_xor(x, 16));
     return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ __forceinline__ uint32_t wave_row_or(uint32_t x) {
+    x |= (uint32_t)__shfl_xor((int)x, 16);
+    return x | (uint32_t)__shfl_xor((int)x, 32);
+}
+
+// M^T of a bf16 [in ch][out ch] matrix into LDS rows of 256 bytes ([out ch][in
+// ch]): thread (row pair rp, column octet oc) stores the two rows' elements of
+// each column as one 4-byte word; chunk c of row r at slot c ^ swz_t(r).
+__device__ __forceinline__ void stage_transposed(const uint16_t *__restrict__ M, uint32_t ks) {
+    for (int it = threadIdx.x; it < (D / 2) * (D / 8); it += 256) {
+        const int rp = it & (D / 2 - 1), oc = it / (D / 2);
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(M + (size_t)(2 * rp) * D + oc * 8);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(M + (size_t)(2 * rp + 1) * D + oc * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int row = oc * 8 + e;
+            const uint32_t word = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+            lds_st<uint32_t>(ks + row * 256 + ((((uint32_t)rp >> 2) ^ swz_t(row)) << 4) + (rp & 3) * 4, word);
+        }
+    }
+}
+
+// Fragments of the staged M^T for output channels 32 w + 16 nt + n and the
+// four 32-deep k-steps (k-octet G), kept in VGPRs for all pages of a run.
+__device__ __forceinline__ void load_frags(uint32_t ks, bf16x8 (&f)[2][4]) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int G = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            const int row = 32 * w + 16 * nt + n;
+            f[nt][kk] = lds_ld<bf16x8>(ks + row * 256 + (((4 * kk + G) ^ swz_t(row)) << 4));
+        }
 }
 
 // Values of one (token, group) unit from its 64 loaded bytes: 32 channels ->
@@ -138,6 +185,83 @@ __device__ __forceinline__ void values_of_page(const dqk_cache &c, const uint16_
     }
 }
 
+// Rotated values of the page whose value tile is in LDS at ks: wave w
+// computes v' = v R_V for value group w (channels 32w..32w+31) and all 128
+// tokens, two token tiles at a time, and packs them: per token the group's
+// extremes (in-lane over 8 channels, then across the four 16-lane rows),
+// the clipped grid, one code byte per lane and channel tile, gathered into
+// the group's 8 bytes by OR across the rows.
+template <bool FULL, bool DBG>
+__device__ __forceinline__ void values_rot_of_page(const dqk_cache &c, uint32_t ks, const bf16x8 (&rop)[2][4],
+                                                   size_t pg, int g, int hkv, int nvalid, int64_t t0, float clip,
+                                                   float *__restrict__ vprime_dbg) {
+    const int tid = fresh_tid(), lane = tid & 63, w = tid >> 6;
+    const int G = lane >> 4, n = lane & 15;
+    // B fragment of token tile tt, k-step kk: row 16 tt + n, chunk 4 kk + G
+    const uint32_t brow = ks + (uint32_t)n * 256;
+#pragma unroll
+    for (int tp = 0; tp < 4; ++tp) {
+        f32x4 acc[2][2];
+        bf16x8 bv[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                bv[j][kk] = lds_ld<bf16x8>(brow + (uint32_t)(2 * tp + j) * 4096 + (((uint32_t)(4 * kk + G) ^ (uint32_t)n) << 4));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) acc[j][ct] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    acc[j][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rop[ct][kk], bv[j][kk], acc[j][ct], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            // lane holds channels 32 w + 16 ct + 4 G + r of token tok
+            const int tok = 16 * (2 * tp + j) + n;
+            const bool valid = FULL || tok < nvalid;
+            if (DBG && vprime_dbg && valid) {
+                float *dst = vprime_dbg + ((size_t)(t0 + tok) * hkv + g) * D + 32 * w + 4 * G;
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[16 * ct + r] = acc[j][ct][r];
+            }
+            float mn = acc[j][0][0], mx = acc[j][0][0];
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    mn = fminf(mn, acc[j][ct][r]);
+                    mx = fmaxf(mx, acc[j][ct][r]);
+                }
+            mn = wave_row_min(mn);
+            mx = wave_row_max(mx);
+            const Grid gr = make_grid(__fmul_rn(clip, mn), __fmul_rn(clip, mx));
+            const Thresholds th = thresholds(gr);
+            uint32_t e = 0, o = 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                e |= code2(acc[j][0][r], th) << (2 * r);
+                o |= code2(acc[j][1][r], th) << (2 * r);
+            }
+            // group bytes 0..3 come from channel tile 0 (rows G = 0..3), 4..7 from tile 1
+            const uint32_t lo = wave_row_or(e << (8 * G)), hi = wave_row_or(o << (8 * G));
+            if (G == 0) {
+                const uint64_t bits = valid ? ((uint64_t)lo | ((uint64_t)hi << 32)) : 0ull;
+                *reinterpret_cast<uint64_t *>(c.v_codes + (pg * PG + tok) * ROW_BYTES + 8 * w) = bits;
+                c.v_meta[(pg * 2 + 0) * VGROUPS * PG + w * PG + tok] = valid ? gr.sb : (uint16_t)0;
+                c.v_meta[(pg * 2 + 1) * VGROUPS * PG + w * PG + tok] = valid ? gr.zb : (uint16_t)0;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one token-tile pair live at a time
+    }
+}
+
 // k' of the tile in LDS for 16 output channels (channel tile nt of this
 // wave's 32), then the packed key rows, metadata and channel 0.  FULL: all 128
 // tokens valid; DBG: k' also goes to kprime_dbg.
@@ -167,7 +291,7 @@ __device__ __forceinline__ void keys_of_page(const dqk_cache &c, uint32_t ks, co
     const size_t pg = (size_t)p * hkv + g;
     // lane holds tokens 32G .. 32G+31 of channel 32w + 16nt + n
     const int ch = 32 * w + 16 * nt + n;
-    if (DBG) {
+    if (DBG && kprime_dbg) {
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -239,14 +363,18 @@ struct AppendSrc {
     const int32_t *cu_tokens;
     const int32_t *lens_before;
     const uint16_t *tail_kraw, *tail_v;
+    const uint16_t *r_v;  // rotated values only: R_V bf16 [Hkv][128][128], the clip ratio, v' output or null
+    float clip;
+    float *vprime_dbg;
 };
 
 __device__ __forceinline__ int64_t tier_pages_of(int64_t L) {
     return L >= TIER_SINK + TIER_RECENT ? (L - TIER_SINK - TIER_RECENT) / PG : 0;
 }
 
-template <bool DBG, int MODE>
-__global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, AppendSrc src, const uint16_t *__restrict__ t_k,
+// Rotated values keep a second set of fragments in VGPRs: two workgroups a CU.
+template <bool DBG, int MODE, bool VROT>
+__global__ __launch_bounds__(256, VROT ? 2 : 4) void append_kernel(dqk_cache c, AppendSrc src, const uint16_t *__restrict__ t_k,
                                                      const int32_t *__restrict__ page_table, int max_pages,
                                                      float *__restrict__ kprime_dbg) {
     // T_K^T [out ch][in ch] first, then each page's key tile [token][in ch]; rows of 256 bytes
@@ -273,31 +401,19 @@ __global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, AppendSrc s
         pi_end = (int)min<int64_t>(min(pi0 + NPW, max_pages), npg);
     }
     const int64_t L_plain = MODE == APPEND_PLAIN ? (int64_t)src.cu_tokens[sq + 1] - tok0 : 0;
-    // ---- T_K^T: thread (row pair rp, column octet oc) stores the two rows'
-    //      elements of each column as one 4-byte word
-    const uint16_t *T = t_k + (size_t)g * D * D;
-    for (int it = threadIdx.x; it < (D / 2) * (D / 8); it += 256) {
-        const int rp = it & (D / 2 - 1), oc = it / (D / 2);
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(T + (size_t)(2 * rp) * D + oc * 8);
-        const u32x4 b = *reinterpret_cast<const u32x4 *>(T + (size_t)(2 * rp + 1) * D + oc * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int row = oc * 8 + e;
-            const uint32_t word = __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-            lds_st<uint32_t>(ks + row * 256 + ((((uint32_t)rp >> 2) ^ swz_t(row)) << 4) + (rp & 3) * 4, word);
-        }
-    }
+    // ---- T_K^T (and R_V^T) staged in turn, their fragments kept in VGPRs
+    stage_transposed(t_k + (size_t)g * D * D, ks);
     __syncthreads();
     bf16x8 bop[2][4];  // [channel tile][k-step]
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int G = lane >> 4, n = lane & 15;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int row = 32 * w + 16 * nt + n;
-            bop[nt][kk] = lds_ld<bf16x8>(ks + row * 256 + (((4 * kk + G) ^ swz_t(row)) << 4));
-        }
+    load_frags(ks, bop);
+    bf16x8 rop[2][4];
+    if constexpr (VROT) {
+        __syncthreads();
+        stage_transposed(src.r_v + (size_t)g * D * D, ks);
+        __syncthreads();
+        load_frags(ks, rop);
+    }
+    const int G = ((int)threadIdx.x & 63) >> 4;
 
     for (int pi = pi0; pi < pi_end; ++pi) {
         const int nvalid = MODE == APPEND_PLAIN ? (int)min<int64_t>(PG, L_plain - (int64_t)pi * PG) : PG;
@@ -343,10 +459,12 @@ __global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, AppendSrc s
 
         // ---- values: unit k is (token t, group q0 + 2 k), consecutive lanes on
         //      consecutive tokens; both units of a lane share the token
-        if (nvalid == PG)
-            values_of_page<true>(c, vpage, kstride, tid, pg, nvalid);
-        else
-            values_of_page<false>(c, vpage, kstride, tid, pg, nvalid);
+        if constexpr (!VROT) {
+            if (nvalid == PG)
+                values_of_page<true>(c, vpage, kstride, tid, pg, nvalid);
+            else
+                values_of_page<false>(c, vpage, kstride, tid, pg, nvalid);
+        }
 
         wait_all_barrier();  // the tile has landed
 #pragma unroll
@@ -357,6 +475,25 @@ __global__ __launch_bounds__(256, 4) void append_kernel(dqk_cache c, AppendSrc s
                 keys_of_page<false, DBG>(c, ks, bop[nt], nt, p, g, hkv, nvalid, t0, kprime_dbg);
             __builtin_amdgcn_sched_barrier(0);  // one channel tile's accumulators live at a time
         }
+        if constexpr (VROT) {
+            __syncthreads();  // every wave has read the key tile
+            // ---- value tile: load i of wave w covers rows 32 w + 4 i + G, LDS slot
+            //      lane & 15 of a row receiving input chunk slot ^ swz_v(row)
+            const int tid = fresh_tid(), lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+            const uint32_t tile_w = ks + (uint32_t)(32 * w) * 256;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = 32 * w + 4 * i + G;
+                const int srow = (nvalid == PG || row < nvalid) ? row : 0;
+                const uint32_t chunk = (uint32_t)(lane & 15) ^ swz_v(row);
+                dma16(vpage, (uint32_t)(srow * kstride) * 2 + chunk * 16, tile_w + i * 1024);
+            }
+            wait_all_barrier();
+            if (nvalid == PG)
+                values_rot_of_page<true, DBG>(c, ks, rop, pg, g, hkv, nvalid, t0, src.clip, src.vprime_dbg);
+            else
+                values_rot_of_page<false, DBG>(c, ks, rop, pg, g, hkv, nvalid, t0, src.clip, src.vprime_dbg);
+        }
     }
 }
 
@@ -366,12 +503,12 @@ hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *
                          const int32_t *cu_tokens, const int32_t *page_table, int max_pages, float *kprime_dbg,
                          hipStream_t s) {
     dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
-    const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr};
+    const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr, nullptr, 1.0f, nullptr};
     if (kprime_dbg)
-        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN, false>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                            max_pages, kprime_dbg);
     else
-        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, false>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                            max_pages, kprime_dbg);
     return hipGetLastError();
 }
@@ -380,17 +517,32 @@ hipError_t launch_append_tiered(const dqk_cache &c, const uint16_t *k, const uin
                                 int n_seqs, const int32_t *cu_tokens, const int32_t *page_table, int max_pages,
                                 hipStream_t s) {
     dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
-    const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr};
-    hipLaunchKernelGGL((append_kernel<false, APPEND_TIERED>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+    const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr, nullptr, 1.0f, nullptr};
+    hipLaunchKernelGGL((append_kernel<false, APPEND_TIERED, false>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                        max_pages, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_vrot(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                              const uint16_t *r_v, float clip, int n_seqs, const int32_t *cu_tokens,
+                              const int32_t *page_table, int max_pages, float *kprime_dbg, float *vprime_dbg,
+                              hipStream_t s) {
+    dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
+    const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr, r_v, clip, vprime_dbg};
+    if (kprime_dbg || vprime_dbg)
+        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN, true>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+                           max_pages, kprime_dbg);
+    else
+        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, true>), grid, dim3(256), 0, s, c, src, t_k,
+                           page_table, max_pages, kprime_dbg);
     return hipGetLastError();
 }
 
 hipError_t launch_pack_tail(const dqk_cache &c, const dqk_tiers &t, const uint16_t *t_k, int batch,
                             const int32_t *lens_before, const int32_t *page_table, int max_pages, hipStream_t s) {
     dim3 grid(1, batch, c.num_kv_heads);
-    const AppendSrc src{nullptr, nullptr, nullptr, lens_before, t.tail_kraw, t.tail_v};
-    hipLaunchKernelGGL((append_kernel<false, APPEND_TAIL>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+    const AppendSrc src{nullptr, nullptr, nullptr, lens_before, t.tail_kraw, t.tail_v, nullptr, 1.0f, nullptr};
+    hipLaunchKernelGGL((append_kernel<false, APPEND_TAIL, false>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                        max_pages, nullptr);
     return hipGetLastError();
 }

@@ -206,8 +206,8 @@ __device__ __forceinline__ void merge_row(Part part, int nsplit, int tid, bool a
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_select(const uint16_t *q, const float *t_q, int batch, int hq, int hkv, int n_keep, float *q_prime,
-                         int32_t *sel_idx, hipStream_t s);
+hipError_t launch_select(const uint16_t *q, const float *t_q, const float *sel_scale, int batch, int hq, int hkv,
+                         int n_keep, float *q_prime, int32_t *sel_idx, hipStream_t s);
 
 hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k, int n_seqs,
                          const int32_t *cu_tokens, const int32_t *page_table, int max_pages, float *kprime_dbg,
@@ -215,6 +215,12 @@ hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *
 hipError_t launch_append_tiered(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
                                 int n_seqs, const int32_t *cu_tokens, const int32_t *page_table, int max_pages,
                                 hipStream_t s);
+hipError_t launch_append_vrot(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                              const uint16_t *r_v, float clip, int n_seqs, const int32_t *cu_tokens,
+                              const int32_t *page_table, int max_pages, float *kprime_dbg, float *vprime_dbg,
+                              hipStream_t s);
+// inverse value rotation of decode outputs (dqk_vrot.hip)
+hipError_t launch_value_unrotate(float *out, const float *r_inv, int batch, int hq, int hkv, hipStream_t s);
 hipError_t launch_pack_tail(const dqk_cache &c, const dqk_tiers &t, const uint16_t *t_k, int batch,
                             const int32_t *lens_before, const int32_t *page_table, int max_pages, hipStream_t s);
 // BF16 tiers (dqk_tiers.hip)

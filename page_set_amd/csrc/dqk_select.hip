@@ -5,7 +5,10 @@
 // One workgroup of 256 lanes per (KV head g, sequence b); lane (half, j)
 // owns output channel j of every other query head.  Each q'_{h,j} is an fp32
 // fma chain over ascending input channel (the heads of the group run as
-// independent chains for ILP; each chain's order is unchanged).  S_j accumulates q'^2 over ascending head by fma.
+// independent chains for ILP; each chain's order is unchanged).  S_j accumulates e^2 over ascending head by fma,
+// e = q'_{h,j} or, with per-channel selection scales w (§3.3 diagonal
+// refinement, App. C.2: selection in the base coordinates q A_0 = q' D^-1,
+// w_j = 1 / delta_j), e = fp32(q'_{h,j} w_j); q' itself is left unscaled.
 // Channel j is kept iff fewer than n_keep channels beat it (larger S, or
 // equal S at a lower index); kept channels are written in ascending order.
 // Built with -ffp-contract=off: only the written fmas fuse.
@@ -37,13 +40,14 @@ __device__ __forceinline__ void stage_inputs(const uint16_t *__restrict__ q, con
 
 // Pooled energy of channel j (fma chain over ascending head), then the rank
 // test and the ascending write of the kept channels.
-__device__ __forceinline__ void select_tail(const float *qpl, int grp, int n_keep, float *s_lds,
-                                            unsigned long long *mask0, int32_t *__restrict__ dst) {
+__device__ __forceinline__ void select_tail(const float *qpl, int grp, int n_keep, const float *__restrict__ wsel,
+                                            float *s_lds, unsigned long long *mask0, int32_t *__restrict__ dst) {
     const int tid = threadIdx.x, j = tid & (D - 1);
     if (tid < D) {
+        const float w = wsel ? wsel[j] : 1.0f;  // x * 1 is x exactly
         float S = 0.0f;
         for (int h = 0; h < grp; ++h) {
-            const float v = qpl[h * D + j];
+            const float v = __fmul_rn(qpl[h * D + j], w);
             S = __builtin_fmaf(v, v, S);
         }
         s_lds[j] = S;
@@ -81,7 +85,8 @@ __device__ __forceinline__ void select_tail(const float *qpl, int grp, int n_kee
 template <int GRP>
 __global__ __launch_bounds__(THREADS) void select_kernel_g(const uint16_t *__restrict__ q,
                                                            const float *__restrict__ t_q, int hq, int hkv,
-                                                           int n_keep, float *__restrict__ q_prime,
+                                                           int n_keep, const float *__restrict__ sel_scale,
+                                                           float *__restrict__ q_prime,
                                                            int32_t *__restrict__ sel_idx) {
     constexpr int NH = GRP >= HALVES ? GRP / HALVES : 1;  // chains per lane
     __shared__ __attribute__((aligned(16))) float t_lds[D * D];
@@ -121,12 +126,15 @@ __global__ __launch_bounds__(THREADS) void select_kernel_g(const uint16_t *__res
         }
     }
     __syncthreads();
-    select_tail(qp_lds, GRP, n_keep, s_lds, &mask0, sel_idx + ((size_t)b * hkv + g) * n_keep);
+    select_tail(qp_lds, GRP, n_keep, sel_scale ? sel_scale + (size_t)g * D : nullptr, s_lds, &mask0,
+                sel_idx + ((size_t)b * hkv + g) * n_keep);
 }
 
 // Any group size up to 64 (runtime loop bounds).
 __global__ __launch_bounds__(THREADS) void select_kernel(const uint16_t *__restrict__ q, const float *__restrict__ t_q,
-                                                         int hq, int hkv, int n_keep, float *__restrict__ q_prime,
+                                                         int hq, int hkv, int n_keep,
+                                                         const float *__restrict__ sel_scale,
+                                                         float *__restrict__ q_prime,
                                                          int32_t *__restrict__ sel_idx) {
     __shared__ __attribute__((aligned(16))) float t_lds[D * D];  // T_Q of this KV head (64 KB)
     extern __shared__ __attribute__((aligned(16))) float q_lds[];  // [grp][128] q (bf16 -> fp32), then [grp][128] q'
@@ -148,19 +156,20 @@ __global__ __launch_bounds__(THREADS) void select_kernel(const uint16_t *__restr
         qpl[h * D + j] = acc;
     }
     __syncthreads();
-    select_tail(qpl, grp, n_keep, s_lds, &mask0, sel_idx + ((size_t)b * hkv + g) * n_keep);
+    select_tail(qpl, grp, n_keep, sel_scale ? sel_scale + (size_t)g * D : nullptr, s_lds, &mask0,
+                sel_idx + ((size_t)b * hkv + g) * n_keep);
 }
 
 }  // namespace
 
-hipError_t launch_select(const uint16_t *q, const float *t_q, int batch, int hq, int hkv, int n_keep, float *q_prime,
-                         int32_t *sel_idx, hipStream_t s) {
+hipError_t launch_select(const uint16_t *q, const float *t_q, const float *sel_scale, int batch, int hq, int hkv,
+                         int n_keep, float *q_prime, int32_t *sel_idx, hipStream_t s) {
     const int grp = hq / hkv;
     dim3 grid(hkv, batch);
 #define DQK_SELECT_G(G)                                                                                      \
     case G:                                                                                                   \
-        hipLaunchKernelGGL(select_kernel_g<G>, grid, dim3(THREADS), 0, s, q, t_q, hq, hkv, n_keep, q_prime,   \
-                           sel_idx);                                                                          \
+        hipLaunchKernelGGL(select_kernel_g<G>, grid, dim3(THREADS), 0, s, q, t_q, hq, hkv, n_keep, sel_scale, \
+                           q_prime, sel_idx);                                                                 \
         return hipGetLastError();
     switch (grp) {
         DQK_SELECT_G(1)
@@ -173,7 +182,8 @@ hipError_t launch_select(const uint16_t *q, const float *t_q, int batch, int hq,
     }
 #undef DQK_SELECT_G
     const size_t lds = 2 * (size_t)grp * D * sizeof(float);
-    hipLaunchKernelGGL(select_kernel, grid, dim3(THREADS), lds, s, q, t_q, hq, hkv, n_keep, q_prime, sel_idx);
+    hipLaunchKernelGGL(select_kernel, grid, dim3(THREADS), lds, s, q, t_q, hq, hkv, n_keep, sel_scale, q_prime,
+                       sel_idx);
     return hipGetLastError();
 }
 

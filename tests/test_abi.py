@@ -208,3 +208,45 @@ def test_tiered_validation():
     assert need == 4 * 32 * 4 * 132 * 4 + 4 * 32 * 7 * 132 * 4 + 16   # 7 partials of 64 BF16 tokens
     assert dec(ns=4, wsb=need - 4) == pa.DQK_ERR_WORKSPACE
     assert dec(out=MIS) == pa.DQK_ERR_ALIGN
+
+
+def test_vrot_validation():
+    L = pa.lib()
+    c = _cache()
+
+    def app(c=c, **kw):
+        a = dict(k=A, v=A, tk=A, rv=A, clip=0.92, n=2, cu=A, tot=300, pt=A, mp=4, kd=None, vd=None)
+        a.update(kw)
+        return L.dqk_quantize_append_vrot(ctypes.byref(c), a["k"], a["v"], a["tk"], a["rv"], a["clip"], a["n"],
+                                          a["cu"], a["tot"], a["pt"], a["mp"], a["kd"], a["vd"], None)
+
+    assert app(rv=None) == pa.DQK_ERR_NULL
+    assert app(c=_cache(v_codes=None)) == pa.DQK_ERR_NULL
+    for bad in (0.0, -0.5, 1.5, float("nan"), float("inf")):
+        assert app(clip=bad) == pa.DQK_ERR_SHAPE, bad
+    assert app(n=0) == pa.DQK_ERR_SHAPE
+    assert app(rv=MIS) == pa.DQK_ERR_ALIGN
+    assert app(vd=MIS) == pa.DQK_ERR_ALIGN
+
+    def sel(**kw):
+        a = dict(q=A, tq=A, sc=A, B=1, hq=32, hkv=8, nk=77, qp=A, si=A)
+        a.update(kw)
+        return L.dqk_select_channels_base(a["q"], a["tq"], a["sc"], a["B"], a["hq"], a["hkv"], a["nk"], a["qp"],
+                                          a["si"], None)
+
+    assert sel(sc=None) == pa.DQK_ERR_NULL
+    assert sel(hq=30) == pa.DQK_ERR_SHAPE
+    assert sel(nk=129) == pa.DQK_ERR_SHAPE
+    assert sel(hq=256, hkv=1) == pa.DQK_ERR_UNSUPPORTED
+    assert sel(sc=MIS) == pa.DQK_ERR_ALIGN
+
+    def unrot(**kw):
+        a = dict(out=A, r=A, B=4, hq=32, hkv=8)
+        a.update(kw)
+        return L.dqk_value_unrotate(a["out"], a["r"], a["B"], a["hq"], a["hkv"], None)
+
+    assert unrot(r=None) == pa.DQK_ERR_NULL
+    assert unrot(hq=30) == pa.DQK_ERR_SHAPE
+    assert unrot(B=0) == pa.DQK_ERR_SHAPE
+    assert unrot(hq=65 * 2, hkv=2) == pa.DQK_ERR_UNSUPPORTED
+    assert unrot(out=MIS) == pa.DQK_ERR_ALIGN
