@@ -447,6 +447,96 @@ def tiered_record(shape, seed, pa, torch, steps):
                            "packing a page from the tail"}
 
 
+def vrot_record(shape, seed, pa, torch, steps, clip=0.92):
+    """The headline workload with rotated, clipped values and selection in base
+    coordinates: the cache is built sequence by sequence with
+    dqk_quantize_append_vrot (HIP events), then a step is
+    dqk_select_channels_base + dqk_decode_attn + dqk_value_unrotate over cache
+    copies rotated as in the headline."""
+    from page_set_amd import traffic
+    prob = synth.make_problem(shape, seed, materialize_kv=False)
+    B, hq, hkv, n_keep = shape.batch, shape.hq, shape.hkv, shape.n_keep
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    rv, rinv = synth.make_value_rotation(hkv, seed)
+    wsel = synth.make_selection_scales(hkv, seed)
+    q, t_q, t_k = dev(prob.q.view(np.int16)), dev(prob.t_q), dev(prob.t_k.view(np.int16))
+    rv_d, rinv_d, w_d = dev(rv.view(np.int16)), dev(rinv), dev(wsel)
+    pt, lens = dev(prob.page_table), dev(prob.seq_lens)
+    mp = int(prob.page_table.shape[1])
+    stream = torch.cuda.current_stream()
+    cache = pa.Cache(prob.num_pages, hkv)
+    app_s, tokens = 0.0, 0
+    for b in range(B):
+        kb, vb = synth.make_kv_seq(shape, seed, b, prob.outliers)
+        L = kb.shape[0]
+        k_d, v_d = dev(kb.view(np.int16)), dev(vb.view(np.int16))
+        cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        ptb = pt[b:b + 1].clone()
+        if b == 0:  # untimed first call
+            pa.dqk_quantize_append_vrot(cache, k_d, v_d, t_k, rv_d, clip, cu, ptb, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pa.dqk_quantize_append_vrot(cache, k_d, v_d, t_k, rv_d, clip, cu, ptb, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        app_s += e0.elapsed_time(e1) * 1e-3
+        tokens += L
+        del k_d, v_d
+    caches = [cache]
+    for _ in range(_copies_for(cache.nbytes()) - 1):
+        c2 = pa.Cache(cache.num_pages, hkv)
+        for a, b2 in zip(cache.arrays(), c2.arrays()):
+            b2.copy_(a)
+        caches.append(c2)
+    qp = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, hkv, n_keep), dtype=torch.int32, device="cuda")
+    o_rot = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pa.dqk_decode_workspace_size(B, hq, hkv, mp, 0) // 4 + 4, dtype=torch.float32, device="cuda")
+    calls = [[pa.prepared("dqk_select_channels_base", q, t_q, w_d, B, hq, hkv, n_keep, qp, sel, stream),
+              pa.prepared("dqk_decode_attn", c, qp, sel, n_keep, B, hq, pt, mp, lens, float(prob.sm_scale), 0, ws,
+                          ws.numel() * 4, o_rot, None, stream),
+              pa.prepared("dqk_value_unrotate", o_rot, rinv_d, B, hq, hkv, out, stream)] for c in caches]
+    nc = len(caches)
+    for i in range(100):
+        for f in calls[i % nc]:
+            f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for f in calls[i % nc]:
+            f()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    ne = min(steps, 30)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(ne)]
+    for i in range(ne):
+        evs[i][0].record(stream)
+        for j, f in enumerate(calls[i % nc]):
+            f()
+            evs[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    us = [float(np.mean([e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs])) for j in range(3)]
+    sel_h = sel.cpu().numpy()
+    cache_bytes = traffic.decode_cache_bytes(prob.seq_lens, sel_h)
+    fixed = traffic.decode_fixed_bytes(B, hq, hkv, n_keep, mp)
+    unrot_bytes = 2 * B * hq * 128 * 4 + hkv * 128 * 128 * 4
+    step_bytes = cache_bytes + fixed["decode"] + fixed["select"] + hkv * 128 * 4 + unrot_bytes
+    app = append_roofline(app_s, tokens, prob.num_pages, hkv)
+    app_flops = 4.0 * tokens * hkv * 128 * 128  # k T_K and v R_V
+    app["mfma_tflops"] = round(app_flops / app_s / 1e12, 2)
+    app["mfma_frac"] = round(app["mfma_tflops"] / 2500.0, 4)
+    app["workload"] = f"rotated-value prefill of {shape.seq_lens[0]} tokens x {hkv} KV heads per call, {B} calls"
+    return {"workload": shape.name + "-vrot", "clip": clip,
+            "entries": "dqk_select_channels_base + dqk_decode_attn + dqk_value_unrotate",
+            "t_step_us": round(t_step * 1e6, 2), "tokens_per_s": round(B / t_step, 1),
+            "select_us": round(us[0], 2), "decode_call_us": round(us[1], 2), "unrotate_us": round(us[2], 2),
+            "algorithmic_bytes_per_step": int(step_bytes),
+            "frac_step": round(step_bytes / t_step / 1e9 / PEAK_HBM_GBS, 4), "cache_copies": nc,
+            "append": app}
+
+
 def _summary(name, w, r, n_keep):
     B = w.shape.batch
     rec = {"workload": name, "batch": B, "context": (max(w.shape.seq_lens) if len(set(w.shape.seq_lens)) == 1
@@ -619,6 +709,10 @@ def main():
         configs["3_tiered"] = tiered_record(shape, args.seed, pa, torch, sub)
         log(f"[bench] config 3 tiered: {configs['3_tiered']['t_step_us']} us/step, append token "
             f"{configs['3_tiered']['append_token_us']} us")
+        torch.cuda.empty_cache()
+        configs["3_vrot"] = vrot_record(shape, args.seed, pa, torch, sub)
+        log(f"[bench] config 3 rotated values: {configs['3_vrot']['t_step_us']} us/step (unrotate "
+            f"{configs['3_vrot']['unrotate_us']} us), append {configs['3_vrot']['append']['seconds'] * 1e6:.0f} us")
         rec["configs"] = configs
 
     if not args.no_cpu_baseline:

@@ -346,16 +346,18 @@ int dqk_select_channels_base(const void *q_bf16, const float *t_q, const float *
                              hipStream_t stream);
 
 /*
- * Inverse value rotation of decode outputs, in place: for each sequence b and
- * query head h (KV head g = h / (hq / hkv)), out[b][h][c] = sum_j
- * out[b][h][j] r_v_inv[g][j][c], an fp32 fma chain over ascending j.
- *   out       fp32 [batch][hq][128], the output of a decode entry point.
+ * Inverse value rotation of decode outputs: for each sequence b and query
+ * head h (KV head g = h / (hq / hkv)), out[b][h][c] = sum_j o_rot[b][h][j]
+ * r_v_inv[g][j][c], an fp32 fma chain over ascending j.
+ *   o_rot     fp32 [batch][hq][128], the output of a decode entry point.
  *   r_v_inv   fp32 [hkv][128][128] inverse of the stored R_V, [j][c].
- * Requires hq % hkv == 0 and hq / hkv <= 64 (DQK_ERR_SHAPE /
- * DQK_ERR_UNSUPPORTED).  One kernel, stream-ordered after the decode.
+ *   out       fp32 [batch][hq][128]; must not overlap o_rot
+ *             (DQK_ERR_UNSUPPORTED if it does).
+ * Requires hq % hkv == 0 (DQK_ERR_SHAPE) and hq / hkv <= 64
+ * (DQK_ERR_UNSUPPORTED).  One kernel, stream-ordered after the decode.
  */
-int dqk_value_unrotate(float *out, const float *r_v_inv, int32_t batch, int32_t hq, int32_t hkv,
-                       hipStream_t stream);
+int dqk_value_unrotate(const float *o_rot, const float *r_v_inv, int32_t batch, int32_t hq, int32_t hkv,
+                       float *out, hipStream_t stream);
 
 /*
  * dqk_stream_read -- measurement helper, not part of the attention path: a

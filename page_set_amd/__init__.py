@@ -96,7 +96,7 @@ def lib():
         L.dqk_quantize_append_vrot.restype = ctypes.c_int
         L.dqk_select_channels_base.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P]
         L.dqk_select_channels_base.restype = ctypes.c_int
-        L.dqk_value_unrotate.argtypes = [P, P, i32, i32, i32, P]
+        L.dqk_value_unrotate.argtypes = [P, P, i32, i32, i32, P, P]
         L.dqk_value_unrotate.restype = ctypes.c_int
         L.dqk_stream_read.argtypes = [P, sz, P, P]
         L.dqk_stream_read.restype = ctypes.c_int
@@ -266,10 +266,13 @@ def dqk_select_channels_base(q, t_q, sel_scale, hkv: int, n_keep: int, q_prime=N
     return q_prime, sel_idx
 
 
-def dqk_value_unrotate(out, r_v_inv, hkv: int, stream=None):
-    """out <- out R_V^-1 per query head, in place; returns out."""
-    B, hq = int(out.shape[0]), int(out.shape[1])
-    rc = lib().dqk_value_unrotate(_ptr(out), _ptr(r_v_inv), B, hq, hkv, _stream(stream))
+def dqk_value_unrotate(o_rot, r_v_inv, hkv: int, out=None, stream=None):
+    """out = o_rot R_V^-1 per query head (out must not overlap o_rot); returns out."""
+    import torch
+    B, hq = int(o_rot.shape[0]), int(o_rot.shape[1])
+    if out is None:
+        out = torch.empty_like(o_rot)
+    rc = lib().dqk_value_unrotate(_ptr(o_rot), _ptr(r_v_inv), B, hq, hkv, _ptr(out), _stream(stream))
     _check(rc, "dqk_value_unrotate")
     return out
 

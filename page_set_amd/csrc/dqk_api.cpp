@@ -159,13 +159,16 @@ int dqk_select_channels_base(const void *q_bf16, const float *t_q, const float *
                                          n_keep, q_prime, sel_idx, stream));
 }
 
-int dqk_value_unrotate(float *out, const float *r_v_inv, int32_t batch, int32_t hq, int32_t hkv,
-                       hipStream_t stream) {
-    if (!out || !r_v_inv) return DQK_ERR_NULL;
+int dqk_value_unrotate(const float *o_rot, const float *r_v_inv, int32_t batch, int32_t hq, int32_t hkv,
+                       float *out, hipStream_t stream) {
+    if (!o_rot || !r_v_inv || !out) return DQK_ERR_NULL;
     if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0) return DQK_ERR_SHAPE;
-    if (hq / hkv > 64 || batch > 65535) return DQK_ERR_UNSUPPORTED;
-    if (!aligned16(out) || !aligned16(r_v_inv)) return DQK_ERR_ALIGN;
-    return hip_status(dqk::launch_value_unrotate(out, r_v_inv, batch, hq, hkv, stream));
+    if (hq / hkv > 64 || batch > 65535 || hkv > 65535) return DQK_ERR_UNSUPPORTED;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(o_rot), o = reinterpret_cast<uintptr_t>(out);
+    const uintptr_t n = (uintptr_t)batch * hq * DQK_HEAD_DIM * sizeof(float);
+    if (a < o + n && o < a + n) return DQK_ERR_UNSUPPORTED;  // the rows are read by several workgroups
+    if (!aligned16(o_rot) || !aligned16(out) || !aligned16(r_v_inv)) return DQK_ERR_ALIGN;
+    return hip_status(dqk::launch_value_unrotate(o_rot, r_v_inv, batch, hq, hkv, out, stream));
 }
 
 size_t dqk_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t max_pages, int32_t num_splits) {

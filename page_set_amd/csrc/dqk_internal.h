@@ -220,7 +220,8 @@ hipError_t launch_append_vrot(const dqk_cache &c, const uint16_t *k, const uint1
                               const int32_t *page_table, int max_pages, float *kprime_dbg, float *vprime_dbg,
                               hipStream_t s);
 // inverse value rotation of decode outputs (dqk_vrot.hip)
-hipError_t launch_value_unrotate(float *out, const float *r_inv, int batch, int hq, int hkv, hipStream_t s);
+hipError_t launch_value_unrotate(const float *o_rot, const float *r_inv, int batch, int hq, int hkv, float *out,
+                                 hipStream_t s);
 hipError_t launch_pack_tail(const dqk_cache &c, const dqk_tiers &t, const uint16_t *t_k, int batch,
                             const int32_t *lens_before, const int32_t *page_table, int max_pages, hipStream_t s);
 // BF16 tiers (dqk_tiers.hip)

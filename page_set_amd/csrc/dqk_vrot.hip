@@ -7,11 +7,12 @@
 // so the output is o = o' R_V^-1: one 128 x 128 product per query head, with
 // R_V^-1 shared by the query heads of a KV head.
 //
-// One workgroup of 256 lanes per (KV head g, sequence b): R_V^-1[g] (64 KB)
-// and the group's rows of o' are staged in LDS (every load of the matrix is
-// issued before any is stored), then lane (half, c) computes output channel c
-// of every other query head as an fp32 fma chain over ascending j.  The rows
-// are read completely before any is written, so the product runs in place.
+// One workgroup of 128 lanes per (KV head g, sequence b, quarter of the
+// output channels): the quarter's 32 columns of R_V^-1[g] (16 KB) and the
+// group's rows of o' are staged in LDS (every load of the matrix issued
+// before any is stored), then lane (r, c) computes output channel c of query
+// heads r, r + 4, ... as an fp32 fma chain over ascending j.  Every
+// workgroup reads whole rows of o', so the output must not overlap them.
 // Built with -ffp-contract=off: only the written fmas fuse.
 #include "dqk_internal.h"
 
@@ -19,41 +20,47 @@ namespace dqk {
 
 namespace {
 
-constexpr int THREADS = 256;
-constexpr int HALVES = THREADS / D;
+constexpr int THREADS = 128;
+constexpr int QCOLS = 32;               // output channels per workgroup
+constexpr int ROWS = THREADS / QCOLS;   // query heads computed side by side
 
-__global__ __launch_bounds__(THREADS) void value_unrotate_kernel(float *__restrict__ out,
-                                                                 const float *__restrict__ r_inv, int hq, int hkv) {
-    __shared__ __attribute__((aligned(16))) float r_lds[D * D];
-    extern __shared__ __attribute__((aligned(16))) float o_lds[];  // [grp][128]
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+__global__ __launch_bounds__(THREADS) void value_unrotate_kernel(const float *__restrict__ o_rot,
+                                                                 const float *__restrict__ r_inv, int hq, int hkv,
+                                                                 float *__restrict__ out) {
+    __shared__ __attribute__((aligned(16))) float r_lds[D * QCOLS];  // [j][c]
+    extern __shared__ __attribute__((aligned(16))) float o_lds[];    // [grp][128]
+    const int g = blockIdx.x, b = blockIdx.y, q0 = blockIdx.z * QCOLS, tid = threadIdx.x;
     const int grp = hq / hkv;
-    const float4 *src = reinterpret_cast<const float4 *>(r_inv + (size_t)g * D * D);
-    float4 *dst = reinterpret_cast<float4 *>(r_lds);
-    constexpr int PER = D * D / 4 / THREADS;  // 16 float4 per lane
+    constexpr int PER = D * QCOLS / 4 / THREADS;  // 8 float4 per lane
+    const float *src = r_inv + (size_t)g * D * D + q0;
     float4 stage[PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) stage[k] = src[tid + k * THREADS];
-    float *rows = out + ((size_t)b * hq + (size_t)g * grp) * D;
+    for (int k = 0; k < PER; ++k) {
+        const int idx = tid + k * THREADS, j = idx / (QCOLS / 4), c4 = idx % (QCOLS / 4);
+        stage[k] = *reinterpret_cast<const float4 *>(src + (size_t)j * D + 4 * c4);
+    }
+    const size_t row0 = (size_t)b * hq + (size_t)g * grp;
+    const float *rows = o_rot + row0 * D;
     for (int i = tid; i < grp * D; i += THREADS) o_lds[i] = rows[i];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) dst[tid + k * THREADS] = stage[k];
+    for (int k = 0; k < PER; ++k) reinterpret_cast<float4 *>(r_lds)[tid + k * THREADS] = stage[k];
     __syncthreads();
-    const int c = tid & (D - 1), half = tid >> 7;
-    for (int h = half; h < grp; h += HALVES) {
+    const int c = tid % QCOLS, r = tid / QCOLS;
+    for (int h = r; h < grp; h += ROWS) {
         float acc = 0.0f;
 #pragma unroll 8
-        for (int j = 0; j < D; ++j) acc = __builtin_fmaf(o_lds[h * D + j], r_lds[j * D + c], acc);
-        rows[(size_t)h * D + c] = acc;
+        for (int j = 0; j < D; ++j) acc = __builtin_fmaf(o_lds[h * D + j], r_lds[j * QCOLS + c], acc);
+        out[(row0 + h) * D + q0 + c] = acc;
     }
 }
 
 }  // namespace
 
-hipError_t launch_value_unrotate(float *out, const float *r_inv, int batch, int hq, int hkv, hipStream_t s) {
+hipError_t launch_value_unrotate(const float *o_rot, const float *r_inv, int batch, int hq, int hkv, float *out,
+                                 hipStream_t s) {
     const int grp = hq / hkv;
-    hipLaunchKernelGGL(value_unrotate_kernel, dim3(hkv, batch), dim3(THREADS), (size_t)grp * D * sizeof(float), s,
-                       out, r_inv, hq, hkv);
+    hipLaunchKernelGGL(value_unrotate_kernel, dim3(hkv, batch, D / QCOLS), dim3(THREADS),
+                       (size_t)grp * D * sizeof(float), s, o_rot, r_inv, hq, hkv, out);
     return hipGetLastError();
 }
 

@@ -241,12 +241,15 @@ def test_vrot_validation():
     assert sel(sc=MIS) == pa.DQK_ERR_ALIGN
 
     def unrot(**kw):
-        a = dict(out=A, r=A, B=4, hq=32, hkv=8)
+        a = dict(o=A, r=A, B=4, hq=32, hkv=8, out=ctypes.c_void_p(1 << 20))
         a.update(kw)
-        return L.dqk_value_unrotate(a["out"], a["r"], a["B"], a["hq"], a["hkv"], None)
+        return L.dqk_value_unrotate(a["o"], a["r"], a["B"], a["hq"], a["hkv"], a["out"], None)
 
     assert unrot(r=None) == pa.DQK_ERR_NULL
+    assert unrot(out=None) == pa.DQK_ERR_NULL
+    assert unrot(out=A) == pa.DQK_ERR_UNSUPPORTED                             # in place
+    assert unrot(out=ctypes.c_void_p(4096 + 4 * 32 * 512 - 16)) == pa.DQK_ERR_UNSUPPORTED  # overlapping
     assert unrot(hq=30) == pa.DQK_ERR_SHAPE
     assert unrot(B=0) == pa.DQK_ERR_SHAPE
     assert unrot(hq=65 * 2, hkv=2) == pa.DQK_ERR_UNSUPPORTED
-    assert unrot(out=MIS) == pa.DQK_ERR_ALIGN
+    assert unrot(out=ctypes.c_void_p((1 << 20) + 8)) == pa.DQK_ERR_ALIGN

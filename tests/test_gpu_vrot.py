@@ -154,9 +154,10 @@ def test_value_unrotate_within_the_summation_bound(B, hq, hkv):
     o = rng.standard_normal((B, hq, 128)).astype(np.float32)
     o[0, 0] *= 1e-3
     t = gu.dev(o)
-    pa.dqk_value_unrotate(t, gu.dev(rinv), hkv)
+    res = pa.dqk_value_unrotate(t, gu.dev(rinv), hkv)
     torch.cuda.synchronize()
-    got = gu.host(t).astype(np.float64)
+    np.testing.assert_array_equal(gu.host(t), o)  # the input is left as it was
+    got = gu.host(res).astype(np.float64)
     want = oracle.value_unrotate(o.astype(np.float64), rinv, hkv)
     grp = hq // hkv
     for h in range(hq):
@@ -186,8 +187,8 @@ def test_rotated_path_end_to_end(name, shape):
     cache = pa.Cache(prob.num_pages, shape.hkv)
     pa.dqk_quantize_append_vrot(cache, d["k"], d["v"], d["t_k"], gu.dev(rv), CLIP, d["cu"], d["page_table"])
     qp, sel = pa.dqk_select_channels_base(d["q"], d["t_q"], gu.dev(w), shape.hkv, shape.n_keep)
-    out, lse = pa.dqk_decode_attn(cache, qp, sel, d["page_table"], d["seq_lens"], prob.sm_scale)
-    pa.dqk_value_unrotate(out, gu.dev(rinv), shape.hkv)
+    o_rot, lse = pa.dqk_decode_attn(cache, qp, sel, d["page_table"], d["seq_lens"], prob.sm_scale)
+    out = pa.dqk_value_unrotate(o_rot, gu.dev(rinv), shape.hkv)
     torch.cuda.synchronize()
     host_cache = gu.cache_to_host(cache)
     qp_ref, sel_ref = oracle.select_channels_base(prob.q, prob.t_q, w, shape.hkv, shape.n_keep)
