@@ -167,3 +167,82 @@ def test_bf16_baseline_32k():
     _say(f"  bf16 32k: max row rel err {rel.max():.3e}")
     assert (rel <= gu.TOL).all()
     np.testing.assert_allclose(gu.host(lse), ref_lse, rtol=1e-5, atol=1e-5)
+
+
+def test_rotated_values_at_full_size():
+    """The rotated-value path at the benchmark's shape (batch 4 x 131072
+    tokens, GQA 32/8, n_keep 77, clip 0.92), in the launch configuration
+    bench.py times: the cache built by dqk_quantize_append_vrot sequence by
+    sequence (v' read back for sequence 0), then base selection, decode and
+    the inverse rotation.  Stage by stage on 16 sampled pages of sequence 0
+    (v' within the recursive-summation bound, value bytes equal the oracle's
+    pack of the GPU's own v'); selection bit-exact; 8 sampled (sequence, KV
+    head) units recomputed by the oracle from the same cache bytes, rows
+    within 2e-3."""
+    clip = 0.92
+    shape = synth.config_shape(3)
+    _say("rotated values at full size", shape.name)
+    prob = synth.make_problem(shape, seed=0, materialize_kv=False)
+    rv, rinv = synth.make_value_rotation(shape.hkv, 0)
+    w = synth.make_selection_scales(shape.hkv, 0)
+    d = gu.upload(prob)
+    L0 = shape.seq_lens[0]
+    vdbg = torch.full((L0, shape.hkv, 128), float("nan"), dtype=torch.float32, device="cuda")
+    cache = pa.Cache(prob.num_pages, shape.hkv)
+    rv_d = gu.dev(rv)
+    for b in range(shape.batch):
+        kb, vb = synth.make_kv_seq(shape, prob.seed, b, prob.outliers)
+        cu = torch.tensor([0, kb.shape[0]], dtype=torch.int32, device="cuda")
+        pa.dqk_quantize_append_vrot(cache, gu.dev(kb), gu.dev(vb), d["t_k"], rv_d, clip, cu,
+                                    d["page_table"][b:b + 1].clone(), vprime_dbg=vdbg if b == 0 else None)
+        torch.cuda.synchronize()
+    qp, sel = pa.dqk_select_channels_base(d["q"], d["t_q"], gu.dev(w), shape.hkv, shape.n_keep)
+    o_rot, _ = pa.dqk_decode_attn(cache, qp, sel, d["page_table"], d["seq_lens"], prob.sm_scale)
+    out = pa.dqk_value_unrotate(o_rot, gu.dev(rinv), shape.hkv)
+    torch.cuda.synchronize()
+    qp_ref, sel_ref = oracle.select_channels_base(prob.q, prob.t_q, w, shape.hkv, shape.n_keep)
+    np.testing.assert_array_equal(gu.host(sel), sel_ref)
+    np.testing.assert_array_equal(gu.host(qp).view(np.uint32), qp_ref.view(np.uint32))
+    pm = cache.page_major()
+    # stage by stage on sampled pages of sequence 0
+    kb, vb = synth.make_kv_seq(shape, prob.seed, 0, prob.outliers)
+    gam = 128 * 2.0 ** -24 / (1 - 128 * 2.0 ** -24)
+    r64 = np.abs(synth.bf16_bits_to_f32(rv).astype(np.float64))
+    for pi in np.random.default_rng(12).choice(L0 // 128, size=16, replace=False):
+        p = int(prob.page_table[0, pi])
+        t0 = int(pi) * 128
+        vseg = np.ascontiguousarray(vb[t0:t0 + 128])
+        vp_gpu = gu.host(vdbg[t0:t0 + 128])
+        vp_ref = oracle.value_transform(vseg, rv)
+        absdot = np.einsum("tgi,gij->tgj", np.abs(synth.bf16_bits_to_f32(vseg).astype(np.float64)), r64)
+        err = np.abs(vp_gpu.astype(np.float64) - vp_ref.astype(np.float64))
+        assert (err <= gam * absdot + np.spacing(np.abs(vp_ref))).all(), pi
+        kp = oracle.key_transform(np.ascontiguousarray(kb[t0:t0 + 128]), prob.t_k)
+        want = oracle.pack_cache_vrot(kp, vp_gpu, clip, np.array([0, 128], np.int32), np.zeros((1, 1), np.int32), 1)
+        want_pm = want.page_major()
+        for g in range(shape.hkv):
+            got = _unit_cache(pm, [p], g).page_major()
+            for nm, i in (("v_codes", 3), ("v_meta", 4)):
+                np.testing.assert_array_equal(got[i][0, 0], want_pm[i][0, g], err_msg=f"{nm} page {pi} head {g}")
+    # sampled units end to end
+    grp = shape.hq // shape.hkv
+    out_h = gu.host(out)
+    rng = np.random.default_rng(13)
+    units = [(int(b), int(g)) for b, g in zip(rng.integers(0, shape.batch, 8), rng.integers(0, shape.hkv, 8))]
+
+    def check(unit):
+        b, g = unit
+        L = int(prob.seq_lens[b])
+        npg = (L + 127) // 128
+        sub = _unit_cache(pm, prob.page_table[b, :npg], g)
+        heads = slice(g * grp, (g + 1) * grp)
+        o_ref, _ = oracle.decode_attn(sub, np.ascontiguousarray(qp_ref[b:b + 1, heads]),
+                                      np.ascontiguousarray(sel_ref[b:b + 1, g:g + 1]),
+                                      np.arange(npg, dtype=np.int32)[None], np.array([L], np.int32), prob.sm_scale)
+        ref = oracle.value_unrotate(o_ref, np.ascontiguousarray(rinv[g:g + 1]), 1)
+        return float(gu.row_rel_err(out_h[b, heads], ref[0]).max())
+
+    with cf.ThreadPoolExecutor(max_workers=THREADS) as ex:
+        errs = list(ex.map(check, units))
+    _say(f"  16 sampled pages stagewise; {len(units)} sampled units: worst row rel err {max(errs):.3e}")
+    assert max(errs) <= gu.TOL
