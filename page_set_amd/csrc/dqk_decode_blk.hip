@@ -4,7 +4,7 @@
 // bf16 copy, channel-major INT2 key rows and token-major values with separate
 // metadata (§3.3); one softmax over the whole context (§3.4).
 //
-// Work decomposition.  A workgroup (8 waves, one per CU) owns one split (a run
+// Work decomposition.  A workgroup (12 waves, one per CU) owns one split (a run
 // of 8-page blocks) of one (sequence, KV head) and walks it in steps of four
 // pages.  Loads go straight from HBM to LDS: the selected key rows of a whole
 // 8-page block (one 256-byte run per channel), its key metadata and channel 0
@@ -13,9 +13,10 @@
 // issuing a fixed share.  Waves 0-3 score: at step u wave w takes page w of
 // half u (all 128 tokens, four heads), keeps the online softmax of that page
 // stream and leaves the fp16 probabilities and the per-head rescale factor in
-// LDS.  Waves 4-7 multiply: wave 4 + w takes the values of page w of half
-// u - 1.  Each SIMD thus runs one VALU-heavy and one MFMA-heavy wave.  The
-// four page streams are combined in LDS at the end of the split.
+// LDS.  Waves 4-11 multiply: waves 4 + w and 8 + w take the values of page w
+// of half u - 1, tokens 0-63 and 64-127.  Each SIMD thus runs one scoring and
+// two multiplying waves.  The four page streams (two token halves each) are
+// combined in LDS at the end of the split.
 //
 // Scores (v_mfma_f32_16x16x32_f16).  The 32-deep k dimension is (token group
 // tg, 16 selected channels): A row i of tile m holds token 64 tg + 4 i + m,
@@ -1022,14 +1023,14 @@ static int ks_of(int n_keep) {
 
 int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep) {
     (void)n_keep;
-    // one 8-wave workgroup per CU (LDS-bound): enough splits to give each of the
-    // 256 CUs one, at least 4 blocks (32 pages) per split; long contexts split so
-    // that no split exceeds 16 blocks (ragged batches stay balanced)
+    // one workgroup per CU (LDS-bound): enough splits to give each of the 256
+    // CUs one (down to one 8-page block per split: a short batch is latency-
+    // bound, and more workgroups in flight beat a longer pipeline in each);
+    // long contexts split so that no split exceeds 16 blocks (ragged batches
+    // stay balanced)
     const int units = batch * hkv;
     const int nblk = (max_pages + KBLK - 1) / KBLK;
     int s = (256 + units - 1) / units;
-    const int cap = (nblk + 3) / 4;
-    if (s > cap) s = cap;
     const int need = (nblk + 15) / 16;
     if (s < need) s = need;
     if (s > nblk) s = nblk;
