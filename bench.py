@@ -569,6 +569,9 @@ def main():
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a --calib-copy run "
                          "into the per-launch HBM traffic record and exit")
+    ap.add_argument("--only", choices=["tiered", "vrot"],
+                    help="run only this variant of the config's workload (protected BF16 tiers, or rotated "
+                         "values with base selection) and print its record (for profiling)")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
@@ -584,6 +587,10 @@ def main():
 
     shape = synth.config_shape(args.config, args.seed, args.sparsity)
     n_keep = shape.n_keep
+    if args.only:
+        fn = tiered_record if args.only == "tiered" else vrot_record
+        print(json.dumps(fn(shape, args.seed, pa, torch, args.steps)), flush=True)
+        return
     log(f"[bench] workload {shape.name}: B={shape.batch} Hq/Hkv={shape.hq}/{shape.hkv} ctx={max(shape.seq_lens)} "
         f"n_keep={n_keep}")
     t0 = time.time()
