@@ -662,11 +662,12 @@ def main():
         configs["3_sparsity_sweep"] = sweep
         del w
         torch.cuda.empty_cache()
-        # group sizes other than 4 run the VALU decode (config 0 is MHA)
+        # group sizes other than 4 (config 0 is MHA): the same MFMA decode over sets of four query heads
         s0 = synth.config_shape(0, args.seed)
         w0 = Int2Workload(s0, args.seed, pa, torch)
         configs["0"] = _summary(s0.name, w0, w0.time_steps(s0.n_keep, sub, 100, fused=True), s0.n_keep)
-        configs["0"]["kernel"] = "decode_int2_kernel (VALU, any group size) + merge, after select_kernel_g<1>"
+        configs["0"]["kernel"] = ("decode_blk_kernel (one set of four query heads per KV head, three of them "
+                                  "padding) + merge, after select_kernel_g<1>")
         log(f"[bench] config 0: {configs['0']['t_step_us']} us/step")
         del w0
         gen = {}
@@ -674,10 +675,10 @@ def main():
             sg = synth.Shape(4, hq, 8, [32768] * 4, 77, name=f"gqa{hq}x8-32k-b4")
             wg = Int2Workload(sg, args.seed, pa, torch)
             gen[f"g{hq // 8}"] = _summary(sg.name, wg, wg.time_steps(77, sub, 100, fused=True), 77)
-            gen[f"g{hq // 8}"]["kernel"] = "decode_int2_kernel (VALU) + merge, after select_kernel_g"
+            gen[f"g{hq // 8}"]["kernel"] = "decode_blk_kernel over sets of four query heads + merge, after select_kernel_g"
             log(f"[bench] group {hq // 8}: {gen[f'g{hq // 8}']['t_step_us']} us/step")
             del wg
-        configs["generic_groups"] = gen
+        configs["other_groups"] = gen
         torch.cuda.empty_cache()
         s1 = synth.config_shape(1, args.seed)
         w1 = Int2Workload(s1, args.seed, pa, torch)

@@ -154,8 +154,11 @@ size_t dqk_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t
  *   workspace   device scratch of at least dqk_decode_workspace_size() bytes.
  *   out         fp32 [batch][hq][128].
  *   lse         fp32 [batch][hq] or NULL: log-sum-exp of the logits.
- * Arithmetic of the group-4 MFMA decode (hq = 4 hkv, n_keep <= 128; other
- * groups run a VALU decode with fp32 dequantisation, fma(code, scale, zero)):
+ * Requires hq / hkv <= 16 (DQK_ERR_UNSUPPORTED).  Every group size runs the
+ * same MFMA decode: the query heads of a KV head are taken in sets of four
+ * (ceil(g / 4) workgroups per KV head and split, each reading the KV head's
+ * pages; a set of fewer than four is padded with zero queries).
+ * Arithmetic of the MFMA decode:
  *   - logits: fp32 sums; the query-side operand C q'_j s_j (C = sm_scale
  *     log2 e, s_j the key scale) enters as two binary16 limbs (>= 21
  *     significant bits) scaled per page by a power of two that brings the

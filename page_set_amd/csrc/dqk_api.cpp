@@ -43,8 +43,7 @@ int check_tiers(const dqk_tiers *t, const dqk_cache *c) {
 // n_keep = 0: the largest count any n_keep can resolve to (workspace sizing)
 int resolve_splits(int batch, int hq, int hkv, int max_pages, int num_splits, int n_keep) {
     if (num_splits > 0) return num_splits;
-    if (dqk::use_mfma_decode(hq, hkv, n_keep)) return dqk::decode_splits_mfma(batch, hkv, max_pages, n_keep);
-    return dqk::decode_splits_generic(batch, hkv, max_pages);
+    return dqk::decode_splits_mfma(batch, hkv * dqk::mfma_head_sets(hq, hkv), max_pages, n_keep);
 }
 
 // ---- scratch of the entry point that allocates nothing: split partials in a
@@ -173,10 +172,10 @@ int dqk_value_unrotate(const float *o_rot, const float *r_v_inv, int32_t batch, 
 
 size_t dqk_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t max_pages, int32_t num_splits) {
     if (batch < 1 || hq < 1 || hkv < 1 || max_pages < 1 || num_splits < 0) return 0;
-    // enough for either decode entry point
+    // enough for either decode entry point (INT2 or the BF16 baseline)
     int s = resolve_splits(batch, hq, hkv, max_pages, num_splits, 0);
-    const int s_gen = num_splits > 0 ? num_splits : dqk::decode_splits_generic(batch, hkv, max_pages);
-    if (s_gen > s) s = s_gen;
+    const int s_bf = num_splits > 0 ? num_splits : dqk::decode_splits_bf16(batch, hkv, max_pages);
+    if (s_bf > s) s = s_bf;
     return (size_t)batch * hq * s * dqk::PART_FLOATS * sizeof(float);
 }
 
@@ -191,9 +190,9 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
     if (batch < 1 || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM || max_pages < 1 ||
         num_splits < 0 || num_splits > max_pages)
         return DQK_ERR_SHAPE;
-    const bool mfma = dqk::use_mfma_decode(hq, hkv, n_keep);
-    if (!mfma && hq / hkv > dqk::GENERIC_MAX_GROUP) return DQK_ERR_UNSUPPORTED;
-    if ((int64_t)batch * hkv > 65535 || batch * hq > 2147483647 / 2) return DQK_ERR_UNSUPPORTED;
+    if (!dqk::use_mfma_decode(hq, hkv, n_keep)) return DQK_ERR_UNSUPPORTED;  // more than MAX_GROUP heads per KV head
+    if ((int64_t)batch * hkv * dqk::mfma_head_sets(hq, hkv) > 65535 || batch * hq > 2147483647 / 2)
+        return DQK_ERR_UNSUPPORTED;
     if (!aligned16(q_prime) || !aligned16(sel_idx) || !aligned16(page_table) || !aligned16(seq_lens) ||
         !aligned16(workspace) || !aligned16(out) || (lse && !aligned16(lse)))
         return DQK_ERR_ALIGN;
@@ -201,7 +200,7 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
     if (ws_bytes < (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float)) return DQK_ERR_WORKSPACE;
     dqk::DecodeArgs a{c,         q_prime,  sel_idx, n_keep, batch,  hq, hkv, page_table, max_pages, seq_lens,
                       sm_scale, splits, static_cast<float *>(workspace), out, lse};
-    hipError_t e = mfma ? dqk::launch_decode_mfma(a, stream) : dqk::launch_decode_generic(a, stream);
+    hipError_t e = dqk::launch_decode_mfma(a, stream);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(dqk::launch_merge(a.partials, batch, hq, splits, out, lse, stream));
 }
@@ -318,10 +317,7 @@ size_t tiered_ws_bytes(int batch, int hq, int splits) {
 size_t dqk_decode_tiered_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t max_pages,
                                         int32_t num_splits) {
     if (batch < 1 || hq < 1 || hkv < 1 || max_pages < 1 || num_splits < 0) return 0;
-    int s = resolve_splits(batch, hq, hkv, max_pages, num_splits, 0);
-    const int s_gen = num_splits > 0 ? num_splits : dqk::decode_splits_generic(batch, hkv, max_pages);
-    if (s_gen > s) s = s_gen;
-    return tiered_ws_bytes(batch, hq, s);
+    return tiered_ws_bytes(batch, hq, resolve_splits(batch, hq, hkv, max_pages, num_splits, 0));
 }
 
 int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const float *q_prime, const int32_t *sel_idx,
@@ -337,9 +333,9 @@ int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const flo
     if (batch < 1 || batch > tiers->batch || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM ||
         max_pages < 1 || num_splits < 0 || num_splits > max_pages)
         return DQK_ERR_SHAPE;
-    const bool mfma = dqk::use_mfma_decode(hq, hkv, n_keep);
-    if (hq / hkv > dqk::GENERIC_MAX_GROUP) return DQK_ERR_UNSUPPORTED;
-    if ((int64_t)batch * hkv > 65535 || batch * hq > 2147483647 / 2) return DQK_ERR_UNSUPPORTED;
+    if (!dqk::use_mfma_decode(hq, hkv, n_keep)) return DQK_ERR_UNSUPPORTED;  // more than MAX_GROUP heads per KV head
+    if ((int64_t)batch * hkv * dqk::mfma_head_sets(hq, hkv) > 65535 || batch * hq > 2147483647 / 2)
+        return DQK_ERR_UNSUPPORTED;
     if (!aligned16(q_prime) || !aligned16(sel_idx) || !aligned16(page_table) || !aligned16(seq_lens) ||
         !aligned16(workspace) || !aligned16(out) || (lse && !aligned16(lse)))
         return DQK_ERR_ALIGN;
@@ -355,7 +351,7 @@ int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const flo
     if (e != hipSuccess) return hip_status(e);
     dqk::DecodeArgs a{c,         q_prime,  sel_idx, n_keep, batch, hq, hkv, page_table, max_pages, int2_lens,
                       sm_scale, splits, parts,   out,    lse};
-    e = mfma ? dqk::launch_decode_mfma(a, stream) : dqk::launch_decode_generic(a, stream);
+    e = dqk::launch_decode_mfma(a, stream);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(
         dqk::launch_merge_extra(parts, batch, hq, splits, tier_parts, dqk::TIER_PARTIALS, out, lse, stream));
@@ -369,11 +365,11 @@ int dqk_decode_attn_bf16(const void *k_pages, const void *v_pages, int32_t hkv, 
     if (hkv < 1 || num_pages < 1 || batch < 1 || hq < 1 || hq % hkv != 0 || max_pages < 1 || num_splits < 0 ||
         num_splits > max_pages)
         return DQK_ERR_SHAPE;
-    if (hq / hkv > dqk::GENERIC_MAX_GROUP || (int64_t)batch * hkv > 65535) return DQK_ERR_UNSUPPORTED;
+    if (hq / hkv > dqk::MAX_GROUP || (int64_t)batch * hkv > 65535) return DQK_ERR_UNSUPPORTED;
     if (!aligned16(k_pages) || !aligned16(v_pages) || !aligned16(q_bf16) || !aligned16(page_table) ||
         !aligned16(seq_lens) || !aligned16(workspace) || !aligned16(out) || (lse && !aligned16(lse)))
         return DQK_ERR_ALIGN;
-    const int splits = num_splits > 0 ? num_splits : dqk::decode_splits_generic(batch, hkv, max_pages);
+    const int splits = num_splits > 0 ? num_splits : dqk::decode_splits_bf16(batch, hkv, max_pages);
     if (ws_bytes < (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float)) return DQK_ERR_WORKSPACE;
     dqk::DecodeBf16Args a{static_cast<const uint16_t *>(k_pages), static_cast<const uint16_t *>(v_pages), hkv,
                           static_cast<const uint16_t *>(q_bf16), batch, hq, page_table, max_pages, seq_lens,

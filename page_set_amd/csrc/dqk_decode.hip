@@ -1,19 +1,11 @@
-// Decode attention over the paged INT2 cache -- generic path (any group size
-// up to 16 query heads per KV head), the split-K log-sum-exp merge, and the
-// unpruned BF16 baseline.
+// The split-K log-sum-exp merge of the INT2 decode, the unpruned BF16
+// baseline decode and a streaming-read reference kernel.  The INT2 decode
+// itself (every group size) is the MFMA kernel of dqk_decode_blk.hip.
 //
-// Dual-QK paper: scores use only the KV head's selected channels and keep the
-// full 1/sqrt(d) normalisation (§3.2); channel 0 comes from its bf16 copy,
-// the others are dequantized from the channel-major rows (§3.3); values are
-// read for every token (§3.2); one softmax spans the whole context (§3.4),
-// realised as an online softmax per split and a log-sum-exp merge.
-//
-// Workgroup (256 lanes) per (split, sequence x KV head).  Per page: the
-// selected key rows, their metadata, channel 0 and the value page are staged
-// in LDS; lane (token, half) scores its token for half of the group's heads;
-// one wave per head updates the running max/sum; lane (channel, half)
-// accumulates its channel for half of the heads.  The group size 4 case runs
-// on the MFMA kernel in dqk_decode_mfma.hip instead.
+// Dual-QK paper: one softmax spans the whole context (§3.4), realised as an
+// online softmax per split and a log-sum-exp merge of the splits.  The BF16
+// baseline is the unpruned reference of §4.4: full-width scores on the bf16
+// keys and values in their original coordinates.
 #include "dqk_internal.h"
 
 namespace dqk {
@@ -59,153 +51,6 @@ __device__ __forceinline__ void softmax_page(float *lg, int nvalid, float *m_lds
         *a_lds = alpha;
         *l_lds = *l_lds * alpha + ps;
         *m_lds = m_new;
-    }
-}
-
-// The cache description is passed by value (kernel arguments live in constant memory).
-__global__ __launch_bounds__(256) void decode_int2_kernel(dqk_cache c, const float *__restrict__ q_prime,
-                                                          const int32_t *__restrict__ sel_idx, int n_keep, int hq,
-                                                          const int32_t *__restrict__ page_table, int max_pages,
-                                                          const int32_t *__restrict__ seq_lens, float sm_scale,
-                                                          int nsplit, float *__restrict__ partials) {
-    __shared__ float q_lds[MAXG][D];
-    __shared__ int jrow[D];                // compacted selected INT2 channels
-    __shared__ __attribute__((aligned(16))) uint8_t krows[D][ROW_BYTES];
-    __shared__ float ks_lds[D], kz_lds[D];
-    __shared__ float k0_lds[PG];
-    __shared__ __attribute__((aligned(16))) uint8_t vrows[PG][ROW_BYTES];
-    __shared__ float vs_lds[VGROUPS][PG], vz_lds[VGROUPS][PG];
-    __shared__ float lg[MAXG][PG];
-    __shared__ float m_lds[MAXG], l_lds[MAXG], a_lds[MAXG];
-    __shared__ int nrow_lds, has0_lds;
-
-    const int split = blockIdx.x;
-    const int bg = blockIdx.y;
-    const int hkv = c.num_kv_heads;
-    const int b = bg / hkv, g = bg % hkv;
-    const int grp = hq / hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int L = seq_lens[b];
-    const int npages = (L + PG - 1) / PG;
-    int p0, p1;
-    split_range(npages, nsplit, split, p0, p1);
-
-    for (int i = tid; i < grp * D; i += 256) q_lds[i / D][i % D] = q_prime[((size_t)b * hq + (size_t)g * grp) * D + i];
-    if (tid == 0) {
-        const int32_t *sel = sel_idx + ((size_t)b * hkv + g) * n_keep;
-        int nr = 0, h0 = 0;
-        for (int m = 0; m < n_keep; ++m) {
-            const int j = sel[m];
-            if (j == 0)
-                h0 = 1;
-            else
-                jrow[nr++] = j;
-        }
-        nrow_lds = nr;
-        has0_lds = h0;
-    }
-    if (tid < MAXG) {
-        m_lds[tid] = -__builtin_huge_valf();
-        l_lds[tid] = 0.0f;
-    }
-    __syncthreads();
-    const int nrow = nrow_lds, has0 = has0_lds;
-
-    const int t = tid & (PG - 1), half = tid >> 7;
-    float o[HPER];
-#pragma unroll
-    for (int k = 0; k < HPER; ++k) o[k] = 0.0f;
-
-    for (int pi = p0; pi < p1; ++pi) {
-        const int64_t p = page_table[(size_t)b * max_pages + pi];
-        const size_t pg = (size_t)p * hkv + g;
-        const int nvalid = min(PG, L - pi * PG);
-        // ---- stage the page
-        for (int r = tid; r < nrow * 2; r += 256) {
-            const int jj = r >> 1, hf = r & 1;
-            const int j = jrow[jj];
-            *reinterpret_cast<uint4 *>(&krows[jj][hf * 16]) =
-                *reinterpret_cast<const uint4 *>(c.k_codes + krow(p, g, hkv, j) * ROW_BYTES + hf * 16);
-            if (hf == 0) {
-                const uint32_t sz = *reinterpret_cast<const uint32_t *>(c.k_meta + krow(p, g, hkv, j) * 2);
-                ks_lds[jj] = h2f((uint16_t)(sz & 0xFFFFu));
-                kz_lds[jj] = h2f((uint16_t)(sz >> 16));
-            }
-        }
-        if (tid < PG) k0_lds[tid] = has0 ? bf2f(c.k_ch0[pg * PG + tid]) : 0.0f;
-        {
-            const uint4 *src = reinterpret_cast<const uint4 *>(c.v_codes + pg * PG * ROW_BYTES);
-            uint4 *dst = reinterpret_cast<uint4 *>(&vrows[0][0]);
-            dst[tid] = src[tid];  // 4096 bytes = 256 x 16
-            const uint16_t *vm = c.v_meta + pg * 2 * VGROUPS * PG;
-            for (int i = tid; i < VGROUPS * PG; i += 256) {
-                vs_lds[i / PG][i % PG] = h2f(vm[i]);
-                vz_lds[i / PG][i % PG] = h2f(vm[VGROUPS * PG + i]);
-            }
-        }
-        __syncthreads();
-        // ---- logits: lane (t, half) for heads half, half+2, ...
-        {
-            float acc[HPER];
-#pragma unroll
-            for (int k = 0; k < HPER; ++k) acc[k] = 0.0f;
-            const int byte = t >> 2, sh = 2 * (t & 3);
-            for (int jj = 0; jj < nrow; ++jj) {
-                const float code = (float)((krows[jj][byte] >> sh) & 3);
-                const float kv = __builtin_fmaf(code, ks_lds[jj], kz_lds[jj]);
-                const int j = jrow[jj];
-#pragma unroll
-                for (int k = 0; k < HPER; ++k) {
-                    const int h = half + 2 * k;
-                    if (h < grp) acc[k] = __builtin_fmaf(q_lds[h][j], kv, acc[k]);
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < HPER; ++k) {
-                const int h = half + 2 * k;
-                if (h < grp) {
-                    float x = acc[k];
-                    if (has0) x = __builtin_fmaf(q_lds[h][0], k0_lds[t], x);
-                    lg[h][t] = x * sm_scale;
-                }
-            }
-        }
-        __syncthreads();
-        for (int h = wv; h < grp; h += 4) softmax_page(lg[h], nvalid, &m_lds[h], &l_lds[h], &a_lds[h], lane);
-        __syncthreads();
-        // ---- values: lane (channel t, half)
-        {
-            const int cch = t, q = cch >> 5, byte = cch >> 2, sh = 2 * (cch & 3);
-#pragma unroll
-            for (int k = 0; k < HPER; ++k) {
-                const int h = half + 2 * k;
-                if (h < grp) o[k] *= a_lds[h];
-            }
-            for (int tt = 0; tt < nvalid; ++tt) {
-                const float code = (float)((vrows[tt][byte] >> sh) & 3);
-                const float vv = __builtin_fmaf(code, vs_lds[q][tt], vz_lds[q][tt]);
-#pragma unroll
-                for (int k = 0; k < HPER; ++k) {
-                    const int h = half + 2 * k;
-                    if (h < grp) o[k] = __builtin_fmaf(lg[h][tt], vv, o[k]);
-                }
-            }
-        }
-        __syncthreads();
-    }
-    // ---- partials
-#pragma unroll
-    for (int k = 0; k < HPER; ++k) {
-        const int h = half + 2 * k;
-        if (h < grp) {
-            float *dst = partials + (((size_t)b * hq + (size_t)g * grp + h) * nsplit + split) * PART_FLOATS;
-            dst[t] = o[k];
-            if (t == 0) {
-                dst[D] = m_lds[h];
-                dst[D + 1] = l_lds[h];
-                dst[D + 2] = l_lds[h];  // fp32 probabilities: the same sum
-            }
-        }
     }
 }
 
@@ -377,18 +222,11 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hip
     return hipGetLastError();
 }
 
-int decode_splits_generic(int batch, int hkv, int max_pages) {
+int decode_splits_bf16(int batch, int hkv, int max_pages) {
     const int units = batch * hkv;
     int s = (1024 + units - 1) / units;
     if (s > max_pages) s = max_pages;
     return s < 1 ? 1 : s;
-}
-
-hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
-    dim3 grid(a.num_splits, a.batch * a.hkv);
-    hipLaunchKernelGGL(decode_int2_kernel, grid, dim3(256), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep, a.hq,
-                       a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials);
-    return hipGetLastError();
 }
 
 hipError_t launch_decode_bf16(const DecodeBf16Args &a, hipStream_t s) {

@@ -578,7 +578,13 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
 
     const int split = blockIdx.x, bg = blockIdx.y;
     const int hkv = c.num_kv_heads;
-    const int b = bg / hkv, g = bg - b * hkv;
+    // grid.y runs over (sequence, KV head, set of up to four of its query
+    // heads): a KV head with grp query heads takes ceil(grp / 4) workgroups
+    // per split, each reading the KV head's pages for its heads h0 .. h0+nh-1
+    // (a set of fewer than four leaves the rest of the tile at q' = 0)
+    const int grp = hq / hkv, nsub = (grp + GRP - 1) / GRP;
+    const int b = bg / (hkv * nsub), gs = bg - b * (hkv * nsub), g = gs / nsub, sub = gs - g * nsub;
+    const int h0 = g * grp + sub * GRP, nh = min(GRP, grp - sub * GRP);
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     // page of the half this wave scores (waves 0-3) or multiplies (waves 4-11, token half th)
     const int w = wv < 4 ? wv : (wv - 4) & 3;
@@ -591,14 +597,14 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const int nb = B1 - B0;   // 8-page blocks of this split
     const int nst = 2 * nb;   // 4-page halves
     const int32_t *ptab = page_table + (size_t)b * max_pages;
-    float *part_base = partials + (((size_t)b * hq + (size_t)g * GRP) * nsplit + split) * PART_FLOATS;
+    float *part_base = partials + (((size_t)b * hq + (size_t)h0) * nsplit + split) * PART_FLOATS;
     const size_t hstride = (size_t)nsplit * PART_FLOATS;
 
     if (FUSED && nb <= 0 && split == 0) {  // still deliver the selection of this (sequence, KV head)
         select_into_lds<KS>(S, S + Ly::SCR, q_bf16, t_q, b, g, hq, hkv, n_keep, qp_out, sel_out);
     }
     if (nb <= 0) {  // nothing of this sequence falls in this split: an empty partial
-        if (tid >= GRP * D) return;
+        if (tid >= nh * D) return;
         const int h = tid >> 7, ch = tid & (D - 1);
         part_base[h * hstride + ch] = 0.0f;
         if (ch == 0) {
@@ -638,9 +644,9 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
         for (int i = tid; i < KS * 64; i += NTHR) lds_st<uint32_t>(S + Ly::ZERO + i * 4, 0u);
         if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
     } else {
-        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q_prime + ((size_t)b * hq + (size_t)g * GRP) * D);
+        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q_prime + ((size_t)b * hq + (size_t)h0) * D);
         const int32_t *ssrc = sel_idx + ((size_t)b * hkv + g) * n_keep;
-        if (tid < 128) lds_st<u32x4>(scr + tid * 16, qsrc[tid]);
+        if (tid < 128) lds_st<u32x4>(scr + tid * 16, tid < 32 * nh ? qsrc[tid] : u32x4{0u, 0u, 0u, 0u});
         if (tid < 128) lds_st<int32_t>(scr + GRP * D * 4 + tid * 4, tid < n_keep ? ssrc[tid] : 0);
         for (int i = tid; i < KS * 64; i += NTHR) lds_st<uint32_t>(S + Ly::ZERO + i * 4, 0u);
         if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
@@ -981,7 +987,7 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     }
     __syncthreads();
     // ---- combine the four page streams (two token halves each): thread (h, ch)
-    if (tid < GRP * D) {
+    if (tid < nh * D) {
         const int h = tid >> 7, ch = tid & (D - 1);
         auto slot = [&](int v, int half) { return S + (uint32_t)(((2 * v + half) * GRP + h) * PART_FLOATS) * 4; };
         float M = -__builtin_huge_valf();
@@ -1013,22 +1019,25 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
 }  // namespace
 
 bool use_mfma_decode(int hq, int hkv, int n_keep) {
-    return hkv > 0 && hq == GRP * hkv && n_keep <= 16 * MAX_KS;
+    return hkv > 0 && hq % hkv == 0 && hq / hkv <= MAX_GROUP && n_keep <= 16 * MAX_KS;
 }
+
+int mfma_head_sets(int hq, int hkv) { return (hq / hkv + GRP - 1) / GRP; }
 
 static int ks_of(int n_keep) {
     const int k = (n_keep + 15) / 16;
     return k < 1 ? 1 : k > MAX_KS ? MAX_KS : k;
 }
 
-int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep) {
+// units_per_seq: workgroups of one split and sequence (KV heads x head sets)
+int decode_splits_mfma(int batch, int units_per_seq, int max_pages, int n_keep) {
     (void)n_keep;
     // one workgroup per CU (LDS-bound): enough splits to give each of the 256
     // CUs one (down to one 8-page block per split: a short batch is latency-
     // bound, and more workgroups in flight beat a longer pipeline in each);
     // long contexts split so that no split exceeds 16 blocks (ragged batches
     // stay balanced)
-    const int units = batch * hkv;
+    const int units = batch * units_per_seq;
     const int nblk = (max_pages + KBLK - 1) / KBLK;
     int s = (256 + units - 1) / units;
     const int need = (nblk + 15) / 16;
@@ -1038,7 +1047,7 @@ int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep) {
 }
 
 bool fused_select_ok(int hq, int hkv, int n_keep) {
-    if (!use_mfma_decode(hq, hkv, n_keep)) return false;
+    if (!use_mfma_decode(hq, hkv, n_keep) || hq != GRP * hkv) return false;  // the prologue pools four heads
     switch (ks_of(n_keep)) {
         case 1: return Lay<1>::FUSABLE;
         case 2: return Lay<2>::FUSABLE;
@@ -1053,7 +1062,7 @@ bool fused_select_ok(int hq, int hkv, int n_keep) {
 
 template <int KS, bool FUSED>
 static hipError_t launch_ks2(const DecodeArgs &a, hipStream_t s) {
-    dim3 grid(a.num_splits, a.batch * a.hkv);
+    dim3 grid(a.num_splits, a.batch * a.hkv * mfma_head_sets(a.hq, a.hkv));
     hipLaunchKernelGGL((decode_blk_kernel<KS, FUSED>), grid, dim3(NTHR), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep,
                        a.hq, a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials, a.q_bf16,
                        a.t_q, a.qp_out, a.sel_out);

@@ -254,15 +254,18 @@ struct DecodeArgs {
     int32_t *sel_out = nullptr;
 };
 
-// Generic path: any group size up to 16.
-constexpr int GENERIC_MAX_GROUP = 16;
-int decode_splits_generic(int batch, int hkv, int max_pages);
-hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
+// Query heads per KV head that the decode entry points serve.
+constexpr int MAX_GROUP = 16;
 
-// MFMA path (group size 4, the GQA 32/8 shape).
+// The INT2 decode on MFMA: any group size up to MAX_GROUP, the query heads of
+// a KV head taken in sets of four (one workgroup per set and split; a set of
+// fewer than four is padded with zero queries).
 bool use_mfma_decode(int hq, int hkv, int n_keep);  // n_keep 0: any count it serves
-int decode_splits_mfma(int batch, int hkv, int max_pages, int n_keep);  // n_keep 0: the largest
+int mfma_head_sets(int hq, int hkv);                // sets of four query heads per KV head
+int decode_splits_mfma(int batch, int units_per_seq, int max_pages, int n_keep);  // n_keep 0: the largest
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
+// Split count of the BF16 baseline decode.
+int decode_splits_bf16(int batch, int hkv, int max_pages);
 // Whether the MFMA decode can run the selection itself for this n_keep.
 bool fused_select_ok(int hq, int hkv, int n_keep);
 

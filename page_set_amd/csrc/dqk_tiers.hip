@@ -117,7 +117,7 @@ __global__ __launch_bounds__(D) void tier_token_kernel(dqk_tiers t, const uint16
 
 constexpr int MAX_TIER = TIER_SINK + TIER_RECENT + PG - 1;  // 447 tier tokens at most
 constexpr int TD_MAXG = 16;                                  // query heads per KV head, at most
-static_assert(TD_MAXG == GENERIC_MAX_GROUP, "the tiered decode takes the generic decode's groups");
+static_assert(TD_MAXG == MAX_GROUP, "the tiered decode serves every group the INT2 decode serves");
 constexpr int TCH = 64;                                      // tier tokens per workgroup
 constexpr int N_TCH = (MAX_TIER + TCH - 1) / TCH;           // 7 partials per (sequence, query head)
 

@@ -129,6 +129,8 @@ DECODE_CASES = [
     ("g2", synth.Shape(2, 16, 8, [900, 1300], 77)),
     ("g8", synth.Shape(1, 16, 2, [2100], 77)),
     ("g16", synth.Shape(1, 16, 1, [700], 64)),
+    ("g3", synth.Shape(1, 6, 2, [1500], 77)),
+    ("g6-ragged", synth.Shape(2, 24, 4, [600, 1100], 77, shuffle_pages=True)),
 ]
 
 
@@ -151,13 +153,13 @@ def test_decode_config1_full():
     assert (rel <= gu.TOL).all()
 
 
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 8)], ids=["mfma-g4", "generic-g2"])
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (16, 8), (48, 4)], ids=["g4", "g2", "g12"])
 def test_decode_split_invariance_and_permutation(hq, hkv):
-    """Split count changes only rounding.  The group-4 MFMA path rounds the
+    """Split count changes only rounding.  The MFMA decode rounds the
     probabilities and P * scale to binary16 relative to each split's running
     maximum: two split counts agree within the bound derived from those
-    roundings (gpu_util.split_bound), element by element.  The generic path
-    keeps fp32 throughout (1e-5 of the row)."""
+    roundings (gpu_util.split_bound), element by element, for every group
+    size (a group of 2 is one padded set of four heads, 12 three sets)."""
     _say("decode splits/permutation", hq, hkv)
     shape = synth.Shape(2, hq, hkv, [4000, 2500], 77)
     outs = []
@@ -165,15 +167,11 @@ def test_decode_split_invariance_and_permutation(hq, hkv):
         prob, cache, qp, sel, ref, ref_lse, out, lse = _decode_case(shape, 9, num_splits=ns)
         outs.append(out)
         assert (gu.row_rel_err(out, ref) <= gu.TOL).all()
-    if hq == 4 * hkv:
-        bound = gu.split_bound(cache, qp, sel, prob.page_table, prob.seq_lens, prob.sm_scale)
-        for o in outs[1:]:
-            diff = np.abs(o.astype(np.float64) - outs[0])
-            _say(f"  split difference / derived bound: max {(diff / bound).max():.3f}")
-            assert (diff <= bound).all()
-    else:
-        for o in outs[1:]:
-            assert (gu.row_rel_err(o, outs[0]) <= 1e-5).all()
+    bound = gu.split_bound(cache, qp, sel, prob.page_table, prob.seq_lens, prob.sm_scale)
+    for o in outs[1:]:
+        diff = np.abs(o.astype(np.float64) - outs[0])
+        _say(f"  split difference / derived bound: max {(diff / bound).max():.3f}")
+        assert (diff <= bound).all()
 
     def permute(cache, prob):
         perm = np.random.default_rng(4).permutation(prob.num_pages)

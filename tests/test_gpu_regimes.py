@@ -118,7 +118,7 @@ def _check(prob, splits=(0, 1, 7), label="", kprime_fn=None):
 
 
 LONG = synth.Shape(1, 8, 2, [32768], 77)          # group of 4: MFMA path
-LONG_G2 = synth.Shape(1, 4, 2, [32768], 77)       # group of 2: generic path
+LONG_G2 = synth.Shape(1, 4, 2, [32768], 77)       # group of 2: one padded set of four heads
 
 
 @pytest.mark.parametrize("shape", [LONG, LONG_G2], ids=["g4", "g2"])

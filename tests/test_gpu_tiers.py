@@ -167,7 +167,7 @@ DECODE_CASES = [
     ("page-edges", synth.Shape(4, 32, 8, [320, 447, 448, 449], 77, shuffle_pages=True)),
     ("long-g4", synth.Shape(2, 32, 8, [5000, 1300], 77, shuffle_pages=True)),
     ("nk128", synth.Shape(1, 32, 8, [3000], 128)),
-    ("g2-generic", synth.Shape(2, 16, 8, [2000, 700], 77)),
+    ("g2", synth.Shape(2, 16, 8, [2000, 700], 77)),
     ("mha", synth.Shape(1, 4, 4, [900], 52)),
 ]
 

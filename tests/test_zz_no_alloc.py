@@ -24,7 +24,7 @@ def _case(shape, seed):
 def test_noalloc_equals_workspace_entry_twice():
     cases = [(synth.Shape(4, 32, 8, [20000, 5000, 131, 9000], 77), 1, 0),
              (synth.Shape(2, 32, 8, [3000, 700], 52), 2, 3),        # smaller, explicit split count
-             (synth.Shape(3, 24, 4, [1500, 40, 900], 30), 3, 0)]    # group 6: generic kernels
+             (synth.Shape(3, 24, 4, [1500, 40, 900], 30), 3, 0)]    # group 6: two head sets (4 + 2)
     for shape, seed, ns in cases:
         print("noalloc", shape.batch, shape.hq, shape.hkv, shape.seq_lens, "splits", ns, flush=True)
         prob, gc, qp, sel, pt, sl = _case(shape, seed)
