@@ -363,6 +363,24 @@ int dqk_value_unrotate(const float *o_rot, const float *r_v_inv, int32_t batch, 
                        float *out, hipStream_t stream);
 
 /*
+ * The rotated-value decode step as one call: selection in base coordinates
+ * (as dqk_select_channels_base), decode (as dqk_decode_attn) and the split
+ * merge followed by the inverse value rotation (as dqk_value_unrotate) in the
+ * merge kernel.  For hq = 4 hkv and 17 <= n_keep <= 128 the selection runs in
+ * the decode launch (two launches in all); otherwise the selection is a
+ * launch of its own.  q_prime, sel_idx, out and lse are bit-identical to
+ * those of dqk_select_channels_base + dqk_decode_attn + dqk_value_unrotate
+ * (lse being that of the rotated output, which the rotation leaves as is).
+ * Arguments as dqk_select_decode_attn, plus sel_scale (fp32 [hkv][128]) and
+ * r_v_inv (fp32 [hkv][128][128]); errors as those calls.
+ */
+int dqk_select_decode_attn_vrot(const dqk_cache *c, const void *q_bf16, const float *t_q, const float *sel_scale,
+                                const float *r_v_inv, int32_t n_keep, int32_t batch, int32_t hq,
+                                const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                                float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
+                                float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream);
+
+/*
  * dqk_stream_read -- measurement helper, not part of the attention path: a
  * plain streaming read of `bytes` bytes (a multiple of 16 KiB) at `src`,
  * 16 bytes per lane through LDS, as the reference point for the decode

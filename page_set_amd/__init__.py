@@ -73,6 +73,9 @@ def lib():
         L.dqk_select_decode_attn.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, P, i32, P,
                                              ctypes.c_float, i32, P, sz, P, P, P, P, P]
         L.dqk_select_decode_attn.restype = ctypes.c_int
+        L.dqk_select_decode_attn_vrot.argtypes = [ctypes.POINTER(dqk_cache), P, P, P, P, i32, i32, i32, P, i32, P,
+                                                  ctypes.c_float, i32, P, sz, P, P, P, P, P]
+        L.dqk_select_decode_attn_vrot.restype = ctypes.c_int
         L.dqk_decode_attn_noalloc.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, P, i32, P,
                                               ctypes.c_float, i32, P, P, P]
         L.dqk_decode_attn_noalloc.restype = ctypes.c_int
@@ -333,6 +336,36 @@ def dqk_select_decode_attn(cache: Cache, q, t_q, n_keep: int, page_table, seq_le
                                       workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                       _ptr(q_prime), _ptr(sel_idx), _stream(stream))
     _check(rc, "dqk_select_decode_attn")
+    return out, lse, q_prime, sel_idx
+
+
+def dqk_select_decode_attn_vrot(cache: Cache, q, t_q, sel_scale, r_v_inv, n_keep: int, page_table, seq_lens,
+                                sm_scale: float, num_splits: int = 0, workspace=None, out=None, lse=None,
+                                want_lse: bool = True, q_prime=None, sel_idx=None, stream=None):
+    """Base selection, decode and merge with the inverse value rotation in one
+    call; returns (out, lse, q_prime, sel_idx)."""
+    import torch
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    hkv = cache.num_kv_heads
+    max_pages = int(page_table.shape[1])
+    dev = q.device
+    if workspace is None:
+        workspace = _workspace(B, hq, hkv, max_pages, num_splits, dev)
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    if q_prime is None:
+        q_prime = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, hkv, n_keep), dtype=torch.int32, device=dev)
+    s = cache.struct()
+    rc = lib().dqk_select_decode_attn_vrot(ctypes.byref(s), _ptr(q), _ptr(t_q), _ptr(sel_scale), _ptr(r_v_inv),
+                                           int(n_keep), B, hq, _ptr(page_table), max_pages, _ptr(seq_lens),
+                                           float(sm_scale), int(num_splits), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                                           _ptr(q_prime), _ptr(sel_idx), _stream(stream))
+    _check(rc, "dqk_select_decode_attn_vrot")
     return out, lse, q_prime, sel_idx
 
 

@@ -179,10 +179,12 @@ size_t dqk_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t
     return (size_t)batch * hq * s * dqk::PART_FLOATS * sizeof(float);
 }
 
-int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep, int32_t batch,
-                    int32_t hq, const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
-                    float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out, float *lse,
-                    hipStream_t stream) {
+// Decode over the INT2 cache, then the split merge (r_inv non-null: the merge
+// followed by the inverse value rotation).
+static int decode_core(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
+                       int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                       const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes,
+                       const float *r_inv, float *out, float *lse, hipStream_t stream) {
     int st = check_cache(c);
     if (st) return st;
     if (!q_prime || !sel_idx || !page_table || !seq_lens || !workspace || !out) return DQK_ERR_NULL;
@@ -202,13 +204,18 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
                       sm_scale, splits, static_cast<float *>(workspace), out, lse};
     hipError_t e = dqk::launch_decode_mfma(a, stream);
     if (e != hipSuccess) return hip_status(e);
+    if (r_inv) return hip_status(dqk::launch_merge_unrotate(a.partials, batch, hq, hkv, splits, r_inv, out, lse, stream));
     return hip_status(dqk::launch_merge(a.partials, batch, hq, splits, out, lse, stream));
 }
 
-int dqk_select_decode_attn(const dqk_cache *c, const void *q_bf16, const float *t_q, int32_t n_keep, int32_t batch,
-                           int32_t hq, const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
-                           float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
-                           float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream) {
+// Selection (sel_scale non-null: in base coordinates), decode and merge
+// (r_inv non-null: with the inverse value rotation), the selection inside the
+// decode launch where the kernel can run it.
+static int select_decode_core(const dqk_cache *c, const void *q_bf16, const float *t_q, const float *sel_scale,
+                              const float *r_inv, int32_t n_keep, int32_t batch, int32_t hq,
+                              const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens, float sm_scale,
+                              int32_t num_splits, void *workspace, size_t ws_bytes, float *out, float *lse,
+                              float *q_prime, int32_t *sel_idx, hipStream_t stream) {
     int st = check_cache(c);
     if (st) return st;
     if (!q_bf16 || !t_q || !page_table || !seq_lens || !workspace || !out || !q_prime || !sel_idx) return DQK_ERR_NULL;
@@ -216,28 +223,63 @@ int dqk_select_decode_attn(const dqk_cache *c, const void *q_bf16, const float *
     if (batch < 1 || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM || max_pages < 1 ||
         num_splits < 0 || num_splits > max_pages)
         return DQK_ERR_SHAPE;
-    if (!dqk::fused_select_ok(hq, hkv, n_keep)) {  // two launches: selection, then decode
-        st = dqk_select_channels(q_bf16, t_q, batch, hq, hkv, n_keep, q_prime, sel_idx, stream);
-        if (st) return st;
-        return dqk_decode_attn(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale,
-                               num_splits, workspace, ws_bytes, out, lse, stream);
-    }
-    if ((int64_t)batch * hkv > 65535) return DQK_ERR_UNSUPPORTED;
+    // every check of both paths before anything is enqueued
+    if (!dqk::use_mfma_decode(hq, hkv, n_keep)) return DQK_ERR_UNSUPPORTED;  // more than MAX_GROUP heads per KV head
+    if ((int64_t)batch * hkv * dqk::mfma_head_sets(hq, hkv) > 65535 || batch * hq > 2147483647 / 2)
+        return DQK_ERR_UNSUPPORTED;
     if (!aligned16(q_bf16) || !aligned16(t_q) || !aligned16(q_prime) || !aligned16(sel_idx) ||
         !aligned16(page_table) || !aligned16(seq_lens) || !aligned16(workspace) || !aligned16(out) ||
         (lse && !aligned16(lse)))
         return DQK_ERR_ALIGN;
     const int splits = resolve_splits(batch, hq, hkv, max_pages, num_splits, n_keep);
     if (ws_bytes < (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float)) return DQK_ERR_WORKSPACE;
+    if (!dqk::fused_select_ok(hq, hkv, n_keep)) {  // separate launches: selection, then decode
+        st = sel_scale ? dqk_select_channels_base(q_bf16, t_q, sel_scale, batch, hq, hkv, n_keep, q_prime, sel_idx,
+                                                  stream)
+                       : dqk_select_channels(q_bf16, t_q, batch, hq, hkv, n_keep, q_prime, sel_idx, stream);
+        if (st) return st;
+        return decode_core(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale,
+                           num_splits, workspace, ws_bytes, r_inv, out, lse, stream);
+    }
     dqk::DecodeArgs a{c,         nullptr,  nullptr, n_keep, batch,  hq, hkv, page_table, max_pages, seq_lens,
                       sm_scale, splits, static_cast<float *>(workspace), out, lse};
     a.q_bf16 = static_cast<const uint16_t *>(q_bf16);
     a.t_q = t_q;
     a.qp_out = q_prime;
     a.sel_out = sel_idx;
+    a.sel_scale = sel_scale;
     hipError_t e = dqk::launch_decode_mfma(a, stream);
     if (e != hipSuccess) return hip_status(e);
+    if (r_inv) return hip_status(dqk::launch_merge_unrotate(a.partials, batch, hq, hkv, splits, r_inv, out, lse, stream));
     return hip_status(dqk::launch_merge(a.partials, batch, hq, splits, out, lse, stream));
+}
+
+int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep, int32_t batch,
+                    int32_t hq, const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                    float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out, float *lse,
+                    hipStream_t stream) {
+    return decode_core(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale, num_splits,
+                       workspace, ws_bytes, nullptr, out, lse, stream);
+}
+
+int dqk_select_decode_attn(const dqk_cache *c, const void *q_bf16, const float *t_q, int32_t n_keep, int32_t batch,
+                           int32_t hq, const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                           float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
+                           float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream) {
+    return select_decode_core(c, q_bf16, t_q, nullptr, nullptr, n_keep, batch, hq, page_table, max_pages, seq_lens,
+                              sm_scale, num_splits, workspace, ws_bytes, out, lse, q_prime, sel_idx, stream);
+}
+
+int dqk_select_decode_attn_vrot(const dqk_cache *c, const void *q_bf16, const float *t_q, const float *sel_scale,
+                                const float *r_v_inv, int32_t n_keep, int32_t batch, int32_t hq,
+                                const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                                float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
+                                float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream) {
+    if (!sel_scale || !r_v_inv) return DQK_ERR_NULL;
+    if (!aligned16(sel_scale) || !aligned16(r_v_inv)) return DQK_ERR_ALIGN;
+    return select_decode_core(c, q_bf16, t_q, sel_scale, r_v_inv, n_keep, batch, hq, page_table, max_pages,
+                              seq_lens, sm_scale, num_splits, workspace, ws_bytes, out, lse, q_prime, sel_idx,
+                              stream);
 }
 
 int dqk_decode_attn_noalloc(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,

@@ -486,11 +486,13 @@ struct Feeder {
 // computes it (the same fp32 fma chains in the same order, the same rank
 // rule), into the LDS scratch the decode prologue reads: q' [4][128] at scr,
 // the ascending channel list after it.  qp_out / sel_out (may be null)
-// receive the same values in global memory.
+// receive the same values in global memory.  wsel (may be null): the KV
+// head's selection scales, as dqk_select_channels_base applies them.
 template <int KS>
 __device__ __forceinline__ void select_into_lds(uint32_t S, uint32_t scr, const uint16_t *__restrict__ q_bf16,
-                                                const float *__restrict__ t_q, int b, int g, int hq, int hkv,
-                                                int n_keep, float *__restrict__ qp_out, int32_t *__restrict__ sel_out) {
+                                                const float *__restrict__ t_q, const float *__restrict__ wsel, int b,
+                                                int g, int hq, int hkv, int n_keep, float *__restrict__ qp_out,
+                                                int32_t *__restrict__ sel_out) {
     using Ly = Lay<KS>;
     const int tid = threadIdx.x;
     // every load of the transform is issued before any is stored
@@ -527,10 +529,11 @@ __device__ __forceinline__ void select_into_lds(uint32_t S, uint32_t scr, const 
     __syncthreads();
     // pooled energy S_j: fma chain over ascending head
     if (tid < D) {
+        const float w = wsel ? wsel[tid] : 1.0f;  // x * 1 is x exactly
         float e = 0.0f;
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
-            const float v = lds_ld<float>(scr + (h * D + tid) * 4);
+            const float v = __fmul_rn(lds_ld<float>(scr + (h * D + tid) * 4), w);
             e = __builtin_fmaf(v, v, e);
         }
         lds_st<float>(S + Ly::FS + tid * 4, e);
@@ -570,7 +573,9 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                                                           const int32_t *__restrict__ seq_lens, float sm_scale,
                                                           int nsplit, float *__restrict__ partials,
                                                           const uint16_t *__restrict__ q_bf16,
-                                                          const float *__restrict__ t_q, float *__restrict__ qp_out,
+                                                          const float *__restrict__ t_q,
+                                                          const float *__restrict__ sel_scale,
+                                                          float *__restrict__ qp_out,
                                                           int32_t *__restrict__ sel_out) {
     using Ly = Lay<KS>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[Ly::TOTAL];
@@ -601,7 +606,8 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const size_t hstride = (size_t)nsplit * PART_FLOATS;
 
     if (FUSED && nb <= 0 && split == 0) {  // still deliver the selection of this (sequence, KV head)
-        select_into_lds<KS>(S, S + Ly::SCR, q_bf16, t_q, b, g, hq, hkv, n_keep, qp_out, sel_out);
+        select_into_lds<KS>(S, S + Ly::SCR, q_bf16, t_q, sel_scale ? sel_scale + (size_t)g * D : nullptr, b, g, hq,
+                            hkv, n_keep, qp_out, sel_out);
     }
     if (nb <= 0) {  // nothing of this sequence falls in this split: an empty partial
         if (tid >= nh * D) return;
@@ -639,8 +645,8 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const uint32_t scr = S + Ly::SCR;
     if constexpr (FUSED) {
         static_assert(Ly::FUSABLE, "selection scratch");
-        select_into_lds<KS>(S, scr, q_bf16, t_q, b, g, hq, hkv, n_keep, split == 0 ? qp_out : nullptr,
-                            split == 0 ? sel_out : nullptr);
+        select_into_lds<KS>(S, scr, q_bf16, t_q, sel_scale ? sel_scale + (size_t)g * D : nullptr, b, g, hq, hkv,
+                            n_keep, split == 0 ? qp_out : nullptr, split == 0 ? sel_out : nullptr);
         for (int i = tid; i < KS * 64; i += NTHR) lds_st<uint32_t>(S + Ly::ZERO + i * 4, 0u);
         if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
     } else {
@@ -1065,7 +1071,7 @@ static hipError_t launch_ks2(const DecodeArgs &a, hipStream_t s) {
     dim3 grid(a.num_splits, a.batch * a.hkv * mfma_head_sets(a.hq, a.hkv));
     hipLaunchKernelGGL((decode_blk_kernel<KS, FUSED>), grid, dim3(NTHR), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep,
                        a.hq, a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials, a.q_bf16,
-                       a.t_q, a.qp_out, a.sel_out);
+                       a.t_q, a.sel_scale, a.qp_out, a.sel_out);
     return hipGetLastError();
 }
 

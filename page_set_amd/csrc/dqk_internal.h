@@ -219,9 +219,11 @@ hipError_t launch_append_vrot(const dqk_cache &c, const uint16_t *k, const uint1
                               const uint16_t *r_v, float clip, int n_seqs, const int32_t *cu_tokens,
                               const int32_t *page_table, int max_pages, float *kprime_dbg, float *vprime_dbg,
                               hipStream_t s);
-// inverse value rotation of decode outputs (dqk_vrot.hip)
+// inverse value rotation of decode outputs (dqk_vrot.hip); the split merge followed by it
 hipError_t launch_value_unrotate(const float *o_rot, const float *r_inv, int batch, int hq, int hkv, float *out,
                                  hipStream_t s);
+hipError_t launch_merge_unrotate(const float *partials, int batch, int hq, int hkv, int num_splits,
+                                 const float *r_inv, float *out, float *lse, hipStream_t s);
 hipError_t launch_pack_tail(const dqk_cache &c, const dqk_tiers &t, const uint16_t *t_k, int batch,
                             const int32_t *lens_before, const int32_t *page_table, int max_pages, hipStream_t s);
 // BF16 tiers (dqk_tiers.hip)
@@ -252,6 +254,8 @@ struct DecodeArgs {
     const float *t_q = nullptr;
     float *qp_out = nullptr;
     int32_t *sel_out = nullptr;
+    // selection in base coordinates (fused selection only): fp32 [hkv][128] or null
+    const float *sel_scale = nullptr;
 };
 
 // Query heads per KV head that the decode entry points serve.
@@ -288,6 +292,8 @@ struct DecodeBf16Args {
     const float *t_q = nullptr;
     float *qp_out = nullptr;
     int32_t *sel_out = nullptr;
+    // selection in base coordinates (fused selection only): fp32 [hkv][128] or null
+    const float *sel_scale = nullptr;
 };
 
 hipError_t launch_decode_bf16(const DecodeBf16Args &a, hipStream_t s);

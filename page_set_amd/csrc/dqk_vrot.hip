@@ -54,7 +54,38 @@ __global__ __launch_bounds__(THREADS) void value_unrotate_kernel(const float *__
     }
 }
 
+// The split merge of one (sequence, query head) row followed by the inverse
+// rotation: block (b, h) of 128 lanes merges its partials into LDS (the log-
+// sum-exp merge of the plain decode), then lane c forms out_c = sum_j o'_j
+// R_V^-1[g][j][c] with the fp32 fma chain over ascending j of
+// value_unrotate_kernel, reading R_V^-1 (shared by the KV head's query heads,
+// so mostly from L2) one coalesced 512-byte row per j.
+__global__ __launch_bounds__(D) void merge_unrotate_kernel(const float *__restrict__ partials, int nsplit,
+                                                           const float *__restrict__ r_inv, int hq, int hkv,
+                                                           float *__restrict__ out, float *__restrict__ lse) {
+    __shared__ float w_lds[D];
+    __shared__ float red[3][D / 64];
+    __shared__ float o_lds[D];
+    const int bh = blockIdx.x, h = bh % hq, g = h / (hq / hkv), c = threadIdx.x;
+    const float *P = partials + (size_t)bh * nsplit * PART_FLOATS;
+    auto part = [&](int s) { return P + (size_t)s * PART_FLOATS; };
+    merge_row(part, nsplit, c, true, o_lds, lse ? lse + bh : nullptr, w_lds, red);
+    __syncthreads();
+    const float *r = r_inv + (size_t)g * D * D + c;
+    float acc = 0.0f;
+#pragma unroll 16
+    for (int j = 0; j < D; ++j) acc = __builtin_fmaf(o_lds[j], r[(size_t)j * D], acc);
+    out[(size_t)bh * D + c] = acc;
+}
+
 }  // namespace
+
+hipError_t launch_merge_unrotate(const float *partials, int batch, int hq, int hkv, int num_splits,
+                                 const float *r_inv, float *out, float *lse, hipStream_t s) {
+    hipLaunchKernelGGL(merge_unrotate_kernel, dim3(batch * hq), dim3(D), 0, s, partials, num_splits, r_inv, hq, hkv,
+                       out, lse);
+    return hipGetLastError();
+}
 
 hipError_t launch_value_unrotate(const float *o_rot, const float *r_inv, int batch, int hq, int hkv, float *out,
                                  hipStream_t s) {

@@ -253,3 +253,26 @@ def test_vrot_validation():
     assert unrot(B=0) == pa.DQK_ERR_SHAPE
     assert unrot(hq=65 * 2, hkv=2) == pa.DQK_ERR_UNSUPPORTED
     assert unrot(out=ctypes.c_void_p((1 << 20) + 8)) == pa.DQK_ERR_ALIGN
+
+
+def test_one_call_vrot_validation():
+    L = pa.lib()
+
+    def call(c=None, **kw):
+        c = c or _cache()
+        a = dict(q=A, tq=A, sc=A, ri=A, nk=77, B=4, hq=32, pt=A, mp=16, sl=A, sm=0.088, ns=0, ws=A, wsb=1 << 30,
+                 out=A, lse=None, qp=A, si=A)
+        a.update(kw)
+        return L.dqk_select_decode_attn_vrot(ctypes.byref(c), a["q"], a["tq"], a["sc"], a["ri"], a["nk"], a["B"],
+                                             a["hq"], a["pt"], a["mp"], a["sl"], a["sm"], a["ns"], a["ws"], a["wsb"],
+                                             a["out"], a["lse"], a["qp"], a["si"], None)
+
+    assert call(sc=None) == pa.DQK_ERR_NULL
+    assert call(ri=None) == pa.DQK_ERR_NULL
+    assert call(q=None) == pa.DQK_ERR_NULL
+    assert call(ri=MIS) == pa.DQK_ERR_ALIGN
+    assert call(hq=30) == pa.DQK_ERR_SHAPE
+    assert call(nk=0) == pa.DQK_ERR_SHAPE
+    assert call(hq=8 * 32) == pa.DQK_ERR_UNSUPPORTED
+    need = pa.dqk_decode_workspace_size(4, 32, 8, 16, 4)
+    assert call(ns=4, wsb=need - 4) == pa.DQK_ERR_WORKSPACE

@@ -198,3 +198,45 @@ def test_rotated_path_end_to_end(name, shape):
     e = gu.row_rel_err(gu.host(out), ref)
     _say(f"  max row rel err {e.max():.3e}")
     assert e.max() <= gu.TOL
+
+
+ONE_CALL_CASES = [
+    ("g4-nk77", synth.Shape(2, 32, 8, [3000, 701], 77, shuffle_pages=True), 0),
+    ("g4-nk128-3splits", synth.Shape(1, 32, 8, [2000], 128), 3),
+    ("g4-nk9", synth.Shape(2, 32, 8, [900, 300], 9), 0),      # n_keep < 17: the selection is a launch of its own
+    ("g2", synth.Shape(2, 16, 8, [1200, 600], 77), 0),       # group 2: the same
+]
+
+
+@pytest.mark.parametrize("name,shape,ns", ONE_CALL_CASES, ids=[c[0] for c in ONE_CALL_CASES])
+def test_one_call_equals_three_calls(name, shape, ns):
+    """dqk_select_decode_attn_vrot (the selection in the decode launch where
+    possible, the inverse rotation in the merge) gives bit for bit the
+    results of dqk_select_channels_base + dqk_decode_attn +
+    dqk_value_unrotate, and stays within 2e-3 of the oracle."""
+    _say("vrot one call", name)
+    prob = synth.make_problem(shape, seed=36)
+    rv, rinv = synth.make_value_rotation(shape.hkv, seed=36)
+    w = synth.make_selection_scales(shape.hkv, seed=36)
+    d = gu.upload(prob)
+    w_d, rinv_d = gu.dev(w), gu.dev(rinv)
+    cache = pa.Cache(prob.num_pages, shape.hkv)
+    pa.dqk_quantize_append_vrot(cache, d["k"], d["v"], d["t_k"], gu.dev(rv), CLIP, d["cu"], d["page_table"])
+    out1, lse1, qp1, sel1 = pa.dqk_select_decode_attn_vrot(cache, d["q"], d["t_q"], w_d, rinv_d, shape.n_keep,
+                                                           d["page_table"], d["seq_lens"], prob.sm_scale,
+                                                           num_splits=ns)
+    qp2, sel2 = pa.dqk_select_channels_base(d["q"], d["t_q"], w_d, shape.hkv, shape.n_keep)
+    o_rot, lse2 = pa.dqk_decode_attn(cache, qp2, sel2, d["page_table"], d["seq_lens"], prob.sm_scale, num_splits=ns)
+    out2 = pa.dqk_value_unrotate(o_rot, rinv_d, shape.hkv)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gu.host(qp1).view(np.uint32), gu.host(qp2).view(np.uint32))
+    np.testing.assert_array_equal(gu.host(sel1), gu.host(sel2))
+    np.testing.assert_array_equal(gu.host(out1).view(np.uint32), gu.host(out2).view(np.uint32))
+    np.testing.assert_array_equal(gu.host(lse1).view(np.uint32), gu.host(lse2).view(np.uint32))
+    qp_ref, sel_ref = oracle.select_channels_base(prob.q, prob.t_q, w, shape.hkv, shape.n_keep)
+    np.testing.assert_array_equal(gu.host(sel1), sel_ref)
+    o_ref, _ = oracle.decode_attn(gu.cache_to_host(cache), qp_ref, sel_ref, prob.page_table, prob.seq_lens,
+                                  prob.sm_scale)
+    e = gu.row_rel_err(gu.host(out1), oracle.value_unrotate(o_ref, rinv, shape.hkv))
+    _say(f"  max row rel err {e.max():.3e}")
+    assert e.max() <= gu.TOL
