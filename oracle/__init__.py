@@ -53,6 +53,14 @@ value_unrotate         permutation R_V: rotate, pack, decode and unrotate give
                        decode_attn of the unrotated cache exactly; a Haar
                        rotation and its inverse return the input (fp64 bound)
                        (tests/test_oracle_vrot.py)
+pack_cache_tokgrid     every token's codes are the nearest levels of its own
+                       grid, which covers channels 1..127 tightly; channel 0
+                       outside the range (changing it moves nothing else); the
+                       layout read back by an independent numpy decoder
+decode_attn_tokgrid    textbook attention (torch, fp64) over the cache decoded
+                       by that reader; tiny brute force; with every token's
+                       channels alike it equals decode_attn on a per-channel
+                       pack of the same keys (tests/test_oracle_tokgrid.py)
 =====================  ==========================================================
 
 Parity unpinned: the accuracy tables of the paper (need models and datasets).
@@ -116,6 +124,10 @@ def _load():
         _lib.orc_value_unrotate.restype = i32
         _lib.orc_select_channels_base.argtypes = [P, P, P, i32, i32, i32, i32, P, P]
         _lib.orc_select_channels_base.restype = i32
+        _lib.orc_pack_cache_tokgrid.argtypes = [P, P, i32, i32, P, P, i32, P, P, P, P, P]
+        _lib.orc_pack_cache_tokgrid.restype = None
+        _lib.orc_decode_attn_tokgrid.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, P, i32, P, f64, P, P]
+        _lib.orc_decode_attn_tokgrid.restype = i32
         _lib.orc_tier_pages.argtypes = [i64]
         _lib.orc_tier_pages.restype = i64
         _lib.orc_decode_tiered.argtypes = [P, P, P, P, P, i32, P, P, P, P, P, P, i32, i32, i32, P, i32, P, f64, P,
@@ -257,6 +269,29 @@ def quantize_append(k_bf16, v_bf16, t_k_bf16, cu_tokens, page_table, num_pages: 
     return pack_cache(kp, v_bf16, cu_tokens, page_table, num_pages, cache), kp
 
 
+def pack_cache_tokgrid(kprime: np.ndarray, v_bf16: np.ndarray, cu_tokens, page_table, num_pages: int,
+                       cache: Optional[Cache] = None) -> Cache:
+    """pack_cache with one key grid per token and KV head over channels 1..127
+    (per-token (scale, zero) pairs in k_meta, [P/8][Hkv][8][128][2])."""
+    kp = _c(kprime, np.float32)
+    v = _c(v_bf16, np.uint16)
+    cu = _c(cu_tokens, np.int32)
+    pt = _c(page_table, np.int32)
+    hkv = kp.shape[1]
+    if cache is None:
+        cache = Cache(num_pages, hkv)
+    _load().orc_pack_cache_tokgrid(_p(kp), _p(v), hkv, len(cu) - 1, _p(cu), _p(pt), pt.shape[1],
+                                   *[_p(a) for a in cache.arrays()])
+    return cache
+
+
+def quantize_append_tokgrid(k_bf16, v_bf16, t_k_bf16, cu_tokens, page_table, num_pages: int,
+                            cache: Optional[Cache] = None):
+    """quantize_append with per-token key grids; returns (cache, k')."""
+    kp = key_transform(k_bf16, t_k_bf16)
+    return pack_cache_tokgrid(kp, v_bf16, cu_tokens, page_table, num_pages, cache), kp
+
+
 def value_transform(v_bf16: np.ndarray, r_v_bf16: np.ndarray) -> np.ndarray:
     """v' = v R_V per token and KV head (the same row-vector product as k T_K)."""
     return key_transform(v_bf16, r_v_bf16)
@@ -337,6 +372,23 @@ def decode_attn(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_scale: 
                                  _p(pt), pt.shape[1], _p(sl), float(sm_scale), _p(out), _p(lse))
     if rc:
         raise ValueError(f"decode_attn failed (rc={rc})")
+    return out, lse
+
+
+def decode_attn_tokgrid(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_scale: float):
+    """decode_attn over a cache with per-token key grids."""
+    qp = _c(q_prime, np.float32)
+    sel = _c(sel_idx, np.int32)
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    B, hq = qp.shape[0], qp.shape[1]
+    out = np.empty((B, hq, HEAD_DIM), dtype=np.float64)
+    lse = np.empty((B, hq), dtype=np.float64)
+    rc = _load().orc_decode_attn_tokgrid(*[_p(a) for a in cache.arrays()], cache.hkv, _p(qp), _p(sel),
+                                         sel.shape[2], B, hq, _p(pt), pt.shape[1], _p(sl), float(sm_scale),
+                                         _p(out), _p(lse))
+    if rc:
+        raise ValueError(f"decode_attn_tokgrid failed (rc={rc})")
     return out, lse
 
 

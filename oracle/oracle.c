@@ -50,6 +50,15 @@ static size_t krow(int64_t p, int g, int hkv, int j)
     return ((((size_t)(p >> 3) * (size_t)hkv + (size_t)g) * HD + (size_t)j) * 8) + (size_t)(p & 7);
 }
 
+/* Per-token key grid (§3.3 as the paper states it, one grid per token and KV
+ * head over channels 1..127): the (scale, zero) pair of token s of page p in
+ * k_meta, laid out [P/8][Hkv][8 slot][128 tok][2] -- the same bytes as the
+ * per-channel metadata of the block, token-major. */
+static size_t ktok(int64_t p, int g, int hkv, int s)
+{
+    return (((size_t)(p >> 3) * (size_t)hkv + (size_t)g) * 8 + (size_t)(p & 7)) * PG + (size_t)s;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Number formats, from their IEEE 754 definitions (binary16; bfloat16 is the
  * top half of binary32).  Values are handled as exact doubles.              */
@@ -265,9 +274,9 @@ void orc_key_transform(const uint16_t *k, const uint16_t *t_k, int64_t T, int hk
  * page past the sequence end get code 0, ch0 0 and metadata 0.
  *   kprime fp32 [T][Hkv][128], v bf16 [T][Hkv][128]
  *   cu_tokens [n_seqs+1], page_table [n_seqs][max_pages]                    */
-static void pack_impl(const float *kprime, const uint16_t *v, const float *vf32, float vclip, int hkv, int n_seqs,
-                      const int32_t *cu_tokens, const int32_t *page_table, int max_pages, uint8_t *k_codes,
-                      uint16_t *k_meta, uint16_t *k_ch0, uint8_t *v_codes, uint16_t *v_meta)
+static void pack_impl(const float *kprime, const uint16_t *v, const float *vf32, float vclip, int token_grid, int hkv,
+                      int n_seqs, const int32_t *cu_tokens, const int32_t *page_table, int max_pages,
+                      uint8_t *k_codes, uint16_t *k_meta, uint16_t *k_ch0, uint8_t *v_codes, uint16_t *v_meta)
 {
     for (int sq = 0; sq < n_seqs; ++sq) {
         int64_t t0 = cu_tokens[sq], L = (int64_t)cu_tokens[sq + 1] - t0;
@@ -283,8 +292,9 @@ static void pack_impl(const float *kprime, const uint16_t *v, const float *vf32,
                 uint16_t *vm = v_meta + pg * 2 * 4 * PG;
                 for (int j = 0; j < HD; ++j) {
                     memset(k_codes + krow(p, g, hkv, j) * 32, 0, 32);
-                    k_meta[krow(p, g, hkv, j) * 2 + 0] = 0;
-                    k_meta[krow(p, g, hkv, j) * 2 + 1] = 0;
+                    size_t mi = token_grid ? ktok(p, g, hkv, j) : krow(p, g, hkv, j); /* j: token or channel */
+                    k_meta[mi * 2 + 0] = 0;
+                    k_meta[mi * 2 + 1] = 0;
                 }
                 memset(k0, 0, PG * sizeof(uint16_t));
                 memset(vc, 0, PG * 32);
@@ -292,15 +302,26 @@ static void pack_impl(const float *kprime, const uint16_t *v, const float *vf32,
                 const float *kp = kprime + ((size_t)base_tok * hkv + g) * HD; /* token stride hkv*HD */
                 for (int s = 0; s < nvalid; ++s)
                     k0[s] = orc_bf16_round_nearest(kp[(size_t)s * hkv * HD + 0]);
-                for (int j = 1; j < HD; ++j) {
-                    uint8_t *kc = k_codes + krow(p, g, hkv, j) * 32;
-                    uint16_t *km = k_meta + krow(p, g, hkv, j) * 2;
-                    grid_t gr = make_grid(kp + j, nvalid, hkv * HD);
-                    km[0] = gr.s_bits;
-                    km[1] = gr.z_bits;
+                if (!token_grid) {
+                    for (int j = 1; j < HD; ++j) {
+                        uint8_t *kc = k_codes + krow(p, g, hkv, j) * 32;
+                        uint16_t *km = k_meta + krow(p, g, hkv, j) * 2;
+                        grid_t gr = make_grid(kp + j, nvalid, hkv * HD);
+                        km[0] = gr.s_bits;
+                        km[1] = gr.z_bits;
+                        for (int s = 0; s < nvalid; ++s) {
+                            int c = code_of(kp[(size_t)s * hkv * HD + j], &gr);
+                            kc[s >> 2] |= (uint8_t)(c << (2 * (s & 3)));
+                        }
+                    }
+                } else {
                     for (int s = 0; s < nvalid; ++s) {
-                        int c = code_of(kp[(size_t)s * hkv * HD + j], &gr);
-                        kc[s >> 2] |= (uint8_t)(c << (2 * (s & 3)));
+                        const float *kt = kp + (size_t)s * hkv * HD;
+                        grid_t gr = make_grid(kt + 1, HD - 1, 1); /* channel 0 outside the range */
+                        k_meta[ktok(p, g, hkv, s) * 2 + 0] = gr.s_bits;
+                        k_meta[ktok(p, g, hkv, s) * 2 + 1] = gr.z_bits;
+                        for (int j = 1; j < HD; ++j)
+                            k_codes[krow(p, g, hkv, j) * 32 + (s >> 2)] |= (uint8_t)(code_of(kt[j], &gr) << (2 * (s & 3)));
                     }
                 }
                 for (int s = 0; s < nvalid; ++s) {
@@ -325,8 +346,20 @@ void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs,
                     const int32_t *page_table, int max_pages, uint8_t *k_codes, uint16_t *k_meta, uint16_t *k_ch0,
                     uint8_t *v_codes, uint16_t *v_meta)
 {
-    pack_impl(kprime, v, NULL, 1.0f, hkv, n_seqs, cu_tokens, page_table, max_pages, k_codes, k_meta, k_ch0, v_codes,
-              v_meta);
+    pack_impl(kprime, v, NULL, 1.0f, 0, hkv, n_seqs, cu_tokens, page_table, max_pages, k_codes, k_meta, k_ch0,
+              v_codes, v_meta);
+}
+
+/* The same pack with one key grid per token and KV head over channels
+ * 1..127 (§3.3: channel 0 kept in bf16 and left out of the range of the
+ * others); the per-token (scale, zero) pairs at ktok.  Values as
+ * orc_pack_cache.                                                            */
+void orc_pack_cache_tokgrid(const float *kprime, const uint16_t *v, int hkv, int n_seqs, const int32_t *cu_tokens,
+                            const int32_t *page_table, int max_pages, uint8_t *k_codes, uint16_t *k_meta,
+                            uint16_t *k_ch0, uint8_t *v_codes, uint16_t *v_meta)
+{
+    pack_impl(kprime, v, NULL, 1.0f, 1, hkv, n_seqs, cu_tokens, page_table, max_pages, k_codes, k_meta, k_ch0,
+              v_codes, v_meta);
 }
 
 /* The same pack with rotated values (§3.3, values paragraph, and App. B.2,
@@ -339,7 +372,7 @@ void orc_pack_cache_vrot(const float *kprime, const float *vprime, float clip, i
                          const int32_t *cu_tokens, const int32_t *page_table, int max_pages, uint8_t *k_codes,
                          uint16_t *k_meta, uint16_t *k_ch0, uint8_t *v_codes, uint16_t *v_meta)
 {
-    pack_impl(kprime, NULL, vprime, clip, hkv, n_seqs, cu_tokens, page_table, max_pages, k_codes, k_meta, k_ch0,
+    pack_impl(kprime, NULL, vprime, clip, 0, hkv, n_seqs, cu_tokens, page_table, max_pages, k_codes, k_meta, k_ch0,
               v_codes, v_meta);
 }
 
@@ -445,10 +478,10 @@ int orc_select_channels_base(const uint16_t *q, const float *t_q, const float *s
  * out_{h,c} = sum_t p_t v^_{t,c}, lse_h = max + log(sum exp).
  *   q_prime fp32 [B][Hq][128], sel_idx [B][Hkv][n_keep],
  *   page_table [B][max_pages], out fp64 [B][Hq][128], lse fp64 [B][Hq]     */
-int orc_decode_attn(const uint8_t *k_codes, const uint16_t *k_meta, const uint16_t *k_ch0, const uint8_t *v_codes,
-                    const uint16_t *v_meta, int hkv, const float *q_prime, const int32_t *sel_idx, int n_keep,
-                    int batch, int hq, const int32_t *page_table, int max_pages, const int32_t *seq_lens,
-                    double sm_scale, double *out, double *lse)
+static int decode_impl(const uint8_t *k_codes, const uint16_t *k_meta, const uint16_t *k_ch0, const uint8_t *v_codes,
+                       const uint16_t *v_meta, int token_grid, int hkv, const float *q_prime, const int32_t *sel_idx,
+                       int n_keep, int batch, int hq, const int32_t *page_table, int max_pages,
+                       const int32_t *seq_lens, double sm_scale, double *out, double *lse)
 {
     if (hkv <= 0 || hq % hkv || n_keep < 1 || n_keep > HD)
         return -2;
@@ -475,8 +508,9 @@ int orc_decode_attn(const uint8_t *k_codes, const uint16_t *k_meta, const uint16
                         kv = orc_bf16_value(k_ch0[pg * PG + s]);
                     } else {
                         size_t r = krow(p, g, hkv, j);
+                        size_t mi = token_grid ? ktok(p, g, hkv, s) : r;
                         int c = (k_codes[r * 32 + (s >> 2)] >> (2 * (s & 3))) & 3;
-                        kv = orc_dequant(c, k_meta[r * 2], k_meta[r * 2 + 1]);
+                        kv = orc_dequant(c, k_meta[mi * 2], k_meta[mi * 2 + 1]);
                     }
                     acc += (double)qp[j] * (double)kv;
                 }
@@ -510,6 +544,26 @@ int orc_decode_attn(const uint8_t *k_codes, const uint16_t *k_meta, const uint16
         free(logit);
     }
     return 0;
+}
+
+int orc_decode_attn(const uint8_t *k_codes, const uint16_t *k_meta, const uint16_t *k_ch0, const uint8_t *v_codes,
+                    const uint16_t *v_meta, int hkv, const float *q_prime, const int32_t *sel_idx, int n_keep,
+                    int batch, int hq, const int32_t *page_table, int max_pages, const int32_t *seq_lens,
+                    double sm_scale, double *out, double *lse)
+{
+    return decode_impl(k_codes, k_meta, k_ch0, v_codes, v_meta, 0, hkv, q_prime, sel_idx, n_keep, batch, hq,
+                       page_table, max_pages, seq_lens, sm_scale, out, lse);
+}
+
+/* orc_decode_attn over a cache packed with per-token key grids: k^_{t,j} =
+ * fmaf(code, s_t, z_t) with token t's own (scale, zero), j >= 1.           */
+int orc_decode_attn_tokgrid(const uint8_t *k_codes, const uint16_t *k_meta, const uint16_t *k_ch0,
+                            const uint8_t *v_codes, const uint16_t *v_meta, int hkv, const float *q_prime,
+                            const int32_t *sel_idx, int n_keep, int batch, int hq, const int32_t *page_table,
+                            int max_pages, const int32_t *seq_lens, double sm_scale, double *out, double *lse)
+{
+    return decode_impl(k_codes, k_meta, k_ch0, v_codes, v_meta, 1, hkv, q_prime, sel_idx, n_keep, batch, hq,
+                       page_table, max_pages, seq_lens, sm_scale, out, lse);
 }
 
 /* ------------------------------------------------------------------------ */

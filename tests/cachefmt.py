@@ -77,3 +77,30 @@ def gather_vparts(cache, page_table, b, L, g):
         ss.append(f16(cache.v_meta[p, g, 0])[grp].T)
         zs.append(f16(cache.v_meta[p, g, 1])[grp].T)
     return np.concatenate(cs)[:L], np.concatenate(ss)[:L], np.concatenate(zs)[:L]
+
+
+def k_token_meta(cache, p, g):
+    """Per-token key (scale, zero) of page p, KV head g in the per-token grid
+    layout k_meta [P/8][Hkv][8 slot][128 tok][2] (the block's metadata bytes
+    read token-major): fp32 arrays [128] each."""
+    flat = cache.k_meta.reshape(cache.k_meta.shape[0], cache.k_meta.shape[1], -1)   # [P/8][Hkv][2048]
+    m = flat[p >> 3, g].reshape(8, 128, 2)[p & 7]
+    return f16(m[:, 0]), f16(m[:, 1])
+
+
+def decode_k_tokgrid(cache, p, g):
+    """Dequantized k' of a page with per-token grids: [128 tok][128 ch] fp32."""
+    c = k_codes(cache, p, g).astype(np.float32).T             # [tok][ch]
+    s, z = k_token_meta(cache, p, g)
+    k = c * s[:, None] + z[:, None]
+    k[:, 0] = bf16(cache.k_ch0[p, g])
+    return k
+
+
+def gather_seq_tokgrid(cache, page_table, b, L, g):
+    ks, vs = [], []
+    for pi in range((L + 127) // 128):
+        p = int(page_table[b, pi])
+        ks.append(decode_k_tokgrid(cache, p, g))
+        vs.append(decode_v(cache, p, g))
+    return np.concatenate(ks)[:L], np.concatenate(vs)[:L]

@@ -30,6 +30,13 @@ void orc_pack_cache(const float *kprime, const uint16_t *v, int hkv, int n_seqs,
 void orc_pack_cache_vrot(const float *kprime, const float *vprime, float clip, int hkv, int n_seqs,
                          const int32_t *cu, const int32_t *pt, int max_pages, uint8_t *kc, uint16_t *km,
                          uint16_t *k0, uint8_t *vc, uint16_t *vm);
+void orc_pack_cache_tokgrid(const float *kprime, const uint16_t *v, int hkv, int n_seqs, const int32_t *cu,
+                            const int32_t *pt, int max_pages, uint8_t *kc, uint16_t *km, uint16_t *k0, uint8_t *vc,
+                            uint16_t *vm);
+int orc_decode_attn_tokgrid(const uint8_t *kc, const uint16_t *km, const uint16_t *k0, const uint8_t *vc,
+                            const uint16_t *vm, int hkv, const float *qp, const int32_t *sel, int n_keep, int batch,
+                            int hq, const int32_t *pt, int max_pages, const int32_t *lens, double sm, double *out,
+                            double *lse);
 int orc_value_unrotate(const double *o, const float *r_inv, int batch, int hq, int hkv, double *out);
 int orc_select_channels(const uint16_t *q, const float *t_q, int batch, int hq, int hkv, int n_keep, float *qp,
                         int32_t *sel);
@@ -176,6 +183,11 @@ static void run_case(int hkv, int grp, int n_seqs, const int32_t *lens, int n_ke
                           out, lse) == 0,
           "decode rc");
     CHECK(finite_all(out, (size_t)n_seqs * hq * HD) && finite_all(lse, (size_t)n_seqs * hq), "decode finite");
+    orc_pack_cache_tokgrid(kp, v, hkv, n_seqs, cu, pt, max_pages, c.kc, c.km, c.k0, c.vc, c.vm);
+    CHECK(orc_decode_attn_tokgrid(c.kc, c.km, c.k0, c.vc, c.vm, hkv, qp, sel, n_keep, n_seqs, hq, pt, max_pages,
+                                  lens, sm, out, lse) == 0,
+          "decode (per-token key grids) rc");
+    CHECK(finite_all(out, (size_t)n_seqs * hq * HD), "decode (per-token key grids) finite");
     orc_pack_cache_vrot(kp, vp, 0.92f, hkv, n_seqs, cu, pt, max_pages, c.kc, c.km, c.k0, c.vc, c.vm);
     CHECK(orc_decode_attn(c.kc, c.km, c.k0, c.vc, c.vm, hkv, qp, sel, n_keep, n_seqs, hq, pt, max_pages, lens, sm,
                           out, NULL) == 0,
