@@ -380,6 +380,39 @@ int dqk_select_decode_attn_vrot(const dqk_cache *c, const void *q_bf16, const fl
                                 float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
                                 float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Per-token key grids (§3.3 as the paper states it: one asymmetric INT2 grid
+ * per token and KV head over channels 1..127, channel 0 kept in bf16 and left
+ * out of the range).  The cache buffers are those of dqk_cache; only k_meta
+ * is read differently: the (scale, zero) pairs of a block's eight pages are
+ * token-major, [P/8][Hkv][8 slot][128 tok][2] fp16 (the same 4 KB per block
+ * and KV head).  A cache is written and read in one of the two layouts only.
+ */
+
+/*
+ * dqk_quantize_append with one key grid per (token, KV head): the grid of
+ * token t is fitted to k'_{t,1..127} (z = round-down of the minimum, s =
+ * round-up of (max - z)/3, both binary16), the codes are those of that grid.
+ * Channel 0 and the values as dqk_quantize_append.  Arguments, slots past a
+ * sequence's end and errors as dqk_quantize_append.
+ */
+int dqk_quantize_append_tokgrid(const dqk_cache *c, const void *k_bf16, const void *v_bf16, const void *t_k_bf16,
+                                int32_t n_seqs, const int32_t *cu_tokens, int64_t total_tokens,
+                                const int32_t *page_table, int32_t max_pages, float *kprime_dbg, hipStream_t stream);
+
+/*
+ * dqk_decode_attn over a cache written by dqk_quantize_append_tokgrid:
+ * k^_{t,j} = code * s_t + z_t for j >= 1.  On MFMA the dot product of the
+ * codes with q~ = C q' (two binary16 limbs, scaled once per split) is scaled
+ * per token by s_t, and z_t multiplies the fp32 sum of C q'_j over the
+ * selected channels; the rest as dqk_decode_attn.  Requires |C q'_j| s_t
+ * finite in fp32.  Arguments, workspace and errors as dqk_decode_attn.
+ */
+int dqk_decode_attn_tokgrid(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
+                            int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                            const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
+                            size_t ws_bytes, float *out, float *lse, hipStream_t stream);
+
 /*
  * dqk_stream_read -- measurement helper, not part of the attention path: a
  * plain streaming read of `bytes` bytes (a multiple of 16 KiB) at `src`,

@@ -101,6 +101,11 @@ def lib():
         L.dqk_select_channels_base.restype = ctypes.c_int
         L.dqk_value_unrotate.argtypes = [P, P, i32, i32, i32, P, P]
         L.dqk_value_unrotate.restype = ctypes.c_int
+        L.dqk_quantize_append_tokgrid.argtypes = [ctypes.POINTER(dqk_cache), P, P, P, i32, P, i64, P, i32, P, P]
+        L.dqk_quantize_append_tokgrid.restype = ctypes.c_int
+        L.dqk_decode_attn_tokgrid.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, P, i32, P,
+                                              ctypes.c_float, i32, P, sz, P, P, P]
+        L.dqk_decode_attn_tokgrid.restype = ctypes.c_int
         L.dqk_stream_read.argtypes = [P, sz, P, P]
         L.dqk_stream_read.restype = ctypes.c_int
         _lib = L
@@ -233,6 +238,15 @@ def dqk_quantize_append(cache: Cache, k, v, t_k, cu_tokens, page_table, kprime_d
     _check(rc, "dqk_quantize_append")
 
 
+def dqk_quantize_append_tokgrid(cache: Cache, k, v, t_k, cu_tokens, page_table, kprime_dbg=None, stream=None):
+    n_seqs = cu_tokens.numel() - 1
+    s = cache.struct()
+    rc = lib().dqk_quantize_append_tokgrid(ctypes.byref(s), _ptr(k), _ptr(v), _ptr(t_k), n_seqs, _ptr(cu_tokens),
+                                           int(k.shape[0]), _ptr(page_table), int(page_table.shape[1]),
+                                           _ptr(kprime_dbg), _stream(stream))
+    _check(rc, "dqk_quantize_append_tokgrid")
+
+
 def dqk_select_channels(q, t_q, hkv: int, n_keep: int, q_prime=None, sel_idx=None, stream=None):
     import torch
     B, hq = int(q.shape[0]), int(q.shape[1])
@@ -291,7 +305,9 @@ def _workspace(batch, hq, hkv, max_pages, num_splits, device):
 
 
 def dqk_decode_attn(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_scale: float, num_splits: int = 0,
-                    workspace=None, out=None, lse=None, want_lse: bool = True, stream=None):
+                    workspace=None, out=None, lse=None, want_lse: bool = True, stream=None, token_grid: bool = False):
+    """Decode over the INT2 cache; token_grid: the cache was written by
+    dqk_quantize_append_tokgrid (calls dqk_decode_attn_tokgrid)."""
     import torch
     B, hq = int(q_prime.shape[0]), int(q_prime.shape[1])
     n_keep = int(sel_idx.shape[2])
@@ -304,10 +320,11 @@ def dqk_decode_attn(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_sca
     if lse is None and want_lse:
         lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
     s = cache.struct()
-    rc = lib().dqk_decode_attn(ctypes.byref(s), _ptr(q_prime), _ptr(sel_idx), n_keep, B, hq, _ptr(page_table),
-                               max_pages, _ptr(seq_lens), float(sm_scale), int(num_splits), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream))
-    _check(rc, "dqk_decode_attn")
+    name = "dqk_decode_attn_tokgrid" if token_grid else "dqk_decode_attn"
+    rc = getattr(lib(), name)(ctypes.byref(s), _ptr(q_prime), _ptr(sel_idx), n_keep, B, hq, _ptr(page_table),
+                              max_pages, _ptr(seq_lens), float(sm_scale), int(num_splits), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream))
+    _check(rc, name)
     return out, lse
 
 

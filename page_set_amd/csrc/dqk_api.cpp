@@ -184,7 +184,7 @@ size_t dqk_decode_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t
 static int decode_core(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
                        int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
                        const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes,
-                       const float *r_inv, float *out, float *lse, hipStream_t stream) {
+                       const float *r_inv, float *out, float *lse, hipStream_t stream, bool token_grid = false) {
     int st = check_cache(c);
     if (st) return st;
     if (!q_prime || !sel_idx || !page_table || !seq_lens || !workspace || !out) return DQK_ERR_NULL;
@@ -202,6 +202,7 @@ static int decode_core(const dqk_cache *c, const float *q_prime, const int32_t *
     if (ws_bytes < (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float)) return DQK_ERR_WORKSPACE;
     dqk::DecodeArgs a{c,         q_prime,  sel_idx, n_keep, batch,  hq, hkv, page_table, max_pages, seq_lens,
                       sm_scale, splits, static_cast<float *>(workspace), out, lse};
+    a.token_grid = token_grid;
     hipError_t e = dqk::launch_decode_mfma(a, stream);
     if (e != hipSuccess) return hip_status(e);
     if (r_inv) return hip_status(dqk::launch_merge_unrotate(a.partials, batch, hq, hkv, splits, r_inv, out, lse, stream));
@@ -260,6 +261,31 @@ int dqk_decode_attn(const dqk_cache *c, const float *q_prime, const int32_t *sel
                     hipStream_t stream) {
     return decode_core(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale, num_splits,
                        workspace, ws_bytes, nullptr, out, lse, stream);
+}
+
+int dqk_decode_attn_tokgrid(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
+                            int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                            const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
+                            size_t ws_bytes, float *out, float *lse, hipStream_t stream) {
+    return decode_core(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale, num_splits,
+                       workspace, ws_bytes, nullptr, out, lse, stream, true);
+}
+
+int dqk_quantize_append_tokgrid(const dqk_cache *c, const void *k_bf16, const void *v_bf16, const void *t_k_bf16,
+                                int32_t n_seqs, const int32_t *cu_tokens, int64_t total_tokens,
+                                const int32_t *page_table, int32_t max_pages, float *kprime_dbg, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!k_bf16 || !v_bf16 || !t_k_bf16 || !cu_tokens || !page_table) return DQK_ERR_NULL;
+    if (n_seqs < 1 || max_pages < 1 || total_tokens < 1) return DQK_ERR_SHAPE;
+    if (n_seqs > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(t_k_bf16) || !aligned16(cu_tokens) ||
+        !aligned16(page_table) || (kprime_dbg && !aligned16(kprime_dbg)))
+        return DQK_ERR_ALIGN;
+    return hip_status(dqk::launch_append_tokgrid(*c, static_cast<const uint16_t *>(k_bf16),
+                                                 static_cast<const uint16_t *>(v_bf16),
+                                                 static_cast<const uint16_t *>(t_k_bf16), n_seqs, cu_tokens,
+                                                 page_table, max_pages, kprime_dbg, stream));
 }
 
 int dqk_select_decode_attn(const dqk_cache *c, const void *q_bf16, const float *t_q, int32_t n_keep, int32_t batch,

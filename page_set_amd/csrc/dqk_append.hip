@@ -41,6 +41,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NPW = 4;                     // logical pages per workgroup
@@ -95,6 +96,25 @@ __device__ __forceinline__ float wave_row_max(float x) {
 __device__ __forceinline__ uint32_t wave_row_or(uint32_t x) {
     x |= (uint32_t)__shfl_xor((int)x, 16);
     return x | (uint32_t)__shfl_xor((int)x, 32);
+}
+
+// Reductions over the 16 lanes of a DPP row (rotations by 8 and 4, then the
+// quad permutations xor 2 and xor 1 cover every lane of the row).
+template <int CTL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_min(float x) {
+    x = fminf(x, dpp<0x128>(x));  // row_ror:8
+    x = fminf(x, dpp<0x124>(x));  // row_ror:4
+    x = fminf(x, dpp<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+    return fminf(x, dpp<0xB1>(x));  // quad_perm [1, 0, 3, 2]
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp<0x128>(x));
+    x = fmaxf(x, dpp<0x124>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    return fmaxf(x, dpp<0xB1>(x));
 }
 
 // M^T of a bf16 [in ch][out ch] matrix into LDS rows of 256 bytes ([out ch][in
@@ -346,6 +366,135 @@ __device__ __forceinline__ void keys_of_page(const dqk_cache &c, uint32_t ks, co
         *reinterpret_cast<uint32_t *>(c.k_meta + krow(p, g, hkv, ch) * 2) = (uint32_t)gr.sb | ((uint32_t)gr.zb << 16);
 }
 
+// Keys of the page with one grid per token and KV head over channels 1..127
+// (§3.3 as the paper states it; channel 0 stays in bf16, outside the range).
+// A token's grid needs all its channels, so both channel tiles of the wave
+// are computed first.  Per-token extremes: in-lane over the lane's two
+// channels (channel 0 left out), over the 16 lanes of a row by DPP, over the
+// four waves through LDS, which reuses the key tile once every wave has read
+// it; thread t < 128 then fits token t's grid, writes its (scale, zero) and
+// leaves the thresholds in LDS for the code pass.
+template <bool FULL, bool DBG>
+__device__ __forceinline__ void keys_of_page_tok(const dqk_cache &c, uint32_t ks, const bf16x8 (&bop)[2][4],
+                                                 int64_t p, int g, int hkv, int nvalid, int64_t t0,
+                                                 float *__restrict__ kprime_dbg) {
+    const int tid = fresh_tid(), lane = tid & 63, w = tid >> 6;
+    const int G = lane >> 4, n = lane & 15;
+    f32x4 acc[2][8];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t arow = ks + (uint32_t)(32 * (n >> 2) + (n & 3)) * 256;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const uint32_t ak = arow + ((uint32_t)((4 * kk + G) ^ n) << 4);
+        bf16x8 aop[8];
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) aop[mt] = lds_ld<bf16x8>(ak + mt * 1024);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+                acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mt], bop[nt][kk], acc[nt][mt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const size_t pg = (size_t)p * hkv + g;
+    // lane holds tokens 32G .. 32G+31 of channels 32w + n (tile 0) and 32w + 16 + n (tile 1)
+    if (DBG && kprime_dbg) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = 32 * G + 4 * mt + r;
+                    if (FULL || tok < nvalid)
+                        kprime_dbg[((size_t)(t0 + tok) * hkv + g) * D + 32 * w + 16 * nt + n] = acc[nt][mt][r];
+                }
+    }
+    const bool has_ch0 = w == 0 && n == 0;  // tile 0 of this lane is channel 0
+    if (has_ch0) {
+        uint16_t *k0 = c.k_ch0 + pg * PG + 32 * G;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = 32 * G + 4 * mt + r;
+                k0[4 * mt + r] = (FULL || tok < nvalid) ? f2bf_rne(acc[0][mt][r]) : (uint16_t)0;
+            }
+    }
+    float mn[32], mx[32];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float a0 = acc[0][mt][r], a1 = acc[1][mt][r];
+            mn[4 * mt + r] = has_ch0 ? a1 : fminf(a0, a1);
+            mx[4 * mt + r] = has_ch0 ? a1 : fmaxf(a0, a1);
+        }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        mn[k] = row16_min(mn[k]);
+        mx[k] = row16_max(mx[k]);
+    }
+    __syncthreads();  // every wave has read the key tile: it now holds [4 waves][128 tokens][min, max]
+    if (n == 0) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            f32x2 e;
+            e[0] = mn[k];
+            e[1] = mx[k];
+            lds_st<f32x2>(ks + (uint32_t)((w * PG + 32 * G + k) * 8), e);
+        }
+    }
+    __syncthreads();
+    const uint32_t thr = ks + 4 * PG * 8;  // [128 tokens][4] thresholds after the extremes
+    if (tid < PG) {
+        float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const f32x2 e = lds_ld<f32x2>(ks + (uint32_t)((v * PG + tid) * 8));
+            lo = fminf(lo, e[0]);
+            hi = fmaxf(hi, e[1]);
+        }
+        const bool valid = FULL || tid < nvalid;
+        const Grid gr = make_grid(lo, hi);
+        const Thresholds th = thresholds(gr);
+        f32x4 t4;
+        t4[0] = th.t0;
+        t4[1] = th.t1;
+        t4[2] = th.t2;
+        t4[3] = 0.0f;
+        lds_st<f32x4>(thr + tid * 16, t4);
+        *reinterpret_cast<uint32_t *>(c.k_meta + ktok(p, g, hkv, tid) * 2) =
+            valid ? ((uint32_t)gr.sb | ((uint32_t)gr.zb << 16)) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int ch = 32 * w + 16 * nt + n;
+        uint32_t lo = 0, hi = 0;
+        if (ch != 0) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = 32 * G + 4 * mt + r;
+                    const f32x4 t4 = lds_ld<f32x4>(thr + tok * 16);
+                    const Thresholds th{t4[0], t4[1], t4[2]};
+                    const uint32_t cd = (FULL || tok < nvalid) ? code2(acc[nt][mt][r], th) : 0u;
+                    if (mt < 4)
+                        lo |= cd << (8 * mt + 2 * r);
+                    else
+                        hi |= cd << (8 * (mt - 4) + 2 * r);
+                }
+        }
+        *reinterpret_cast<uint64_t *>(c.k_codes + krow(p, g, hkv, ch) * ROW_BYTES + 8 * G) =
+            (uint64_t)lo | ((uint64_t)hi << 32);
+    }
+}
+
 // Where the pages of a launch come from.
 //   APPEND_PLAIN   sequence sq = blockIdx.y, tokens cu_tokens[sq] ..; logical
 //                  page i holds tokens 128 i .. (the last one may be partial).
@@ -372,9 +521,13 @@ __device__ __forceinline__ int64_t tier_pages_of(int64_t L) {
     return L >= TIER_SINK + TIER_RECENT ? (L - TIER_SINK - TIER_RECENT) / PG : 0;
 }
 
-// Rotated values keep a second set of fragments in VGPRs: two workgroups a CU.
-template <bool DBG, int MODE, bool VROT>
-__global__ __launch_bounds__(256, VROT ? 2 : 4) void append_kernel(dqk_cache c, AppendSrc src, const uint16_t *__restrict__ t_k,
+// Variants: plain; rotated values (a second set of fragments in VGPRs);
+// per-token key grids (both channel tiles' accumulators live at once).  The
+// last two run two workgroups a CU.
+enum { VAR_PLAIN = 0, VAR_VROT = 1, VAR_TOKGRID = 2 };
+
+template <bool DBG, int MODE, int VAR>
+__global__ __launch_bounds__(256, VAR == VAR_PLAIN ? 4 : 2) void append_kernel(dqk_cache c, AppendSrc src, const uint16_t *__restrict__ t_k,
                                                      const int32_t *__restrict__ page_table, int max_pages,
                                                      float *__restrict__ kprime_dbg) {
     // T_K^T [out ch][in ch] first, then each page's key tile [token][in ch]; rows of 256 bytes
@@ -407,7 +560,7 @@ __global__ __launch_bounds__(256, VROT ? 2 : 4) void append_kernel(dqk_cache c, 
     bf16x8 bop[2][4];  // [channel tile][k-step]
     load_frags(ks, bop);
     bf16x8 rop[2][4];
-    if constexpr (VROT) {
+    if constexpr (VAR == VAR_VROT) {
         __syncthreads();
         stage_transposed(src.r_v + (size_t)g * D * D, ks);
         __syncthreads();
@@ -459,7 +612,7 @@ __global__ __launch_bounds__(256, VROT ? 2 : 4) void append_kernel(dqk_cache c, 
 
         // ---- values: unit k is (token t, group q0 + 2 k), consecutive lanes on
         //      consecutive tokens; both units of a lane share the token
-        if constexpr (!VROT) {
+        if constexpr (VAR != VAR_VROT) {
             if (nvalid == PG)
                 values_of_page<true>(c, vpage, kstride, tid, pg, nvalid);
             else
@@ -467,15 +620,22 @@ __global__ __launch_bounds__(256, VROT ? 2 : 4) void append_kernel(dqk_cache c, 
         }
 
         wait_all_barrier();  // the tile has landed
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        if constexpr (VAR == VAR_TOKGRID) {
             if (nvalid == PG)
-                keys_of_page<true, DBG>(c, ks, bop[nt], nt, p, g, hkv, nvalid, t0, kprime_dbg);
+                keys_of_page_tok<true, DBG>(c, ks, bop, p, g, hkv, nvalid, t0, kprime_dbg);
             else
-                keys_of_page<false, DBG>(c, ks, bop[nt], nt, p, g, hkv, nvalid, t0, kprime_dbg);
-            __builtin_amdgcn_sched_barrier(0);  // one channel tile's accumulators live at a time
+                keys_of_page_tok<false, DBG>(c, ks, bop, p, g, hkv, nvalid, t0, kprime_dbg);
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                if (nvalid == PG)
+                    keys_of_page<true, DBG>(c, ks, bop[nt], nt, p, g, hkv, nvalid, t0, kprime_dbg);
+                else
+                    keys_of_page<false, DBG>(c, ks, bop[nt], nt, p, g, hkv, nvalid, t0, kprime_dbg);
+                __builtin_amdgcn_sched_barrier(0);  // one channel tile's accumulators live at a time
+            }
         }
-        if constexpr (VROT) {
+        if constexpr (VAR == VAR_VROT) {
             __syncthreads();  // every wave has read the key tile
             // ---- value tile: load i of wave w covers rows 32 w + 4 i + G, LDS slot
             //      lane & 15 of a row receiving input chunk slot ^ swz_v(row)
@@ -505,10 +665,10 @@ hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *
     dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
     const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr, nullptr, 1.0f, nullptr};
     if (kprime_dbg)
-        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN, false>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN, VAR_PLAIN>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                            max_pages, kprime_dbg);
     else
-        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, false>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, VAR_PLAIN>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                            max_pages, kprime_dbg);
     return hipGetLastError();
 }
@@ -518,7 +678,7 @@ hipError_t launch_append_tiered(const dqk_cache &c, const uint16_t *k, const uin
                                 hipStream_t s) {
     dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
     const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr, nullptr, 1.0f, nullptr};
-    hipLaunchKernelGGL((append_kernel<false, APPEND_TIERED, false>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+    hipLaunchKernelGGL((append_kernel<false, APPEND_TIERED, VAR_PLAIN>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                        max_pages, nullptr);
     return hipGetLastError();
 }
@@ -530,10 +690,24 @@ hipError_t launch_append_vrot(const dqk_cache &c, const uint16_t *k, const uint1
     dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
     const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr, r_v, clip, vprime_dbg};
     if (kprime_dbg || vprime_dbg)
-        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN, true>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN, VAR_VROT>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                            max_pages, kprime_dbg);
     else
-        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, true>), grid, dim3(256), 0, s, c, src, t_k,
+        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, VAR_VROT>), grid, dim3(256), 0, s, c, src, t_k,
+                           page_table, max_pages, kprime_dbg);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_tokgrid(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                                 int n_seqs, const int32_t *cu_tokens, const int32_t *page_table, int max_pages,
+                                 float *kprime_dbg, hipStream_t s) {
+    dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
+    const AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr, nullptr, 1.0f, nullptr};
+    if (kprime_dbg)
+        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN, VAR_TOKGRID>), grid, dim3(256), 0, s, c, src, t_k,
+                           page_table, max_pages, kprime_dbg);
+    else
+        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, VAR_TOKGRID>), grid, dim3(256), 0, s, c, src, t_k,
                            page_table, max_pages, kprime_dbg);
     return hipGetLastError();
 }
@@ -542,7 +716,7 @@ hipError_t launch_pack_tail(const dqk_cache &c, const dqk_tiers &t, const uint16
                             const int32_t *lens_before, const int32_t *page_table, int max_pages, hipStream_t s) {
     dim3 grid(1, batch, c.num_kv_heads);
     const AppendSrc src{nullptr, nullptr, nullptr, lens_before, t.tail_kraw, t.tail_v, nullptr, 1.0f, nullptr};
-    hipLaunchKernelGGL((append_kernel<false, APPEND_TAIL, false>), grid, dim3(256), 0, s, c, src, t_k, page_table,
+    hipLaunchKernelGGL((append_kernel<false, APPEND_TAIL, VAR_PLAIN>), grid, dim3(256), 0, s, c, src, t_k, page_table,
                        max_pages, nullptr);
     return hipGetLastError();
 }

@@ -59,15 +59,21 @@ constexpr float LN2 = 0.6931471805599453f;
 static_assert(KBLK == 8, "the kernel walks 8-page blocks in halves of four pages");
 
 // ---------------------------------------------------------------- LDS layout
-template <int KS>
+// KSX = KS + 16 KG: KS 16-channel k-steps; KG = 1 for one key grid per token
+// (the block's key metadata then is [8 pages][128 tokens] pairs, 4 KB).
+template <int KSX>
 struct Lay {
+    static constexpr int KS = KSX & 15;
+    static constexpr bool KG = (KSX >> 4) != 0;
     static constexpr int NR = 16 * KS;              // key row slots (selected INT2 channels, padded)
     static constexpr int NMR = (NR + 31) / 32 * 32;  // key metadata rows (whole load instructions)
     // key stage: rows [NR][256 B] (16-byte chunk c of row r at c ^ (2 ((r >> 3) & 1))),
-    // metadata [NMR][8 pages] (scale | zero << 16), channel 0 [8 pages][128] bf16
+    // metadata [NMR][8 pages] (scale | zero << 16) or, KG, [8 pages][128 tokens],
+    // channel 0 [8 pages][128] bf16
+    static constexpr int KMB = KG ? KBLK * PG * 4 : NMR * 32;
     static constexpr int KC = 0;
     static constexpr int KM = KC + NR * 256;
-    static constexpr int K0 = KM + NMR * 32;
+    static constexpr int K0 = KM + KMB;
     static constexpr int KST = K0 + 2048;
     // value stage: codes [token group G 4][32-token step 4][4 pages][8 tokens][32 B], each
     // group followed by 64 bytes of padding (the four groups read together fall in
@@ -104,7 +110,7 @@ struct Lay {
     // global -> LDS loads: a key block is NRI row, NMI metadata and 2 channel-0
     // instructions; a value half is 16 code and 8 metadata instructions
     static constexpr int NRI = NR / 4;
-    static constexpr int NMI = NMR / 32;
+    static constexpr int NMI = KMB / 1024;
     static constexpr int NKI = NRI + NMI + 2;
     static constexpr int KN = (NKI + NW - 1) / NW;  // key instructions per wave per block
     static constexpr int VN = 24 / NW;              // value instructions per wave per half
@@ -242,7 +248,9 @@ __device__ __forceinline__ uint32_t key_lds(int idx) {
 template <int KS>
 __device__ __forceinline__ int key_row(int idx, int lane) {
     using Ly = Lay<KS>;
-    return idx < Ly::NRI ? 4 * idx + (lane >> 4) : idx < Ly::NRI + Ly::NMI ? 32 * (idx - Ly::NRI) + (lane >> 1) : 0;
+    return idx < Ly::NRI                            ? 4 * idx + (lane >> 4)
+           : idx < Ly::NRI + Ly::NMI && !Ly::KG ? 32 * (idx - Ly::NRI) + (lane >> 1)
+                                                  : 0;
 }
 // Per-lane byte offset of key instruction idx from the base of an aligned block.
 template <int KS>
@@ -253,7 +261,8 @@ __device__ __forceinline__ uint32_t key_aoff(int idx, int lane, int chan, int hk
         const int cd = (lane & 15) ^ (2 * ((r >> 3) & 1));
         return (uint32_t)(chan * (KBLK * ROW_BYTES) + cd * 16);
     }
-    if (idx < Ly::NRI + Ly::NMI) return (uint32_t)(chan * (KBLK * 4) + (lane & 1) * 16);
+    if (idx < Ly::NRI + Ly::NMI)  // per channel: two lanes a row; per token: 1 KB of the block's 4 KB
+        return Ly::KG ? (uint32_t)((idx - Ly::NRI) * 1024 + lane * 16) : (uint32_t)(chan * (KBLK * 4) + (lane & 1) * 16);
     const int i = idx - Ly::NRI - Ly::NMI;
     return (uint32_t)(4 * i + (lane >> 4)) * (uint32_t)(hkv * PG * 2) + (uint32_t)((lane & 15) * 16);
 }
@@ -337,10 +346,15 @@ __device__ __forceinline__ void slow_key(int idx, int lane, int chan, const Bloc
         const int pp = p(cd >> 1);
         v = *reinterpret_cast<const u32x4 *>(c.k_codes + krow(pp, g, hkv, chan) * ROW_BYTES + (cd & 1) * 16);
     } else if (idx < Ly::NRI + Ly::NMI) {
-        const int h = lane & 1;
+        if constexpr (Ly::KG) {  // bytes 1024 j + 16 lane of the block: page slot 2 j + lane / 32, 4 tokens
+            const int j = idx - Ly::NRI;
+            v = *reinterpret_cast<const u32x4 *>(c.k_meta + ktok(p(2 * j + (lane >> 5)), g, hkv, (lane & 31) * 4) * 2);
+        } else {
+            const int h = lane & 1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v[i] = *reinterpret_cast<const uint32_t *>(c.k_meta + krow(p(4 * h + i), g, hkv, chan) * 2);
+            for (int i = 0; i < 4; ++i)
+                v[i] = *reinterpret_cast<const uint32_t *>(c.k_meta + krow(p(4 * h + i), g, hkv, chan) * 2);
+        }
     } else {
         const int i = idx - Ly::NRI - Ly::NMI;
         const int pp = p(4 * i + (lane >> 4));
@@ -566,7 +580,7 @@ __device__ __forceinline__ void select_into_lds(uint32_t S, uint32_t scr, const 
     }
 }
 
-template <int KS, bool FUSED>
+template <int KSX, bool FUSED>
 __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const float *__restrict__ q_prime,
                                                           const int32_t *__restrict__ sel_idx, int n_keep, int hq,
                                                           const int32_t *__restrict__ page_table, int max_pages,
@@ -577,7 +591,9 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                                                           const float *__restrict__ sel_scale,
                                                           float *__restrict__ qp_out,
                                                           int32_t *__restrict__ sel_out) {
-    using Ly = Lay<KS>;
+    using Ly = Lay<KSX>;
+    constexpr int KS = Ly::KS;
+    constexpr bool KG = Ly::KG;
     __shared__ __attribute__((aligned(16))) uint8_t smem[Ly::TOTAL];
     const uint32_t S = lds_addr(smem);
 
@@ -606,7 +622,7 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const size_t hstride = (size_t)nsplit * PART_FLOATS;
 
     if (FUSED && nb <= 0 && split == 0) {  // still deliver the selection of this (sequence, KV head)
-        select_into_lds<KS>(S, S + Ly::SCR, q_bf16, t_q, sel_scale ? sel_scale + (size_t)g * D : nullptr, b, g, hq,
+        select_into_lds<KSX>(S, S + Ly::SCR, q_bf16, t_q, sel_scale ? sel_scale + (size_t)g * D : nullptr, b, g, hq,
                             hkv, n_keep, qp_out, sel_out);
     }
     if (nb <= 0) {  // nothing of this sequence falls in this split: an empty partial
@@ -624,7 +640,7 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     auto page_valid = [&](int j, int ps) { return min(PG, max(0, L - PG * (KBLK * (B0 + j) + ps))); };
 
     // ---- the loader: value plans first (they do not depend on the selection)
-    Feeder<KS> fd;
+    Feeder<KSX> fd;
     fd.S = S;
     fd.c = &c;
     fd.ptab = ptab;
@@ -645,7 +661,7 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const uint32_t scr = S + Ly::SCR;
     if constexpr (FUSED) {
         static_assert(Ly::FUSABLE, "selection scratch");
-        select_into_lds<KS>(S, scr, q_bf16, t_q, sel_scale ? sel_scale + (size_t)g * D : nullptr, b, g, hq, hkv,
+        select_into_lds<KSX>(S, scr, q_bf16, t_q, sel_scale ? sel_scale + (size_t)g * D : nullptr, b, g, hq, hkv,
                             n_keep, split == 0 ? qp_out : nullptr, split == 0 ? sel_out : nullptr);
         for (int i = tid; i < KS * 64; i += NTHR) lds_st<uint32_t>(S + Ly::ZERO + i * 4, 0u);
         if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
@@ -700,18 +716,12 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
         const int tok0 = 64 * tgc + 16 * Gk + 2 * ll;       // this lane's tokens: tok0 + 4 r + mm
         float m_run = -__builtin_huge_valf();  // integer running maximum (log2 units) of head hh
         float l32 = 0.0f;                      // fp32 sum of 2^(x - m) over this lane's tokens
-
-        for (int u = 0; u <= nst; ++u) {
-            fd.top(u, halfpages);
-            if (u >= nst) continue;
-            const int ps = 4 * (u & 1) + w;
-            const int nv = page_valid(u >> 1, ps);
-            if (nv <= 0) continue;
-            const uint32_t kst = fd.kstage(u >> 1);
-
-            // ---- q~ limbs of the page into this wave's fragments, bias sum_j z_j C q'_j in fp32.
-            //      q~ is scaled by 2^kq (largest |q~| of the page near 2^14) so that its
-            //      products with the codes stay far above the binary16 subnormal range.
+        // ---- per-token key grids: the q~ limbs (q~_j = C q'_j, scaled by 2^kq as
+        //      below) and the bias sum_j C q'_j, once per split; each token then
+        //      scales its dot product by s_t and the bias by z_t.  The per-channel
+        //      form in the loop is the same computation with the page's scales and
+        //      zero points.
+        auto prep_qt = [&](float &bias, float &comp0, float &comp1) {
             float bacc = 0.0f, vmax = 0.0f;
             float vq[NPI][2];
 #pragma unroll
@@ -719,13 +729,11 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                 const int c0 = 2 * (j16 + 16 * i);
                 vq[i][0] = vq[i][1] = 0.0f;
                 if (c0 < 16 * KS) {
-                    const uint32_t d0 = lds_ld<uint32_t>(kst + Ly::KM + c0 * 32 + ps * 4);
-                    const uint32_t d1 = lds_ld<uint32_t>(kst + Ly::KM + (c0 + 1) * 32 + ps * 4);
-                    vq[i][0] = QC[i][0] * h2f(d0 & 0xFFFFu);
-                    vq[i][1] = QC[i][1] * h2f(d1 & 0xFFFFu);
+                    vq[i][0] = QC[i][0];
+                    vq[i][1] = QC[i][1];
                     vmax = fmaxf(vmax, fmaxf(__builtin_fabsf(vq[i][0]), __builtin_fabsf(vq[i][1])));
-                    bacc = __builtin_fmaf(QC[i][0], h2f(d0 >> 16), bacc);
-                    bacc = __builtin_fmaf(QC[i][1], h2f(d1 >> 16), bacc);
+                    bacc += QC[i][0];
+                    bacc += QC[i][1];
                 }
             }
             vmax = fmaxf(vmax, dpp<DPP_XOR1>(vmax));
@@ -751,15 +759,86 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                 }
             }
             // code units: tiles 0, 2 at 2^-20, tiles 1, 3 at 2^-18; undo them and 2^kq
-            const float comp0 = __uint_as_float((uint32_t)(127 + 20 - kq) << 23);
-            const float comp1 = __uint_as_float((uint32_t)(127 + 18 - kq) << 23);
+            comp0 = __uint_as_float((uint32_t)(127 + 20 - kq) << 23);
+            comp1 = __uint_as_float((uint32_t)(127 + 18 - kq) << 23);
             bacc += dpp<DPP_XOR1>(bacc);
             bacc += dpp<DPP_XOR2>(bacc);
             bacc += dpp<DPP_ROR4>(bacc);
             bacc += dpp<DPP_ROR8>(bacc);  // every lane of row h holds head h's bias
             const float b0 = bcast_lane(bacc, 0), b1 = bcast_lane(bacc, 16), b2 = bcast_lane(bacc, 32),
                         b3 = bcast_lane(bacc, 48);
-            const float bias = hh == 0 ? b0 : hh == 1 ? b1 : hh == 2 ? b2 : b3;
+            bias = hh == 0 ? b0 : hh == 1 ? b1 : hh == 2 ? b2 : b3;
+        };
+        float bias_t = 0.0f, comp0_t = 0.0f, comp1_t = 0.0f;  // per-token key grids: fixed for the split
+        if constexpr (KG) prep_qt(bias_t, comp0_t, comp1_t);
+
+
+        for (int u = 0; u <= nst; ++u) {
+            fd.top(u, halfpages);
+            if (u >= nst) continue;
+            const int ps = 4 * (u & 1) + w;
+            const int nv = page_valid(u >> 1, ps);
+            if (nv <= 0) continue;
+            const uint32_t kst = fd.kstage(u >> 1);
+
+            float bias, comp0, comp1;
+            if constexpr (KG) {
+                bias = bias_t;
+                comp0 = comp0_t;
+                comp1 = comp1_t;
+            } else {
+                // ---- q~ limbs of the page into this wave's fragments, bias sum_j z_j C q'_j in fp32.
+                //      q~ is scaled by 2^kq (largest |q~| of the page near 2^14) so that its
+                //      products with the codes stay far above the binary16 subnormal range.
+                float bacc = 0.0f, vmax = 0.0f;
+                float vq[NPI][2];
+    #pragma unroll
+                for (int i = 0; i < NPI; ++i) {
+                    const int c0 = 2 * (j16 + 16 * i);
+                    vq[i][0] = vq[i][1] = 0.0f;
+                    if (c0 < 16 * KS) {
+                        const uint32_t d0 = lds_ld<uint32_t>(kst + Ly::KM + c0 * 32 + ps * 4);
+                        const uint32_t d1 = lds_ld<uint32_t>(kst + Ly::KM + (c0 + 1) * 32 + ps * 4);
+                        vq[i][0] = QC[i][0] * h2f(d0 & 0xFFFFu);
+                        vq[i][1] = QC[i][1] * h2f(d1 & 0xFFFFu);
+                        vmax = fmaxf(vmax, fmaxf(__builtin_fabsf(vq[i][0]), __builtin_fabsf(vq[i][1])));
+                        bacc = __builtin_fmaf(QC[i][0], h2f(d0 >> 16), bacc);
+                        bacc = __builtin_fmaf(QC[i][1], h2f(d1 >> 16), bacc);
+                    }
+                }
+                vmax = fmaxf(vmax, dpp<DPP_XOR1>(vmax));
+                vmax = fmaxf(vmax, dpp<DPP_XOR2>(vmax));
+                vmax = fmaxf(vmax, dpp<DPP_ROR4>(vmax));
+                vmax = fmaxf(vmax, dpp<DPP_ROR8>(vmax));
+                vmax = max_x32(max_x16(vmax));
+                const int ev = (int)((__float_as_uint(vmax) >> 23) & 255u) - 127;  // floor(log2 vmax)
+                const int kq = vmax > 0.0f ? min(100, max(-100, 14 - ev)) : 0;
+                const float sq = __uint_as_float((uint32_t)(127 + kq) << 23);
+    #pragma unroll
+                for (int i = 0; i < NPI; ++i) {
+                    const int c0 = 2 * (j16 + 16 * i);
+                    if (c0 < 16 * KS) {
+                        const float v0 = vq[i][0] * sq, v1 = vq[i][1] * sq;
+                        const _Float16 hi0 = (_Float16)v0, hi1 = (_Float16)v1;
+                        const uint32_t off = (c0 >> 4) * 256 + ((c0 >> 3) & 1) * 128 + hp * 32 + (c0 & 7) * 2;
+                        half2v hi;
+                        hi[0] = hi0;
+                        hi[1] = hi1;
+                        lds_st<uint32_t>(qt_w + off, as_u32(hi));
+                        lds_st<uint32_t>(qt_w + off + 16, pack_h2(v0 - (float)hi0, v1 - (float)hi1));
+                    }
+                }
+                // code units: tiles 0, 2 at 2^-20, tiles 1, 3 at 2^-18; undo them and 2^kq
+                comp0 = __uint_as_float((uint32_t)(127 + 20 - kq) << 23);
+                comp1 = __uint_as_float((uint32_t)(127 + 18 - kq) << 23);
+                bacc += dpp<DPP_XOR1>(bacc);
+                bacc += dpp<DPP_XOR2>(bacc);
+                bacc += dpp<DPP_ROR4>(bacc);
+                bacc += dpp<DPP_ROR8>(bacc);  // every lane of row h holds head h's bias
+                const float b0 = bcast_lane(bacc, 0), b1 = bcast_lane(bacc, 16), b2 = bcast_lane(bacc, 32),
+                            b3 = bcast_lane(bacc, 48);
+                bias = hh == 0 ? b0 : hh == 1 ? b1 : hh == 2 ? b2 : b3;
+            }
 
             // ---- scores: four token tiles
             f32x4 Sc[4];
@@ -790,11 +869,18 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const uint32_t kw = lds_ld<uint32_t>(k0a + r * 8);
+                u32x2 szt = {0u, 0u};  // per-token key grids: (scale, zero) of tokens tok0 + 4 r + {0, 1}
+                if constexpr (KG) szt = lds_ld<u32x2>(kst + Ly::KM + (uint32_t)(ps * PG + tok0 + 4 * r) * 4);
 #pragma unroll
                 for (int mm = 0; mm < 2; ++mm) {
                     const float mine = ll ? Sc[2 + mm][r] : Sc[mm][r];
                     const float give = ll ? Sc[mm][r] : Sc[2 + mm][r];
-                    float v = __builtin_fmaf(mine + dpp<DPP_XOR1>(give), mm ? comp1 : comp0, bias);
+                    float cm = mm ? comp1 : comp0, bz = bias;
+                    if constexpr (KG) {
+                        cm *= h2f(szt[mm] & 0xFFFFu);
+                        bz *= h2f(szt[mm] >> 16);
+                    }
+                    float v = __builtin_fmaf(mine + dpp<DPP_XOR1>(give), cm, bz);
                     v = __builtin_fmaf(q0c, __uint_as_float(mm ? (kw & 0xFFFF0000u) : (kw << 16)), v);
                     x[r][mm] = v;
                 }
@@ -1066,10 +1152,10 @@ bool fused_select_ok(int hq, int hkv, int n_keep) {
     }
 }
 
-template <int KS, bool FUSED>
+template <int KSX, bool FUSED>
 static hipError_t launch_ks2(const DecodeArgs &a, hipStream_t s) {
     dim3 grid(a.num_splits, a.batch * a.hkv * mfma_head_sets(a.hq, a.hkv));
-    hipLaunchKernelGGL((decode_blk_kernel<KS, FUSED>), grid, dim3(NTHR), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep,
+    hipLaunchKernelGGL((decode_blk_kernel<KSX, FUSED>), grid, dim3(NTHR), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep,
                        a.hq, a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials, a.q_bf16,
                        a.t_q, a.sel_scale, a.qp_out, a.sel_out);
     return hipGetLastError();
@@ -1077,6 +1163,10 @@ static hipError_t launch_ks2(const DecodeArgs &a, hipStream_t s) {
 
 template <int KS>
 static hipError_t launch_ks(const DecodeArgs &a, hipStream_t s) {
+    if (a.token_grid) {  // per-token key grids: the selection is a launch of its own
+        if (a.q_bf16) return hipErrorInvalidValue;
+        return launch_ks2<KS + 16, false>(a, s);
+    }
     if constexpr (Lay<KS>::FUSABLE) {
         if (a.q_bf16) return launch_ks2<KS, true>(a, s);
     } else {

@@ -30,6 +30,13 @@ __host__ __device__ __forceinline__ size_t krow(int64_t p, int g, int hkv, int j
     return ((((size_t)(p / KBLK) * (size_t)hkv + (size_t)g) * D + (size_t)j) * KBLK) + (size_t)(p % KBLK);
 }
 
+// With one key grid per token (the layout of dqk_quantize_append_tokgrid):
+// index of the (scale, zero) pair of token s of physical page p, KV head g --
+// the block's key metadata read token-major, [P/8][Hkv][8 slot][128 tok][2].
+__host__ __device__ __forceinline__ size_t ktok(int64_t p, int g, int hkv, int s) {
+    return (((size_t)(p / KBLK) * (size_t)hkv + (size_t)g) * KBLK + (size_t)(p % KBLK)) * PG + (size_t)s;
+}
+
 // Partial of one (b, h, split): o[128] (unnormalised, relative to m), m (natural
 // log units), l (the denominator matching o), l32 (fp32 sum of the unrounded
 // probabilities, for the log-sum-exp), pad.
@@ -215,6 +222,9 @@ hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *
 hipError_t launch_append_tiered(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
                                 int n_seqs, const int32_t *cu_tokens, const int32_t *page_table, int max_pages,
                                 hipStream_t s);
+hipError_t launch_append_tokgrid(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                                 int n_seqs, const int32_t *cu_tokens, const int32_t *page_table, int max_pages,
+                                 float *kprime_dbg, hipStream_t s);
 hipError_t launch_append_vrot(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
                               const uint16_t *r_v, float clip, int n_seqs, const int32_t *cu_tokens,
                               const int32_t *page_table, int max_pages, float *kprime_dbg, float *vprime_dbg,
@@ -256,6 +266,8 @@ struct DecodeArgs {
     int32_t *sel_out = nullptr;
     // selection in base coordinates (fused selection only): fp32 [hkv][128] or null
     const float *sel_scale = nullptr;
+    // one key grid per token (dqk_quantize_append_tokgrid's layout)
+    bool token_grid = false;
 };
 
 // Query heads per KV head that the decode entry points serve.
@@ -294,6 +306,8 @@ struct DecodeBf16Args {
     int32_t *sel_out = nullptr;
     // selection in base coordinates (fused selection only): fp32 [hkv][128] or null
     const float *sel_scale = nullptr;
+    // one key grid per token (dqk_quantize_append_tokgrid's layout)
+    bool token_grid = false;
 };
 
 hipError_t launch_decode_bf16(const DecodeBf16Args &a, hipStream_t s);

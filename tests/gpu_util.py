@@ -55,7 +55,7 @@ def row_rel_err(got, want):
     return num / np.maximum(den, 1e-30)
 
 
-def lse_bound(cache, qp, sel, page_table, seq_lens, sm_scale, lse_ref):
+def lse_bound(cache, qp, sel, page_table, seq_lens, sm_scale, lse_ref, gather=None):
     """Allowed |lse_gpu - lse_oracle| per (b, h) row.
 
     The kernels form each logit as an fp32 sum over the selected channels of
@@ -66,6 +66,7 @@ def lse_bound(cache, qp, sel, page_table, seq_lens, sm_scale, lse_ref):
     mean of the logits, so its error is bounded by the largest logit error,
     plus the fp32 rounding of exp2/log2 and of the merge (2^-20 |lse|)."""
     from tests import cachefmt as cf
+    gather = gather or cf.gather_seq
     B, hq = qp.shape[0], qp.shape[1]
     hkv = sel.shape[1]
     grp = hq // hkv
@@ -73,7 +74,7 @@ def lse_bound(cache, qp, sel, page_table, seq_lens, sm_scale, lse_ref):
     for b in range(B):
         L = int(seq_lens[b])
         for g in range(hkv):
-            kh, _ = cf.gather_seq(cache, page_table, b, L, g)
+            kh, _ = gather(cache, page_table, b, L, g)
             mask = np.zeros(128)
             mask[sel[b, g]] = 1.0
             qa = np.abs(qp[b, g * grp:(g + 1) * grp].astype(np.float64)) * mask
@@ -86,7 +87,7 @@ def assert_lse(lse, lse_ref, bound):
     assert (err <= bound).all(), f"lse error {err.max():.3e} above the derived bound (worst ratio {(err / bound).max():.2f})"
 
 
-def split_bound(cache, qp, sel, page_table, seq_lens, sm_scale):
+def split_bound(cache, qp, sel, page_table, seq_lens, sm_scale, gather=None):
     """Allowed |o(one split count) - o(another)| per (b, h, channel) for the
     group-4 MFMA decode.
 
@@ -102,6 +103,7 @@ def split_bound(cache, qp, sel, page_table, seq_lens, sm_scale):
       + L 2^-38 max_t |v_t|                                  subnormal P,
     two splits by twice that."""
     from tests import cachefmt as cf
+    gather = gather or cf.gather_seq
     u = 2.0 ** -11
     B, hq = qp.shape[0], qp.shape[1]
     hkv = sel.shape[1]
@@ -110,7 +112,7 @@ def split_bound(cache, qp, sel, page_table, seq_lens, sm_scale):
     for b in range(B):
         L = int(seq_lens[b])
         for g in range(hkv):
-            kh, vh = cf.gather_seq(cache, page_table, b, L, g)
+            kh, vh = gather(cache, page_table, b, L, g)
             codes, sc, zp = cf.gather_vparts(cache, page_table, b, L, g)
             mask = np.zeros(128)
             mask[sel[b, g]] = 1.0
