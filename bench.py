@@ -562,6 +562,99 @@ def vrot_record(shape, seed, pa, torch, steps, clip=0.92):
             "append": app}
 
 
+def tokgrid_record(shape, seed, pa, torch, steps):
+    """The headline workload with one key grid per token (the paper's key
+    format): the cache is built sequence by sequence with
+    dqk_quantize_append_tokgrid (HIP events), then a step is one
+    dqk_select_decode_attn_tokgrid call over cache copies rotated as in the
+    headline; the same step as two calls (dqk_select_channels +
+    dqk_decode_attn_tokgrid) is reported beside it."""
+    from page_set_amd import traffic
+    prob = synth.make_problem(shape, seed, materialize_kv=False)
+    B, hq, hkv, n_keep = shape.batch, shape.hq, shape.hkv, shape.n_keep
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    q, t_q, t_k = dev(prob.q.view(np.int16)), dev(prob.t_q), dev(prob.t_k.view(np.int16))
+    pt, lens = dev(prob.page_table), dev(prob.seq_lens)
+    mp = int(prob.page_table.shape[1])
+    stream = torch.cuda.current_stream()
+    cache = pa.Cache(prob.num_pages, hkv)
+    app_s, tokens = 0.0, 0
+    for b in range(B):
+        kb, vb = synth.make_kv_seq(shape, seed, b, prob.outliers)
+        L = kb.shape[0]
+        k_d, v_d = dev(kb.view(np.int16)), dev(vb.view(np.int16))
+        cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        ptb = pt[b:b + 1].clone()
+        if b == 0:  # untimed first call
+            pa.dqk_quantize_append_tokgrid(cache, k_d, v_d, t_k, cu, ptb, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pa.dqk_quantize_append_tokgrid(cache, k_d, v_d, t_k, cu, ptb, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        app_s += e0.elapsed_time(e1) * 1e-3
+        tokens += L
+        del k_d, v_d
+    caches = [cache]
+    for _ in range(_copies_for(cache.nbytes()) - 1):
+        c2 = pa.Cache(cache.num_pages, hkv)
+        for a, b2 in zip(cache.arrays(), c2.arrays()):
+            b2.copy_(a)
+        caches.append(c2)
+    qp = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, hkv, n_keep), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pa.dqk_decode_workspace_size(B, hq, hkv, mp, 0) // 4 + 4, dtype=torch.float32, device="cuda")
+    sel_call = pa.prepared("dqk_select_channels", q, t_q, B, hq, hkv, n_keep, qp, sel, stream)
+    dec = [pa.prepared("dqk_decode_attn_tokgrid", c, qp, sel, n_keep, B, hq, pt, mp, lens, float(prob.sm_scale), 0,
+                       ws, ws.numel() * 4, out, None, stream) for c in caches]
+    one = [pa.prepared("dqk_select_decode_attn_tokgrid", c, q, t_q, n_keep, B, hq, pt, mp, lens,
+                       float(prob.sm_scale), 0, ws, ws.numel() * 4, out, None, qp, sel, stream) for c in caches]
+    nc = len(caches)
+    for i in range(100):
+        one[i % nc]()
+        sel_call()
+        dec[i % nc]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one[i % nc]()
+    torch.cuda.synchronize()
+    t_one = (time.perf_counter() - t0) / steps
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sel_call()
+        dec[i % nc]()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    ne = min(steps, 30)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ne)]
+    for i in range(ne):
+        sel_call()
+        evs[i][0].record(stream)
+        dec[i % nc]()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    sel_h = sel.cpu().numpy()
+    cache_bytes = traffic.decode_cache_bytes_tokgrid(prob.seq_lens, sel_h)
+    fixed = traffic.decode_fixed_bytes(B, hq, hkv, n_keep, mp)
+    step_bytes = cache_bytes + fixed["decode"] + fixed["select"]
+    app = append_roofline(app_s, tokens, prob.num_pages, hkv)
+    app["workload"] = f"per-token key grid prefill of {shape.seq_lens[0]} tokens x {hkv} KV heads per call, {B} calls"
+    return {"workload": shape.name + "-tokgrid",
+            "entry": "dqk_select_decode_attn_tokgrid (the selection in the decode launch, then merge)",
+            "t_step_us": round(t_one * 1e6, 2), "tokens_per_s": round(B / t_one, 1),
+            "two_calls": {"entries": "dqk_select_channels + dqk_decode_attn_tokgrid",
+                          "t_step_us": round(t_step * 1e6, 2), "decode_call_us": round(dec_us, 2)},
+            "algorithmic_bytes_per_step": int(step_bytes),
+            "bytes_per_token_head": round(cache_bytes / (hkv * float(np.sum(prob.seq_lens))), 3),
+            "frac_step": round(step_bytes / t_one / 1e9 / PEAK_HBM_GBS, 4),
+            "frac_call": round((cache_bytes + fixed["decode"]) / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "cache_copies": nc, "append": app}
+
+
 def _summary(name, w, r, n_keep):
     B = w.shape.batch
     rec = {"workload": name, "batch": B, "context": (max(w.shape.seq_lens) if len(set(w.shape.seq_lens)) == 1
@@ -594,9 +687,9 @@ def main():
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a --calib-copy run "
                          "into the per-launch HBM traffic record and exit")
-    ap.add_argument("--only", choices=["tiered", "vrot"],
-                    help="run only this variant of the config's workload (protected BF16 tiers, or rotated "
-                         "values with base selection) and print its record (for profiling)")
+    ap.add_argument("--only", choices=["tiered", "vrot", "tokgrid"],
+                    help="run only this variant of the config's workload (protected BF16 tiers, rotated values "
+                         "with base selection, or per-token key grids) and print its record (for profiling)")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
@@ -613,7 +706,7 @@ def main():
     shape = synth.config_shape(args.config, args.seed, args.sparsity)
     n_keep = shape.n_keep
     if args.only:
-        fn = tiered_record if args.only == "tiered" else vrot_record
+        fn = {"tiered": tiered_record, "vrot": vrot_record, "tokgrid": tokgrid_record}[args.only]
         print(json.dumps(fn(shape, args.seed, pa, torch, args.steps)), flush=True)
         return
     log(f"[bench] workload {shape.name}: B={shape.batch} Hq/Hkv={shape.hq}/{shape.hkv} ctx={max(shape.seq_lens)} "
@@ -759,6 +852,10 @@ def main():
         configs["3_tiered"] = tiered_record(shape, args.seed, pa, torch, sub)
         log(f"[bench] config 3 tiered: {configs['3_tiered']['t_step_us']} us/step, append token "
             f"{configs['3_tiered']['append_token_us']} us")
+        torch.cuda.empty_cache()
+        configs["3_tokgrid"] = tokgrid_record(shape, args.seed, pa, torch, sub)
+        log(f"[bench] config 3 per-token key grids: {configs['3_tokgrid']['t_step_us']} us/step, append "
+            f"{configs['3_tokgrid']['append']['seconds'] * 1e6:.0f} us")
         torch.cuda.empty_cache()
         configs["3_vrot"] = vrot_record(shape, args.seed, pa, torch, sub)
         log(f"[bench] config 3 rotated values: {configs['3_vrot']['t_step_us']} us/step one call, "

@@ -414,6 +414,19 @@ int dqk_decode_attn_tokgrid(const dqk_cache *c, const float *q_prime, const int3
                             size_t ws_bytes, float *out, float *lse, hipStream_t stream);
 
 /*
+ * dqk_select_decode_attn over a cache with per-token key grids: selection (in
+ * the decode launch for hq = 4 hkv and 17 <= n_keep <= 128), decode as
+ * dqk_decode_attn_tokgrid, merge.  Arguments and errors as
+ * dqk_select_decode_attn; results identical to dqk_select_channels +
+ * dqk_decode_attn_tokgrid.
+ */
+int dqk_select_decode_attn_tokgrid(const dqk_cache *c, const void *q_bf16, const float *t_q, int32_t n_keep,
+                                   int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                                   const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
+                                   size_t ws_bytes, float *out, float *lse, float *q_prime, int32_t *sel_idx,
+                                   hipStream_t stream);
+
+/*
  * dqk_stream_read -- measurement helper, not part of the attention path: a
  * plain streaming read of `bytes` bytes (a multiple of 16 KiB) at `src`,
  * 16 bytes per lane through LDS, as the reference point for the decode

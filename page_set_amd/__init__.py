@@ -106,6 +106,9 @@ def lib():
         L.dqk_decode_attn_tokgrid.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, P, i32, P,
                                               ctypes.c_float, i32, P, sz, P, P, P]
         L.dqk_decode_attn_tokgrid.restype = ctypes.c_int
+        L.dqk_select_decode_attn_tokgrid.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, P, i32, P,
+                                                     ctypes.c_float, i32, P, sz, P, P, P, P, P]
+        L.dqk_select_decode_attn_tokgrid.restype = ctypes.c_int
         L.dqk_stream_read.argtypes = [P, sz, P, P]
         L.dqk_stream_read.restype = ctypes.c_int
         _lib = L
@@ -330,8 +333,9 @@ def dqk_decode_attn(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_sca
 
 def dqk_select_decode_attn(cache: Cache, q, t_q, n_keep: int, page_table, seq_lens, sm_scale: float,
                            num_splits: int = 0, workspace=None, out=None, lse=None, want_lse: bool = True,
-                           q_prime=None, sel_idx=None, stream=None):
-    """Selection and decode in one call; returns (out, lse, q_prime, sel_idx)."""
+                           q_prime=None, sel_idx=None, stream=None, token_grid: bool = False):
+    """Selection and decode in one call; returns (out, lse, q_prime, sel_idx).
+    token_grid: the cache holds per-token key grids."""
     import torch
     B, hq = int(q.shape[0]), int(q.shape[1])
     hkv = cache.num_kv_heads
@@ -348,11 +352,12 @@ def dqk_select_decode_attn(cache: Cache, q, t_q, n_keep: int, page_table, seq_le
     if sel_idx is None:
         sel_idx = torch.empty((B, hkv, n_keep), dtype=torch.int32, device=dev)
     s = cache.struct()
-    rc = lib().dqk_select_decode_attn(ctypes.byref(s), _ptr(q), _ptr(t_q), int(n_keep), B, hq, _ptr(page_table),
-                                      max_pages, _ptr(seq_lens), float(sm_scale), int(num_splits), _ptr(workspace),
-                                      workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
-                                      _ptr(q_prime), _ptr(sel_idx), _stream(stream))
-    _check(rc, "dqk_select_decode_attn")
+    name = "dqk_select_decode_attn_tokgrid" if token_grid else "dqk_select_decode_attn"
+    rc = getattr(lib(), name)(ctypes.byref(s), _ptr(q), _ptr(t_q), int(n_keep), B, hq, _ptr(page_table),
+                              max_pages, _ptr(seq_lens), float(sm_scale), int(num_splits), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                              _ptr(q_prime), _ptr(sel_idx), _stream(stream))
+    _check(rc, name)
     return out, lse, q_prime, sel_idx
 
 

@@ -216,7 +216,7 @@ static int select_decode_core(const dqk_cache *c, const void *q_bf16, const floa
                               const float *r_inv, int32_t n_keep, int32_t batch, int32_t hq,
                               const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens, float sm_scale,
                               int32_t num_splits, void *workspace, size_t ws_bytes, float *out, float *lse,
-                              float *q_prime, int32_t *sel_idx, hipStream_t stream) {
+                              float *q_prime, int32_t *sel_idx, hipStream_t stream, bool token_grid = false) {
     int st = check_cache(c);
     if (st) return st;
     if (!q_bf16 || !t_q || !page_table || !seq_lens || !workspace || !out || !q_prime || !sel_idx) return DQK_ERR_NULL;
@@ -234,13 +234,13 @@ static int select_decode_core(const dqk_cache *c, const void *q_bf16, const floa
         return DQK_ERR_ALIGN;
     const int splits = resolve_splits(batch, hq, hkv, max_pages, num_splits, n_keep);
     if (ws_bytes < (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float)) return DQK_ERR_WORKSPACE;
-    if (!dqk::fused_select_ok(hq, hkv, n_keep)) {  // separate launches: selection, then decode
+    if (!dqk::fused_select_ok(hq, hkv, n_keep, token_grid)) {  // separate launches: selection, then decode
         st = sel_scale ? dqk_select_channels_base(q_bf16, t_q, sel_scale, batch, hq, hkv, n_keep, q_prime, sel_idx,
                                                   stream)
                        : dqk_select_channels(q_bf16, t_q, batch, hq, hkv, n_keep, q_prime, sel_idx, stream);
         if (st) return st;
         return decode_core(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale,
-                           num_splits, workspace, ws_bytes, r_inv, out, lse, stream);
+                           num_splits, workspace, ws_bytes, r_inv, out, lse, stream, token_grid);
     }
     dqk::DecodeArgs a{c,         nullptr,  nullptr, n_keep, batch,  hq, hkv, page_table, max_pages, seq_lens,
                       sm_scale, splits, static_cast<float *>(workspace), out, lse};
@@ -249,6 +249,7 @@ static int select_decode_core(const dqk_cache *c, const void *q_bf16, const floa
     a.qp_out = q_prime;
     a.sel_out = sel_idx;
     a.sel_scale = sel_scale;
+    a.token_grid = token_grid;
     hipError_t e = dqk::launch_decode_mfma(a, stream);
     if (e != hipSuccess) return hip_status(e);
     if (r_inv) return hip_status(dqk::launch_merge_unrotate(a.partials, batch, hq, hkv, splits, r_inv, out, lse, stream));
@@ -269,6 +270,15 @@ int dqk_decode_attn_tokgrid(const dqk_cache *c, const float *q_prime, const int3
                             size_t ws_bytes, float *out, float *lse, hipStream_t stream) {
     return decode_core(c, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens, sm_scale, num_splits,
                        workspace, ws_bytes, nullptr, out, lse, stream, true);
+}
+
+int dqk_select_decode_attn_tokgrid(const dqk_cache *c, const void *q_bf16, const float *t_q, int32_t n_keep,
+                                   int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                                   const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
+                                   size_t ws_bytes, float *out, float *lse, float *q_prime, int32_t *sel_idx,
+                                   hipStream_t stream) {
+    return select_decode_core(c, q_bf16, t_q, nullptr, nullptr, n_keep, batch, hq, page_table, max_pages, seq_lens,
+                              sm_scale, num_splits, workspace, ws_bytes, out, lse, q_prime, sel_idx, stream, true);
 }
 
 int dqk_quantize_append_tokgrid(const dqk_cache *c, const void *k_bf16, const void *v_bf16, const void *t_k_bf16,

@@ -1138,9 +1138,10 @@ int decode_splits_mfma(int batch, int units_per_seq, int max_pages, int n_keep) 
     return s < 1 ? 1 : s;
 }
 
-bool fused_select_ok(int hq, int hkv, int n_keep) {
+bool fused_select_ok(int hq, int hkv, int n_keep, bool token_grid) {
     if (!use_mfma_decode(hq, hkv, n_keep) || hq != GRP * hkv) return false;  // the prologue pools four heads
-    switch (ks_of(n_keep)) {
+    const int g = token_grid ? 16 : 0;
+    switch (ks_of(n_keep) + g) {
         case 1: return Lay<1>::FUSABLE;
         case 2: return Lay<2>::FUSABLE;
         case 3: return Lay<3>::FUSABLE;
@@ -1148,7 +1149,15 @@ bool fused_select_ok(int hq, int hkv, int n_keep) {
         case 5: return Lay<5>::FUSABLE;
         case 6: return Lay<6>::FUSABLE;
         case 7: return Lay<7>::FUSABLE;
-        default: return Lay<8>::FUSABLE;
+        case 8: return Lay<8>::FUSABLE;
+        case 17: return Lay<17>::FUSABLE;
+        case 18: return Lay<18>::FUSABLE;
+        case 19: return Lay<19>::FUSABLE;
+        case 20: return Lay<20>::FUSABLE;
+        case 21: return Lay<21>::FUSABLE;
+        case 22: return Lay<22>::FUSABLE;
+        case 23: return Lay<23>::FUSABLE;
+        default: return Lay<24>::FUSABLE;
     }
 }
 
@@ -1163,8 +1172,12 @@ static hipError_t launch_ks2(const DecodeArgs &a, hipStream_t s) {
 
 template <int KS>
 static hipError_t launch_ks(const DecodeArgs &a, hipStream_t s) {
-    if (a.token_grid) {  // per-token key grids: the selection is a launch of its own
-        if (a.q_bf16) return hipErrorInvalidValue;
+    if (a.token_grid) {  // per-token key grids (KSX = KS + 16)
+        if constexpr (Lay<KS + 16>::FUSABLE) {
+            if (a.q_bf16) return launch_ks2<KS + 16, true>(a, s);
+        } else {
+            if (a.q_bf16) return hipErrorInvalidValue;
+        }
         return launch_ks2<KS + 16, false>(a, s);
     }
     if constexpr (Lay<KS>::FUSABLE) {

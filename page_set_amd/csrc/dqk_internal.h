@@ -283,7 +283,7 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 // Split count of the BF16 baseline decode.
 int decode_splits_bf16(int batch, int hkv, int max_pages);
 // Whether the MFMA decode can run the selection itself for this n_keep.
-bool fused_select_ok(int hq, int hkv, int n_keep);
+bool fused_select_ok(int hq, int hkv, int n_keep, bool token_grid = false);
 
 struct DecodeBf16Args {
     const uint16_t *k_pages, *v_pages;

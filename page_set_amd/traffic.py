@@ -102,6 +102,23 @@ def decode_cache_bytes(seq_lens, sel_idx) -> int:
     return total
 
 
+def decode_cache_bytes_tokgrid(seq_lens, sel_idx) -> int:
+    """decode_cache_bytes for the per-token key grid layout: per page the
+    selected INT2 rows (32 B each), per valid token its key (scale, zero)
+    (4 B, read whatever the mask), channel 0 when selected, and the values."""
+    total = 0
+    B, hkv, _ = sel_idx.shape
+    for b in range(B):
+        L = int(seq_lens[b])
+        pages = (L + PAGE - 1) // PAGE
+        for g in range(hkv):
+            sel = sel_idx[b, g]
+            has0 = bool((sel == 0).any())
+            r = len(sel) - (1 if has0 else 0)
+            total += pages * r * K_ROW_BYTES + L * (K_META_BYTES + (CH0_BYTES if has0 else 0) + V_TOKEN_BYTES)
+    return total
+
+
 TIER_SINK, TIER_RECENT = 64, 256
 
 

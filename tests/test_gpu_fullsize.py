@@ -246,3 +246,72 @@ def test_rotated_values_at_full_size():
         errs = list(ex.map(check, units))
     _say(f"  16 sampled pages stagewise; {len(units)} sampled units: worst row rel err {max(errs):.3e}")
     assert max(errs) <= gu.TOL
+
+
+def test_token_grid_at_full_size():
+    """The per-token key grid layout at the benchmark's shape (batch 4 x
+    131072 tokens, GQA 32/8, n_keep 77) in the launch configuration bench.py
+    times: the cache built by dqk_quantize_append_tokgrid sequence by
+    sequence (k' read back for sequence 0), selection and
+    dqk_decode_attn_tokgrid.  Stage by stage on 16 sampled pages of sequence
+    0 (every byte equals the oracle's pack of the GPU's own k'); 8 sampled
+    units recomputed by the oracle from the same cache bytes, rows within
+    2e-3."""
+    shape = synth.config_shape(3)
+    _say("per-token key grids at full size", shape.name)
+    prob = synth.make_problem(shape, seed=0, materialize_kv=False)
+    d = gu.upload(prob)
+    L0 = shape.seq_lens[0]
+    kdbg = torch.full((L0, shape.hkv, 128), float("nan"), dtype=torch.float32, device="cuda")
+    cache = pa.Cache(prob.num_pages, shape.hkv)
+    for b in range(shape.batch):
+        kb, vb = synth.make_kv_seq(shape, prob.seed, b, prob.outliers)
+        cu = torch.tensor([0, kb.shape[0]], dtype=torch.int32, device="cuda")
+        pa.dqk_quantize_append_tokgrid(cache, gu.dev(kb), gu.dev(vb), d["t_k"], cu, d["page_table"][b:b + 1].clone(),
+                                       kprime_dbg=kdbg if b == 0 else None)
+        torch.cuda.synchronize()
+    qp, sel = pa.dqk_select_channels(d["q"], d["t_q"], shape.hkv, shape.n_keep)
+    out, _ = pa.dqk_decode_attn(cache, qp, sel, d["page_table"], d["seq_lens"], prob.sm_scale, token_grid=True)
+    torch.cuda.synchronize()
+    pm = cache.page_major()
+    # the key metadata token-major per block: [P/8][Hkv][8 slot][128 tok][2]
+    km_tok = gu.host(cache.k_meta, np.uint16).reshape(prob.num_pages // 8, shape.hkv, 8, 128, 2)
+    kb, vb = synth.make_kv_seq(shape, prob.seed, 0, prob.outliers)
+    for pi in np.random.default_rng(14).choice(L0 // 128, size=16, replace=False):
+        p = int(prob.page_table[0, pi])
+        t0 = int(pi) * 128
+        kp_gpu = gu.host(kdbg[t0:t0 + 128])
+        want = oracle.pack_cache_tokgrid(kp_gpu, np.ascontiguousarray(vb[t0:t0 + 128]), np.array([0, 128], np.int32),
+                                         np.zeros((1, 1), np.int32), 8)
+        want_pm = want.page_major()
+        want_tok = want.k_meta.reshape(1, shape.hkv, 8, 128, 2)
+        for g in range(shape.hkv):
+            for nm, i in (("k_codes", 0), ("k_ch0", 2), ("v_codes", 3), ("v_meta", 4)):
+                got_i = gu.host(pm[i][p:p + 1, g].contiguous(), want_pm[i].dtype)
+                np.testing.assert_array_equal(got_i[0], want_pm[i][0, g], err_msg=f"{nm} page {pi} head {g}")
+            np.testing.assert_array_equal(km_tok[p // 8, g, p % 8], want_tok[0, g, 0], err_msg=f"k_meta page {pi}")
+    grp = shape.hq // shape.hkv
+    out_h, qp_h, sel_h = gu.host(out), gu.host(qp), gu.host(sel)
+    rng = np.random.default_rng(15)
+    units = [(int(b), int(g)) for b, g in zip(rng.integers(0, shape.batch, 8), rng.integers(0, shape.hkv, 8))]
+
+    def check(unit):
+        b, g = unit
+        L = int(prob.seq_lens[b])
+        npg = (L + 127) // 128
+        pages = prob.page_table[b, :npg]
+        sub = _unit_cache(pm, pages, g)
+        sub_tok = sub.k_meta.reshape(sub.num_pages // 8, 1, 8, 128, 2)  # a view: the token layout of the unit
+        for i, p in enumerate(pages):
+            sub_tok[i // 8, 0, i % 8] = km_tok[p // 8, g, p % 8]
+        heads = slice(g * grp, (g + 1) * grp)
+        ref, _ = oracle.decode_attn_tokgrid(sub, np.ascontiguousarray(qp_h[b:b + 1, heads]),
+                                            np.ascontiguousarray(sel_h[b:b + 1, g:g + 1]),
+                                            np.arange(npg, dtype=np.int32)[None], np.array([L], np.int32),
+                                            prob.sm_scale)
+        return float(gu.row_rel_err(out_h[b, heads], ref[0]).max())
+
+    with cf.ThreadPoolExecutor(max_workers=THREADS) as ex:
+        errs = list(ex.map(check, units))
+    _say(f"  16 sampled pages stagewise; {len(units)} sampled units: worst row rel err {max(errs):.3e}")
+    assert max(errs) <= gu.TOL

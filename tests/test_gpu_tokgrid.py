@@ -141,3 +141,29 @@ def test_gpu_built_tokgrid_cache_end_to_end():
     e = gu.row_rel_err(gu.host(out), ref)
     _say(f"  max row rel err {e.max():.3e}")
     assert e.max() <= gu.TOL
+
+
+@pytest.mark.parametrize("shape,ns", [(synth.Shape(2, 32, 8, [3000, 701], 77, shuffle_pages=True), 0),
+                                      (synth.Shape(1, 32, 8, [2000], 128), 3),
+                                      (synth.Shape(2, 32, 8, [900, 300], 9), 0),
+                                      (synth.Shape(2, 16, 8, [1200, 600], 77), 0)],
+                         ids=["g4-nk77", "g4-nk128-3splits", "g4-nk9", "g2"])
+def test_one_call_equals_two_calls(shape, ns):
+    """dqk_select_decode_attn_tokgrid (the selection in the decode launch
+    where possible) gives bit for bit dqk_select_channels +
+    dqk_decode_attn_tokgrid."""
+    _say("tokgrid one call", shape.hq, shape.n_keep, ns)
+    prob = synth.make_problem(shape, seed=54)
+    d = gu.upload(prob)
+    cache = pa.Cache(prob.num_pages, shape.hkv)
+    pa.dqk_quantize_append_tokgrid(cache, d["k"], d["v"], d["t_k"], d["cu"], d["page_table"])
+    out1, lse1, qp1, sel1 = pa.dqk_select_decode_attn(cache, d["q"], d["t_q"], shape.n_keep, d["page_table"],
+                                                      d["seq_lens"], prob.sm_scale, num_splits=ns, token_grid=True)
+    qp2, sel2 = pa.dqk_select_channels(d["q"], d["t_q"], shape.hkv, shape.n_keep)
+    out2, lse2 = pa.dqk_decode_attn(cache, qp2, sel2, d["page_table"], d["seq_lens"], prob.sm_scale, num_splits=ns,
+                                    token_grid=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gu.host(qp1).view(np.uint32), gu.host(qp2).view(np.uint32))
+    np.testing.assert_array_equal(gu.host(sel1), gu.host(sel2))
+    np.testing.assert_array_equal(gu.host(out1).view(np.uint32), gu.host(out2).view(np.uint32))
+    np.testing.assert_array_equal(gu.host(lse1).view(np.uint32), gu.host(lse2).view(np.uint32))

@@ -67,3 +67,24 @@ def test_tiered_bytes_by_enumeration():
             assert n_int2 == 128 * P
             want += P * r * 36
         assert tr.decode_tiered_bytes([L], sel) == want
+
+
+def test_tokgrid_bytes_by_enumeration():
+    """decode_cache_bytes_tokgrid against a count page by page and token by
+    token: a selected INT2 row is 32 bytes of a page, every valid token reads
+    its 4-byte key grid, channel 0 (2 bytes) when selected, 48 value bytes."""
+    rng = np.random.default_rng(5)
+    lens = np.array([1, 128, 129, 3000], np.int32)
+    sel = np.sort(rng.choice(128, size=(4, 2, 77), replace=True), axis=-1).astype(np.int32)
+    sel[:, 0, 0] = 0
+    sel[:, 1] = np.arange(1, 78)
+    want = 0
+    for b, L in enumerate(lens):
+        for g in range(2):
+            s = sel[b, g]
+            has0 = bool((s == 0).any())
+            for p in range((int(L) + 127) // 128):
+                want += (len(s) - has0) * 32
+            for t in range(int(L)):
+                want += 4 + 2 * has0 + 32 + 16
+    assert traffic.decode_cache_bytes_tokgrid(lens, sel) == want
