@@ -61,6 +61,19 @@ decode_attn_tokgrid    textbook attention (torch, fp64) over the cache decoded
                        by that reader; tiny brute force; with every token's
                        channels alike it equals decode_attn on a per-channel
                        pack of the same keys (tests/test_oracle_tokgrid.py)
+key_transform_rope     identity tables equal key_transform exactly; with T_K = I
+                       the rotation matches a complex fp64 rotation of each
+                       channel pair (i, i + 64) within bf16 rounding; scores of
+                       query and key rotated by one bucket's table equal the
+                       unrotated ones (App. C.4); relative-position identity of
+                       absolute RoPE (fp64)
+select_channels_rope   identity tables give select_channels in every bucket;
+                       each bucket equals select_channels of the query rotated
+                       by an independent fp64 complex rotation (up to near-ties)
+decode_attn_rope       textbook attention (torch, fp64) with each token scored
+                       by its own bucket's masked query, one softmax over all;
+                       equal buckets equal decode_attn exactly
+                       (tests/test_oracle_rope.py)
 =====================  ==========================================================
 
 Parity unpinned: the accuracy tables of the paper (need models and datasets).
@@ -128,6 +141,12 @@ def _load():
         _lib.orc_pack_cache_tokgrid.restype = None
         _lib.orc_decode_attn_tokgrid.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, P, i32, P, f64, P, P]
         _lib.orc_decode_attn_tokgrid.restype = i32
+        _lib.orc_key_transform_rope.argtypes = [P, P, i32, P, i32, P, P, P]
+        _lib.orc_key_transform_rope.restype = None
+        _lib.orc_select_channels_rope.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P, P]
+        _lib.orc_select_channels_rope.restype = i32
+        _lib.orc_decode_attn_rope.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, i32, P, i32, P, f64, P, P]
+        _lib.orc_decode_attn_rope.restype = i32
         _lib.orc_tier_pages.argtypes = [i64]
         _lib.orc_tier_pages.restype = i64
         _lib.orc_decode_tiered.argtypes = [P, P, P, P, P, i32, P, P, P, P, P, P, i32, i32, i32, P, i32, P, f64, P,
@@ -389,6 +408,65 @@ def decode_attn_tokgrid(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm
                                          _p(out), _p(lse))
     if rc:
         raise ValueError(f"decode_attn_tokgrid failed (rc={rc})")
+    return out, lse
+
+
+# ---------------------------------------------------------------- bucket-relative RoPE
+ROPE_BUCKET = 2048
+
+
+def key_transform_rope(k_bf16, t_k_bf16, cu_tokens, rope_cos, rope_sin) -> np.ndarray:
+    """k' = bf16(k rotated by its bucket's table) T_K: token t of sequence b
+    (bucket (t - cu_tokens[b]) // 2048) uses rope_cos/rope_sin [n_buckets][64]."""
+    k = _c(k_bf16, np.uint16)
+    tk = _c(t_k_bf16, np.uint16)
+    cu = _c(cu_tokens, np.int32)
+    cs = _c(rope_cos, np.float32)
+    sn = _c(rope_sin, np.float32)
+    lens = np.diff(cu)
+    if len(lens) and int(lens.max()) > cs.shape[0] * ROPE_BUCKET:
+        raise ValueError("key_transform_rope: a sequence is longer than its bucket tables cover")
+    T, hkv = k.shape[0], k.shape[1]
+    out = np.empty((T, hkv, HEAD_DIM), dtype=np.float32)
+    _load().orc_key_transform_rope(_p(k), _p(tk), len(cu) - 1, _p(cu), hkv, _p(cs), _p(sn), _p(out))
+    return out
+
+
+def quantize_append_rope(k_bf16, v_bf16, t_k_bf16, rope_cos, rope_sin, cu_tokens, page_table, num_pages: int,
+                         cache: Optional[Cache] = None):
+    """quantize_append with every key stored in its bucket frame; returns (cache, k')."""
+    kp = key_transform_rope(k_bf16, t_k_bf16, cu_tokens, rope_cos, rope_sin)
+    return pack_cache(kp, v_bf16, cu_tokens, page_table, num_pages, cache), kp
+
+
+def select_channels_rope(q_bf16, t_q, rope_cos, rope_sin, hkv: int, n_keep: int):
+    """Per-bucket selection: q' [B][n_buckets][Hq][128], sel [B][n_buckets][Hkv][n_keep]."""
+    q = _c(q_bf16, np.uint16)
+    tq = _c(t_q, np.float32)
+    cs = _c(rope_cos, np.float32)
+    sn = _c(rope_sin, np.float32)
+    B, hq, nb = q.shape[0], q.shape[1], cs.shape[0]
+    qp = np.empty((B, nb, hq, HEAD_DIM), dtype=np.float32)
+    sel = np.empty((B, nb, hkv, n_keep), dtype=np.int32)
+    rc = _load().orc_select_channels_rope(_p(q), _p(tq), _p(cs), _p(sn), nb, B, hq, hkv, n_keep, _p(qp), _p(sel))
+    if rc:
+        raise ValueError(f"select_channels_rope: bad shape (rc={rc})")
+    return qp, sel
+
+
+def decode_attn_rope(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_scale: float):
+    """decode_attn where token t scores with q_prime[b][t // 2048] and sel_idx[b][t // 2048]."""
+    qp = _c(q_prime, np.float32)
+    sel = _c(sel_idx, np.int32)
+    pt = _c(page_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    B, nb, hq = qp.shape[0], qp.shape[1], qp.shape[2]
+    out = np.empty((B, hq, HEAD_DIM), dtype=np.float64)
+    lse = np.empty((B, hq), dtype=np.float64)
+    rc = _load().orc_decode_attn_rope(*[_p(a) for a in cache.arrays()], cache.hkv, _p(qp), _p(sel), sel.shape[3],
+                                      nb, B, hq, _p(pt), pt.shape[1], _p(sl), float(sm_scale), _p(out), _p(lse))
+    if rc:
+        raise ValueError(f"decode_attn_rope failed (rc={rc})")
     return out, lse
 
 

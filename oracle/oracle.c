@@ -265,6 +265,52 @@ void orc_key_transform(const uint16_t *k, const uint16_t *t_k, int64_t T, int hk
         }
 }
 
+/* RoPE rotation of one 128-channel vector in the rotate-half pairing
+ * (channel i with channel i + 64): y_i = x_i c_i - x_{i+64} s_i and
+ * y_{i+64} = x_{i+64} c_i + x_i s_i, every product and sum rounded to fp32.
+ * With (c_i, s_i) = (cos(a theta_i), -sin(a theta_i)) it takes a vector
+ * rotated for position n to position n - a (§3.4, App. C.4).               */
+static void rope_rotate(const float *x, const float *cs, const float *sn, float *y)
+{
+    for (int i = 0; i < HD / 2; ++i) {
+        float a = x[i] * cs[i], b = x[i + HD / 2] * sn[i];
+        float c = x[i + HD / 2] * cs[i], d = x[i] * sn[i];
+        y[i] = a - b;
+        y[i + HD / 2] = c + d;
+    }
+}
+
+/* Key transform in the bucket frame (§3.4 z_n = k_n T_b B, App. C.4): token
+ * t of sequence sq (bucket (t - cu_tokens[sq]) / 2048) is rotated by its
+ * bucket's table, rounded to bf16 (the MFMA operand, round to nearest even),
+ * then multiplied by T_K as in orc_key_transform.                           */
+#define ROPE_BUCKET 2048
+void orc_key_transform_rope(const uint16_t *k, const uint16_t *t_k, int n_seqs, const int32_t *cu_tokens, int hkv,
+                            const float *rope_cos, const float *rope_sin, float *kprime)
+{
+    for (int sq = 0; sq < n_seqs; ++sq)
+        for (int64_t t = cu_tokens[sq]; t < cu_tokens[sq + 1]; ++t) {
+            int64_t bk = (t - cu_tokens[sq]) / ROPE_BUCKET;
+            for (int g = 0; g < hkv; ++g) {
+                const uint16_t *kr = k + ((size_t)t * hkv + g) * HD;
+                const uint16_t *tg = t_k + (size_t)g * HD * HD;
+                float x[HD], y[HD];
+                uint16_t yb[HD];
+                for (int i = 0; i < HD; ++i)
+                    x[i] = orc_bf16_value(kr[i]);
+                rope_rotate(x, rope_cos + (size_t)bk * (HD / 2), rope_sin + (size_t)bk * (HD / 2), y);
+                for (int i = 0; i < HD; ++i)
+                    yb[i] = orc_bf16_round_nearest(y[i]);
+                for (int j = 0; j < HD; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < HD; ++i)
+                        acc += (double)orc_bf16_value(yb[i]) * (double)orc_bf16_value(tg[(size_t)i * HD + j]);
+                    kprime[((size_t)t * hkv + g) * HD + j] = (float)acc;
+                }
+            }
+        }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Pack transformed keys and raw values of n_seqs sequences into 128-token
  * pages (§3.3: channel-major keys with channel 0 in bf16 outside the INT2
@@ -409,13 +455,18 @@ int orc_value_unrotate(const double *o, const float *r_inv, int batch, int hq, i
  * are written in ascending channel order.
  *   q bf16 [B][Hq][128], t_q fp32 [Hkv][128][128]
  *   q_prime fp32 [B][Hq][128], sel_idx int32 [B][Hkv][n_keep]               */
-static int select_impl(const uint16_t *q, const float *t_q, const float *sel_scale, int batch, int hq, int hkv,
-                       int n_keep, float *q_prime, int32_t *sel_idx)
+/* rope_cs / rope_sn (may be NULL): per-bucket rotation tables [nb][64]; the
+ * query of (b, h) for bucket k is q[b][h] rotated by table k, and the results
+ * go to q_prime[b][k][h], sel_idx[b][k][g]. */
+static int select_impl_rope(const uint16_t *q, const float *t_q, const float *sel_scale, const float *rope_cs,
+                            const float *rope_sn, int nb, int batch, int hq, int hkv, int n_keep, float *q_prime,
+                            int32_t *sel_idx)
 {
-    if (hkv <= 0 || hq % hkv || n_keep < 1 || n_keep > HD)
+    if (hkv <= 0 || hq % hkv || n_keep < 1 || n_keep > HD || nb < 1)
         return -2;
     int grp = hq / hkv;
     for (int b = 0; b < batch; ++b)
+        for (int k = 0; k < nb; ++k)
         for (int g = 0; g < hkv; ++g) {
             const float *tq = t_q + (size_t)g * HD * HD;
             float S[HD];
@@ -424,11 +475,18 @@ static int select_impl(const uint16_t *q, const float *t_q, const float *sel_sca
             for (int hh = 0; hh < grp; ++hh) {
                 int h = g * grp + hh;
                 const uint16_t *qr = q + ((size_t)b * hq + h) * HD;
-                float *qp = q_prime + ((size_t)b * hq + h) * HD;
+                float *qp = q_prime + (((size_t)b * nb + k) * hq + h) * HD;
+                float qf[HD], qx[HD];
+                for (int i = 0; i < HD; ++i)
+                    qf[i] = orc_bf16_value(qr[i]);
+                if (rope_cs) {
+                    rope_rotate(qf, rope_cs + (size_t)k * (HD / 2), rope_sn + (size_t)k * (HD / 2), qx);
+                    memcpy(qf, qx, sizeof qf);
+                }
                 for (int j = 0; j < HD; ++j) {
                     float acc = 0.0f;
                     for (int i = 0; i < HD; ++i)
-                        acc = fmaf(orc_bf16_value(qr[i]), tq[(size_t)i * HD + j], acc);
+                        acc = fmaf(qf[i], tq[(size_t)i * HD + j], acc);
                     qp[j] = acc;
                 }
                 for (int j = 0; j < HD; ++j) {
@@ -436,7 +494,7 @@ static int select_impl(const uint16_t *q, const float *t_q, const float *sel_sca
                     S[j] = fmaf(e, e, S[j]);
                 }
             }
-            int32_t *out = sel_idx + ((size_t)b * hkv + g) * n_keep;
+            int32_t *out = sel_idx + (((size_t)b * nb + k) * hkv + g) * n_keep;
             int w = 0;
             for (int j = 0; j < HD; ++j) {
                 int rank = 0;
@@ -448,6 +506,23 @@ static int select_impl(const uint16_t *q, const float *t_q, const float *sel_sca
             }
         }
     return 0;
+}
+
+static int select_impl(const uint16_t *q, const float *t_q, const float *sel_scale, int batch, int hq, int hkv,
+                       int n_keep, float *q_prime, int32_t *sel_idx)
+{
+    return select_impl_rope(q, t_q, sel_scale, NULL, NULL, 1, batch, hq, hkv, n_keep, q_prime, sel_idx);
+}
+
+/* Selection per bucket (§3.4: each bucket's anchor adjustment is applied to
+ * the current queries, then Eq. 4; masks may differ across buckets).
+ * q'_{b,k,h} = (q_{b,h} rotated by table k) T_Q.
+ *   rope_cos, rope_sin fp32 [n_buckets][64]
+ *   q_prime fp32 [B][n_buckets][Hq][128], sel_idx int32 [B][n_buckets][Hkv][n_keep] */
+int orc_select_channels_rope(const uint16_t *q, const float *t_q, const float *rope_cos, const float *rope_sin,
+                             int n_buckets, int batch, int hq, int hkv, int n_keep, float *q_prime, int32_t *sel_idx)
+{
+    return select_impl_rope(q, t_q, NULL, rope_cos, rope_sin, n_buckets, batch, hq, hkv, n_keep, q_prime, sel_idx);
 }
 
 int orc_select_channels(const uint16_t *q, const float *t_q, int batch, int hq, int hkv, int n_keep, float *q_prime,
@@ -478,13 +553,17 @@ int orc_select_channels_base(const uint16_t *q, const float *t_q, const float *s
  * out_{h,c} = sum_t p_t v^_{t,c}, lse_h = max + log(sum exp).
  *   q_prime fp32 [B][Hq][128], sel_idx [B][Hkv][n_keep],
  *   page_table [B][max_pages], out fp64 [B][Hq][128], lse fp64 [B][Hq]     */
+/* nb >= 1 buckets: token t scores with q_prime[b][t / 2048][h] and the
+ * selection sel_idx[b][t / 2048][g] (a token past the last bucket is an
+ * error); nb = 0: one query and one mask for the whole sequence. */
 static int decode_impl(const uint8_t *k_codes, const uint16_t *k_meta, const uint16_t *k_ch0, const uint8_t *v_codes,
-                       const uint16_t *v_meta, int token_grid, int hkv, const float *q_prime, const int32_t *sel_idx,
-                       int n_keep, int batch, int hq, const int32_t *page_table, int max_pages,
-                       const int32_t *seq_lens, double sm_scale, double *out, double *lse)
+                       const uint16_t *v_meta, int token_grid, int nb, int hkv, const float *q_prime,
+                       const int32_t *sel_idx, int n_keep, int batch, int hq, const int32_t *page_table,
+                       int max_pages, const int32_t *seq_lens, double sm_scale, double *out, double *lse)
 {
-    if (hkv <= 0 || hq % hkv || n_keep < 1 || n_keep > HD)
+    if (hkv <= 0 || hq % hkv || n_keep < 1 || n_keep > HD || nb < 0)
         return -2;
+    const int nq = nb > 0 ? nb : 1;
     int grp = hq / hkv;
     for (int b = 0; b < batch; ++b) {
         int64_t L = seq_lens[b];
@@ -493,10 +572,15 @@ static int decode_impl(const uint8_t *k_codes, const uint16_t *k_meta, const uin
             return -7;
         for (int h = 0; h < hq; ++h) {
             int g = h / grp;
-            const float *qp = q_prime + ((size_t)b * hq + h) * HD;
-            const int32_t *M = sel_idx + ((size_t)b * hkv + g) * n_keep;
             double mx = -INFINITY;
             for (int64_t t = 0; t < L; ++t) {
+                int64_t bk = nb > 0 ? t / ROPE_BUCKET : 0;
+                if (bk >= nq) {
+                    free(logit);
+                    return -2;
+                }
+                const float *qp = q_prime + (((size_t)b * nq + bk) * hq + h) * HD;
+                const int32_t *M = sel_idx + (((size_t)b * nq + bk) * hkv + g) * n_keep;
                 int64_t p = page_table[(size_t)b * max_pages + (t >> 7)];
                 int s = (int)(t & (PG - 1));
                 size_t pg = (size_t)p * hkv + g;
@@ -551,7 +635,7 @@ int orc_decode_attn(const uint8_t *k_codes, const uint16_t *k_meta, const uint16
                     int batch, int hq, const int32_t *page_table, int max_pages, const int32_t *seq_lens,
                     double sm_scale, double *out, double *lse)
 {
-    return decode_impl(k_codes, k_meta, k_ch0, v_codes, v_meta, 0, hkv, q_prime, sel_idx, n_keep, batch, hq,
+    return decode_impl(k_codes, k_meta, k_ch0, v_codes, v_meta, 0, 0, hkv, q_prime, sel_idx, n_keep, batch, hq,
                        page_table, max_pages, seq_lens, sm_scale, out, lse);
 }
 
@@ -562,8 +646,24 @@ int orc_decode_attn_tokgrid(const uint8_t *k_codes, const uint16_t *k_meta, cons
                             const int32_t *sel_idx, int n_keep, int batch, int hq, const int32_t *page_table,
                             int max_pages, const int32_t *seq_lens, double sm_scale, double *out, double *lse)
 {
-    return decode_impl(k_codes, k_meta, k_ch0, v_codes, v_meta, 1, hkv, q_prime, sel_idx, n_keep, batch, hq,
+    return decode_impl(k_codes, k_meta, k_ch0, v_codes, v_meta, 1, 0, hkv, q_prime, sel_idx, n_keep, batch, hq,
                        page_table, max_pages, seq_lens, sm_scale, out, lse);
+}
+
+/* Decode with bucket-relative RoPE (§3.4): token t of sequence b scores with
+ * its bucket's adjusted query and mask, q_prime[b][t / 2048][h] and
+ * sel_idx[b][t / 2048][g], under one softmax over all tokens; the cache as
+ * orc_decode_attn (keys stored in their bucket frames).                    */
+int orc_decode_attn_rope(const uint8_t *k_codes, const uint16_t *k_meta, const uint16_t *k_ch0,
+                         const uint8_t *v_codes, const uint16_t *v_meta, int hkv, const float *q_prime,
+                         const int32_t *sel_idx, int n_keep, int n_buckets, int batch, int hq,
+                         const int32_t *page_table, int max_pages, const int32_t *seq_lens, double sm_scale,
+                         double *out, double *lse)
+{
+    if (n_buckets < 1)
+        return -2;
+    return decode_impl(k_codes, k_meta, k_ch0, v_codes, v_meta, 0, n_buckets, hkv, q_prime, sel_idx, n_keep, batch,
+                       hq, page_table, max_pages, seq_lens, sm_scale, out, lse);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -174,6 +174,27 @@ def make_selection_scales(hkv: int, seed: int) -> np.ndarray:
     return out
 
 
+ROPE_BUCKET = 2048
+
+
+def rope_buckets(max_len: int) -> int:
+    """Buckets of 2048 positions that cover max_len tokens (at least one)."""
+    return max(1, -(-int(max_len) // ROPE_BUCKET))
+
+
+def make_rope_tables(n_buckets: int, base: float = 10000.0):
+    """Anchor tables of bucket-relative RoPE (§3.4, App. C.4), fp32 [n_buckets][64].
+
+    Stands in for a checkpoint's rotary frequencies: theta_i = base^(-i/64)
+    for the channel pair (i, i + 64), bucket k's anchor a_k = 2048 k, and the
+    entries cos(a_k theta_i) and -sin(a_k theta_i) (the rotation back by the
+    anchor), computed in fp64 and rounded to fp32.  No random draws."""
+    i = np.arange(HEAD_DIM // 2, dtype=np.float64)
+    theta = base ** (-i / (HEAD_DIM // 2))
+    ang = (ROPE_BUCKET * np.arange(n_buckets, dtype=np.float64))[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), (-np.sin(ang)).astype(np.float32)
+
+
 def outlier_channels(hkv: int, n: int, seed: int) -> np.ndarray:
     rng = _rng(seed, _ID_OUTLIER)
     out = np.zeros((hkv, n), dtype=np.int64)
