@@ -655,6 +655,109 @@ def tokgrid_record(shape, seed, pa, torch, steps):
             "cache_copies": nc, "append": app}
 
 
+def rope_record(shape, seed, pa, torch, steps):
+    """The headline workload with bucket-relative RoPE (2048-token buckets,
+    64 at 128K): the cache is built sequence by sequence with
+    dqk_quantize_append_rope (HIP events), then a step is one
+    dqk_select_decode_attn_rope call (per-bucket turned queries and masks,
+    bucket merge) over cache copies rotated as in the headline; the same step
+    as two calls (dqk_select_channels_rope + dqk_decode_attn_rope) is
+    reported beside it."""
+    from page_set_amd import traffic
+    prob = synth.make_problem(shape, seed, materialize_kv=False)
+    B, hq, hkv, n_keep = shape.batch, shape.hq, shape.hkv, shape.n_keep
+    nb = synth.rope_buckets(max(shape.seq_lens))
+    cs_h, sn_h = synth.make_rope_tables(nb)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+    q, t_q, t_k = dev(prob.q.view(np.int16)), dev(prob.t_q), dev(prob.t_k.view(np.int16))
+    cs, sn = dev(cs_h), dev(sn_h)
+    pt, lens = dev(prob.page_table), dev(prob.seq_lens)
+    mp = int(prob.page_table.shape[1])
+    stream = torch.cuda.current_stream()
+    cache = pa.Cache(prob.num_pages, hkv)
+    app_s, tokens = 0.0, 0
+    for b in range(B):
+        kb, vb = synth.make_kv_seq(shape, seed, b, prob.outliers)
+        L = kb.shape[0]
+        k_d, v_d = dev(kb.view(np.int16)), dev(vb.view(np.int16))
+        cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+        ptb = pt[b:b + 1].clone()
+        if b == 0:  # untimed first call
+            pa.dqk_quantize_append_rope(cache, k_d, v_d, t_k, cs, sn, cu, ptb, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pa.dqk_quantize_append_rope(cache, k_d, v_d, t_k, cs, sn, cu, ptb, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        app_s += e0.elapsed_time(e1) * 1e-3
+        tokens += L
+        del k_d, v_d
+    caches = [cache]
+    for _ in range(_copies_for(cache.nbytes()) - 1):
+        c2 = pa.Cache(cache.num_pages, hkv)
+        for a, b2 in zip(cache.arrays(), c2.arrays()):
+            b2.copy_(a)
+        caches.append(c2)
+    qp = torch.empty((B, nb, hq, 128), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, nb, hkv, n_keep), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pa.dqk_decode_rope_workspace_size(B, hq, hkv, nb, 0) // 4 + 4, dtype=torch.float32,
+                     device="cuda")
+    sel_call = pa.prepared("dqk_select_channels_rope", q, t_q, cs, sn, nb, B, hq, hkv, n_keep, qp, sel, stream)
+    dec = [pa.prepared("dqk_decode_attn_rope", c, qp, sel, n_keep, nb, B, hq, pt, mp, lens, float(prob.sm_scale), 0,
+                       ws, ws.numel() * 4, out, None, stream) for c in caches]
+    one = [pa.prepared("dqk_select_decode_attn_rope", c, q, t_q, cs, sn, n_keep, nb, B, hq, pt, mp, lens,
+                       float(prob.sm_scale), 0, ws, ws.numel() * 4, out, None, qp, sel, stream) for c in caches]
+    nc = len(caches)
+    for i in range(100):
+        one[i % nc]()
+        sel_call()
+        dec[i % nc]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        one[i % nc]()
+    torch.cuda.synchronize()
+    t_one = (time.perf_counter() - t0) / steps
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sel_call()
+        dec[i % nc]()
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / steps
+    ne = min(steps, 30)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ne)]
+    sevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ne)]
+    for i in range(ne):
+        sevs[i][0].record(stream)
+        sel_call()
+        sevs[i][1].record(stream)
+        evs[i][0].record(stream)
+        dec[i % nc]()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    dec_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    sel_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in sevs]))
+    sel_h = sel.cpu().numpy()
+    cache_bytes = traffic.decode_rope_bytes(prob.seq_lens, sel_h)
+    fixed = traffic.decode_fixed_bytes(B * nb, hq, hkv, n_keep, 16)
+    step_bytes = cache_bytes + fixed["decode"] + fixed["select"] + 2 * nb * 64 * 4
+    app = append_roofline(app_s, tokens, prob.num_pages, hkv)
+    app["workload"] = f"bucket-frame prefill of {shape.seq_lens[0]} tokens x {hkv} KV heads per call, {B} calls"
+    return {"workload": shape.name + "-rope", "n_buckets": nb,
+            "entry": "dqk_select_decode_attn_rope (per-bucket selection, decode switching buckets per split, merge)",
+            "t_step_us": round(t_one * 1e6, 2), "tokens_per_s": round(B / t_one, 1),
+            "two_calls": {"entries": "dqk_select_channels_rope + dqk_decode_attn_rope",
+                          "t_step_us": round(t_step * 1e6, 2), "select_call_us": round(sel_us, 2),
+                          "decode_call_us": round(dec_us, 2)},
+            "algorithmic_bytes_per_step": int(step_bytes),
+            "bytes_per_token_head": round(cache_bytes / (hkv * float(np.sum(prob.seq_lens))), 3),
+            "frac_step": round(step_bytes / t_one / 1e9 / PEAK_HBM_GBS, 4),
+            "frac_call": round((cache_bytes + fixed["decode"]) / (dec_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "cache_copies": nc, "append": app}
+
+
 def _summary(name, w, r, n_keep):
     B = w.shape.batch
     rec = {"workload": name, "batch": B, "context": (max(w.shape.seq_lens) if len(set(w.shape.seq_lens)) == 1
@@ -687,9 +790,10 @@ def main():
     ap.add_argument("--write-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_JSON"),
                     help="turn two rocprofv3 --pmc counter files (FETCH_SIZE, WRITE_SIZE) of a --calib-copy run "
                          "into the per-launch HBM traffic record and exit")
-    ap.add_argument("--only", choices=["tiered", "vrot", "tokgrid"],
+    ap.add_argument("--only", choices=["tiered", "vrot", "tokgrid", "rope"],
                     help="run only this variant of the config's workload (protected BF16 tiers, rotated values "
-                         "with base selection, or per-token key grids) and print its record (for profiling)")
+                         "with base selection, per-token key grids, or bucket-relative RoPE) and print its record "
+                         "(for profiling)")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
@@ -706,7 +810,8 @@ def main():
     shape = synth.config_shape(args.config, args.seed, args.sparsity)
     n_keep = shape.n_keep
     if args.only:
-        fn = {"tiered": tiered_record, "vrot": vrot_record, "tokgrid": tokgrid_record}[args.only]
+        fn = {"tiered": tiered_record, "vrot": vrot_record, "tokgrid": tokgrid_record,
+              "rope": rope_record}[args.only]
         print(json.dumps(fn(shape, args.seed, pa, torch, args.steps)), flush=True)
         return
     log(f"[bench] workload {shape.name}: B={shape.batch} Hq/Hkv={shape.hq}/{shape.hkv} ctx={max(shape.seq_lens)} "
@@ -861,6 +966,11 @@ def main():
         log(f"[bench] config 3 rotated values: {configs['3_vrot']['t_step_us']} us/step one call, "
             f"{configs['3_vrot']['three_calls']['t_step_us']} us as three calls, append "
             f"{configs['3_vrot']['append']['seconds'] * 1e6:.0f} us")
+        torch.cuda.empty_cache()
+        configs["3_rope"] = rope_record(shape, args.seed, pa, torch, sub)
+        log(f"[bench] config 3 bucket-relative RoPE: {configs['3_rope']['t_step_us']} us/step one call, "
+            f"{configs['3_rope']['two_calls']['t_step_us']} us as two calls, append "
+            f"{configs['3_rope']['append']['seconds'] * 1e6:.0f} us")
         rec["configs"] = configs
 
     if not args.no_cpu_baseline:

@@ -426,6 +426,84 @@ int dqk_select_decode_attn_tokgrid(const dqk_cache *c, const void *q_bf16, const
                                    size_t ws_bytes, float *out, float *lse, float *q_prime, int32_t *sel_idx,
                                    hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Bucket-relative RoPE (§3.4 and App. C.4).  Positions of a sequence fall in
+ * buckets of 2048 (bucket k: positions 2048 k .. 2048 k + 2047, counted from
+ * the sequence's start, i.e. logical pages 16 k .. 16 k + 15), with anchor
+ * a_k = 2048 k.  A stored key is moved from its position n to n - a_k before
+ * the key transform; for each bucket the current query is moved by the same
+ * anchor before the query transform, gets its own channel mask, and scores
+ * that bucket's tokens; one softmax spans every bucket.
+ *   rope_cos, rope_sin  fp32 [n_buckets][64] device: cos(a_k theta_i) and
+ *               -sin(a_k theta_i) for the rotate-half channel pairs (i, i + 64)
+ *               (the checkpoint's rotary frequencies theta_i, any scaling
+ *               included).  Vector x turned by table k: y_i = x_i c - x_{i+64} s,
+ *               y_{i+64} = x_{i+64} c + x_i s, every product and sum in fp32.
+ *   n_buckets   >= 1, with 16 n_buckets >= max_pages (every page of a
+ *               sequence lies in a bucket that has a table).
+ * The cache layout is that of dqk_quantize_append (per-channel key grids).
+ */
+
+/*
+ * dqk_quantize_append with keys in their bucket frames: the key of token t
+ * (position p = t - cu_tokens[i] in its sequence) is turned by table p / 2048,
+ * rounded to bf16 (to nearest even), then multiplied by T_K.  kprime_dbg
+ * receives that k'.  Other arguments, slots past a sequence's end and errors
+ * as dqk_quantize_append; DQK_ERR_SHAPE also if n_buckets < 1 or
+ * 16 n_buckets < max_pages.
+ */
+int dqk_quantize_append_rope(const dqk_cache *c, const void *k_bf16, const void *v_bf16, const void *t_k_bf16,
+                             const float *rope_cos, const float *rope_sin, int32_t n_buckets, int32_t n_seqs,
+                             const int32_t *cu_tokens, int64_t total_tokens, const int32_t *page_table,
+                             int32_t max_pages, float *kprime_dbg, hipStream_t stream);
+
+/*
+ * Per-bucket selection: for sequence b and bucket k, q turned by table k (fp32)
+ * then q' = q T_Q and the mask of dqk_select_channels.
+ *   q_prime     fp32 [batch][n_buckets][Hq][128] device (output).
+ *   sel_idx     int32 [batch][n_buckets][Hkv][n_keep] device (output).
+ * Other arguments and errors as dqk_select_channels; DQK_ERR_UNSUPPORTED if
+ * batch * n_buckets > 65535.
+ */
+int dqk_select_channels_rope(const void *q_bf16, const float *t_q, const float *rope_cos, const float *rope_sin,
+                             int32_t n_buckets, int32_t batch, int32_t hq, int32_t hkv, int32_t n_keep,
+                             float *q_prime, int32_t *sel_idx, hipStream_t stream);
+
+/*
+ * Workspace bytes for dqk_decode_attn_rope / dqk_select_decode_attn_rope
+ * (num_splits: splits per bucket, 0 = automatic); 0 on invalid sizes.
+ */
+size_t dqk_decode_rope_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t n_buckets,
+                                      int32_t num_splits);
+
+/*
+ * Decode over a cache written by dqk_quantize_append_rope: token t of sequence
+ * b scores with q_prime[b][t / 2048] masked by sel_idx[b][t / 2048] (the
+ * output layout of dqk_select_channels_rope), and the scores of all buckets
+ * share one softmax.  A split covers whole buckets and keeps their queries
+ * and channel lists in LDS, switching at each bucket's first page;
+ * num_splits (0 = automatic) is raised where a split would hold more buckets
+ * than fit (8, or 4 to 5 for n_keep in 81..96 and above 112).  Other
+ * arguments, outputs and errors as dqk_decode_attn; DQK_ERR_SHAPE also if
+ * n_buckets < 1 or 16 n_buckets < max_pages; DQK_ERR_UNSUPPORTED also if
+ * batch * n_buckets > 65535.
+ */
+int dqk_decode_attn_rope(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
+                         int32_t n_buckets, int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                         const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
+                         size_t ws_bytes, float *out, float *lse, hipStream_t stream);
+
+/*
+ * dqk_select_channels_rope + dqk_decode_attn_rope in one call; q_prime and
+ * sel_idx receive the selection as dqk_select_channels_rope writes it.
+ * Results identical to the two calls.
+ */
+int dqk_select_decode_attn_rope(const dqk_cache *c, const void *q_bf16, const float *t_q, const float *rope_cos,
+                                const float *rope_sin, int32_t n_keep, int32_t n_buckets, int32_t batch, int32_t hq,
+                                const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                                float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
+                                float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream);
+
 /*
  * dqk_stream_read -- measurement helper, not part of the attention path: a
  * plain streaming read of `bytes` bytes (a multiple of 16 KiB) at `src`,

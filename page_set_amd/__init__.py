@@ -109,6 +109,19 @@ def lib():
         L.dqk_select_decode_attn_tokgrid.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, P, i32, P,
                                                      ctypes.c_float, i32, P, sz, P, P, P, P, P]
         L.dqk_select_decode_attn_tokgrid.restype = ctypes.c_int
+        L.dqk_quantize_append_rope.argtypes = [ctypes.POINTER(dqk_cache), P, P, P, P, P, i32, i32, P, i64, P, i32,
+                                               P, P]
+        L.dqk_quantize_append_rope.restype = ctypes.c_int
+        L.dqk_select_channels_rope.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, P, P, P]
+        L.dqk_select_channels_rope.restype = ctypes.c_int
+        L.dqk_decode_rope_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+        L.dqk_decode_rope_workspace_size.restype = sz
+        L.dqk_decode_attn_rope.argtypes = [ctypes.POINTER(dqk_cache), P, P, i32, i32, i32, i32, P, i32, P,
+                                           ctypes.c_float, i32, P, sz, P, P, P]
+        L.dqk_decode_attn_rope.restype = ctypes.c_int
+        L.dqk_select_decode_attn_rope.argtypes = [ctypes.POINTER(dqk_cache), P, P, P, P, i32, i32, i32, i32, P, i32,
+                                                  P, ctypes.c_float, i32, P, sz, P, P, P, P, P]
+        L.dqk_select_decode_attn_rope.restype = ctypes.c_int
         L.dqk_stream_read.argtypes = [P, sz, P, P]
         L.dqk_stream_read.restype = ctypes.c_int
         _lib = L
@@ -388,6 +401,90 @@ def dqk_select_decode_attn_vrot(cache: Cache, q, t_q, sel_scale, r_v_inv, n_keep
                                            workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
                                            _ptr(q_prime), _ptr(sel_idx), _stream(stream))
     _check(rc, "dqk_select_decode_attn_vrot")
+    return out, lse, q_prime, sel_idx
+
+
+# ---- bucket-relative RoPE: tables rope_cos / rope_sin fp32 [n_buckets][64]
+def dqk_quantize_append_rope(cache: Cache, k, v, t_k, rope_cos, rope_sin, cu_tokens, page_table, kprime_dbg=None,
+                             stream=None):
+    n_seqs = cu_tokens.numel() - 1
+    s = cache.struct()
+    rc = lib().dqk_quantize_append_rope(ctypes.byref(s), _ptr(k), _ptr(v), _ptr(t_k), _ptr(rope_cos), _ptr(rope_sin),
+                                        int(rope_cos.shape[0]), n_seqs, _ptr(cu_tokens), int(k.shape[0]),
+                                        _ptr(page_table), int(page_table.shape[1]), _ptr(kprime_dbg),
+                                        _stream(stream))
+    _check(rc, "dqk_quantize_append_rope")
+
+
+def dqk_select_channels_rope(q, t_q, rope_cos, rope_sin, hkv: int, n_keep: int, q_prime=None, sel_idx=None,
+                             stream=None):
+    """Per-bucket selection; returns q_prime [B][n_buckets][Hq][128], sel_idx [B][n_buckets][Hkv][n_keep]."""
+    import torch
+    B, hq, nb = int(q.shape[0]), int(q.shape[1]), int(rope_cos.shape[0])
+    if q_prime is None:
+        q_prime = torch.empty((B, nb, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, nb, hkv, n_keep), dtype=torch.int32, device=q.device)
+    rc = lib().dqk_select_channels_rope(_ptr(q), _ptr(t_q), _ptr(rope_cos), _ptr(rope_sin), nb, B, hq, hkv, n_keep,
+                                        _ptr(q_prime), _ptr(sel_idx), _stream(stream))
+    _check(rc, "dqk_select_channels_rope")
+    return q_prime, sel_idx
+
+
+def dqk_decode_rope_workspace_size(batch: int, hq: int, hkv: int, n_buckets: int, num_splits: int = 0) -> int:
+    return int(lib().dqk_decode_rope_workspace_size(batch, hq, hkv, n_buckets, num_splits))
+
+
+def _rope_outputs(B, hq, nb, hkv, num_splits, want_lse, workspace, out, lse, dev):
+    import torch
+    if workspace is None:
+        n = dqk_decode_rope_workspace_size(B, hq, hkv, nb, num_splits)
+        workspace = torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    return workspace, out, lse
+
+
+def dqk_decode_attn_rope(cache: Cache, q_prime, sel_idx, page_table, seq_lens, sm_scale: float, num_splits: int = 0,
+                         workspace=None, out=None, lse=None, want_lse: bool = True, stream=None):
+    """Decode over a cache written by dqk_quantize_append_rope, with
+    q_prime / sel_idx as dqk_select_channels_rope returns them."""
+    B, nb, hq = int(q_prime.shape[0]), int(q_prime.shape[1]), int(q_prime.shape[2])
+    n_keep = int(sel_idx.shape[3])
+    workspace, out, lse = _rope_outputs(B, hq, nb, cache.num_kv_heads, num_splits, want_lse, workspace, out, lse,
+                                        q_prime.device)
+    s = cache.struct()
+    rc = lib().dqk_decode_attn_rope(ctypes.byref(s), _ptr(q_prime), _ptr(sel_idx), n_keep, nb, B, hq,
+                                    _ptr(page_table), int(page_table.shape[1]), _ptr(seq_lens), float(sm_scale),
+                                    int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _ptr(out), _ptr(lse), _stream(stream))
+    _check(rc, "dqk_decode_attn_rope")
+    return out, lse
+
+
+def dqk_select_decode_attn_rope(cache: Cache, q, t_q, rope_cos, rope_sin, n_keep: int, page_table, seq_lens,
+                                sm_scale: float, num_splits: int = 0, workspace=None, out=None, lse=None,
+                                want_lse: bool = True, q_prime=None, sel_idx=None, stream=None):
+    """Per-bucket selection, decode and bucket merge in one call; returns
+    (out, lse, q_prime, sel_idx)."""
+    import torch
+    B, hq, nb = int(q.shape[0]), int(q.shape[1]), int(rope_cos.shape[0])
+    hkv = cache.num_kv_heads
+    dev = q.device
+    workspace, out, lse = _rope_outputs(B, hq, nb, hkv, num_splits, want_lse, workspace, out, lse, dev)
+    if q_prime is None:
+        q_prime = torch.empty((B, nb, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, nb, hkv, n_keep), dtype=torch.int32, device=dev)
+    s = cache.struct()
+    rc = lib().dqk_select_decode_attn_rope(ctypes.byref(s), _ptr(q), _ptr(t_q), _ptr(rope_cos), _ptr(rope_sin),
+                                           int(n_keep), nb, B, hq, _ptr(page_table), int(page_table.shape[1]),
+                                           _ptr(seq_lens), float(sm_scale), int(num_splits), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                                           _ptr(q_prime), _ptr(sel_idx), _stream(stream))
+    _check(rc, "dqk_select_decode_attn_rope")
     return out, lse, q_prime, sel_idx
 
 

@@ -318,6 +318,129 @@ int dqk_select_decode_attn_vrot(const dqk_cache *c, const void *q_bf16, const fl
                               stream);
 }
 
+// ---- bucket-relative RoPE (Dual-QK §3.4, App. C.4)
+
+int dqk_quantize_append_rope(const dqk_cache *c, const void *k_bf16, const void *v_bf16, const void *t_k_bf16,
+                             const float *rope_cos, const float *rope_sin, int32_t n_buckets, int32_t n_seqs,
+                             const int32_t *cu_tokens, int64_t total_tokens, const int32_t *page_table,
+                             int32_t max_pages, float *kprime_dbg, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    if (!k_bf16 || !v_bf16 || !t_k_bf16 || !rope_cos || !rope_sin || !cu_tokens || !page_table) return DQK_ERR_NULL;
+    if (n_seqs < 1 || max_pages < 1 || total_tokens < 1 || n_buckets < 1 ||
+        (int64_t)n_buckets * dqk::ROPE_PAGES < max_pages)
+        return DQK_ERR_SHAPE;
+    if (n_seqs > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(t_k_bf16) || !aligned16(rope_cos) ||
+        !aligned16(rope_sin) || !aligned16(cu_tokens) || !aligned16(page_table) ||
+        (kprime_dbg && !aligned16(kprime_dbg)))
+        return DQK_ERR_ALIGN;
+    return hip_status(dqk::launch_append_rope(*c, static_cast<const uint16_t *>(k_bf16),
+                                              static_cast<const uint16_t *>(v_bf16),
+                                              static_cast<const uint16_t *>(t_k_bf16), rope_cos, rope_sin, n_seqs,
+                                              cu_tokens, page_table, max_pages, kprime_dbg, stream));
+}
+
+int dqk_select_channels_rope(const void *q_bf16, const float *t_q, const float *rope_cos, const float *rope_sin,
+                             int32_t n_buckets, int32_t batch, int32_t hq, int32_t hkv, int32_t n_keep,
+                             float *q_prime, int32_t *sel_idx, hipStream_t stream) {
+    if (!q_bf16 || !t_q || !rope_cos || !rope_sin || !q_prime || !sel_idx) return DQK_ERR_NULL;
+    if (batch < 1 || hq < 1 || hkv < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM || n_buckets < 1)
+        return DQK_ERR_SHAPE;
+    if (hq / hkv > 64 || (int64_t)batch * n_buckets > 65535) return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(q_bf16) || !aligned16(t_q) || !aligned16(rope_cos) || !aligned16(rope_sin) ||
+        !aligned16(q_prime) || !aligned16(sel_idx))
+        return DQK_ERR_ALIGN;
+    return hip_status(dqk::launch_select(static_cast<const uint16_t *>(q_bf16), t_q, nullptr, batch, hq, hkv, n_keep,
+                                         q_prime, sel_idx, stream, rope_cos, rope_sin, n_buckets));
+}
+
+namespace {
+// splits of the bucketed decode: the usual choice, raised so that every split
+// holds few enough buckets for the kernel's LDS
+int resolve_splits_rope(int batch, int hq, int hkv, int max_pages, int num_splits, int n_keep) {
+    const int s = resolve_splits(batch, hq, hkv, max_pages, num_splits, n_keep);
+    const int m = dqk::decode_splits_rope(max_pages, n_keep);
+    return s > m ? s : m;
+}
+
+// Decode of a cache in bucket frames (one_call: the per-bucket selection
+// first) and the split merge.
+int rope_decode_core(const dqk_cache *c, const void *q_bf16, const float *t_q, const float *rope_cos,
+                     const float *rope_sin, const float *q_prime_in, const int32_t *sel_in, int32_t n_keep,
+                     int32_t n_buckets, int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                     const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes,
+                     float *out, float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    const bool one_call = q_bf16 != nullptr;
+    if (one_call ? (!t_q || !rope_cos || !rope_sin || !q_prime || !sel_idx) : (!q_prime_in || !sel_in))
+        return DQK_ERR_NULL;
+    if (!page_table || !seq_lens || !workspace || !out) return DQK_ERR_NULL;
+    const int hkv = c->num_kv_heads;
+    if (batch < 1 || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM || max_pages < 1 ||
+        n_buckets < 1 || (int64_t)n_buckets * dqk::ROPE_PAGES < max_pages || num_splits < 0 ||
+        num_splits > max_pages)
+        return DQK_ERR_SHAPE;
+    if (!dqk::use_mfma_decode(hq, hkv, n_keep)) return DQK_ERR_UNSUPPORTED;  // more than MAX_GROUP heads per KV head
+    if ((int64_t)batch * hkv * dqk::mfma_head_sets(hq, hkv) > 65535 || (int64_t)batch * n_buckets > 65535 ||
+        (int64_t)batch * n_buckets * hq > 2147483647 / 2)
+        return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(page_table) || !aligned16(seq_lens) || !aligned16(workspace) || !aligned16(out) ||
+        (lse && !aligned16(lse)))
+        return DQK_ERR_ALIGN;
+    if (one_call ? (!aligned16(q_bf16) || !aligned16(t_q) || !aligned16(rope_cos) || !aligned16(rope_sin) ||
+                    !aligned16(q_prime) || !aligned16(sel_idx))
+                 : (!aligned16(q_prime_in) || !aligned16(sel_in)))
+        return DQK_ERR_ALIGN;
+    const int splits = resolve_splits_rope(batch, hq, hkv, max_pages, num_splits, n_keep);
+    if (ws_bytes < (size_t)batch * hq * splits * dqk::PART_FLOATS * sizeof(float)) return DQK_ERR_WORKSPACE;
+    dqk::DecodeArgs a{c,         q_prime_in, sel_in, n_keep, batch, hq, hkv, page_table, max_pages, seq_lens,
+                      sm_scale, splits,     static_cast<float *>(workspace), out, lse};
+    a.n_buckets = n_buckets;
+    if (one_call) {  // the per-bucket selection, then the decode reads it
+        hipError_t e = dqk::launch_select(static_cast<const uint16_t *>(q_bf16), t_q, nullptr, batch, hq, hkv, n_keep,
+                                          q_prime, sel_idx, stream, rope_cos, rope_sin, n_buckets);
+        if (e != hipSuccess) return hip_status(e);
+        a.q_prime = q_prime;
+        a.sel_idx = sel_idx;
+    }
+    hipError_t e = dqk::launch_decode_mfma(a, stream);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(dqk::launch_merge(a.partials, batch, hq, splits, out, lse, stream));
+}
+}  // namespace
+
+size_t dqk_decode_rope_workspace_size(int32_t batch, int32_t hq, int32_t hkv, int32_t n_buckets,
+                                      int32_t num_splits) {
+    if (batch < 1 || hq < 1 || hkv < 1 || n_buckets < 1 || num_splits < 0) return 0;
+    // the splits grow with the page count: size for the most pages n_buckets cover
+    const int mp = (int)((int64_t)n_buckets * dqk::ROPE_PAGES > 2147483647 ? 2147483647
+                                                                            : n_buckets * dqk::ROPE_PAGES);
+    return (size_t)batch * hq * resolve_splits_rope(batch, hq, hkv, mp, num_splits, 0) * dqk::PART_FLOATS *
+           sizeof(float);
+}
+
+int dqk_decode_attn_rope(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
+                         int32_t n_buckets, int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
+                         const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
+                         size_t ws_bytes, float *out, float *lse, hipStream_t stream) {
+    return rope_decode_core(c, nullptr, nullptr, nullptr, nullptr, q_prime, sel_idx, n_keep, n_buckets, batch, hq,
+                            page_table, max_pages, seq_lens, sm_scale, num_splits, workspace, ws_bytes, out, lse,
+                            nullptr, nullptr, stream);
+}
+
+int dqk_select_decode_attn_rope(const dqk_cache *c, const void *q_bf16, const float *t_q, const float *rope_cos,
+                                const float *rope_sin, int32_t n_keep, int32_t n_buckets, int32_t batch, int32_t hq,
+                                const int32_t *page_table, int32_t max_pages, const int32_t *seq_lens,
+                                float sm_scale, int32_t num_splits, void *workspace, size_t ws_bytes, float *out,
+                                float *lse, float *q_prime, int32_t *sel_idx, hipStream_t stream) {
+    if (!q_bf16) return DQK_ERR_NULL;
+    return rope_decode_core(c, q_bf16, t_q, rope_cos, rope_sin, nullptr, nullptr, n_keep, n_buckets, batch, hq,
+                            page_table, max_pages, seq_lens, sm_scale, num_splits, workspace, ws_bytes, out, lse,
+                            q_prime, sel_idx, stream);
+}
+
 int dqk_decode_attn_noalloc(const dqk_cache *c, const float *q_prime, const int32_t *sel_idx, int32_t n_keep,
                             int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
                             const int32_t *seq_lens, float sm_scale, int32_t num_splits, float *out, float *lse,

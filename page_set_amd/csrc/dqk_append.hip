@@ -32,6 +32,12 @@
 // slot c ^ (r & 15)); the 16 x 16 output tiles are (channel, token), so a lane
 // holds four consecutive channels of one token (one code byte) and the
 // group's other 24 channels sit in the lanes 16 and 32 apart.
+//
+// Bucket-relative RoPE (§3.4, App. C.4): a page lies inside one 2048-token
+// bucket (logical page i in bucket i / 16), so once its key tile has landed
+// each lane turns the channel pairs (i, i + 64) of its chunk pair back by the
+// bucket's anchor in place (fp32, rounded to bf16 to nearest even) before the
+// MFMA reads the tile.
 // Built with -ffp-contract=off: the grid arithmetic must round as written.
 #include "dqk_internal.h"
 
@@ -515,6 +521,7 @@ struct AppendSrc {
     const uint16_t *r_v;  // rotated values only: R_V bf16 [Hkv][128][128], the clip ratio, v' output or null
     float clip;
     float *vprime_dbg;
+    const float *rope_cos = nullptr, *rope_sin = nullptr;  // bucket-relative RoPE only: tables [n_buckets][64]
 };
 
 __device__ __forceinline__ int64_t tier_pages_of(int64_t L) {
@@ -522,12 +529,52 @@ __device__ __forceinline__ int64_t tier_pages_of(int64_t L) {
 }
 
 // Variants: plain; rotated values (a second set of fragments in VGPRs);
-// per-token key grids (both channel tiles' accumulators live at once).  The
-// last two run two workgroups a CU.
-enum { VAR_PLAIN = 0, VAR_VROT = 1, VAR_TOKGRID = 2 };
+// per-token key grids (both channel tiles' accumulators live at once);
+// bucket-relative RoPE (plain, with the key tile turned in LDS).  Rotated
+// values and per-token grids run two workgroups a CU.
+enum { VAR_PLAIN = 0, VAR_VROT = 1, VAR_TOKGRID = 2, VAR_ROPE = 3 };
+
+// Turn the key tile at ks (rows = tokens, chunk c of row r at slot
+// c ^ swz_k(r)) back by one bucket's anchor: lane tid owns chunk pair
+// (c, c + 8), c = tid % 8 (channels 8c .. 8c + 7 and their partners 64 later),
+// of rows tid / 8 + 32 j.  Rows past the sequence end hold token 0 again;
+// turning them is harmless (their k' is never used).
+__device__ __forceinline__ void rope_turn_tile(uint32_t ks, const float *__restrict__ cs,
+                                               const float *__restrict__ sn) {
+    const int tid = fresh_tid(), c = tid & 7;
+    float cv[8], sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        cv[e] = cs[8 * c + e];
+        sv[e] = sn[8 * c + e];
+    }
+#pragma unroll
+    for (int j = 0; j < PG * 8 / 256; ++j) {
+        const int r = (tid >> 3) + 32 * j;
+        const uint32_t alo = ks + (uint32_t)r * 256 + (((uint32_t)c ^ swz_k(r)) << 4);
+        const uint32_t ahi = ks + (uint32_t)r * 256 + (((uint32_t)(c + 8) ^ swz_k(r)) << 4);
+        const u32x4 lo = lds_ld<u32x4>(alo), hi = lds_ld<u32x4>(ahi);
+        u32x4 ylo, yhi;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t pl = 0, ph = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 2 * w + h;
+                const float x = bf2f((uint16_t)(lo[w] >> (16 * h))), xp = bf2f((uint16_t)(hi[w] >> (16 * h)));
+                pl |= (uint32_t)f2bf_rne(rope_turn(x, xp, cv[e], sv[e], true)) << (16 * h);
+                ph |= (uint32_t)f2bf_rne(rope_turn(xp, x, cv[e], sv[e], false)) << (16 * h);
+            }
+            ylo[w] = pl;
+            yhi[w] = ph;
+        }
+        lds_st<u32x4>(alo, ylo);
+        lds_st<u32x4>(ahi, yhi);
+    }
+}
 
 template <bool DBG, int MODE, int VAR>
-__global__ __launch_bounds__(256, VAR == VAR_PLAIN ? 4 : 2) void append_kernel(dqk_cache c, AppendSrc src, const uint16_t *__restrict__ t_k,
+__global__ __launch_bounds__(256, (VAR == VAR_PLAIN || VAR == VAR_ROPE) ? 4 : 2) void append_kernel(dqk_cache c, AppendSrc src, const uint16_t *__restrict__ t_k,
                                                      const int32_t *__restrict__ page_table, int max_pages,
                                                      float *__restrict__ kprime_dbg) {
     // T_K^T [out ch][in ch] first, then each page's key tile [token][in ch]; rows of 256 bytes
@@ -620,6 +667,11 @@ __global__ __launch_bounds__(256, VAR == VAR_PLAIN ? 4 : 2) void append_kernel(d
         }
 
         wait_all_barrier();  // the tile has landed
+        if constexpr (VAR == VAR_ROPE) {
+            const int bk = pi / ROPE_PAGES;
+            rope_turn_tile(ks, src.rope_cos + bk * (D / 2), src.rope_sin + bk * (D / 2));
+            __syncthreads();
+        }
         if constexpr (VAR == VAR_TOKGRID) {
             if (nvalid == PG)
                 keys_of_page_tok<true, DBG>(c, ks, bop, p, g, hkv, nvalid, t0, kprime_dbg);
@@ -708,6 +760,22 @@ hipError_t launch_append_tokgrid(const dqk_cache &c, const uint16_t *k, const ui
                            page_table, max_pages, kprime_dbg);
     else
         hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, VAR_TOKGRID>), grid, dim3(256), 0, s, c, src, t_k,
+                           page_table, max_pages, kprime_dbg);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_rope(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                              const float *rope_cos, const float *rope_sin, int n_seqs, const int32_t *cu_tokens,
+                              const int32_t *page_table, int max_pages, float *kprime_dbg, hipStream_t s) {
+    dim3 grid((max_pages + NPW - 1) / NPW, n_seqs, c.num_kv_heads);
+    AppendSrc src{k, v, cu_tokens, nullptr, nullptr, nullptr, nullptr, 1.0f, nullptr};
+    src.rope_cos = rope_cos;
+    src.rope_sin = rope_sin;
+    if (kprime_dbg)
+        hipLaunchKernelGGL((append_kernel<true, APPEND_PLAIN, VAR_ROPE>), grid, dim3(256), 0, s, c, src, t_k,
+                           page_table, max_pages, kprime_dbg);
+    else
+        hipLaunchKernelGGL((append_kernel<false, APPEND_PLAIN, VAR_ROPE>), grid, dim3(256), 0, s, c, src, t_k,
                            page_table, max_pages, kprime_dbg);
     return hipGetLastError();
 }

@@ -59,12 +59,15 @@ constexpr float LN2 = 0.6931471805599453f;
 static_assert(KBLK == 8, "the kernel walks 8-page blocks in halves of four pages");
 
 // ---------------------------------------------------------------- LDS layout
-// KSX = KS + 16 KG: KS 16-channel k-steps; KG = 1 for one key grid per token
-// (the block's key metadata then is [8 pages][128 tokens] pairs, 4 KB).
+// KSX = KS + 16 KG + 32 RB: KS 16-channel k-steps; KG = 1 for one key grid per
+// token (the block's key metadata then is [8 pages][128 tokens] pairs, 4 KB);
+// RB = 1 for bucket-relative RoPE (a query and a channel list per 2048-token
+// bucket, all of a split's buckets kept in LDS past the usual layout).
 template <int KSX>
 struct Lay {
     static constexpr int KS = KSX & 15;
-    static constexpr bool KG = (KSX >> 4) != 0;
+    static constexpr bool KG = ((KSX >> 4) & 1) != 0;
+    static constexpr bool RB = ((KSX >> 5) & 1) != 0;
     static constexpr int NR = 16 * KS;              // key row slots (selected INT2 channels, padded)
     static constexpr int NMR = (NR + 31) / 32 * 32;  // key metadata rows (whole load instructions)
     // key stage: rows [NR][256 B] (16-byte chunk c of row r at c ^ (2 ((r >> 3) & 1))),
@@ -87,14 +90,22 @@ struct Lay {
     static constexpr int PBPAGE = 4 * PBROW;
     static constexpr int PBBUF = 4 * PBPAGE;
     // three value stages (values two steps ahead); two when the key stages leave no room
-    // for a third (values then one step ahead)
-    static constexpr int NV = KS <= 7 ? 3 : 2;
+    // for a third (values then one step ahead) or, with buckets, for eight buckets' queries
+    static constexpr int NV = KS <= (RB ? 6 : 7) ? 3 : 2;
     static constexpr int PB = VS + NV * VST;        // [2 buffers][4 pages][4 heads][PBROW]
     static constexpr int AL = PB + 2 * PBBUF;       // [2 buffers][4 pages][4 heads] float rescale factors
     static constexpr int QT = AL + 2 * 16 * 4;      // [4 scoring waves][KS][256 B] q~ B fragments
     static constexpr int ZERO = QT + 4 * KS * 256;  // KS * 256 bytes of zeros
     static constexpr int ONES = ZERO + KS * 256;    // 256 bytes of fp16 1.0
     static constexpr int TOTAL = ONES + 256;
+    // buckets (RB): per bucket of the split q' of the four heads [4][128] fp32
+    // and the ascending channel list [128] int32 (the layout of the scratch
+    // below), up to MAXB buckets (a split covers at most 2 MAXB blocks)
+    static constexpr int RBB = GRP * D * 4 + D * 4;
+    static constexpr int RBA = TOTAL;
+    static constexpr int MAXB_ROOM = (160 * 1024 - TOTAL) / RBB;
+    static constexpr int MAXB = MAXB_ROOM < 8 ? MAXB_ROOM : 8;
+    static constexpr int TOTAL_ALL = RB ? RBA + MAXB * RBB : TOTAL;
     // the selection run inside the decode (prologue only): T_Q of the KV head
     // [128][128] fp32 at 0, the four heads' q in fp32, the pooled energies and
     // a ballot word after it; q' and the selected channels go to the usual
@@ -115,7 +126,8 @@ struct Lay {
     static constexpr int KN = (NKI + NW - 1) / NW;  // key instructions per wave per block
     static constexpr int VN = 24 / NW;              // value instructions per wave per half
     static_assert(24 % NW == 0, "value loads split evenly");
-    static_assert(TOTAL <= 160 * 1024, "LDS");
+    static_assert(TOTAL <= 160 * 1024 && TOTAL_ALL <= 160 * 1024, "LDS");
+    static_assert(!RB || (MAXB >= 1 && !KG), "bucket area");
     static_assert(KST % 16 == 0 && KM % 16 == 0 && K0 % 16 == 0 && VS % 16 == 0 && PB % 16 == 0 &&
                       QT % 16 == 0 && ZERO % 16 == 0 && ONES % 16 == 0,
                   "align");
@@ -399,6 +411,8 @@ struct Feeder {
     int g, hkv, lane, wv, npages, B0, nb, nst;
     int tab;   // lane j: aligned index of block B0 + j (j < TABN), or -1
     int pend;  // loads of this wave issued at the previous step (the ones allowed in flight)
+    uint32_t rba;  // buckets (RB): LDS address of bucket B0 / 2's query and channel list
+    int n_keep;
     int kidx[Ly::KN], kchan[Ly::KN];
     uint32_t kaoff[Ly::KN], vaoff[Ly::VN];
     uint64_t kbase[Ly::KN], kstr[Ly::KN], vbase[Ly::VN], vstr[Ly::VN];
@@ -437,6 +451,13 @@ struct Feeder {
             kbase[k] = uniform64(region_base(*c, key_region<KS>(kidx[k]), g));
             kstr[k] = uniform64(region_stride(key_region<KS>(kidx[k]), hkv));
         }
+    }
+    // Key plans of bucket kl of the split (RB): its channel list in the bucket area.
+    __device__ __forceinline__ void plan_bucket(int kl) {
+        const uint32_t lst = rba + (uint32_t)kl * Ly::RBB + GRP * D * 4;
+        const int has0 = lds_ld<int32_t>(lst) == 0;  // the list is ascending
+        const int R = n_keep - has0;
+        plan_keys([&](int r) { return r < R ? lds_ld<int32_t>(lst + (r + has0) * 4) : 0; });
     }
     // Loads of block j's keys / half u's values; true when the block took the
     // register path (which leaves no load of this wave in flight).
@@ -490,7 +511,12 @@ struct Feeder {
         } else {  // values of half u: needed at the next step, so never left in flight
             if (u < nst && halfpages(u)) issue_vals(u);
         }
-        if (!(u & 1) && (u >> 1) + 1 < nb) np = issue_keys((u >> 1) + 1) ? 0 : np + Ly::KN;
+        if (!(u & 1) && (u >> 1) + 1 < nb) {
+            // with buckets, an even block (B0 is even) starts the next bucket: its channels first
+            if constexpr (Ly::RB)
+                if (!(((u >> 1) + 1) & 1)) plan_bucket(((u >> 1) + 1) >> 1);
+            np = issue_keys((u >> 1) + 1) ? 0 : np + Ly::KN;
+        }
         pend = np;
     }
 };
@@ -590,11 +616,12 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                                                           const float *__restrict__ t_q,
                                                           const float *__restrict__ sel_scale,
                                                           float *__restrict__ qp_out,
-                                                          int32_t *__restrict__ sel_out) {
+                                                          int32_t *__restrict__ sel_out, int nbk) {
     using Ly = Lay<KSX>;
     constexpr int KS = Ly::KS;
     constexpr bool KG = Ly::KG;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Ly::TOTAL];
+    static_assert(!(Ly::RB && FUSED), "buckets take their selection from memory");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Ly::TOTAL_ALL];
     const uint32_t S = lds_addr(smem);
 
     const int split = blockIdx.x, bg = blockIdx.y;
@@ -613,8 +640,12 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     const int L = seq_lens[b];
     const int npages = (L + PG - 1) / PG;
     const int nblk = (npages + KBLK - 1) / KBLK;
-    const int per = (nblk + nsplit - 1) / nsplit;
-    const int B0 = min(nblk, split * per), B1 = min(nblk, B0 + per);
+    // with buckets (two blocks each) a split holds whole buckets, at most MAXB
+    // of them (the launch picks enough splits; a larger split is left empty)
+    int per = (nblk + nsplit - 1) / nsplit;
+    if constexpr (Ly::RB) per = (per + 1) & ~1;
+    const bool fits = !Ly::RB || per <= 2 * Ly::MAXB;
+    const int B0 = fits ? min(nblk, split * per) : nblk, B1 = min(nblk, B0 + per);
     const int nb = B1 - B0;   // 8-page blocks of this split
     const int nst = 2 * nb;   // 4-page halves
     const int32_t *ptab = page_table + (size_t)b * max_pages;
@@ -652,6 +683,8 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
     fd.B0 = B0;
     fd.nb = nb;
     fd.nst = nst;
+    fd.rba = S + Ly::RBA;
+    fd.n_keep = n_keep;
     fd.plan_vals();
     // in flight while the selection runs (or q' and the channel list are staged)
     constexpr bool early_v = Ly::NV == 3 && (!FUSED || Ly::EARLY_V);
@@ -665,6 +698,24 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
                             n_keep, split == 0 ? qp_out : nullptr, split == 0 ? sel_out : nullptr);
         for (int i = tid; i < KS * 64; i += NTHR) lds_st<uint32_t>(S + Ly::ZERO + i * 4, 0u);
         if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
+    } else if constexpr (Ly::RB) {
+        // q' of the four heads and the channel list of every bucket of the split
+        // (bucket kb0 + kl at RBA + kl RBB, laid out as the scratch below)
+        const int kb0 = B0 >> 1, nbl = ((B1 + 1) >> 1) - kb0;
+        const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q_prime);
+        for (int i = tid; i < nbl * 128; i += NTHR) {
+            const int kl = i >> 7, r = i & 127, hr = r >> 5;
+            const size_t row = ((size_t)b * nbk + kb0 + kl) * hq + h0 + hr;
+            lds_st<u32x4>(S + Ly::RBA + kl * Ly::RBB + r * 16,
+                          hr < nh ? qsrc[row * (D / 4) + (r & 31)] : u32x4{0u, 0u, 0u, 0u});
+        }
+        for (int i = tid; i < nbl * 128; i += NTHR) {
+            const int kl = i >> 7, r = i & 127;
+            const int32_t *ssrc = sel_idx + (((size_t)b * nbk + kb0 + kl) * hkv + g) * n_keep;
+            lds_st<int32_t>(S + Ly::RBA + kl * Ly::RBB + GRP * D * 4 + r * 4, r < n_keep ? ssrc[r] : 0);
+        }
+        for (int i = tid; i < KS * 64; i += NTHR) lds_st<uint32_t>(S + Ly::ZERO + i * 4, 0u);
+        if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
     } else {
         const u32x4 *qsrc = reinterpret_cast<const u32x4 *>(q_prime + ((size_t)b * hq + (size_t)h0) * D);
         const int32_t *ssrc = sel_idx + ((size_t)b * hkv + g) * n_keep;
@@ -674,11 +725,13 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
         if (tid < 64) lds_st<uint32_t>(S + Ly::ONES + tid * 4, 0x3C003C00u);
     }
     __syncthreads();
-    auto qv = [&](int h, int j) { return lds_ld<float>(scr + (h * D + j) * 4); };
-    const int has0 = lds_ld<int32_t>(scr + GRP * D * 4) == 0;  // the list is ascending
+    // q' and the channel list in force (with buckets: those of the split's first bucket)
+    const uint32_t qsel = Ly::RB ? S + Ly::RBA : scr;
+    auto qv = [&](int h, int j) { return lds_ld<float>(qsel + (h * D + j) * 4); };
+    const int has0 = lds_ld<int32_t>(qsel + GRP * D * 4) == 0;  // the list is ascending
     const int R = n_keep - has0;                                 // selected INT2 channels
     // channel of key row slot r (slots past R read channel 0's all-zero row)
-    auto chan_of = [&](int r) { return r < R ? lds_ld<int32_t>(scr + GRP * D * 4 + (r + has0) * 4) : 0; };
+    auto chan_of = [&](int r) { return r < R ? lds_ld<int32_t>(qsel + GRP * D * 4 + (r + has0) * 4) : 0; };
     // key load plans, the same for every block: key instructions wv + 12k (a
     // wave past the end repeats a real load: same bytes, same place)
     fd.plan_keys(chan_of);
@@ -698,7 +751,23 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
             QC[i][e] = (slot < 16 * KS && slot < R) ? qv(hp, chan_of(slot)) * C : 0.0f;
         }
     const int hh = (ar >> 1) & 3;  // score column head
-    const float q0c = has0 ? qv(hh, 0) * C : 0.0f;
+    float q0c = has0 ? qv(hh, 0) * C : 0.0f;
+    // with buckets: the same constants from bucket kl's q' and channel list
+    auto bucket_qc = [&](int kl) {
+        const uint32_t qb = S + Ly::RBA + (uint32_t)kl * Ly::RBB, lst = qb + GRP * D * 4;
+        const int h0s = lds_ld<int32_t>(lst) == 0;
+        const int Rb = n_keep - h0s;
+#pragma unroll
+        for (int i = 0; i < NPI; ++i)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int slot = 2 * (j16 + 16 * i) + e;
+                QC[i][e] = (slot < 16 * KS && slot < Rb)
+                               ? lds_ld<float>(qb + (hp * D + lds_ld<int32_t>(lst + (slot + h0s) * 4)) * 4) * C
+                               : 0.0f;
+            }
+        q0c = h0s ? lds_ld<float>(qb + hh * D * 4) * C : 0.0f;
+    };
     __syncthreads();  // scratch read by every wave
 
     // ---- prologue loads: keys of block 0, values of half 0 (with two value stages, at step 0)
@@ -776,6 +845,8 @@ __global__ __launch_bounds__(NTHR) void decode_blk_kernel(dqk_cache c, const flo
         for (int u = 0; u <= nst; ++u) {
             fd.top(u, halfpages);
             if (u >= nst) continue;
+            if constexpr (Ly::RB)
+                if (u > 0 && (u & 3) == 0) bucket_qc(u >> 2);  // an even block (B0 is even) starts a bucket
             const int ps = 4 * (u & 1) + w;
             const int nv = page_valid(u >> 1, ps);
             if (nv <= 0) continue;
@@ -1138,6 +1209,29 @@ int decode_splits_mfma(int batch, int units_per_seq, int max_pages, int n_keep) 
     return s < 1 ? 1 : s;
 }
 
+// n_keep 0: the most any n_keep needs (workspace sizing)
+int decode_splits_rope(int max_pages, int n_keep) {
+    int maxb = 8;
+    switch (n_keep > 0 ? ks_of(n_keep) : 0) {
+        case 0: {
+            const int m[8] = {Lay<33>::MAXB, Lay<34>::MAXB, Lay<35>::MAXB, Lay<36>::MAXB,
+                              Lay<37>::MAXB, Lay<38>::MAXB, Lay<39>::MAXB, Lay<40>::MAXB};
+            for (int i = 0; i < 8; ++i) maxb = m[i] < maxb ? m[i] : maxb;
+            break;
+        }
+        case 1: maxb = Lay<1 + 32>::MAXB; break;
+        case 2: maxb = Lay<2 + 32>::MAXB; break;
+        case 3: maxb = Lay<3 + 32>::MAXB; break;
+        case 4: maxb = Lay<4 + 32>::MAXB; break;
+        case 5: maxb = Lay<5 + 32>::MAXB; break;
+        case 6: maxb = Lay<6 + 32>::MAXB; break;
+        case 7: maxb = Lay<7 + 32>::MAXB; break;
+        default: maxb = Lay<8 + 32>::MAXB; break;
+    }
+    const int nblk = (max_pages + KBLK - 1) / KBLK;
+    return (nblk + 2 * maxb - 1) / (2 * maxb);
+}
+
 bool fused_select_ok(int hq, int hkv, int n_keep, bool token_grid) {
     if (!use_mfma_decode(hq, hkv, n_keep) || hq != GRP * hkv) return false;  // the prologue pools four heads
     const int g = token_grid ? 16 : 0;
@@ -1166,12 +1260,16 @@ static hipError_t launch_ks2(const DecodeArgs &a, hipStream_t s) {
     dim3 grid(a.num_splits, a.batch * a.hkv * mfma_head_sets(a.hq, a.hkv));
     hipLaunchKernelGGL((decode_blk_kernel<KSX, FUSED>), grid, dim3(NTHR), 0, s, *a.c, a.q_prime, a.sel_idx, a.n_keep,
                        a.hq, a.page_table, a.max_pages, a.seq_lens, a.sm_scale, a.num_splits, a.partials, a.q_bf16,
-                       a.t_q, a.sel_scale, a.qp_out, a.sel_out);
+                       a.t_q, a.sel_scale, a.qp_out, a.sel_out, a.n_buckets);
     return hipGetLastError();
 }
 
 template <int KS>
 static hipError_t launch_ks(const DecodeArgs &a, hipStream_t s) {
+    if (a.n_buckets > 0) {  // bucket-relative RoPE (KSX = KS + 32), the selection from memory
+        if (a.q_bf16 || a.token_grid) return hipErrorInvalidValue;
+        return launch_ks2<KS + 32, false>(a, s);
+    }
     if (a.token_grid) {  // per-token key grids (KSX = KS + 16)
         if constexpr (Lay<KS + 16>::FUSABLE) {
             if (a.q_bf16) return launch_ks2<KS + 16, true>(a, s);

@@ -57,6 +57,23 @@ __device__ __forceinline__ uint16_t f2bf_rne(float x) {
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// ---------------------------------------------------------------- bucket-relative RoPE
+// Stored keys live in the frame of their bucket's anchor (Dual-QK paper, §3.4
+// and App. C.4): bucket k of a sequence holds positions 2048 k .. 2048 k + 2047
+// (sixteen whole pages), anchor a_k = 2048 k.  A bucket's table holds
+// cos(a_k theta_i) and -sin(a_k theta_i) for the rotate-half channel pairs
+// (i, i + 64), i = 0..63.
+constexpr int ROPE_BUCKET = 2048;
+constexpr int ROPE_PAGES = ROPE_BUCKET / PG;
+
+// Channel j of a vector turned by a table entry (c, s) of its pair: x is
+// channel j, xp its partner j ^ 64; lower half x c - xp s, upper half
+// x c + xp s, each product and the sum rounded to fp32.
+__device__ __forceinline__ float rope_turn(float x, float xp, float c, float s, bool lower) {
+    const float a = __fmul_rn(x, c), b = __fmul_rn(xp, s);
+    return lower ? __fsub_rn(a, b) : __fadd_rn(a, b);
+}
+
 // |x| onto the binary16 grid toward zero: bits of the magnitude, and whether
 // the value was inexact.  Magnitudes above 65504 saturate to 65504 (inexact).
 __device__ __forceinline__ uint32_t f16_mag_trunc(uint32_t ua, bool &inexact) {
@@ -213,8 +230,12 @@ __device__ __forceinline__ void merge_row(Part part, int nsplit, int tid, bool a
 }
 
 // ---------------------------------------------------------------- launchers
+// rope_cos / rope_sin non-null: one selection per (sequence, bucket) of the
+// query turned by the bucket's table, q_prime [batch][n_buckets][hq][128] and
+// sel_idx [batch][n_buckets][hkv][n_keep]; null: n_buckets must be 1.
 hipError_t launch_select(const uint16_t *q, const float *t_q, const float *sel_scale, int batch, int hq, int hkv,
-                         int n_keep, float *q_prime, int32_t *sel_idx, hipStream_t s);
+                         int n_keep, float *q_prime, int32_t *sel_idx, hipStream_t s,
+                         const float *rope_cos = nullptr, const float *rope_sin = nullptr, int n_buckets = 1);
 
 hipError_t launch_append(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k, int n_seqs,
                          const int32_t *cu_tokens, const int32_t *page_table, int max_pages, float *kprime_dbg,
@@ -229,6 +250,10 @@ hipError_t launch_append_vrot(const dqk_cache &c, const uint16_t *k, const uint1
                               const uint16_t *r_v, float clip, int n_seqs, const int32_t *cu_tokens,
                               const int32_t *page_table, int max_pages, float *kprime_dbg, float *vprime_dbg,
                               hipStream_t s);
+// keys turned back to their bucket's anchor before T_K (tables [n_buckets][64])
+hipError_t launch_append_rope(const dqk_cache &c, const uint16_t *k, const uint16_t *v, const uint16_t *t_k,
+                              const float *rope_cos, const float *rope_sin, int n_seqs, const int32_t *cu_tokens,
+                              const int32_t *page_table, int max_pages, float *kprime_dbg, hipStream_t s);
 // inverse value rotation of decode outputs (dqk_vrot.hip); the split merge followed by it
 hipError_t launch_value_unrotate(const float *o_rot, const float *r_inv, int batch, int hq, int hkv, float *out,
                                  hipStream_t s);
@@ -268,6 +293,11 @@ struct DecodeArgs {
     const float *sel_scale = nullptr;
     // one key grid per token (dqk_quantize_append_tokgrid's layout)
     bool token_grid = false;
+    // bucket-relative RoPE: n_buckets > 0 gives q_prime [batch][n_buckets][hq]
+    // [128] and sel_idx [batch][n_buckets][hkv][n_keep]; the pages of bucket
+    // k (16 k .. 16 k + 15) score with row k; num_splits at least
+    // decode_splits_rope (each split holds whole buckets that fit in LDS)
+    int n_buckets = 0;
 };
 
 // Query heads per KV head that the decode entry points serve.
@@ -282,6 +312,8 @@ int decode_splits_mfma(int batch, int units_per_seq, int max_pages, int n_keep);
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t s);
 // Split count of the BF16 baseline decode.
 int decode_splits_bf16(int batch, int hkv, int max_pages);
+// Least split count of the bucketed decode for this context and n_keep.
+int decode_splits_rope(int max_pages, int n_keep);
 // Whether the MFMA decode can run the selection itself for this n_keep.
 bool fused_select_ok(int hq, int hkv, int n_keep, bool token_grid = false);
 
@@ -316,6 +348,7 @@ hipError_t launch_stream_read(const void *src, size_t bytes, uint32_t *sink, hip
 
 hipError_t launch_merge(const float *partials, int batch, int hq, int num_splits, float *out, float *lse,
                         hipStream_t s);
+
 // The merge with n_extra more partials per (sequence, query head) row at
 // extra + (row * n_extra + i) * PART_FLOATS.
 hipError_t launch_merge_extra(const float *partials, int batch, int hq, int num_splits, const float *extra,

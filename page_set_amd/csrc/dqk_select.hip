@@ -11,6 +11,11 @@
 // w_j = 1 / delta_j), e = fp32(q'_{h,j} w_j); q' itself is left unscaled.
 // Channel j is kept iff fewer than n_keep channels beat it (larger S, or
 // equal S at a lower index); kept channels are written in ascending order.
+//
+// Bucket-relative RoPE (§3.4, App. C.4): block y = (sequence b, bucket k)
+// turns q by bucket k's anchor table while it stages it (fp32, each product
+// and sum rounded), then runs the same chains and rank test; its q' and mask
+// go to row (b, k) of [batch][n_buckets][..] outputs.
 // Built with -ffp-contract=off: only the written fmas fuse.
 #include "dqk_internal.h"
 
@@ -21,10 +26,12 @@ namespace {
 constexpr int THREADS = 256;
 constexpr int HALVES = THREADS / D;  // query-head interleave across the two lane halves
 
-// Stage T_Q[g] (64 KB) and q of the group (bf16 -> fp32) into LDS; every
-// load of the transform is issued before any is stored.
+// Stage T_Q[g] (64 KB) and q of the group (bf16 -> fp32, turned by the
+// bucket's table rcs / rsn when they are non-null) into LDS; every load of
+// the transform is issued before any is stored.
 __device__ __forceinline__ void stage_inputs(const uint16_t *__restrict__ q, const float *__restrict__ t_q, int g,
-                                             int b, int hq, int grp, float *t_lds, float *q_lds) {
+                                             int b, int hq, int grp, float *t_lds, float *q_lds,
+                                             const float *__restrict__ rcs, const float *__restrict__ rsn) {
     const int tid = threadIdx.x;
     const float4 *tsrc = reinterpret_cast<const float4 *>(t_q + (size_t)g * D * D);
     float4 *tdst = reinterpret_cast<float4 *>(t_lds);
@@ -33,7 +40,14 @@ __device__ __forceinline__ void stage_inputs(const uint16_t *__restrict__ q, con
 #pragma unroll
     for (int k = 0; k < PER; ++k) stage[k] = tsrc[tid + k * THREADS];
     const uint16_t *qg = q + ((size_t)b * hq + (size_t)g * grp) * D;
-    for (int i = tid; i < grp * D; i += THREADS) q_lds[i] = bf2f(qg[i]);
+    if (rcs) {
+        for (int i = tid; i < grp * D; i += THREADS) {
+            const int j = i & (D - 1), jp = j & (D / 2 - 1);
+            q_lds[i] = rope_turn(bf2f(qg[i]), bf2f(qg[i ^ (D / 2)]), rcs[jp], rsn[jp], j < D / 2);
+        }
+    } else {
+        for (int i = tid; i < grp * D; i += THREADS) q_lds[i] = bf2f(qg[i]);
+    }
 #pragma unroll
     for (int k = 0; k < PER; ++k) tdst[tid + k * THREADS] = stage[k];
 }
@@ -87,15 +101,19 @@ __global__ __launch_bounds__(THREADS) void select_kernel_g(const uint16_t *__res
                                                            const float *__restrict__ t_q, int hq, int hkv,
                                                            int n_keep, const float *__restrict__ sel_scale,
                                                            float *__restrict__ q_prime,
-                                                           int32_t *__restrict__ sel_idx) {
+                                                           int32_t *__restrict__ sel_idx,
+                                                           const float *__restrict__ rope_cos,
+                                                           const float *__restrict__ rope_sin, int nbk) {
     constexpr int NH = GRP >= HALVES ? GRP / HALVES : 1;  // chains per lane
     __shared__ __attribute__((aligned(16))) float t_lds[D * D];
     __shared__ __attribute__((aligned(16))) float q_lds[GRP * D];
     __shared__ __attribute__((aligned(16))) float qp_lds[GRP * D];
     __shared__ __attribute__((aligned(16))) float s_lds[D];
     __shared__ unsigned long long mask0;
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    stage_inputs(q, t_q, g, b, hq, GRP, t_lds, q_lds);
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;  // b: row (sequence, bucket) of the outputs
+    const int sq = b / nbk, bk = b - sq * nbk;
+    stage_inputs(q, t_q, g, sq, hq, GRP, t_lds, q_lds, rope_cos ? rope_cos + bk * (D / 2) : nullptr,
+                 rope_sin ? rope_sin + bk * (D / 2) : nullptr);
     __syncthreads();
     const int j = tid & (D - 1), half = tid >> 7;
     if (GRP >= HALVES || half == 0) {
@@ -135,14 +153,18 @@ __global__ __launch_bounds__(THREADS) void select_kernel(const uint16_t *__restr
                                                          int hq, int hkv, int n_keep,
                                                          const float *__restrict__ sel_scale,
                                                          float *__restrict__ q_prime,
-                                                         int32_t *__restrict__ sel_idx) {
+                                                         int32_t *__restrict__ sel_idx,
+                                                         const float *__restrict__ rope_cos,
+                                                         const float *__restrict__ rope_sin, int nbk) {
     __shared__ __attribute__((aligned(16))) float t_lds[D * D];  // T_Q of this KV head (64 KB)
     extern __shared__ __attribute__((aligned(16))) float q_lds[];  // [grp][128] q (bf16 -> fp32), then [grp][128] q'
     __shared__ __attribute__((aligned(16))) float s_lds[D];
     __shared__ unsigned long long mask0;
-    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;  // b: row (sequence, bucket) of the outputs
     const int grp = hq / hkv;
-    stage_inputs(q, t_q, g, b, hq, grp, t_lds, q_lds);
+    const int sq = b / nbk, bk = b - sq * nbk;
+    stage_inputs(q, t_q, g, sq, hq, grp, t_lds, q_lds, rope_cos ? rope_cos + bk * (D / 2) : nullptr,
+                 rope_sin ? rope_sin + bk * (D / 2) : nullptr);
     __syncthreads();
 
     float *qpl = q_lds + grp * D;  // q' [grp][128]
@@ -160,16 +182,162 @@ __global__ __launch_bounds__(THREADS) void select_kernel(const uint16_t *__restr
                 sel_idx + ((size_t)b * hkv + g) * n_keep);
 }
 
+// Selection of KB = 16 / GRP buckets per workgroup (bucket-relative RoPE):
+// T_Q[g] is staged once for the workgroup's buckets kb0 .. kb0 + KB - 1 of
+// sequence b; the 16 (bucket, head) rows of q, each turned by its bucket's
+// table, sit in LDS and lane (half, j) runs the eight chains of rows half,
+// half + 2, .. for output channel j together, one read of T_Q column j per
+// input channel serving all eight.  Each chain is the fma chain over
+// ascending input channel of select_kernel; the tail takes two buckets at a
+// time (one per lane half) with the pooled energy and rank rule of select_tail.
+template <int GRP>
+__global__ __launch_bounds__(THREADS) void select_rope_kernel(const uint16_t *__restrict__ q,
+                                                              const float *__restrict__ t_q, int hq, int hkv,
+                                                              int n_keep, int nbk, const float *__restrict__ rope_cos,
+                                                              const float *__restrict__ rope_sin,
+                                                              float *__restrict__ q_prime,
+                                                              int32_t *__restrict__ sel_idx) {
+    constexpr int KB = 16 / GRP, NCH = 8;
+    __shared__ __attribute__((aligned(16))) float t_lds[D * D];
+    __shared__ __attribute__((aligned(16))) float q_lds[16 * D];  // row (bucket kl, head h) = kl GRP + h
+    __shared__ __attribute__((aligned(16))) float s_lds[2][D];
+    __shared__ unsigned long long mask0[2];
+    const int g = blockIdx.x, b = blockIdx.y, kb0 = blockIdx.z * KB, tid = threadIdx.x;
+    const int nbl = min(KB, nbk - kb0);
+    {
+        const float4 *tsrc = reinterpret_cast<const float4 *>(t_q + (size_t)g * D * D);
+        constexpr int PER = D * D / 4 / THREADS;
+        float4 stage[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) stage[k] = tsrc[tid + k * THREADS];
+        // element e = (head h, channel j) of the group's q and its partner
+        // j ^ 64, then every bucket's table entries: all loads issued before use
+        const uint16_t *qg = q + ((size_t)b * hq + (size_t)g * GRP) * D;
+        constexpr int NE = (GRP * D + THREADS - 1) / THREADS;
+        float x[NE], xp[NE], cv[KB][NE], sv[KB][NE];
+#pragma unroll
+        for (int k = 0; k < NE; ++k) {
+            const int e = tid + k * THREADS;
+            const bool ok = e < GRP * D;
+            x[k] = ok ? bf2f(qg[e]) : 0.0f;
+            xp[k] = ok ? bf2f(qg[e ^ (D / 2)]) : 0.0f;
+        }
+#pragma unroll
+        for (int kl = 0; kl < KB; ++kl)
+#pragma unroll
+            for (int k = 0; k < NE; ++k) {
+                const int jp = (tid + k * THREADS) & (D / 2 - 1);
+                const bool ok = kl < nbl;
+                cv[kl][k] = ok ? rope_cos[(size_t)(kb0 + kl) * (D / 2) + jp] : 0.0f;
+                sv[kl][k] = ok ? rope_sin[(size_t)(kb0 + kl) * (D / 2) + jp] : 0.0f;
+            }
+#pragma unroll
+        for (int kl = 0; kl < KB; ++kl)
+#pragma unroll
+            for (int k = 0; k < NE; ++k) {
+                const int e = tid + k * THREADS, j = e & (D - 1);
+                if (e < GRP * D)  // row kl GRP + h holds bucket kl's turned head h (zero past the last bucket)
+                    q_lds[kl * GRP * D + e] = rope_turn(x[k], xp[k], cv[kl][k], sv[kl][k], j < D / 2);
+            }
+        float4 *tdst = reinterpret_cast<float4 *>(t_lds);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) tdst[tid + k * THREADS] = stage[k];
+    }
+    __syncthreads();
+    const int j = tid & (D - 1), half = tid >> 7;
+    float acc[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) acc[c] = 0.0f;
+#pragma unroll 2
+    for (int i = 0; i < D; i += 4) {
+        const float t0 = t_lds[(i + 0) * D + j], t1 = t_lds[(i + 1) * D + j];
+        const float t2 = t_lds[(i + 2) * D + j], t3 = t_lds[(i + 3) * D + j];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const float4 qv = *reinterpret_cast<const float4 *>(&q_lds[(half + 2 * c) * D + i]);
+            float a = acc[c];
+            a = __builtin_fmaf(qv.x, t0, a);
+            a = __builtin_fmaf(qv.y, t1, a);
+            a = __builtin_fmaf(qv.z, t2, a);
+            a = __builtin_fmaf(qv.w, t3, a);
+            acc[c] = a;
+        }
+    }
+    __syncthreads();  // every chain has read the turned q: q' replaces it
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int row = half + 2 * c, kl = row / GRP, h = row - kl * GRP;
+        q_lds[row * D + j] = acc[c];
+        if (kl < nbl) q_prime[(((size_t)b * nbk + kb0 + kl) * hq + (size_t)g * GRP + h) * D + j] = acc[c];
+    }
+    __syncthreads();
+    for (int p = 0; p < KB; p += 2) {
+        const int kl = p + half;  // this lane half's bucket
+        const bool live = kl < nbl;
+        float S = 0.0f;
+        if (live)
+            for (int h = 0; h < GRP; ++h) {
+                const float v = q_lds[(kl * GRP + h) * D + j];
+                S = __builtin_fmaf(v, v, S);
+            }
+        s_lds[half][j] = S;
+        __syncthreads();
+        bool keep = false;
+        if (live) {
+            int rank = 0;
+#pragma unroll 4
+            for (int jj = 0; jj < D; jj += 4) {
+                const float4 o = *reinterpret_cast<const float4 *>(&s_lds[half][jj]);
+                rank += (o.x > S) | ((o.x == S) & (jj < j));
+                rank += (o.y > S) | ((o.y == S) & (jj + 1 < j));
+                rank += (o.z > S) | ((o.z == S) & (jj + 2 < j));
+                rank += (o.w > S) | ((o.w == S) & (jj + 3 < j));
+            }
+            keep = rank < n_keep;
+        }
+        // waves 0, 1 (half 0) and 2, 3 (half 1): channels 0..63, 64..127 of their bucket
+        const unsigned long long m = __ballot(keep);
+        if ((tid & 127) == 0) mask0[half] = m;
+        __syncthreads();
+        if (keep) {
+            const int lane = tid & 63;
+            const unsigned long long below = lane ? (m & ((1ull << lane) - 1ull)) : 0ull;
+            const int pos = __popcll(below) + (j >= 64 ? __popcll(mask0[half]) : 0);
+            if (pos < n_keep) sel_idx[(((size_t)b * nbk + kb0 + kl) * hkv + g) * n_keep + pos] = j;
+        }
+        __syncthreads();  // s_lds and mask0 are rewritten by the next pair
+    }
+}
+
 }  // namespace
 
 hipError_t launch_select(const uint16_t *q, const float *t_q, const float *sel_scale, int batch, int hq, int hkv,
-                         int n_keep, float *q_prime, int32_t *sel_idx, hipStream_t s) {
+                         int n_keep, float *q_prime, int32_t *sel_idx, hipStream_t s, const float *rope_cos,
+                         const float *rope_sin, int n_buckets) {
     const int grp = hq / hkv;
-    dim3 grid(hkv, batch);
+    if (rope_cos && !sel_scale) {  // buckets: 16 / grp of them per workgroup
+#define DQK_SELECT_ROPE(G)                                                                                      \
+    case G: {                                                                                                   \
+        dim3 grid_r(hkv, batch, (n_buckets + 16 / G - 1) / (16 / G));                                           \
+        hipLaunchKernelGGL(select_rope_kernel<G>, grid_r, dim3(THREADS), 0, s, q, t_q, hq, hkv, n_keep,         \
+                           n_buckets, rope_cos, rope_sin, q_prime, sel_idx);                                    \
+        return hipGetLastError();                                                                               \
+    }
+        switch (grp) {
+            DQK_SELECT_ROPE(1)
+            DQK_SELECT_ROPE(2)
+            DQK_SELECT_ROPE(4)
+            DQK_SELECT_ROPE(8)
+            DQK_SELECT_ROPE(16)
+            default: break;
+        }
+#undef DQK_SELECT_ROPE
+    }
+    dim3 grid(hkv, batch * n_buckets);
 #define DQK_SELECT_G(G)                                                                                      \
     case G:                                                                                                   \
         hipLaunchKernelGGL(select_kernel_g<G>, grid, dim3(THREADS), 0, s, q, t_q, hq, hkv, n_keep, sel_scale, \
-                           q_prime, sel_idx);                                                                 \
+                           q_prime, sel_idx, rope_cos, rope_sin, n_buckets);                                  \
         return hipGetLastError();
     switch (grp) {
         DQK_SELECT_G(1)
@@ -183,7 +351,7 @@ hipError_t launch_select(const uint16_t *q, const float *t_q, const float *sel_s
 #undef DQK_SELECT_G
     const size_t lds = 2 * (size_t)grp * D * sizeof(float);
     hipLaunchKernelGGL(select_kernel, grid, dim3(THREADS), lds, s, q, t_q, hq, hkv, n_keep, sel_scale, q_prime,
-                       sel_idx);
+                       sel_idx, rope_cos, rope_sin, n_buckets);
     return hipGetLastError();
 }
 

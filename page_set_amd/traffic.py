@@ -122,6 +122,15 @@ def decode_cache_bytes_tokgrid(seq_lens, sel_idx) -> int:
 TIER_SINK, TIER_RECENT = 64, 256
 
 
+def decode_rope_bytes(seq_lens, sel_idx) -> int:
+    """decode_cache_bytes with bucket-relative RoPE: sel_idx [B][n_buckets]
+    [Hkv][n_keep]; bucket k of sequence b (at most 2048 tokens, 16 pages) is
+    read with its own selected set."""
+    B, nb = sel_idx.shape[0], sel_idx.shape[1]
+    lens = [max(0, min(2048, int(seq_lens[b]) - 2048 * k)) for b in range(B) for k in range(nb)]
+    return decode_cache_bytes(lens, sel_idx.reshape(B * nb, *sel_idx.shape[2:]))
+
+
 def tier_pages(L: int) -> int:
     """INT2 pages of a sequence of L tokens in the tiered layout: pages of
     tokens 64 + 128 i .., all older than the 256 most recent tokens."""

@@ -276,3 +276,68 @@ def test_one_call_vrot_validation():
     assert call(hq=8 * 32) == pa.DQK_ERR_UNSUPPORTED
     need = pa.dqk_decode_workspace_size(4, 32, 8, 16, 4)
     assert call(ns=4, wsb=need - 4) == pa.DQK_ERR_WORKSPACE
+
+
+def test_rope_validation():
+    L = pa.lib()
+    c = _cache()
+
+    def app(c=c, **kw):
+        a = dict(k=A, v=A, tk=A, cs=A, sn=A, nb=1, n=2, cu=A, tot=300, pt=A, mp=4, kd=None)
+        a.update(kw)
+        return L.dqk_quantize_append_rope(ctypes.byref(c), a["k"], a["v"], a["tk"], a["cs"], a["sn"], a["nb"],
+                                          a["n"], a["cu"], a["tot"], a["pt"], a["mp"], a["kd"], None)
+
+    assert app(cs=None) == pa.DQK_ERR_NULL
+    assert app(sn=None) == pa.DQK_ERR_NULL
+    assert app(nb=0) == pa.DQK_ERR_SHAPE
+    assert app(nb=1, mp=17) == pa.DQK_ERR_SHAPE          # pages 16.. have no table
+    assert app(n=0) == pa.DQK_ERR_SHAPE
+    assert app(sn=MIS) == pa.DQK_ERR_ALIGN
+
+    def sel(**kw):
+        a = dict(q=A, tq=A, cs=A, sn=A, nb=4, B=2, hq=32, hkv=8, nk=77, qp=A, si=A)
+        a.update(kw)
+        return L.dqk_select_channels_rope(a["q"], a["tq"], a["cs"], a["sn"], a["nb"], a["B"], a["hq"], a["hkv"],
+                                          a["nk"], a["qp"], a["si"], None)
+
+    assert sel(cs=None) == pa.DQK_ERR_NULL
+    assert sel(nb=0) == pa.DQK_ERR_SHAPE
+    assert sel(hq=30) == pa.DQK_ERR_SHAPE
+    assert sel(nk=129) == pa.DQK_ERR_SHAPE
+    assert sel(B=1024, nb=64) == pa.DQK_ERR_UNSUPPORTED   # 65536 (sequence, bucket) rows
+    assert sel(cs=MIS) == pa.DQK_ERR_ALIGN
+
+    def dec(c=None, one=False, **kw):
+        c = c or _cache()
+        a = dict(q=A, tq=A, cs=A, sn=A, qp=A, si=A, nk=77, nb=4, B=2, hq=32, pt=A, mp=64, sl=A, sm=0.088, ns=0,
+                 ws=A, wsb=1 << 30, out=A, lse=None)
+        a.update(kw)
+        if one:
+            return L.dqk_select_decode_attn_rope(ctypes.byref(c), a["q"], a["tq"], a["cs"], a["sn"], a["nk"],
+                                                 a["nb"], a["B"], a["hq"], a["pt"], a["mp"], a["sl"], a["sm"],
+                                                 a["ns"], a["ws"], a["wsb"], a["out"], a["lse"], a["qp"], a["si"],
+                                                 None)
+        return L.dqk_decode_attn_rope(ctypes.byref(c), a["qp"], a["si"], a["nk"], a["nb"], a["B"], a["hq"],
+                                      a["pt"], a["mp"], a["sl"], a["sm"], a["ns"], a["ws"], a["wsb"], a["out"],
+                                      a["lse"], None)
+
+    for one in (False, True):
+        assert dec(one=one, sl=None) == pa.DQK_ERR_NULL
+        assert dec(one=one, nb=3) == pa.DQK_ERR_SHAPE          # 48 pages < max_pages 64
+        assert dec(one=one, nb=0) == pa.DQK_ERR_SHAPE
+        assert dec(one=one, ns=65) == pa.DQK_ERR_SHAPE          # more splits than pages
+        assert dec(one=one, hq=30) == pa.DQK_ERR_SHAPE
+        assert dec(one=one, hq=8 * 32) == pa.DQK_ERR_UNSUPPORTED
+        assert dec(one=one, B=2048, nb=64, mp=1024) == pa.DQK_ERR_UNSUPPORTED
+        assert dec(one=one, out=MIS) == pa.DQK_ERR_ALIGN
+        need = pa.dqk_decode_rope_workspace_size(2, 32, 8, 4, 2)
+        assert need == 2 * 32 * 2 * 132 * 4                     # partials per sequence and split
+        assert dec(one=one, ns=2, wsb=need - 4) == pa.DQK_ERR_WORKSPACE
+    assert dec(one=True, q=None) == pa.DQK_ERR_NULL
+    assert dec(one=True, cs=None) == pa.DQK_ERR_NULL
+    assert dec(one=True, qp=None) == pa.DQK_ERR_NULL
+    assert dec(one=True, sn=MIS) == pa.DQK_ERR_ALIGN
+    assert dec(one=False, si=None) == pa.DQK_ERR_NULL
+    assert dec(one=False, qp=MIS) == pa.DQK_ERR_ALIGN
+    assert pa.dqk_decode_rope_workspace_size(2, 32, 8, 0, 0) == 0
