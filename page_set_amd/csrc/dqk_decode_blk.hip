@@ -107,9 +107,10 @@ struct Lay {
     static constexpr int MAXB = MAXB_ROOM < 8 ? MAXB_ROOM : 8;
     static constexpr int TOTAL_ALL = RB ? RBA + MAXB * RBB : TOTAL;
     // the selection run inside the decode (prologue only): T_Q of the KV head
-    // [128][128] fp32 at 0, the four heads' q in fp32, the pooled energies and
-    // a ballot word after it; q' and the selected channels go to the usual
-    // scratch in the last value stage, which lies past all of them
+    // [128][128] fp32 at 0, the four heads' q in fp32, then room for the
+    // pooled energies and a mask word (kept in the layout; the energies now
+    // stay in wave 0's registers); q' and the selected channels go to the
+    // usual scratch in the last value stage, which lies past all of them
     static constexpr int SCR = VS + (NV - 1) * VST;
     static constexpr int FT = 0;
     static constexpr int FQ = D * D * 4;
@@ -523,8 +524,8 @@ struct Feeder {
 
 // ---------------------------------------------------------------- the kernel
 // The channel selection of one (sequence, KV head), as dqk_select_channels
-// computes it (the same fp32 fma chains in the same order, the same rank
-// rule), into the LDS scratch the decode prologue reads: q' [4][128] at scr,
+// computes it (the same fp32 fma chains in the same order, the same kept
+// set), into the LDS scratch the decode prologue reads: q' [4][128] at scr,
 // the ascending channel list after it.  qp_out / sel_out (may be null)
 // receive the same values in global memory.  wsel (may be null): the KV
 // head's selection scales, as dqk_select_channels_base applies them.
@@ -567,41 +568,27 @@ __device__ __forceinline__ void select_into_lds(uint32_t S, uint32_t scr, const 
         if (qp_out) qp_out[((size_t)b * hq + (size_t)g * GRP + h) * D + j] = acc;
     }
     __syncthreads();
-    // pooled energy S_j: fma chain over ascending head
-    if (tid < D) {
-        const float w = wsel ? wsel[tid] : 1.0f;  // x * 1 is x exactly
-        float e = 0.0f;
+    // wave 0: pooled energies of channels lane and lane + 64 (fma chains over
+    // ascending head), then the mask (top_k_wave) and the ascending list
+    if (tid < 64) {
+        const float wa = wsel ? wsel[tid] : 1.0f, wb = wsel ? wsel[tid + 64] : 1.0f;  // x * 1 is x exactly
+        float ea = 0.0f, eb = 0.0f;
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
-            const float v = __fmul_rn(lds_ld<float>(scr + (h * D + tid) * 4), w);
-            e = __builtin_fmaf(v, v, e);
+            const float va = __fmul_rn(lds_ld<float>(scr + (h * D + tid) * 4), wa);
+            const float vb = __fmul_rn(lds_ld<float>(scr + (h * D + tid + 64) * 4), wb);
+            ea = __builtin_fmaf(va, va, ea);
+            eb = __builtin_fmaf(vb, vb, eb);
         }
-        lds_st<float>(S + Ly::FS + tid * 4, e);
-    }
-    __syncthreads();
-    // channel j is kept iff fewer than n_keep channels beat it (larger S, or equal S at a lower index)
-    bool keep = false;
-    if (tid < D) {
-        const float e = lds_ld<float>(S + Ly::FS + tid * 4);
-        int rank = 0;
-#pragma unroll
-        for (int jj = 0; jj < D; jj += 4) {
-            const f32x4 o = lds_ld<f32x4>(S + Ly::FS + jj * 4);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) rank += (o[k] > e) | ((o[k] == e) & (jj + k < tid));
+        const KeptPair kp = top_k_wave(ea, eb, n_keep);
+        int32_t *so = sel_out ? sel_out + ((size_t)b * hkv + g) * n_keep : nullptr;
+        if (kp.ka && kp.pa < n_keep) {
+            lds_st<int32_t>(scr + GRP * D * 4 + kp.pa * 4, tid);
+            if (so) so[kp.pa] = tid;
         }
-        keep = rank < n_keep;
-    }
-    const unsigned long long m = __ballot(keep);  // waves 0, 1: channels 0..63, 64..127
-    if (tid == 0) lds_st<unsigned long long>(S + Ly::FM, m);
-    __syncthreads();
-    if (tid < D && keep) {
-        const int ln = tid & 63;
-        const unsigned long long below = ln ? (m & ((1ull << ln) - 1ull)) : 0ull;
-        const int pos = __popcll(below) + (tid >= 64 ? __popcll(lds_ld<unsigned long long>(S + Ly::FM)) : 0);
-        if (pos < n_keep) {
-            lds_st<int32_t>(scr + GRP * D * 4 + pos * 4, tid);
-            if (sel_out) sel_out[((size_t)b * hkv + g) * n_keep + pos] = tid;
+        if (kp.kb && kp.pb < n_keep) {
+            lds_st<int32_t>(scr + GRP * D * 4 + kp.pb * 4, tid + 64);
+            if (so) so[kp.pb] = tid + 64;
         }
     }
 }

@@ -74,6 +74,41 @@ __device__ __forceinline__ float rope_turn(float x, float xp, float c, float s, 
     return lower ? __fsub_rn(a, b) : __fadd_rn(a, b);
 }
 
+// ---------------------------------------------------------------- channel selection
+// The n_keep channels of one mask (Dual-QK paper, §3.2 Eq. 4), found by one
+// wave: lane l holds the pooled energies ea of channel l and eb of channel
+// l + 64.  Channel j is kept iff fewer than n_keep channels beat it (larger
+// energy, or equal energy at a lower index).  Energies are sums of squares
+// (>= +0), whose bit patterns order like their values, so a radix select over
+// the 32 bits (one ballot count per bit, from the top) finds the n_keep-th
+// largest energy T; the channels above T and the lowest-indexed channels equal
+// to T up to n_keep are kept.  pa / pb: output positions of the two channels
+// in the ascending list.  Exactly n_keep channels are kept whatever the bits
+// (NaN energies included), so positions stay below n_keep.
+struct KeptPair {
+    bool ka, kb;
+    int pa, pb;
+};
+__device__ __forceinline__ KeptPair top_k_wave(float ea, float eb, int n_keep) {
+    const int lane = __lane_id();
+    const uint32_t ua = __float_as_uint(ea), ub = __float_as_uint(eb);
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        if (__popcll(__ballot(ua >= cand)) + __popcll(__ballot(ub >= cand)) >= n_keep) thr = cand;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const unsigned long long eqa = __ballot(ua == thr), eqb = __ballot(ub == thr);
+    const int need = n_keep - __popcll(__ballot(ua > thr)) - __popcll(__ballot(ub > thr));  // >= 1
+    KeptPair r;
+    r.ka = ua > thr || (ua == thr && __popcll(eqa & below) < need);
+    r.kb = ub > thr || (ub == thr && __popcll(eqa) + __popcll(eqb & below) < need);
+    const unsigned long long ma = __ballot(r.ka), mb = __ballot(r.kb);
+    r.pa = __popcll(ma & below);
+    r.pb = __popcll(ma) + __popcll(mb & below);
+    return r;
+}
+
 // |x| onto the binary16 grid toward zero: bits of the magnitude, and whether
 // the value was inexact.  Magnitudes above 65504 saturate to 65504 (inexact).
 __device__ __forceinline__ uint32_t f16_mag_trunc(uint32_t ua, bool &inexact) {

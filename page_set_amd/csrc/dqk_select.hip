@@ -52,45 +52,23 @@ __device__ __forceinline__ void stage_inputs(const uint16_t *__restrict__ q, con
     for (int k = 0; k < PER; ++k) tdst[tid + k * THREADS] = stage[k];
 }
 
-// Pooled energy of channel j (fma chain over ascending head), then the rank
-// test and the ascending write of the kept channels.
+// Pooled energies of channels lane and lane + 64 (fma chains over ascending
+// head) and the mask by top_k_wave, all in wave 0; the kept channels are
+// written in ascending order.
 __device__ __forceinline__ void select_tail(const float *qpl, int grp, int n_keep, const float *__restrict__ wsel,
-                                            float *s_lds, unsigned long long *mask0, int32_t *__restrict__ dst) {
-    const int tid = threadIdx.x, j = tid & (D - 1);
-    if (tid < D) {
-        const float w = wsel ? wsel[j] : 1.0f;  // x * 1 is x exactly
-        float S = 0.0f;
-        for (int h = 0; h < grp; ++h) {
-            const float v = __fmul_rn(qpl[h * D + j], w);
-            S = __builtin_fmaf(v, v, S);
-        }
-        s_lds[j] = S;
+                                            int32_t *__restrict__ dst) {
+    const int tid = threadIdx.x;
+    if (tid >= 64) return;
+    const float wa = wsel ? wsel[tid] : 1.0f, wb = wsel ? wsel[tid + 64] : 1.0f;  // x * 1 is x exactly
+    float sa = 0.0f, sb = 0.0f;
+    for (int h = 0; h < grp; ++h) {
+        const float va = __fmul_rn(qpl[h * D + tid], wa), vb = __fmul_rn(qpl[h * D + tid + 64], wb);
+        sa = __builtin_fmaf(va, va, sa);
+        sb = __builtin_fmaf(vb, vb, sb);
     }
-    __syncthreads();
-    bool keep = false;
-    if (tid < D) {
-        const float S = s_lds[j];
-        int rank = 0;
-#pragma unroll 4
-        for (int jj = 0; jj < D; jj += 4) {
-            const float4 o = *reinterpret_cast<const float4 *>(&s_lds[jj]);
-            rank += (o.x > S) | ((o.x == S) & (jj < j));
-            rank += (o.y > S) | ((o.y == S) & (jj + 1 < j));
-            rank += (o.z > S) | ((o.z == S) & (jj + 2 < j));
-            rank += (o.w > S) | ((o.w == S) & (jj + 3 < j));
-        }
-        keep = rank < n_keep;
-    }
-    // ascending output position = kept channels below j (lanes 0..63 are channels 0..63)
-    const unsigned long long m = __ballot(keep);
-    if (tid == 0) *mask0 = m;
-    __syncthreads();
-    if (keep) {
-        const int lane = tid & 63;
-        const unsigned long long below = lane ? (m & ((1ull << lane) - 1ull)) : 0ull;
-        const int pos = __popcll(below) + (tid >= 64 ? __popcll(*mask0) : 0);
-        if (pos < n_keep) dst[pos] = j;  // NaN inputs cannot overrun
-    }
+    const KeptPair kp = top_k_wave(sa, sb, n_keep);
+    if (kp.ka && kp.pa < n_keep) dst[kp.pa] = tid;
+    if (kp.kb && kp.pb < n_keep) dst[kp.pb] = tid + 64;
 }
 
 // Group size fixed at compile time: lane (half, j) runs the chains of heads
@@ -108,8 +86,6 @@ __global__ __launch_bounds__(THREADS) void select_kernel_g(const uint16_t *__res
     __shared__ __attribute__((aligned(16))) float t_lds[D * D];
     __shared__ __attribute__((aligned(16))) float q_lds[GRP * D];
     __shared__ __attribute__((aligned(16))) float qp_lds[GRP * D];
-    __shared__ __attribute__((aligned(16))) float s_lds[D];
-    __shared__ unsigned long long mask0;
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;  // b: row (sequence, bucket) of the outputs
     const int sq = b / nbk, bk = b - sq * nbk;
     stage_inputs(q, t_q, g, sq, hq, GRP, t_lds, q_lds, rope_cos ? rope_cos + bk * (D / 2) : nullptr,
@@ -144,7 +120,7 @@ __global__ __launch_bounds__(THREADS) void select_kernel_g(const uint16_t *__res
         }
     }
     __syncthreads();
-    select_tail(qp_lds, GRP, n_keep, sel_scale ? sel_scale + (size_t)g * D : nullptr, s_lds, &mask0,
+    select_tail(qp_lds, GRP, n_keep, sel_scale ? sel_scale + (size_t)g * D : nullptr,
                 sel_idx + ((size_t)b * hkv + g) * n_keep);
 }
 
@@ -158,8 +134,6 @@ __global__ __launch_bounds__(THREADS) void select_kernel(const uint16_t *__restr
                                                          const float *__restrict__ rope_sin, int nbk) {
     __shared__ __attribute__((aligned(16))) float t_lds[D * D];  // T_Q of this KV head (64 KB)
     extern __shared__ __attribute__((aligned(16))) float q_lds[];  // [grp][128] q (bf16 -> fp32), then [grp][128] q'
-    __shared__ __attribute__((aligned(16))) float s_lds[D];
-    __shared__ unsigned long long mask0;
     const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;  // b: row (sequence, bucket) of the outputs
     const int grp = hq / hkv;
     const int sq = b / nbk, bk = b - sq * nbk;
@@ -178,18 +152,20 @@ __global__ __launch_bounds__(THREADS) void select_kernel(const uint16_t *__restr
         qpl[h * D + j] = acc;
     }
     __syncthreads();
-    select_tail(qpl, grp, n_keep, sel_scale ? sel_scale + (size_t)g * D : nullptr, s_lds, &mask0,
+    select_tail(qpl, grp, n_keep, sel_scale ? sel_scale + (size_t)g * D : nullptr,
                 sel_idx + ((size_t)b * hkv + g) * n_keep);
 }
 
-// Selection of KB = 16 / GRP buckets per workgroup (bucket-relative RoPE):
+// Selection of KB = 32 / GRP buckets per workgroup (bucket-relative RoPE):
 // T_Q[g] is staged once for the workgroup's buckets kb0 .. kb0 + KB - 1 of
-// sequence b; the 16 (bucket, head) rows of q, each turned by its bucket's
-// table, sit in LDS and lane (half, j) runs the eight chains of rows half,
-// half + 2, .. for output channel j together, one read of T_Q column j per
-// input channel serving all eight.  Each chain is the fma chain over
-// ascending input channel of select_kernel; the tail takes two buckets at a
-// time (one per lane half) with the pooled energy and rank rule of select_tail.
+// sequence b, and the 32 (bucket, head) rows of q, each turned by its
+// bucket's table, sit in LDS.  Lane (wave w, half r, quad c) runs the sixteen
+// chains of rows 8w + 4r .. 8w + 4r + 3 and output channels 4c .. 4c + 3: per
+// four input channels one 16-byte read of T_Q per input channel and one
+// 16-byte read of q per row serve sixteen fmas.  Each chain is the fma chain
+// over ascending input channel of select_kernel.  The mask of a bucket is
+// then found by one wave (pooled energy by fma over ascending head, then
+// top_k_wave).
 template <int GRP>
 __global__ __launch_bounds__(THREADS) void select_rope_kernel(const uint16_t *__restrict__ q,
                                                               const float *__restrict__ t_q, int hq, int hkv,
@@ -197,11 +173,9 @@ __global__ __launch_bounds__(THREADS) void select_rope_kernel(const uint16_t *__
                                                               const float *__restrict__ rope_sin,
                                                               float *__restrict__ q_prime,
                                                               int32_t *__restrict__ sel_idx) {
-    constexpr int KB = 16 / GRP, NCH = 8;
+    constexpr int RW = 32, KB = RW / GRP;
     __shared__ __attribute__((aligned(16))) float t_lds[D * D];
-    __shared__ __attribute__((aligned(16))) float q_lds[16 * D];  // row (bucket kl, head h) = kl GRP + h
-    __shared__ __attribute__((aligned(16))) float s_lds[2][D];
-    __shared__ unsigned long long mask0[2];
+    __shared__ __attribute__((aligned(16))) float q_lds[RW * D];  // row (bucket kl, head h) = kl GRP + h
     const int g = blockIdx.x, b = blockIdx.y, kb0 = blockIdx.z * KB, tid = threadIdx.x;
     const int nbl = min(KB, nbk - kb0);
     {
@@ -244,68 +218,82 @@ __global__ __launch_bounds__(THREADS) void select_rope_kernel(const uint16_t *__
         for (int k = 0; k < PER; ++k) tdst[tid + k * THREADS] = stage[k];
     }
     __syncthreads();
-    const int j = tid & (D - 1), half = tid >> 7;
-    float acc[NCH];
+    const int lane = tid & 63, w = tid >> 6;
+    const int c4 = 4 * (lane & 31), r0 = 8 * w + 4 * (lane >> 5);
+    float acc[4][4];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) acc[c] = 0.0f;
-#pragma unroll 2
-    for (int i = 0; i < D; i += 4) {
-        const float t0 = t_lds[(i + 0) * D + j], t1 = t_lds[(i + 1) * D + j];
-        const float t2 = t_lds[(i + 2) * D + j], t3 = t_lds[(i + 3) * D + j];
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const float4 qv = *reinterpret_cast<const float4 *>(&q_lds[(half + 2 * c) * D + i]);
-            float a = acc[c];
-            a = __builtin_fmaf(qv.x, t0, a);
-            a = __builtin_fmaf(qv.y, t1, a);
-            a = __builtin_fmaf(qv.z, t2, a);
-            a = __builtin_fmaf(qv.w, t3, a);
-            acc[c] = a;
+        for (int c = 0; c < 4; ++c) acc[r][c] = 0.0f;
+    // operands of four input channels: T_Q rows i .. i + 3 (this lane's four
+    // columns) and q of the lane's four rows; two sets, so that the reads of
+    // the next four channels are in flight while the fmas of these run
+    float4 tv[2][4], qv[2][4];
+    auto load = [&](int i, int st) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tv[st][k] = *reinterpret_cast<const float4 *>(&t_lds[(i + k) * D + c4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) qv[st][r] = *reinterpret_cast<const float4 *>(&q_lds[(r0 + r) * D + i]);
+    };
+    auto step = [&](int st) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float4 x = qv[st][r];
+            float a0 = acc[r][0], a1 = acc[r][1], a2 = acc[r][2], a3 = acc[r][3];
+            a0 = __builtin_fmaf(x.x, tv[st][0].x, a0);
+            a1 = __builtin_fmaf(x.x, tv[st][0].y, a1);
+            a2 = __builtin_fmaf(x.x, tv[st][0].z, a2);
+            a3 = __builtin_fmaf(x.x, tv[st][0].w, a3);
+            a0 = __builtin_fmaf(x.y, tv[st][1].x, a0);
+            a1 = __builtin_fmaf(x.y, tv[st][1].y, a1);
+            a2 = __builtin_fmaf(x.y, tv[st][1].z, a2);
+            a3 = __builtin_fmaf(x.y, tv[st][1].w, a3);
+            a0 = __builtin_fmaf(x.z, tv[st][2].x, a0);
+            a1 = __builtin_fmaf(x.z, tv[st][2].y, a1);
+            a2 = __builtin_fmaf(x.z, tv[st][2].z, a2);
+            a3 = __builtin_fmaf(x.z, tv[st][2].w, a3);
+            a0 = __builtin_fmaf(x.w, tv[st][3].x, a0);
+            a1 = __builtin_fmaf(x.w, tv[st][3].y, a1);
+            a2 = __builtin_fmaf(x.w, tv[st][3].z, a2);
+            a3 = __builtin_fmaf(x.w, tv[st][3].w, a3);
+            acc[r][0] = a0;
+            acc[r][1] = a1;
+            acc[r][2] = a2;
+            acc[r][3] = a3;
         }
+    };
+    load(0, 0);
+#pragma unroll
+    for (int i = 0; i < D; i += 8) {
+        load(i + 4, 1);
+        step(0);
+        load((i + 8) & (D - 1), 0);  // the last pass rereads channels 0..3, unused
+        step(1);
     }
     __syncthreads();  // every chain has read the turned q: q' replaces it
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int row = half + 2 * c, kl = row / GRP, h = row - kl * GRP;
-        q_lds[row * D + j] = acc[c];
-        if (kl < nbl) q_prime[(((size_t)b * nbk + kb0 + kl) * hq + (size_t)g * GRP + h) * D + j] = acc[c];
+    for (int r = 0; r < 4; ++r) {
+        const int row = r0 + r, kl = row / GRP, h = row - kl * GRP;
+        const float4 v = {acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+        *reinterpret_cast<float4 *>(&q_lds[row * D + c4]) = v;
+        if (kl < nbl)
+            *reinterpret_cast<float4 *>(
+                &q_prime[(((size_t)b * nbk + kb0 + kl) * hq + (size_t)g * GRP + h) * D + c4]) = v;
     }
     __syncthreads();
-    for (int p = 0; p < KB; p += 2) {
-        const int kl = p + half;  // this lane half's bucket
-        const bool live = kl < nbl;
-        float S = 0.0f;
-        if (live)
-            for (int h = 0; h < GRP; ++h) {
-                const float v = q_lds[(kl * GRP + h) * D + j];
-                S = __builtin_fmaf(v, v, S);
-            }
-        s_lds[half][j] = S;
-        __syncthreads();
-        bool keep = false;
-        if (live) {
-            int rank = 0;
-#pragma unroll 4
-            for (int jj = 0; jj < D; jj += 4) {
-                const float4 o = *reinterpret_cast<const float4 *>(&s_lds[half][jj]);
-                rank += (o.x > S) | ((o.x == S) & (jj < j));
-                rank += (o.y > S) | ((o.y == S) & (jj + 1 < j));
-                rank += (o.z > S) | ((o.z == S) & (jj + 2 < j));
-                rank += (o.w > S) | ((o.w == S) & (jj + 3 < j));
-            }
-            keep = rank < n_keep;
+    // wave w selects buckets w, w + 4, ..; lane holds channels lane and lane + 64
+    for (int kl = w; kl < nbl; kl += THREADS / 64) {
+        float sa = 0.0f, sb = 0.0f;
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) {
+            const float va = q_lds[(kl * GRP + h) * D + lane], vb = q_lds[(kl * GRP + h) * D + lane + 64];
+            sa = __builtin_fmaf(va, va, sa);
+            sb = __builtin_fmaf(vb, vb, sb);
         }
-        // waves 0, 1 (half 0) and 2, 3 (half 1): channels 0..63, 64..127 of their bucket
-        const unsigned long long m = __ballot(keep);
-        if ((tid & 127) == 0) mask0[half] = m;
-        __syncthreads();
-        if (keep) {
-            const int lane = tid & 63;
-            const unsigned long long below = lane ? (m & ((1ull << lane) - 1ull)) : 0ull;
-            const int pos = __popcll(below) + (j >= 64 ? __popcll(mask0[half]) : 0);
-            if (pos < n_keep) sel_idx[(((size_t)b * nbk + kb0 + kl) * hkv + g) * n_keep + pos] = j;
-        }
-        __syncthreads();  // s_lds and mask0 are rewritten by the next pair
+        const KeptPair kp = top_k_wave(sa, sb, n_keep);
+        int32_t *dst = sel_idx + (((size_t)b * nbk + kb0 + kl) * hkv + g) * n_keep;
+        if (kp.ka && kp.pa < n_keep) dst[kp.pa] = lane;
+        if (kp.kb && kp.pb < n_keep) dst[kp.pb] = lane + 64;
     }
 }
 
@@ -315,10 +303,10 @@ hipError_t launch_select(const uint16_t *q, const float *t_q, const float *sel_s
                          int n_keep, float *q_prime, int32_t *sel_idx, hipStream_t s, const float *rope_cos,
                          const float *rope_sin, int n_buckets) {
     const int grp = hq / hkv;
-    if (rope_cos && !sel_scale) {  // buckets: 16 / grp of them per workgroup
+    if (rope_cos && !sel_scale) {  // buckets: 32 / grp of them per workgroup
 #define DQK_SELECT_ROPE(G)                                                                                      \
     case G: {                                                                                                   \
-        dim3 grid_r(hkv, batch, (n_buckets + 16 / G - 1) / (16 / G));                                           \
+        dim3 grid_r(hkv, batch, (n_buckets + 32 / G - 1) / (32 / G));                                           \
         hipLaunchKernelGGL(select_rope_kernel<G>, grid_r, dim3(THREADS), 0, s, q, t_q, hq, hkv, n_keep,         \
                            n_buckets, rope_cos, rope_sin, q_prime, sel_idx);                                    \
         return hipGetLastError();                                                                               \

@@ -17,8 +17,10 @@ benchmark suites that are not available here; seeded Gaussians stand in:
   head): T_K = bf16(R diag(u)) with R Haar-orthogonal (QR of a
   Gaussian, sign-fixed) and u ~ U[0.5, 2]; T_Q = (T_K as stored)^{-T}, computed
   in fp64 and rounded to fp32, so that (q T_Q)(k T_K)^T = q k^T (§3.1, Eq. 1).
-* 128-token pages handed out in aligned blocks of four; identity page table
+* 128-token pages handed out in aligned blocks of eight; identity page table
   unless ``shuffle_pages`` (a seeded permutation of the blocks).
+* Bucket-relative RoPE tables (§3.4, App. C.4): rotary frequencies
+  base^(-i/64) stand in for a checkpoint's, with no random draws.
 
 bf16 values are carried as ``numpy.uint16`` bit patterns.
 """

@@ -315,3 +315,79 @@ def test_token_grid_at_full_size():
         errs = list(ex.map(check, units))
     _say(f"  16 sampled pages stagewise; {len(units)} sampled units: worst row rel err {max(errs):.3e}")
     assert max(errs) <= gu.TOL
+
+
+def test_rope_at_full_size():
+    """Bucket-relative RoPE at the benchmark's shape (batch 4 x 131072 tokens,
+    64 buckets of 2048, GQA 32/8, n_keep 77) in the launch configuration
+    bench.py times: the cache built by dqk_quantize_append_rope sequence by
+    sequence (k' read back for sequence 0), then one dqk_select_decode_attn_rope
+    call.  Stage by stage on 16 sampled pages of sequence 0 (k' within the
+    summation bound of the oracle's turned-key product, every byte equal to
+    the oracle's pack of the GPU's own k'); the per-bucket selection bit-exact
+    for the whole batch; 8 sampled units recomputed by the oracle from the
+    same cache bytes, rows within 2e-3."""
+    shape = synth.config_shape(3)
+    _say("bucket-relative RoPE at full size", shape.name)
+    prob = synth.make_problem(shape, seed=0, materialize_kv=False)
+    d = gu.upload(prob)
+    nb = synth.rope_buckets(max(shape.seq_lens))
+    cs, sn = synth.make_rope_tables(nb)
+    dcs, dsn = gu.dev(cs), gu.dev(sn)
+    L0 = shape.seq_lens[0]
+    kdbg = torch.full((L0, shape.hkv, 128), float("nan"), dtype=torch.float32, device="cuda")
+    cache = pa.Cache(prob.num_pages, shape.hkv)
+    for b in range(shape.batch):
+        kb, vb = synth.make_kv_seq(shape, prob.seed, b, prob.outliers)
+        cu = torch.tensor([0, kb.shape[0]], dtype=torch.int32, device="cuda")
+        pa.dqk_quantize_append_rope(cache, gu.dev(kb), gu.dev(vb), d["t_k"], dcs, dsn, cu,
+                                    d["page_table"][b:b + 1].clone(), kprime_dbg=kdbg if b == 0 else None)
+        torch.cuda.synchronize()
+    out, _, qp, sel = pa.dqk_select_decode_attn_rope(cache, d["q"], d["t_q"], dcs, dsn, shape.n_keep,
+                                                     d["page_table"], d["seq_lens"], prob.sm_scale)
+    torch.cuda.synchronize()
+    qp_h, sel_h, out_h = gu.host(qp), gu.host(sel), gu.host(out)
+    qp_ref, sel_ref = oracle.select_channels_rope(prob.q, prob.t_q, cs, sn, shape.hkv, shape.n_keep)
+    np.testing.assert_array_equal(qp_h.view(np.uint32), qp_ref.view(np.uint32))
+    np.testing.assert_array_equal(sel_h, sel_ref)
+    pm = cache.page_major()
+    kb, vb = synth.make_kv_seq(shape, prob.seed, 0, prob.outliers)
+    eye = np.broadcast_to(synth.f32_to_bf16_bits(np.eye(128, dtype=np.float32)), (shape.hkv, 128, 128)).copy()
+    t64 = np.abs(synth.bf16_bits_to_f32(prob.t_k).astype(np.float64))
+    one = np.array([0, 128], np.int32)
+    gam = 128 * 2.0 ** -24 / (1 - 128 * 2.0 ** -24)
+    for pi in np.random.default_rng(16).choice(L0 // 128, size=16, replace=False):
+        p, t0, bk = int(prob.page_table[0, pi]), int(pi) * 128, int(pi) // 16
+        kpage = np.ascontiguousarray(kb[t0:t0 + 128])
+        tabs = (np.ascontiguousarray(cs[bk:bk + 1]), np.ascontiguousarray(sn[bk:bk + 1]))
+        turned = oracle.key_transform_rope(kpage, eye, one, *tabs).astype(np.float64)
+        kp_ref = oracle.key_transform_rope(kpage, prob.t_k, one, *tabs).astype(np.float64)
+        kp_gpu = gu.host(kdbg[t0:t0 + 128])
+        bound = gam * np.einsum("tgi,gij->tgj", np.abs(turned), t64) + np.spacing(np.abs(kp_ref))
+        assert (np.abs(kp_gpu.astype(np.float64) - kp_ref) <= bound).all(), f"k' page {pi}"
+        want_pm = oracle.pack_cache(kp_gpu, np.ascontiguousarray(vb[t0:t0 + 128]), one, np.zeros((1, 1), np.int32),
+                                    1).page_major()
+        for g in range(shape.hkv):
+            got = _unit_cache(pm, [p], g).page_major()
+            for nm, x, w in zip(["k_codes", "k_meta", "k_ch0", "v_codes", "v_meta"], got, want_pm):
+                np.testing.assert_array_equal(x[0, 0], w[0, g], err_msg=f"{nm} page {pi} head {g}")
+    grp = shape.hq // shape.hkv
+    rng = np.random.default_rng(17)
+    units = [(int(b), int(g)) for b, g in zip(rng.integers(0, shape.batch, 8), rng.integers(0, shape.hkv, 8))]
+
+    def check(unit):
+        b, g = unit
+        L = int(prob.seq_lens[b])
+        npg = (L + 127) // 128
+        sub = _unit_cache(pm, prob.page_table[b, :npg], g)
+        heads = slice(g * grp, (g + 1) * grp)
+        ref, _ = oracle.decode_attn_rope(sub, np.ascontiguousarray(qp_h[b:b + 1, :, heads]),
+                                         np.ascontiguousarray(sel_h[b:b + 1, :, g:g + 1]),
+                                         np.arange(npg, dtype=np.int32)[None], np.array([L], np.int32),
+                                         prob.sm_scale)
+        return float(gu.row_rel_err(out_h[b, heads], ref[0]).max())
+
+    with cf.ThreadPoolExecutor(max_workers=THREADS) as ex:
+        errs = list(ex.map(check, units))
+    _say(f"  16 sampled pages stagewise; {len(units)} sampled units: worst row rel err {max(errs):.3e}")
+    assert max(errs) <= gu.TOL

@@ -195,9 +195,9 @@ def test_decode_rope_split_counts(lens, nk, ns):
                                       (synth.Shape(2, 16, 8, [2200, 600], 77), 0)],
                          ids=["g4-nk77", "g4-nk128-2splits", "g4-nk9", "g2"])
 def test_one_call_equals_two_calls(shape, ns):
-    """dqk_select_decode_attn_rope (the turned queries' selection in the
-    decode launch where possible) gives bit for bit dqk_select_channels_rope
-    + dqk_decode_attn_rope, and that selection is the oracle's."""
+    """dqk_select_decode_attn_rope (the per-bucket selection launch, then the
+    decode reading it) gives bit for bit dqk_select_channels_rope +
+    dqk_decode_attn_rope, and that selection is the oracle's."""
     _say("rope one call", shape.hq, shape.n_keep, ns)
     prob = synth.make_problem(shape, seed=75)
     nb, cs, sn = _tables(shape)
