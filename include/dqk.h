@@ -306,6 +306,20 @@ int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const flo
                            const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,
                            size_t ws_bytes, float *out, float *lse, hipStream_t stream);
 
+/*
+ * dqk_select_channels + dqk_decode_attn_tiered as one call (the selection of
+ * §3.2, then the tiered decode of §3.3-§3.4): q_prime and sel_idx receive the
+ * selection as dqk_select_channels writes it, and the results are those of
+ * the two calls (the entry makes them).  Arguments, workspace (of
+ * dqk_decode_tiered_workspace_size bytes) and errors as dqk_select_decode_attn
+ * and dqk_decode_attn_tiered; every check runs before the first launch.
+ */
+int dqk_select_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const void *q_bf16, const float *t_q,
+                                  int32_t n_keep, int32_t batch, int32_t hq, const int32_t *page_table,
+                                  int32_t max_pages, const int32_t *seq_lens, float sm_scale, int32_t num_splits,
+                                  void *workspace, size_t ws_bytes, float *out, float *lse, float *q_prime,
+                                  int32_t *sel_idx, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Rotated values and selection in base coordinates (§3.3: the calibrated
  * value rotation and clipping of App. B.2, and the diagonal refinement

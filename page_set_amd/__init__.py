@@ -94,6 +94,9 @@ def lib():
         L.dqk_decode_attn_tiered.argtypes = [ctypes.POINTER(dqk_cache), T, P, P, i32, i32, i32, P, i32, P,
                                              ctypes.c_float, i32, P, sz, P, P, P]
         L.dqk_decode_attn_tiered.restype = ctypes.c_int
+        L.dqk_select_decode_attn_tiered.argtypes = [ctypes.POINTER(dqk_cache), T, P, P, i32, i32, i32, P, i32, P,
+                                                    ctypes.c_float, i32, P, sz, P, P, P, P, P]
+        L.dqk_select_decode_attn_tiered.restype = ctypes.c_int
         L.dqk_quantize_append_vrot.argtypes = [ctypes.POINTER(dqk_cache), P, P, P, P, ctypes.c_float, i32, P, i64,
                                                P, i32, P, P, P]
         L.dqk_quantize_append_vrot.restype = ctypes.c_int
@@ -243,6 +246,36 @@ def dqk_decode_attn_tiered(cache: Cache, tiers: Tiers, q_prime, sel_idx, page_ta
                                       _ptr(lse), _stream(stream))
     _check(rc, "dqk_decode_attn_tiered")
     return out, lse
+
+
+def dqk_select_decode_attn_tiered(cache: Cache, tiers: Tiers, q, t_q, n_keep: int, page_table, seq_lens,
+                                  sm_scale: float, num_splits: int = 0, workspace=None, out=None, lse=None,
+                                  want_lse: bool = True, q_prime=None, sel_idx=None, stream=None):
+    """Selection and tiered decode in one call; returns (out, lse, q_prime, sel_idx)."""
+    import torch
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    hkv = cache.num_kv_heads
+    max_pages = int(page_table.shape[1])
+    dev = q.device
+    if workspace is None:
+        n = dqk_decode_tiered_workspace_size(B, hq, hkv, max_pages, num_splits)
+        workspace = torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    if q_prime is None:
+        q_prime = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty((B, hkv, n_keep), dtype=torch.int32, device=dev)
+    s, t = cache.struct(), tiers.struct()
+    rc = lib().dqk_select_decode_attn_tiered(ctypes.byref(s), ctypes.byref(t), _ptr(q), _ptr(t_q), int(n_keep), B,
+                                             hq, _ptr(page_table), max_pages, _ptr(seq_lens), float(sm_scale),
+                                             int(num_splits), _ptr(workspace),
+                                             workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+                                             _ptr(q_prime), _ptr(sel_idx), _stream(stream))
+    _check(rc, "dqk_select_decode_attn_tiered")
+    return out, lse, q_prime, sel_idx
 
 
 def dqk_quantize_append(cache: Cache, k, v, t_k, cu_tokens, page_table, kprime_dbg=None, stream=None):

@@ -558,6 +558,42 @@ int dqk_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const flo
         dqk::launch_merge_extra(parts, batch, hq, splits, tier_parts, dqk::TIER_PARTIALS, out, lse, stream));
 }
 
+int dqk_select_decode_attn_tiered(const dqk_cache *c, const dqk_tiers *tiers, const void *q_bf16, const float *t_q,
+                                  int32_t n_keep, int32_t batch, int32_t hq, const int32_t *page_table,
+                                  int32_t max_pages, const int32_t *seq_lens, float sm_scale, int32_t num_splits,
+                                  void *workspace, size_t ws_bytes, float *out, float *lse, float *q_prime,
+                                  int32_t *sel_idx, hipStream_t stream) {
+    int st = check_cache(c);
+    if (st) return st;
+    st = check_tiers(tiers, c);
+    if (st) return st;
+    if (!q_bf16 || !t_q || !q_prime || !sel_idx || !page_table || !seq_lens || !workspace || !out)
+        return DQK_ERR_NULL;
+    const int hkv = c->num_kv_heads;
+    // every check of both paths before anything is enqueued
+    if (batch < 1 || batch > tiers->batch || hq < 1 || hq % hkv != 0 || n_keep < 1 || n_keep > DQK_HEAD_DIM ||
+        max_pages < 1 || num_splits < 0 || num_splits > max_pages)
+        return DQK_ERR_SHAPE;
+    if (hq / hkv > 64) return DQK_ERR_UNSUPPORTED;  // the selection's limit
+    if (!dqk::use_mfma_decode(hq, hkv, n_keep)) return DQK_ERR_UNSUPPORTED;
+    if ((int64_t)batch * hkv * dqk::mfma_head_sets(hq, hkv) > 65535 || batch * hq > 2147483647 / 2)
+        return DQK_ERR_UNSUPPORTED;
+    if (!aligned16(q_bf16) || !aligned16(t_q) || !aligned16(q_prime) || !aligned16(sel_idx) ||
+        !aligned16(page_table) || !aligned16(seq_lens) || !aligned16(workspace) || !aligned16(out) ||
+        (lse && !aligned16(lse)))
+        return DQK_ERR_ALIGN;
+    const int splits = resolve_splits(batch, hq, hkv, max_pages, num_splits, n_keep);
+    if (ws_bytes < tiered_ws_bytes(batch, hq, splits)) return DQK_ERR_WORKSPACE;
+    // the selection, then the tiered decode (the BF16 tokens score with it).
+    // Moving the selection into the INT2 decode's prologue, with the BF16
+    // tokens scored after that launch, measured slower on this path than two
+    // launches, so the entry makes the two calls.
+    st = dqk_select_channels(q_bf16, t_q, batch, hq, hkv, n_keep, q_prime, sel_idx, stream);
+    if (st) return st;
+    return dqk_decode_attn_tiered(c, tiers, q_prime, sel_idx, n_keep, batch, hq, page_table, max_pages, seq_lens,
+                                  sm_scale, num_splits, workspace, ws_bytes, out, lse, stream);
+}
+
 int dqk_decode_attn_bf16(const void *k_pages, const void *v_pages, int32_t hkv, int32_t num_pages,
                          const void *q_bf16, int32_t batch, int32_t hq, const int32_t *page_table, int32_t max_pages,
                          const int32_t *seq_lens, float sm_scale, int32_t num_splits, void *workspace,

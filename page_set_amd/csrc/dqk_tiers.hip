@@ -135,6 +135,7 @@ __global__ __launch_bounds__(256) void tier_decode_kernel(dqk_tiers t, const flo
     __shared__ float qm[GRP][D];
     __shared__ float x[GRP][TCH];
     __shared__ float m_s[GRP], l_s[GRP];
+    __shared__ int keep_s[D];
     constexpr int grp = GRP;
     const int hkv = t.num_kv_heads;
     const int chunk = blockIdx.x;
@@ -194,12 +195,27 @@ __global__ __launch_bounds__(256) void tier_decode_kernel(dqk_tiers t, const flo
         vraw[r] = (s0 ? t.sink_v : t.tail_v)[row * D + c];
     }
 
-    for (int e = tid; e < grp * D; e += 256) qm[e / D][e % D] = 0.0f;
-    __syncthreads();
+    // the masked q' of the group: whole q' rows and the channel list load
+    // together (no load waits for another), the list marks its channels in
+    // LDS, and unmarked channels become 0
+    constexpr int NQ = (GRP * D + 255) / 256;
     const int32_t *sel = sel_idx + ((size_t)b * hkv + g) * n_keep;
-    for (int e = tid; e < grp * n_keep; e += 256) {
-        const int h = e / n_keep, jj = sel[e % n_keep];
-        qm[h][jj] = q_prime[((size_t)b * hq + (size_t)g * grp + h) * D + jj];
+    const float *qrow = q_prime + ((size_t)b * hq + (size_t)g * grp) * D;
+    float qv[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int e = tid + 256 * k;
+        qv[k] = e < grp * D ? qrow[e] : 0.0f;
+    }
+    const int my_sel = tid < n_keep ? sel[tid] : -1;
+    if (tid < D) keep_s[tid] = 0;
+    __syncthreads();
+    if (my_sel >= 0) keep_s[my_sel & (D - 1)] = 1;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int e = tid + 256 * k;
+        if (e < grp * D) qm[e / D][e % D] = keep_s[e % D] ? qv[k] : 0.0f;
     }
     __syncthreads();
     // ---- logits of (token r, head h) pairs

@@ -341,3 +341,29 @@ def test_rope_validation():
     assert dec(one=False, si=None) == pa.DQK_ERR_NULL
     assert dec(one=False, qp=MIS) == pa.DQK_ERR_ALIGN
     assert pa.dqk_decode_rope_workspace_size(2, 32, 8, 0, 0) == 0
+
+
+def test_one_call_tiered_validation():
+    """dqk_select_decode_attn_tiered rejects bad arguments on the host before
+    anything is enqueued (no device is touched)."""
+    L = pa.lib()
+    c = _cache()
+
+    def one(t=None, **kw):
+        a = dict(q=A, tq=A, nk=77, B=4, hq=32, pt=A, mp=16, sl=A, ns=0, ws=A, wsb=1 << 30, out=A, qp=A, sel=A)
+        a.update(kw)
+        return L.dqk_select_decode_attn_tiered(ctypes.byref(c), ctypes.byref(t or _tiers()), a["q"], a["tq"],
+                                               a["nk"], a["B"], a["hq"], a["pt"], a["mp"], a["sl"], 0.088, a["ns"],
+                                               a["ws"], a["wsb"], a["out"], None, a["qp"], a["sel"], None)
+
+    assert one(t=_tiers(sink_k=None)) == pa.DQK_ERR_NULL
+    assert one(q=None) == pa.DQK_ERR_NULL
+    assert one(sel=None) == pa.DQK_ERR_NULL
+    assert one(hq=30) == pa.DQK_ERR_SHAPE
+    assert one(B=5) == pa.DQK_ERR_SHAPE                      # more sequences than the tiers hold
+    assert one(nk=0) == pa.DQK_ERR_SHAPE
+    assert one(hq=8 * 17) == pa.DQK_ERR_UNSUPPORTED          # more query heads per KV head than the decode serves
+    need = pa.dqk_decode_tiered_workspace_size(4, 32, 8, 16, 4)
+    assert one(ns=4, wsb=need - 4) == pa.DQK_ERR_WORKSPACE
+    assert one(qp=MIS) == pa.DQK_ERR_ALIGN
+    assert one(tq=MIS) == pa.DQK_ERR_ALIGN

@@ -211,3 +211,37 @@ def test_decode_tiered_sink_regime():
     rel = gu.row_rel_err(gu.host(out), ref)
     _say(f"  max row rel err {rel.max():.3e}")
     assert (rel <= gu.TOL).all()
+
+
+ONE_CALL_CASES = [
+    ("all-bf16", synth.Shape(3, 32, 8, [1, 63, 300], 77), 0),
+    ("page-edges", synth.Shape(4, 32, 8, [320, 447, 448, 449], 77, shuffle_pages=True), 0),
+    ("long-g4", synth.Shape(2, 32, 8, [5000, 1300], 77, shuffle_pages=True), 0),
+    ("long-g4-3splits", synth.Shape(2, 32, 8, [5000, 1300], 77, shuffle_pages=True), 3),
+    ("nk128", synth.Shape(1, 32, 8, [3000], 128), 0),
+    ("nk9", synth.Shape(1, 32, 8, [3000], 9), 0),
+    ("g2", synth.Shape(2, 16, 8, [2000, 700], 77), 0),
+]
+
+
+@pytest.mark.parametrize("name,shape,ns", ONE_CALL_CASES, ids=[c[0] for c in ONE_CALL_CASES])
+def test_one_call_tiered_equals_two_calls(name, shape, ns):
+    """dqk_select_decode_attn_tiered gives bit for bit dqk_select_channels +
+    dqk_decode_attn_tiered, and that selection is the oracle's."""
+    _say("tiered one call", name)
+    prob = synth.make_problem(shape, seed=74)
+    d, cache, tiers = _prefill(prob, shape)
+    out1, lse1, qp1, sel1 = pa.dqk_select_decode_attn_tiered(cache, tiers, d["q"], d["t_q"], shape.n_keep,
+                                                             d["page_table"], d["seq_lens"], prob.sm_scale,
+                                                             num_splits=ns)
+    qp2, sel2 = pa.dqk_select_channels(d["q"], d["t_q"], shape.hkv, shape.n_keep)
+    out2, lse2 = pa.dqk_decode_attn_tiered(cache, tiers, qp2, sel2, d["page_table"], d["seq_lens"], prob.sm_scale,
+                                           num_splits=ns)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gu.host(qp1).view(np.uint32), gu.host(qp2).view(np.uint32))
+    np.testing.assert_array_equal(gu.host(sel1), gu.host(sel2))
+    np.testing.assert_array_equal(gu.host(out1).view(np.uint32), gu.host(out2).view(np.uint32))
+    np.testing.assert_array_equal(gu.host(lse1).view(np.uint32), gu.host(lse2).view(np.uint32))
+    qp_ref, sel_ref = oracle.select_channels(prob.q, prob.t_q, shape.hkv, shape.n_keep)
+    np.testing.assert_array_equal(gu.host(qp1).view(np.uint32), qp_ref.view(np.uint32))
+    np.testing.assert_array_equal(gu.host(sel1), sel_ref)
